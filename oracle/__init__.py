@@ -1,0 +1,33 @@
+"""CPU oracle for the quantized linear layer -- TEST INFRASTRUCTURE ONLY.
+
+This package is the slow, plain, float64 reference that the HIP path is checked
+against. Only the test suite, the smoke check in ``__graft_entry__`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it. The product path
+(``dequant_matmul_gptq_amd``) never imports, calls or links anything here, and
+nothing here imports the product path: the two share no code.
+
+Every function follows the pages' description of the method:
+
+* GPTQ group-wise weights, one scale and one zero point per group of rows
+  (ExLlamaV2 artifact page, GPTQ paragraph; ExLlamaV2 README, "EXL2 quantization").
+* EXL2 mixed bit widths {2,3,4,5,6,8} per group, rows remapped by act-order
+  (ExLlamaV2 blog, "The Investigation", Finding 3; README, "EXL2 quantization").
+* Fused dequantize-and-multiply with float32 accumulation and a float16 output
+  (ExLlamaV2 blog, "How the Fused CUDA Kernel Works").
+"""
+
+from .qlinear_oracle import (  # noqa: F401
+    BITS_SUPPORTED,
+    GROUP_SIZES_SUPPORTED,
+    block_field_map,
+    group_word_offsets,
+    packed_rows,
+    pack,
+    unpack,
+    zero_points,
+    dequant,
+    dequant_fp16,
+    qlinear,
+    qlinear_gidx,
+    qlinear_bruteforce,
+)

@@ -1,0 +1,292 @@
+"""Float64 CPU oracle of the quantized linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module. It shares no code with the HIP path.
+
+What the layer computes (notation: K input features, N outputs, M tokens,
+gs rows per group, G = K / gs groups, b_g the bit width of group g):
+
+1. The weight matrix is stored in *stored row order*: stored row j holds the
+   weights of original input feature ``perm[j]`` (the act-order remapping of the
+   ExLlamaV2 README, "EXL2 quantization", and the ``q_invperm`` tensor of the
+   ExLlamaV2 blog, "How the EXL2 Quantization Pipeline Works", Step 3).
+2. Integer codes ``q[j][n]`` in ``[0, 2^b_g)`` are packed into uint32 words
+   (``q_weights``: packed variable-bit-width values, same Step 3). The 4-bit
+   nibble order -- row i of a word at bits 4*i..4*i+3, least significant first --
+   is the one the blog's kernel sketch unpacks ("How the Fused CUDA Kernel
+   Works"). The pages give no bit layout for 3-, 5- or 6-bit codes; the layout
+   used here is defined in :func:`block_field_map`.
+3. Dequantization is ``w = s * (q - z)`` with one float16 scale ``s`` and one
+   integer zero point ``z`` per (group, output column); a symmetric group uses
+   ``z = 2^(b-1)`` (the blog's sketch subtracts 8 from a 4-bit code and
+   multiplies by the scale; the GPTQ paragraph of the artifact page gives
+   per-group scaling).
+4. ``y[m][n] = sum_j x[m][perm[j]] * w[j][n]``: the fused matmul of the blog's
+   sketch, here computed exactly in float64 (no float16 rounding of w or y).
+
+Parity unpinned: nothing here. Every function is pinned by tests that do not
+re-use its formula (see ``tests/test_oracle_pins.py``).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+BITS_SUPPORTED = (2, 3, 4, 5, 6, 8)
+GROUP_SIZES_SUPPORTED = (32, 64, 128)
+BLOCK_ROWS = 32  # rows per packing block; a block of b-bit codes is exactly b words
+
+
+# --------------------------------------------------------------------------
+# Packed format
+# --------------------------------------------------------------------------
+
+def block_field_map(b: int) -> np.ndarray:
+    """Where each bit of each code of a 32-row block lives.
+
+    Returns an int array ``F`` of shape ``[32, b, 2]``: bit ``k`` (0 = least
+    significant) of the code of row ``r`` of the block is stored in word
+    ``F[r, k, 0]`` (0..b-1, relative to the block's first word) at bit
+    position ``F[r, k, 1]`` (0..31).
+
+    Layout ("half-word fields"). A block of 32 codes of b bits occupies b
+    words. Each word is seen as two 16-bit halves, h = 0 (bits 0..15) and
+    h = 1 (bits 16..31). With f = floor(16 / b) codes per half:
+
+    * Regular rows r < 2*f*b: word t = r // (2f); inside the word u = r % (2f),
+      half h = u // f, slot i = u % f; code bit k is at bit 16*h + b*i + k.
+      For b in {2, 4, 8} every row is regular and this is the plain
+      least-significant-first stream (4-bit: row i of a word at bits 4i..4i+3).
+    * b in {3, 5} (rows 30 and 31 are left over, f*b = 15 leaves bit 15 of each
+      half free): row 30 + h keeps its code bit k at word k, bit 16*h + 15.
+    * b = 6 (rows 24..31 are left over, bits 12..15 of each half are free):
+      row 24 + 4h + v (v = 0..3) keeps code bits 0..3 at word v, bits
+      16h + 12 .. 16h + 15, and code bits 4, 5 at word 4 + v // 2, bits
+      16h + 12 + 2*(v % 2) and the bit above it.
+
+    Every one of the 32*b bits of the block is used exactly once (a tested
+    property), so the map is a bijection between codes and block bits.
+    """
+    if b not in BITS_SUPPORTED:
+        raise ValueError(f"unsupported bit width {b}")
+    f = 16 // b
+    regular = 2 * f * b
+    F = np.zeros((BLOCK_ROWS, b, 2), dtype=np.int64)
+    for r in range(BLOCK_ROWS):
+        for k in range(b):
+            if r < regular:
+                t, u = divmod(r, 2 * f)
+                h, i = divmod(u, f)
+                F[r, k] = (t, 16 * h + b * i + k)
+            elif b in (3, 5):
+                h = r - 30
+                F[r, k] = (k, 16 * h + 15)
+            else:  # b == 6, rows 24..31
+                h, v = divmod(r - 24, 4)
+                if k < 4:
+                    F[r, k] = (v, 16 * h + 12 + k)
+                else:
+                    F[r, k] = (4 + v // 2, 16 * h + 12 + 2 * (v % 2) + (k - 4))
+    return F
+
+
+def _check_bits(bits: np.ndarray, K: int, gs: int) -> np.ndarray:
+    bits = np.asarray(bits, dtype=np.int64).reshape(-1)
+    if gs not in GROUP_SIZES_SUPPORTED:
+        raise ValueError(f"unsupported group size {gs}")
+    if K % gs != 0:
+        raise ValueError("K must be a multiple of the group size")
+    if bits.shape[0] != K // gs:
+        raise ValueError("bits must hold one entry per group")
+    for b in np.unique(bits):
+        if int(b) not in BITS_SUPPORTED:
+            raise ValueError(f"unsupported bit width {b}")
+    return bits
+
+
+def group_word_offsets(bits, gs: int) -> np.ndarray:
+    """Word-row offset of each group: goff[g] = sum over g' < g of gs*b_g'/32.
+
+    Group g occupies packed rows goff[g] .. goff[g+1]-1; its 32-row block c
+    (c = 0 .. gs/32-1) occupies rows goff[g] + c*b_g .. goff[g] + (c+1)*b_g - 1.
+    """
+    bits = np.asarray(bits, dtype=np.int64).reshape(-1)
+    goff = np.zeros(bits.shape[0] + 1, dtype=np.int64)
+    goff[1:] = np.cumsum(bits * (gs // BLOCK_ROWS))
+    return goff
+
+
+def packed_rows(bits, gs: int) -> int:
+    """Total number of packed word rows R; the packed matrix is uint32 [R][N]."""
+    return int(group_word_offsets(bits, gs)[-1])
+
+
+def pack(q: np.ndarray, bits, gs: int) -> np.ndarray:
+    """Pack codes ``q`` (uint8 [K][N], stored row order) into uint32 [R][N].
+
+    Column n of packed row (goff[g] + c*b + t) holds word t of 32-row block c of
+    group g for output column n, laid out by :func:`block_field_map`. Output
+    columns are the fastest-varying index, as the blog's kernel sketch indexes
+    scales by group then output ("How the Fused CUDA Kernel Works").
+    """
+    q = np.asarray(q)
+    K, N = q.shape
+    bits = _check_bits(bits, K, gs)
+    for b in np.unique(bits):
+        rows = np.repeat(bits == b, gs)
+        if rows.any() and int(q[rows].max(initial=0)) >= (1 << int(b)):
+            raise ValueError(f"code out of range for {b}-bit group")
+    goff = group_word_offsets(bits, gs)
+    out = np.zeros((int(goff[-1]), N), dtype=np.uint32)
+    nblk = gs // BLOCK_ROWS
+    for g in range(bits.shape[0]):
+        b = int(bits[g])
+        F = block_field_map(b)
+        for c in range(nblk):
+            blk = q[g * gs + c * BLOCK_ROWS: g * gs + (c + 1) * BLOCK_ROWS].astype(np.uint32)
+            words = np.zeros((b, N), dtype=np.uint32)
+            for r in range(BLOCK_ROWS):
+                for k in range(b):
+                    t, pos = F[r, k]
+                    words[t] |= ((blk[r] >> np.uint32(k)) & np.uint32(1)) << np.uint32(pos)
+            base = int(goff[g]) + c * b
+            out[base: base + b] = words
+    return out
+
+
+def unpack(packed: np.ndarray, bits, gs: int, K: int) -> np.ndarray:
+    """Inverse of :func:`pack`: uint32 [R][N] -> uint8 codes [K][N]."""
+    packed = np.asarray(packed, dtype=np.uint32)
+    bits = _check_bits(bits, K, gs)
+    goff = group_word_offsets(bits, gs)
+    if packed.shape[0] != int(goff[-1]):
+        raise ValueError("packed row count does not match the bit map")
+    N = packed.shape[1]
+    q = np.zeros((K, N), dtype=np.uint8)
+    nblk = gs // BLOCK_ROWS
+    for g in range(bits.shape[0]):
+        b = int(bits[g])
+        F = block_field_map(b)
+        for c in range(nblk):
+            base = int(goff[g]) + c * b
+            for r in range(BLOCK_ROWS):
+                code = np.zeros(N, dtype=np.uint32)
+                for k in range(b):
+                    t, pos = F[r, k]
+                    code |= ((packed[base + t] >> np.uint32(pos)) & np.uint32(1)) << np.uint32(k)
+                q[g * gs + c * BLOCK_ROWS + r] = code.astype(np.uint8)
+    return q
+
+
+# --------------------------------------------------------------------------
+# Dequantization and the layer
+# --------------------------------------------------------------------------
+
+def zero_points(zeros, bits, N: int) -> np.ndarray:
+    """Per-(group, column) zero point as float64 [G][N].
+
+    ``zeros`` is an integer array [G][N], or None for symmetric groups, whose
+    zero point is the midpoint 2^(b-1) of the code range (8 for 4-bit codes,
+    as in the blog's kernel sketch).
+    """
+    bits = np.asarray(bits, dtype=np.int64).reshape(-1)
+    if zeros is None:
+        return np.repeat((2.0 ** (bits - 1))[:, None], N, axis=1)
+    z = np.asarray(zeros, dtype=np.float64)
+    if z.shape != (bits.shape[0], N):
+        raise ValueError("zeros must be [G][N]")
+    return z
+
+
+def dequant(q, scales, zeros, bits, gs: int) -> np.ndarray:
+    """Dequantized weights w[j][n] = s[g][n] * (q[j][n] - z[g][n]), g = j // gs, in float64.
+
+    Exact: s has 11 significant bits and |q - z| <= 255, so the product needs
+    at most 19 bits and float64 holds it without rounding.
+    """
+    q = np.asarray(q)
+    K, N = q.shape
+    bits = _check_bits(bits, K, gs)
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    if s.shape != (bits.shape[0], N):
+        raise ValueError("scales must be [G][N]")
+    z = zero_points(zeros, bits, N)
+    s_rows = np.repeat(s, gs, axis=0)
+    z_rows = np.repeat(z, gs, axis=0)
+    return s_rows * (q.astype(np.float64) - z_rows)
+
+
+def dequant_fp16(q, scales, zeros, bits, gs: int) -> np.ndarray:
+    """The dequantized weights rounded once to float16 (round to nearest even).
+
+    numpy converts float64 to float16 with a single correctly rounded step.
+    """
+    return dequant(q, scales, zeros, bits, gs).astype(np.float16)
+
+
+def _perm_or_identity(perm, K: int) -> np.ndarray:
+    if perm is None:
+        return np.arange(K, dtype=np.int64)
+    p = np.asarray(perm, dtype=np.int64).reshape(-1)
+    if p.shape[0] != K or not np.array_equal(np.sort(p), np.arange(K)):
+        raise ValueError("perm must be a permutation of 0..K-1")
+    return p
+
+
+def qlinear(x, q, scales, zeros, bits, gs: int, perm=None) -> np.ndarray:
+    """y = x[:, perm] @ w in float64, with w unrounded (the layer's exact value).
+
+    ``x`` is [M][K] in original feature order (float16 values); ``q`` is in
+    stored row order; ``perm[j]`` is the original feature held by stored row j.
+    """
+    x = np.asarray(x, dtype=np.float16).astype(np.float64)
+    q = np.asarray(q)
+    K = q.shape[0]
+    if x.ndim != 2 or x.shape[1] != K:
+        raise ValueError("x must be [M][K]")
+    p = _perm_or_identity(perm, K)
+    w = dequant(q, scales, zeros, bits, gs)
+    return x[:, p] @ w
+
+
+def qlinear_gidx(x, q, scales, zeros, bits, gs: int, perm=None) -> np.ndarray:
+    """Second path: scatter the weights back to original feature order.
+
+    The GPTQ view of act-order: original feature k belongs to group
+    g_idx[k] = invperm[k] // gs, with invperm the inverse permutation. Build
+    W_orig[k][n] = s[g_idx[k]][n] * (q[invperm[k]][n] - z[g_idx[k]][n]) and
+    return x @ W_orig. Equal to :func:`qlinear` up to float64 summation order.
+    """
+    x = np.asarray(x, dtype=np.float16).astype(np.float64)
+    q = np.asarray(q)
+    K, N = q.shape
+    bits = _check_bits(bits, K, gs)
+    p = _perm_or_identity(perm, K)
+    invperm = np.empty(K, dtype=np.int64)
+    invperm[p] = np.arange(K)
+    g_idx = invperm // gs
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    z = zero_points(zeros, bits, N)
+    w_orig = s[g_idx] * (q[invperm].astype(np.float64) - z[g_idx])
+    return x @ w_orig
+
+
+def qlinear_bruteforce(x, q, scales, zeros, bits, gs: int, perm=None) -> np.ndarray:
+    """Pure-Python triple loop of the same definition (tiny inputs only)."""
+    x = np.asarray(x, dtype=np.float16)
+    q = np.asarray(q)
+    K, N = q.shape
+    M = x.shape[0]
+    bits = [int(b) for b in np.asarray(bits).reshape(-1)]
+    p = list(range(K)) if perm is None else [int(v) for v in np.asarray(perm).reshape(-1)]
+    s = np.asarray(scales, dtype=np.float16)
+    y = [[0.0] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for j in range(K):
+                g = j // gs
+                zz = float(2 ** (bits[g] - 1)) if zeros is None else float(zeros[g][n])
+                acc += float(x[m][p[j]]) * (float(s[g][n]) * (float(q[j][n]) - zz))
+            y[m][n] = acc
+    return np.array(y, dtype=np.float64)

@@ -1,0 +1,324 @@
+"""Throughput of the quantized linear layer on one MI355X.
+
+Primary line (value): qgemv weight GB/s at M = 1 on a Llama-2-7B-shaped decode
+step, GPTQ 4-bit, group size 128, act-order. One step = one token through the
+linear layers of 32 decoder layers; each layer has q, k, v, o (4096 -> 4096),
+gate, up (4096 -> 11008) and down (11008 -> 4096). All 224 packed matrices are
+distinct buffers resident in HBM (3.36 GB), so the 256 MB Infinity Cache cannot
+serve repeated weights. The step is captured in a HIP graph and replayed.
+
+Secondary (qgemm): dequant-GEMM TFLOP/s at M = 2048 on the Llama-2-13B MLP
+shape 5120 -> 13824, GPTQ 4-bit, group size 128, act-order.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, decimal GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix throughput
+METRIC = "qgemv weight GB/s (% of HBM peak) at M=1; dequant-GEMM TFLOP/s at M=2048"
+N_LAYERS = 32
+LAYER_MIX = ((0, 4), (1, 2), (2, 1))   # (index into the 7B decode shapes, matrices per layer)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--gemm-iters", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Launch:
+    """Pre-marshalled arguments of one qlinear_qgemv / qlinear_qgemm call."""
+
+    def __init__(self, fn, layout, x, M, qweight, scales, zeros, perm, y, ws, stream):
+        self.fn = fn
+        self.layout = layout  # keeps the ctypes struct alive
+        self.args = (layout.ref, x.data_ptr(), M, qweight.data_ptr(), scales.data_ptr(),
+                     None if zeros is None else zeros.data_ptr(), None if perm is None else perm.data_ptr(),
+                     y.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"launch failed with status {st}")
+
+
+def setup_decode(torch, dq, wl, dev):
+    """Pack the three 7B decode shapes once, then clone them into 32 layers."""
+    shapes = []
+    for spec in wl.LLAMA7B_DECODE:
+        inp = wl.generate(spec, M=1)
+        L = dq.Layout(spec.K, spec.N, spec.group_size, inp.bits)
+        qw = dq.pack_weights(L, torch.from_numpy(inp.q).to(dev))
+        sc = torch.from_numpy(inp.scales).to(dev)
+        zr = torch.from_numpy(inp.zeros).to(dev)
+        pm = torch.from_numpy(inp.perm).to(dev)
+        shapes.append(dict(spec=spec, inp=inp, L=L, qw=qw, sc=sc, zr=zr, pm=pm))
+    torch.cuda.synchronize()
+    mats = []
+    for _ in range(N_LAYERS):
+        for si, count in LAYER_MIX:
+            s = shapes[si]
+            for _ in range(count):
+                mats.append(dict(shape=si, qw=s["qw"].clone(), sc=s["sc"].clone(), zr=s["zr"].clone(),
+                                 pm=s["pm"].clone()))
+    torch.cuda.synchronize()
+    return shapes, mats
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the layer's sharding across GPUs is described in DESIGN.md, not implemented).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dequant_matmul_gptq_amd as dq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = dq.lib()
+    # All work runs on one side stream (default priority): graph capture
+    # cannot use the legacy default stream.
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
+    sh = stream.cuda_stream
+
+    # ---------------------------------------------------------------- decode setup
+    t0 = time.time()
+    shapes, mats = setup_decode(torch, dq, wl, dev)
+    wbytes = [wl.weight_bytes(s["spec"]) for s in shapes]
+    step_bytes = sum(wbytes[m["shape"]] for m in mats)
+    ws = dq.qgemv_workspace(shapes[1]["L"], dev)  # N = 11008 covers every shape in the step
+    xs = [torch.from_numpy(s["inp"].x[:1].copy()).to(dev) for s in shapes]
+    ys = [torch.empty((1, s["spec"].N), dtype=torch.float16, device=dev) for s in shapes]
+    launches = [Launch(lib.qlinear_qgemv, shapes[m["shape"]]["L"], xs[m["shape"]], 1, m["qw"], m["sc"], m["zr"],
+                       m["pm"], ys[m["shape"]], ws, sh) for m in mats]
+    log(f"decode setup {time.time() - t0:.1f}s: {len(mats)} matrices, {step_bytes / 1e9:.3f} GB per step")
+
+    def step():
+        for ln in launches:
+            ln()
+
+    # correctness at timing time: one launch per shape against the oracle
+    import oracle
+    for si, s in enumerate(shapes):
+        y = dq.qgemv(s["L"], xs[si], s["qw"], s["sc"], s["zr"], s["pm"], ws)
+        inp = s["inp"]
+        ref = oracle.qlinear(inp.x[:1], inp.q, inp.scales, inp.zeros, inp.bits, s["spec"].group_size, inp.perm)
+        d = y.float().cpu().numpy() - ref
+        rel = float(np.linalg.norm(d) / np.linalg.norm(ref))
+        if rel > 1e-3:
+            raise RuntimeError(f"qgemv disagrees with the oracle on {s['spec'].name}: rel_fro={rel:.2e}")
+    log("decode outputs match the oracle")
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+    run = graph.replay if graph is not None else step
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"decode step {ms_step * 1e3:.1f} us -> {value:.0f} GB/s ({value / HBM_PEAK_GBS:.1%} of HBM peak)")
+
+    # per-launch durations with HIP events on the launch stream (eager)
+    n_ev = len(launches)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    dur = {0: [], 1: [], 2: []}
+    reps = max(1, min(args.steps, 10))
+    for _ in range(reps):
+        for ln, (a, b) in zip(launches, evs):
+            a.record(stream)
+            ln()
+            b.record(stream)
+        torch.cuda.synchronize()
+        for m, (a, b) in zip(mats, evs):
+            dur[m["shape"]].append(a.elapsed_time(b) * 1e3)
+    per_shape = []
+    tot_bytes, tot_us = 0, 0.0
+    for si, s in enumerate(shapes):
+        us = float(np.mean(dur[si]))
+        gbs = wbytes[si] / (us * 1e-6) / 1e9
+        per_shape.append(dict(shape=f"{s['spec'].K}x{s['spec'].N}", weight_bytes=wbytes[si], avg_us=round(us, 3),
+                              gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4)))
+        tot_bytes += wbytes[si] * len(dur[si])
+        tot_us += float(np.sum(dur[si]))
+    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
+    n_launch = sum(len(v) for v in dur.values())
+    log(f"qgemv per launch: avg {tot_us / n_launch:.2f} us, {achieved:.0f} GB/s; " +
+        ", ".join(f"{p['shape']}: {p['avg_us']} us {p['gbs']} GB/s" for p in per_shape))
+
+    # ---------------------------------------------------------------- prefill
+    spec = wl.PREFILL_13B
+    inp = wl.generate(spec)
+    L = dq.Layout(spec.K, spec.N, spec.group_size, inp.bits)
+    qw = dq.pack_weights(L, torch.from_numpy(inp.q).to(dev))
+    sc = torch.from_numpy(inp.scales).to(dev)
+    zr = torch.from_numpy(inp.zeros).to(dev)
+    pm = torch.from_numpy(inp.perm).to(dev)
+    x = torch.from_numpy(inp.x).to(dev)
+    M = x.shape[0]
+    y = torch.empty((M, spec.N), dtype=torch.float16, device=dev)
+    gws = torch.empty(dq.qgemm_workspace_bytes(L, M), dtype=torch.uint8, device=dev)
+    gl = Launch(lib.qlinear_qgemm, L, x, M, qw, sc, zr, pm, y, gws, sh)
+    rows = np.arange(0, M, 64)
+    gl()
+    torch.cuda.synchronize()
+    ref = oracle.qlinear(inp.x[rows], inp.q, inp.scales, inp.zeros, inp.bits, spec.group_size, inp.perm)
+    d = y[torch.from_numpy(rows).to(dev)].float().cpu().numpy() - ref
+    rel = float(np.linalg.norm(d) / np.linalg.norm(ref))
+    if rel > 1e-3:
+        raise RuntimeError(f"qgemm disagrees with the oracle: rel_fro={rel:.2e}")
+    for _ in range(3):
+        gl()
+    flops = 2.0 * M * spec.K * spec.N
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    for _ in range(args.gemm_iters):
+        gl()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = g0.elapsed_time(g1) / args.gemm_iters
+    tflops = flops / (gemm_ms * 1e-3) / 1e12
+    log(f"qgemm M={M}: {gemm_ms * 1e3:.1f} us per call -> {tflops:.1f} TFLOP/s "
+        f"({tflops / MFMA_F16_PEAK_TFLOPS:.1%} of fp16 MFMA peak), rel_fro={rel:.1e}")
+
+    # ---------------------------------------------------------------- oracle on the host
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(shapes[1]["inp"], wbytes[1])
+        log(f"oracle on host: {cpu['value']} GB/s with {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-2-7B-shaped decode, GPTQ 4-bit g128 act-order, M=1: 32 layers x "
+                        "(4 x 4096->4096, 2 x 4096->11008, 1 x 11008->4096), weights resident in HBM",
+            "M": 1,
+            "matrices_per_step": len(mats),
+            "weight_bytes_per_step": step_bytes,
+            "hbm_peak_gbs": HBM_PEAK_GBS,
+            "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+            "launch": "hip_graph" if graph is not None else "eager",
+            "accumulate": "fp32",
+        },
+        "roofline": {
+            "kernel": "qgemv_kernel<1>",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(tot_us / n_launch, 3),
+            "per_shape": per_shape,
+        },
+        "cpu_baseline": cpu,
+        "qgemm": {
+            "workload": "Llama-2-13B MLP prefill 5120->13824, GPTQ 4-bit g128 act-order, M=2048",
+            "value": round(tflops, 2),
+            "unit": "TFLOP/s",
+            "ms_per_call": round(gemm_ms, 5),
+            "roofline": {
+                "bound": "mfma",
+                "achieved": round(tflops, 2),
+                "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": None,
+            },
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(inp, wbytes):
+    """The float64 oracle timed on the host on one 4096 -> 11008 layer at M = 1
+    (dequantize, gather, matmul), repeated for about 10 s."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                           or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        blas_threads = 1
+    sp = inp.spec
+    x = inp.x[:1]
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.qlinear(x, inp.q, inp.scales, inp.zeros, inp.bits, sp.group_size, inp.perm)
+        n += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or n >= 50:
+            break
+    gbs = wbytes * n / el / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "cores": blas_threads,
+        "kind": "oracle",
+        "sample": f"{n} x oracle.qlinear on the {sp.K}x{sp.N} GPTQ-4bit layer at M=1 "
+                  f"({el:.1f} s; float64 dequantize + gather + BLAS matmul; elementwise steps single-threaded, "
+                  f"matmul on {blas_threads} BLAS threads; host has {os.cpu_count()} logical CPUs)",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,26 @@
+"""MI355X (gfx950) quantized linear layer: GPTQ 4-bit and EXL2 mixed-bit codes
+unpacked, scaled and fused into the matmul against float16 activations.
+
+The compute lives in libqlinear.so (hand-written HIP, C ABI in
+include/qlinear.h); this package is its thin Python binding. PyTorch provides
+device memory and streams only.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    GEMV_MAX_M,
+    LIB_PATH,
+    MAX_RUNS,
+    Layout,
+    QlinearError,
+    dequant,
+    lib,
+    pack_weights,
+    qgemm,
+    qgemm_workspace_bytes,
+    qgemv,
+    qgemv_workspace,
+    qgemv_workspace_bytes,
+    status_string,
+    unpack,
+)

@@ -1,0 +1,224 @@
+"""ctypes binding of libqlinear.so (argument marshalling only).
+
+Every function here checks tensor devices and shapes, passes raw pointers and
+the current HIP stream to the C entry point of the same name, and raises
+QlinearError on a non-zero status. All computation happens in the library's
+gfx950 kernels; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqlinear.so")
+
+MAX_RUNS = 64
+GEMV_MAX_M = 16
+
+OK = 0
+ERR_INVALID_ARGUMENT = 1
+ERR_UNSUPPORTED = 2
+ERR_MISALIGNED = 3
+ERR_WORKSPACE = 4
+ERR_HIP = 5
+
+EXPORTS = (
+    "qlinear_status_string",
+    "qlinear_layout_init",
+    "qlinear_pack_weights",
+    "qlinear_unpack",
+    "qlinear_dequant",
+    "qlinear_qgemv_workspace_bytes",
+    "qlinear_qgemv",
+    "qlinear_qgemm_workspace_bytes",
+    "qlinear_qgemm",
+)
+
+
+class QlinearError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class qlinear_layout(ctypes.Structure):
+    _fields_ = [
+        ("K", ctypes.c_int32),
+        ("N", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("groups", ctypes.c_int32),
+        ("packed_rows", ctypes.c_int32),
+        ("nruns", ctypes.c_int32),
+        ("run_group", ctypes.c_int32 * (MAX_RUNS + 1)),
+        ("run_row", ctypes.c_int32 * (MAX_RUNS + 1)),
+        ("run_bits", ctypes.c_int32 * MAX_RUNS),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqlinear.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m dequant_matmul_gptq_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        lp = ctypes.POINTER(qlinear_layout)
+        L.qlinear_status_string.restype = ctypes.c_char_p
+        L.qlinear_status_string.argtypes = [ctypes.c_int]
+        L.qlinear_layout_init.argtypes = [lp, i32, i32, i32, vp]
+        L.qlinear_pack_weights.argtypes = [lp, vp, vp, vp]
+        L.qlinear_unpack.argtypes = [lp, vp, vp, vp]
+        L.qlinear_dequant.argtypes = [lp, vp, vp, vp, vp, vp]
+        L.qlinear_qgemv_workspace_bytes.argtypes = [lp, ctypes.POINTER(sz)]
+        L.qlinear_qgemv.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.qlinear_qgemm_workspace_bytes.argtypes = [lp, i32, ctypes.POINTER(sz)]
+        L.qlinear_qgemm.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name in EXPORTS[1:]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qlinear_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise QlinearError(status, what)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple | None = None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+class Layout:
+    """Host description of a packed K x N matrix (wraps qlinear_layout_init)."""
+
+    def __init__(self, K: int, N: int, group_size: int, bits):
+        b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint8).reshape(-1))
+        self.bits = b
+        self.c = qlinear_layout()
+        _check(lib().qlinear_layout_init(ctypes.byref(self.c), int(K), int(N), int(group_size),
+                                         b.ctypes.data_as(ctypes.c_void_p)), "qlinear_layout_init")
+        self.K, self.N, self.group_size = int(K), int(N), int(group_size)
+        self.groups = int(self.c.groups)
+        self.packed_rows = int(self.c.packed_rows)
+        self.nruns = int(self.c.nruns)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def pack_weights(layout: Layout, q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """q uint8 [K][N] (stored order) -> packed int32 [packed_rows][N] (uint32 bit patterns)."""
+    _dev(q, "q", torch.uint8, (layout.K, layout.N))
+    if out is None:
+        out = torch.empty((layout.packed_rows, layout.N), dtype=torch.int32, device=q.device)
+    _dev(out, "qweight", torch.int32, (layout.packed_rows, layout.N))
+    _check(lib().qlinear_pack_weights(layout.ref, _ptr(q), _ptr(out), _stream(q.device)), "qlinear_pack_weights")
+    return out
+
+
+def unpack(layout: Layout, qweight: torch.Tensor) -> torch.Tensor:
+    _dev(qweight, "qweight", torch.int32, (layout.packed_rows, layout.N))
+    q = torch.empty((layout.K, layout.N), dtype=torch.uint8, device=qweight.device)
+    _check(lib().qlinear_unpack(layout.ref, _ptr(qweight), _ptr(q), _stream(q.device)), "qlinear_unpack")
+    return q
+
+
+def dequant(layout: Layout, qweight: torch.Tensor, scales: torch.Tensor,
+            zeros: torch.Tensor | None) -> torch.Tensor:
+    _dev(qweight, "qweight", torch.int32, (layout.packed_rows, layout.N))
+    _dev(scales, "scales", torch.float16, (layout.groups, layout.N))
+    if zeros is not None:
+        _dev(zeros, "zeros", torch.uint8, (layout.groups, layout.N))
+    w = torch.empty((layout.K, layout.N), dtype=torch.float16, device=qweight.device)
+    _check(lib().qlinear_dequant(layout.ref, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(w),
+                                 _stream(w.device)), "qlinear_dequant")
+    return w
+
+
+def qgemv_workspace_bytes(layout: Layout) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().qlinear_qgemv_workspace_bytes(layout.ref, ctypes.byref(n)), "qlinear_qgemv_workspace_bytes")
+    return int(n.value)
+
+
+def qgemv_workspace(layout: Layout, device) -> torch.Tensor:
+    """A zero-filled qgemv workspace (it stays zero-filled between calls)."""
+    return torch.zeros(qgemv_workspace_bytes(layout), dtype=torch.uint8, device=device)
+
+
+def qgemm_workspace_bytes(layout: Layout, M: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().qlinear_qgemm_workspace_bytes(layout.ref, int(M), ctypes.byref(n)), "qlinear_qgemm_workspace_bytes")
+    return int(n.value)
+
+
+def _gemm_operands(layout, x, qweight, scales, zeros, perm, y):
+    if x.dim() != 2 or x.shape[1] != layout.K:
+        raise ValueError(f"x must be [M][{layout.K}]")
+    M = int(x.shape[0])
+    _dev(x, "x", torch.float16)
+    _dev(qweight, "qweight", torch.int32, (layout.packed_rows, layout.N))
+    _dev(scales, "scales", torch.float16, (layout.groups, layout.N))
+    if zeros is not None:
+        _dev(zeros, "zeros", torch.uint8, (layout.groups, layout.N))
+    if perm is not None:
+        _dev(perm, "perm", torch.int32, (layout.K,))
+    if y is None:
+        y = torch.empty((M, layout.N), dtype=torch.float16, device=x.device)
+    _dev(y, "y", torch.float16, (M, layout.N))
+    return M, y
+
+
+def qgemv(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
+          zeros: torch.Tensor | None, perm: torch.Tensor | None, workspace: torch.Tensor,
+          y: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode layer, M = x.shape[0] <= 16. Returns y float16 [M][N]."""
+    M, y = _gemm_operands(layout, x, qweight, scales, zeros, perm, y)
+    _dev(workspace, "workspace", torch.uint8)
+    _check(lib().qlinear_qgemv(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
+                               _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemv")
+    return y
+
+
+def qgemm(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
+          zeros: torch.Tensor | None, perm: torch.Tensor | None, workspace: torch.Tensor | None = None,
+          y: torch.Tensor | None = None) -> torch.Tensor:
+    """Prefill layer, any M. Returns y float16 [M][N]."""
+    M, y = _gemm_operands(layout, x, qweight, scales, zeros, perm, y)
+    need = qgemm_workspace_bytes(layout, M)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    _check(lib().qlinear_qgemm(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
+                               _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemm")
+    return y

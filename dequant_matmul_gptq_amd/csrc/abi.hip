@@ -1,0 +1,192 @@
+// extern "C" entry points of libqlinear: host-side validation, then launches
+// on the caller's stream. Nothing here allocates memory or synchronizes.
+#include <stdint.h>
+#include <string.h>
+
+#include "qlinear_kernels.hpp"
+
+namespace qlinear {
+
+Runs make_runs(const qlinear_layout& L) {
+  Runs r;
+  memset(&r, 0, sizeof(r));
+  const int bpg = L.group_size / kBlockRows;
+  r.nruns = L.nruns;
+  r.blocks_per_group = bpg;
+  for (int i = 0; i <= L.nruns; ++i) {
+    r.run_block[i] = L.run_group[i] * bpg;
+    r.run_row[i] = L.run_row[i];
+  }
+  for (int i = 0; i < L.nruns; ++i) r.run_bits[i] = L.run_bits[i];
+  return r;
+}
+
+}  // namespace qlinear
+
+namespace {
+
+using namespace qlinear;
+
+// Largest K accepted: the block count is a grid dimension (< 65536).
+constexpr int64_t kMaxK = (int64_t)65535 * kBlockRows;
+// Largest M of qlinear_qgemm: row tiles of 128 in one grid dimension.
+constexpr int64_t kMaxGemmM = (int64_t)65535 * 128;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported_bits(int b) { return b == 2 || b == 3 || b == 4 || b == 5 || b == 6 || b == 8; }
+
+// Structural check of a layout that the caller may have modified.
+int check_layout(const qlinear_layout* L) {
+  if (!L) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (L->K <= 0 || L->N <= 0) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (L->group_size != 32 && L->group_size != 64 && L->group_size != 128) return QLINEAR_ERR_UNSUPPORTED;
+  if (L->K % L->group_size != 0 || L->N % 8 != 0 || L->K > kMaxK) return QLINEAR_ERR_UNSUPPORTED;
+  if (L->groups != L->K / L->group_size) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (L->nruns < 1 || L->nruns > QLINEAR_MAX_RUNS) return QLINEAR_ERR_UNSUPPORTED;
+  if (L->run_group[0] != 0 || L->run_row[0] != 0 || L->run_group[L->nruns] != L->groups)
+    return QLINEAR_ERR_INVALID_ARGUMENT;
+  const int bpg = L->group_size / kBlockRows;
+  for (int r = 0; r < L->nruns; ++r) {
+    if (!supported_bits(L->run_bits[r])) return QLINEAR_ERR_UNSUPPORTED;
+    const int ng = L->run_group[r + 1] - L->run_group[r];
+    if (ng <= 0) return QLINEAR_ERR_INVALID_ARGUMENT;
+    if (L->run_row[r + 1] - L->run_row[r] != ng * bpg * L->run_bits[r]) return QLINEAR_ERR_INVALID_ARGUMENT;
+  }
+  if (L->run_row[L->nruns] != L->packed_rows) return QLINEAR_ERR_INVALID_ARGUMENT;
+  return QLINEAR_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QLINEAR_OK : QLINEAR_ERR_HIP; }
+
+int check_gemm_operands(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                        const uint16_t* scales, const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                        void* workspace) {
+  int st = check_layout(layout);
+  if (st != QLINEAR_OK) return st;
+  if (M < 0) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (M == 0) return QLINEAR_OK;  // quick return: no operand is touched (empty tensors may be NULL)
+  if (!x || !qweight || !scales || !y) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (!workspace) return QLINEAR_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y) || !aligned16(workspace) ||
+      (zeros && !aligned16(zeros)) || (perm && !aligned16(perm)))
+    return QLINEAR_ERR_MISALIGNED;
+  return QLINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlinear_status_string(int status) {
+  switch (status) {
+    case QLINEAR_OK: return "ok";
+    case QLINEAR_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case QLINEAR_ERR_UNSUPPORTED: return "unsupported shape, group size, bit width or run count";
+    case QLINEAR_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case QLINEAR_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLINEAR_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int qlinear_layout_init(qlinear_layout* layout, int32_t K, int32_t N, int32_t group_size,
+                        const uint8_t* bits_host) {
+  if (!layout || !bits_host) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (K <= 0 || N <= 0) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (group_size != 32 && group_size != 64 && group_size != 128) return QLINEAR_ERR_UNSUPPORTED;
+  if (K % group_size != 0 || N % 8 != 0 || K > kMaxK) return QLINEAR_ERR_UNSUPPORTED;
+  qlinear_layout L;
+  memset(&L, 0, sizeof(L));
+  L.K = K;
+  L.N = N;
+  L.group_size = group_size;
+  L.groups = K / group_size;
+  const int bpg = group_size / kBlockRows;
+  int nruns = 0;
+  int64_t row = 0;
+  for (int g = 0; g < L.groups; ++g) {
+    const int b = bits_host[g];
+    if (!supported_bits(b)) return QLINEAR_ERR_UNSUPPORTED;
+    if (nruns == 0 || L.run_bits[nruns - 1] != b) {
+      if (nruns == QLINEAR_MAX_RUNS) return QLINEAR_ERR_UNSUPPORTED;
+      L.run_group[nruns] = g;
+      L.run_row[nruns] = (int32_t)row;
+      L.run_bits[nruns] = b;
+      ++nruns;
+    }
+    row += (int64_t)bpg * b;
+  }
+  L.nruns = nruns;
+  L.run_group[nruns] = L.groups;
+  L.run_row[nruns] = (int32_t)row;
+  L.packed_rows = (int32_t)row;
+  *layout = L;
+  return QLINEAR_OK;
+}
+
+int qlinear_pack_weights(const qlinear_layout* layout, const uint8_t* q, uint32_t* qweight, void* stream) {
+  int st = check_layout(layout);
+  if (st != QLINEAR_OK) return st;
+  if (!q || !qweight) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(qweight)) return QLINEAR_ERR_MISALIGNED;
+  return hip_status(launch_pack(*layout, make_runs(*layout), q, qweight, (hipStream_t)stream));
+}
+
+int qlinear_unpack(const qlinear_layout* layout, const uint32_t* qweight, uint8_t* q, void* stream) {
+  int st = check_layout(layout);
+  if (st != QLINEAR_OK) return st;
+  if (!q || !qweight) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(qweight)) return QLINEAR_ERR_MISALIGNED;
+  return hip_status(launch_unpack(*layout, make_runs(*layout), qweight, q, (hipStream_t)stream));
+}
+
+int qlinear_dequant(const qlinear_layout* layout, const uint32_t* qweight, const uint16_t* scales,
+                    const uint8_t* zeros, uint16_t* w, void* stream) {
+  int st = check_layout(layout);
+  if (st != QLINEAR_OK) return st;
+  if (!qweight || !scales || !w) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(qweight) || !aligned16(scales) || !aligned16(w) || (zeros && !aligned16(zeros)))
+    return QLINEAR_ERR_MISALIGNED;
+  return hip_status(launch_dequant(*layout, make_runs(*layout), qweight, scales, zeros, w, (hipStream_t)stream));
+}
+
+int qlinear_qgemv_workspace_bytes(const qlinear_layout* layout, size_t* bytes) {
+  int st = check_layout(layout);
+  if (st != QLINEAR_OK) return st;
+  if (!bytes) return QLINEAR_ERR_INVALID_ARGUMENT;
+  *bytes = qgemv_workspace_bytes(layout->N);
+  return QLINEAR_OK;
+}
+
+int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                  const uint16_t* scales, const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gemm_operands(layout, x, M, qweight, scales, zeros, perm, y, workspace);
+  if (st != QLINEAR_OK || M == 0) return st;
+  if (M > QLINEAR_GEMV_MAX_M) return QLINEAR_ERR_UNSUPPORTED;
+  if (workspace_bytes < qgemv_workspace_bytes(layout->N)) return QLINEAR_ERR_WORKSPACE;
+  return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, qweight, scales, zeros, perm, y, workspace,
+                                 (hipStream_t)stream));
+}
+
+int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes) {
+  int st = check_layout(layout);
+  if (st != QLINEAR_OK) return st;
+  if (!bytes || M < 0) return QLINEAR_ERR_INVALID_ARGUMENT;
+  *bytes = qgemm_workspace_bytes(M, layout->K);
+  return QLINEAR_OK;
+}
+
+int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                  const uint16_t* scales, const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gemm_operands(layout, x, M, qweight, scales, zeros, perm, y, workspace);
+  if (st != QLINEAR_OK || M == 0) return st;
+  if (M > kMaxGemmM) return QLINEAR_ERR_UNSUPPORTED;
+  if (workspace_bytes < qgemm_workspace_bytes(M, layout->K)) return QLINEAR_ERR_WORKSPACE;
+  return hip_status(launch_qgemm(*layout, make_runs(*layout), x, M, qweight, scales, zeros, perm, y, workspace,
+                                 (hipStream_t)stream));
+}
+
+}  // extern "C"

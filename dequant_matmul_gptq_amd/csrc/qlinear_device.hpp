@@ -1,0 +1,150 @@
+// Device-side building blocks shared by the gfx950 kernels of the quantized
+// linear layer: the run table passed as a kernel argument, the packed-format
+// field placement, and the unpack of two codes at a time into a float16 pair.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include <utility>
+
+#include "qlinear.h"
+
+namespace qlinear {
+
+constexpr int kBlockRows = 32;          // rows per packing block (b words per block and column)
+constexpr int kPairsPerBlock = 16;      // a block unpacks into 16 float16 pairs
+constexpr uint32_t kMagic = 0x64006400u;  // float16 1024.0 in both halves
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// Run table in units of 32-row blocks, copied into the kernel arguments.
+struct Runs {
+  int nruns;
+  int blocks_per_group;                   // group_size / 32
+  int run_block[QLINEAR_MAX_RUNS + 1];    // first block of run r; [nruns] = K / 32
+  int run_row[QLINEAR_MAX_RUNS + 1];      // first packed row of run r
+  int run_bits[QLINEAR_MAX_RUNS];
+};
+
+// Bit width and first packed row of 32-row block `blk`.
+__device__ __forceinline__ void block_info(const Runs& R, int blk, int& bits, int& row) {
+  int r = 0;
+  while (r + 1 < R.nruns && blk >= R.run_block[r + 1]) ++r;
+  bits = R.run_bits[r];
+  row = R.run_row[r] + (blk - R.run_block[r]) * bits;
+}
+
+// Last block (exclusive) of the run that contains `blk`.
+__device__ __forceinline__ int run_end_block(const Runs& R, int blk) {
+  int r = 0;
+  while (r + 1 < R.nruns && blk >= R.run_block[r + 1]) ++r;
+  return R.run_block[r + 1];
+}
+
+// ---------------------------------------------------------------------------
+// Packed format. A block of 32 b-bit codes of one column is b words; every
+// code lies inside one 16-bit half of a word, f = 16 / b codes per half.
+// Unpacking produces 16 float16 pairs per block. Pair p holds two codes of
+// the same column, one in each half, as 1024 + code: OR-ing a field that
+// sits at the bottom of a half into the exponent bits of 1024.0 yields the
+// float16 value 1024 + code exactly (codes are below 1024).
+//
+//   regular pair p < b*f: word t = p / f, slot i = p % f,
+//       rows (2f*t + i, 2f*t + f + i)
+//   b in {3, 5}, p = 15: rows (30, 31), code bit k in word k, bits 15 / 31
+//   b = 6, p = 12 + v:   rows (24 + v, 28 + v), low nibble in word v bits
+//       12..15 / 28..31, top two bits in word 4 + v/2
+// ---------------------------------------------------------------------------
+
+// Rows (within the block) held by pair p for width b; runtime version for staging.
+__host__ __device__ __forceinline__ void pair_rows(int b, int p, int& lo, int& hi) {
+  const int f = 16 / b;
+  if (p < b * f) {
+    const int t = p / f, i = p % f;
+    lo = 2 * f * t + i;
+    hi = lo + f;
+  } else if (b == 6) {
+    lo = 24 + (p - 12);
+    hi = lo + 4;
+  } else {
+    lo = 30;
+    hi = 31;
+  }
+}
+
+template <int B>
+struct Fmt {
+  static constexpr int F = 16 / B;            // codes per half-word
+  static constexpr int kRegular = B * F;      // regular pairs
+  static constexpr uint32_t kMask = ((1u << B) - 1u) * 0x00010001u;
+};
+
+// Pair P of a block whose b words (one column) are w[0..B-1]; returns two
+// float16 values 1024 + code packed in a uint32 (low half = lower row).
+template <int B, int P>
+__host__ __device__ __forceinline__ uint32_t extract_pair(const uint32_t* w) {
+  using Fm = Fmt<B>;
+  if constexpr (P < Fm::kRegular) {
+    constexpr int t = P / Fm::F, i = P % Fm::F;
+    if constexpr (i == 0) {
+      return (w[t] & Fm::kMask) | kMagic;
+    } else {
+      return ((w[t] >> (B * i)) & Fm::kMask) | kMagic;
+    }
+  } else if constexpr (B == 6) {
+    constexpr int v = P - 12;
+    const uint32_t lo = (w[v] >> 12) & 0x000F000Fu;
+    const uint32_t hi = (w[4 + v / 2] >> (8 + 2 * (v % 2))) & 0x00300030u;
+    return lo | hi | kMagic;
+  } else {
+    static_assert(B == 3 || B == 5, "spare rows exist only for 3, 5 and 6 bits");
+    uint32_t r = kMagic | ((w[0] >> 15) & 0x00010001u);
+#pragma unroll
+    for (int k = 1; k < B; ++k) r |= (w[k] >> (15 - k)) & (0x00010001u << k);
+    return r;
+  }
+}
+
+// Runtime-P dispatcher for the helper kernels (pack tests, dequant export).
+template <int B>
+__host__ __device__ __forceinline__ void extract_all_pairs(const uint32_t* w, uint32_t* out) {
+  [&]<int... P>(std::integer_sequence<int, P...>) {
+    ((out[P] = extract_pair<B, P>(w)), ...);
+  }(std::make_integer_sequence<int, kPairsPerBlock>{});
+}
+
+// Write the code of block row r into the b words of its column (packing side).
+template <int B>
+__host__ __device__ __forceinline__ void place_code(uint32_t* w, int r, uint32_t code) {
+  constexpr int F = 16 / B;
+  code &= (1u << B) - 1u;
+  if (r < 2 * F * B) {
+    const int t = r / (2 * F), u = r % (2 * F);
+    w[t] |= code << (16 * (u / F) + B * (u % F));
+  } else if constexpr (B == 6) {
+    const int h = (r - 24) / 4, v = (r - 24) % 4;
+    w[v] |= (code & 0xFu) << (16 * h + 12);
+    w[4 + v / 2] |= (code >> 4) << (16 * h + 12 + 2 * (v % 2));
+  } else if constexpr (B == 3 || B == 5) {
+    const int h = r - 30;
+#pragma unroll
+    for (int k = 0; k < B; ++k) w[k] |= ((code >> k) & 1u) << (16 * h + 15);
+  }
+}
+
+__device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+__device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Exact float16 weights of a pair: RNE(s * ((1024 + q) - (1024 + z))).
+// The subtraction of two integers below 2048 is exact in float16 and the
+// product is rounded once, so the result is the correctly rounded s * (q - z).
+__device__ __forceinline__ half2_t dequant_pair(uint32_t pair, half2_t neg_bias, half2_t scale) {
+  const half2_t d = as_half2(pair) + neg_bias;
+  return d * scale;
+}
+
+}  // namespace qlinear

@@ -1,0 +1,30 @@
+// Host-side launchers of the gfx950 kernels. Arguments are validated by the
+// C entry points before any of these is called.
+#pragma once
+
+#include "qlinear_device.hpp"
+
+namespace qlinear {
+
+Runs make_runs(const qlinear_layout& L);
+
+hipError_t launch_pack(const qlinear_layout& L, const Runs& runs, const uint8_t* q, uint32_t* qweight,
+                       hipStream_t stream);
+hipError_t launch_unpack(const qlinear_layout& L, const Runs& runs, const uint32_t* qweight, uint8_t* q,
+                         hipStream_t stream);
+hipError_t launch_dequant(const qlinear_layout& L, const Runs& runs, const uint32_t* qweight,
+                          const uint16_t* scales, const uint8_t* zeros, uint16_t* w, hipStream_t stream);
+
+// Decode layer (M <= 16). ws_acc: float [16][N], ws_cnt: uint32 per 256-column strip.
+size_t qgemv_workspace_bytes(int N);
+hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
+                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                        const int32_t* perm, uint16_t* y, void* ws, hipStream_t stream);
+
+// Prefill layer. ws holds the gathered activations, float16 [M][K].
+size_t qgemm_workspace_bytes(int M, int K);
+hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
+                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                        const int32_t* perm, uint16_t* y, void* ws, hipStream_t stream);
+
+}  // namespace qlinear

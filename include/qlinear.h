@@ -1,0 +1,174 @@
+/*
+ * qlinear.h -- C ABI of the MI355X (gfx950) quantized linear layer.
+ *
+ * The layer is the fused dequantize-and-multiply of ExLlamaV2's quantized
+ * matmul (ExLlamaV2 blog, "How the Fused CUDA Kernel Works"; ExLlamaV2
+ * README, "EXL2 quantization"): GPTQ group-wise codes and EXL2 mixed 2/3/4/5/6/8-bit
+ * codes, rows remapped by act-order, dequantized as w = s * (q - z) and
+ * multiplied against float16 activations with float32 accumulation and a
+ * float16 result.
+ *
+ *   y[m][n] = RNE_fp16( sum_j x[m][perm[j]] * s[g(j)][n] * (q[j][n] - z[g(j)][n]) )
+ *
+ * Notation: K input features, N outputs, M tokens, gs rows per group
+ * (32, 64 or 128), G = K / gs groups, b_g the bit width of group g. Rows of
+ * the weight matrix are in *stored order*: stored row j holds the weights of
+ * original input feature perm[j] (the act-order permutation).
+ *
+ * Conventions for every call below:
+ *  - All data pointers are DEVICE pointers unless the argument name ends in
+ *    _host. Matrices are row-major. The caller allocates and owns every
+ *    buffer and every stream; the library allocates nothing, keeps no global
+ *    state and never synchronizes the host.
+ *  - float16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    asynchronously; a QLINEAR_OK return means the launch was accepted.
+ *  - Every call validates its host-visible arguments first and returns a
+ *    status without launching anything when they are wrong. Device contents
+ *    (codes in range, perm being a permutation) are not checked.
+ *  - Pointers to device data must be 16-byte aligned (QLINEAR_ERR_MISALIGNED).
+ *  - N must be a multiple of 8; K a multiple of gs.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call. */
+#define QLINEAR_OK 0
+#define QLINEAR_ERR_INVALID_ARGUMENT 1 /* NULL pointer, negative or zero size where not allowed */
+#define QLINEAR_ERR_UNSUPPORTED 2      /* bit width, group size, M, N or run count outside the supported set */
+#define QLINEAR_ERR_MISALIGNED 3       /* a device pointer is not 16-byte aligned */
+#define QLINEAR_ERR_WORKSPACE 4        /* workspace missing or smaller than required */
+#define QLINEAR_ERR_HIP 5              /* the HIP runtime rejected a launch */
+
+/* Runs of consecutive groups sharing one bit width. Act-order remapping puts
+ * the rows quantized at one width next to each other (ExLlamaV2 README,
+ * "EXL2 quantization"), so a matrix has only a few runs; up to this many are
+ * supported. */
+#define QLINEAR_MAX_RUNS 64
+/* Largest M accepted by qlinear_qgemv (decode). */
+#define QLINEAR_GEMV_MAX_M 16
+
+/*
+ * Description of one packed weight matrix: shape, group size and the
+ * row-group -> bit-width map, run-length encoded. Filled on the host by
+ * qlinear_layout_init and passed by pointer (host memory) to every call.
+ *
+ * Packed format. The packed matrix is uint32 [packed_rows][N]. Each group is
+ * cut into 32-row blocks; a block of b-bit codes for one output column is b
+ * words, stored in consecutive packed rows of that column. Group g starts at
+ * packed row goff[g] = sum_{g'<g} gs * b_g' / 32, its block c at
+ * goff[g] + c * b_g. Inside a block each word is two 16-bit halves
+ * (h = 0: bits 0..15, h = 1: bits 16..31) and every code lies inside one half.
+ * With f = floor(16 / b) codes per half:
+ *   - row r < 2*f*b: word r / (2f); u = r % (2f); half u / f; slot u % f;
+ *     code bits at 16*h + b*(u % f) upward. For b = 2, 4, 8 this covers all
+ *     32 rows and is the plain least-significant-first order (4-bit: row i of
+ *     a word at bits 4i..4i+3, the nibble order of the blog's kernel sketch).
+ *   - b = 3, 5: rows 30 + h keep code bit k in word k, bit 16*h + 15.
+ *   - b = 6: rows 24 + 4*h + v (v < 4) keep code bits 0..3 in word v at
+ *     bits 16*h + 12..15, and code bits 4, 5 in word 4 + v/2 at bits
+ *     16*h + 12 + 2*(v % 2) and the bit above it.
+ */
+typedef struct qlinear_layout {
+  int32_t K;            /* input features (rows of the weight matrix) */
+  int32_t N;            /* output features (columns) */
+  int32_t group_size;   /* rows per scale group: 32, 64 or 128 */
+  int32_t groups;       /* G = K / group_size */
+  int32_t packed_rows;  /* R: rows of the uint32 [R][N] packed matrix */
+  int32_t nruns;        /* number of runs, 1..QLINEAR_MAX_RUNS */
+  int32_t run_group[QLINEAR_MAX_RUNS + 1]; /* first group of run r; [nruns] = groups */
+  int32_t run_row[QLINEAR_MAX_RUNS + 1];   /* first packed row of run r; [nruns] = packed_rows */
+  int32_t run_bits[QLINEAR_MAX_RUNS];      /* code width of run r: 2, 3, 4, 5, 6 or 8 */
+} qlinear_layout;
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* qlinear_status_string(int status);
+
+/*
+ * Fill `layout` for a K x N matrix with `group_size` rows per group and the
+ * per-group bit widths bits_host[0 .. K/group_size - 1] (HOST memory, read
+ * only during the call). Host-only; touches no GPU.
+ * Errors: INVALID_ARGUMENT (NULL, K <= 0, N <= 0), UNSUPPORTED (group size
+ * not 32/64/128, K % group_size != 0, N % 8 != 0, a width outside
+ * {2,3,4,5,6,8}, more than QLINEAR_MAX_RUNS runs).
+ */
+int qlinear_layout_init(qlinear_layout* layout, int32_t K, int32_t N, int32_t group_size,
+                        const uint8_t* bits_host);
+
+/*
+ * Pack codes into the format above.
+ *   q       : uint8 [K][N], stored row order, each code < 2^b of its group
+ *             (larger codes are truncated to their low b bits).
+ *   qweight : uint32 [packed_rows][N], written entirely.
+ */
+int qlinear_pack_weights(const qlinear_layout* layout, const uint8_t* q, uint32_t* qweight,
+                         void* stream);
+
+/* Inverse of qlinear_pack_weights: qweight -> q uint8 [K][N] (stored order). */
+int qlinear_unpack(const qlinear_layout* layout, const uint32_t* qweight, uint8_t* q,
+                   void* stream);
+
+/*
+ * Dequantize to float16 in stored row order:
+ *   w[j][n] = RNE_fp16(s[g][n] * (q[j][n] - z[g][n])), g = j / group_size,
+ * rounded once (the product is exact before rounding).
+ *   scales : float16 [G][N]
+ *   zeros  : uint8 [G][N] integer zero points, or NULL for symmetric groups
+ *            (z = 2^(b_g - 1), the midpoint of the code range)
+ *   w      : float16 [K][N], written entirely.
+ */
+int qlinear_dequant(const qlinear_layout* layout, const uint32_t* qweight, const uint16_t* scales,
+                    const uint8_t* zeros, uint16_t* w, void* stream);
+
+/*
+ * Workspace of qlinear_qgemv, in bytes, for any M <= QLINEAR_GEMV_MAX_M.
+ * The workspace holds float32 partial sums and per-column-strip arrival
+ * counters. It must be zero-filled once before its first use; every call
+ * that completes leaves it zero-filled again, so it can be reused by later
+ * calls on the same stream. Calls that may overlap in time (different
+ * streams) must not share one workspace.
+ */
+int qlinear_qgemv_workspace_bytes(const qlinear_layout* layout, size_t* bytes);
+
+/*
+ * Decode-sized layer, 1 <= M <= QLINEAR_GEMV_MAX_M. M == 0 returns OK after
+ * checking the layout only, and launches nothing (operands may then be NULL).
+ *   x       : float16 [M][K], original feature order
+ *   qweight : uint32 [packed_rows][N] from qlinear_pack_weights
+ *   scales  : float16 [G][N]
+ *   zeros   : uint8 [G][N] or NULL (symmetric)
+ *   perm    : int32 [K], stored row j holds feature perm[j]; NULL = identity.
+ *             Must be a permutation of 0..K-1 (not checked).
+ *   y       : float16 [M][N], written entirely
+ *   workspace, workspace_bytes : see qlinear_qgemv_workspace_bytes
+ */
+int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M,
+                  const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                  const int32_t* perm, uint16_t* y, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* Workspace of qlinear_qgemm for M tokens, in bytes (no initialization needed). */
+int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes);
+
+/*
+ * Prefill-sized layer, any M >= 0 (M == 0 as for qlinear_qgemv), same
+ * operands and result as qlinear_qgemv.
+ * The workspace receives the act-order-gathered activations.
+ */
+int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M,
+                  const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                  const int32_t* perm, uint16_t* y, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

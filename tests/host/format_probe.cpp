@@ -1,0 +1,50 @@
+// Host-side probe of the kernels' packed-format helpers (place_code,
+// extract_pair, pair_rows). It packs pseudo-random codes with the kernel
+// packer and unpacks them with the kernel unpacker, printing codes, words and
+// unpacked pairs so that the Python test can compare them with the oracle.
+// Runs on the CPU only; calls no HIP runtime function.
+#include <cstdio>
+
+#include "qlinear_device.hpp"
+
+using namespace qlinear;
+
+static uint32_t lcg(uint32_t& s) {
+  s = s * 1664525u + 1013904223u;
+  return s >> 8;
+}
+
+template <int B>
+static void probe(uint32_t seed, int ncols) {
+  for (int c = 0; c < ncols; ++c) {
+    uint32_t codes[kBlockRows];
+    for (int r = 0; r < kBlockRows; ++r) codes[r] = lcg(seed) & ((1u << B) - 1u);
+    if (c == 1)
+      for (int r = 0; r < kBlockRows; ++r) codes[r] = (1u << B) - 1u;  // all ones
+    uint32_t w[B] = {};
+    for (int r = 0; r < kBlockRows; ++r) place_code<B>(w, r, codes[r]);
+    uint32_t pr[kPairsPerBlock];
+    extract_all_pairs<B>(w, pr);
+    std::printf("B %d\nC", B);
+    for (int r = 0; r < kBlockRows; ++r) std::printf(" %u", codes[r]);
+    std::printf("\nW");
+    for (int t = 0; t < B; ++t) std::printf(" %u", w[t]);
+    std::printf("\nP");
+    for (int p = 0; p < kPairsPerBlock; ++p) {
+      int lo, hi;
+      pair_rows(B, p, lo, hi);
+      std::printf(" %d:%d:%u", lo, hi, pr[p]);
+    }
+    std::printf("\n");
+  }
+}
+
+int main() {
+  probe<2>(1u, 4);
+  probe<3>(2u, 4);
+  probe<4>(3u, 4);
+  probe<5>(4u, 4);
+  probe<6>(5u, 4);
+  probe<8>(6u, 4);
+  return 0;
+}

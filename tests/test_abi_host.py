@@ -1,0 +1,162 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before launching anything (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dequant_matmul_gptq_amd as dq
+from dequant_matmul_gptq_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlinear.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlinear_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = dq.lib()
+    names = declared_functions()
+    assert len(names) == 9, names
+    assert sorted(names) == sorted(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_size_matches_header():
+    # 6 scalars + 2 * (MAX_RUNS + 1) + MAX_RUNS int32
+    assert ctypes.sizeof(_lib.qlinear_layout) == 4 * (6 + 2 * 65 + 64)
+
+
+def test_status_strings():
+    for s in range(6):
+        assert dq.status_string(s)
+    assert dq.status_string(99) == "unknown status"
+
+
+def _layout(K=256, N=512, gs=32, bits=None):
+    bits = np.full(K // gs, 4, np.uint8) if bits is None else bits
+    return dq.Layout(K, N, gs, bits)
+
+
+def test_layout_runs_and_rows():
+    bits = np.array([6] * 3 + [5] * 2 + [4] * 5 + [3] * 4, np.uint8)
+    L = _layout(K=14 * 64, N=64, gs=64, bits=bits)
+    assert L.nruns == 4
+    c = L.c
+    assert list(c.run_group)[:5] == [0, 3, 5, 10, 14]
+    assert list(c.run_bits)[:4] == [6, 5, 4, 3]
+    # 2 blocks per group, b words per block
+    assert list(c.run_row)[:5] == [0, 36, 56, 96, 120]
+    assert L.packed_rows == 120
+
+
+@pytest.mark.parametrize("args,status", [
+    ((256, 512, 48), _lib.ERR_UNSUPPORTED),      # group size
+    ((250, 512, 32), _lib.ERR_UNSUPPORTED),      # K % gs
+    ((256, 500, 32), _lib.ERR_UNSUPPORTED),      # N % 8
+    ((0, 512, 32), _lib.ERR_INVALID_ARGUMENT),
+    ((256, -8, 32), _lib.ERR_INVALID_ARGUMENT),
+])
+def test_layout_init_rejects_shapes(args, status):
+    bits = np.full(64, 4, np.uint8)
+    with pytest.raises(dq.QlinearError) as e:
+        dq.Layout(*args, bits[: max(1, args[0] // args[2]) if args[2] else 1])
+    assert e.value.status == status
+
+
+def test_layout_init_rejects_bits_and_runs():
+    with pytest.raises(dq.QlinearError) as e:
+        _layout(bits=np.array([4, 4, 7, 4, 4, 4, 4, 4], np.uint8))
+    assert e.value.status == _lib.ERR_UNSUPPORTED
+    alt = np.array([4, 3] * 40, np.uint8)   # 80 runs > 64
+    with pytest.raises(dq.QlinearError) as e:
+        _layout(K=80 * 32, N=64, gs=32, bits=alt)
+    assert e.value.status == _lib.ERR_UNSUPPORTED
+    ok = np.array([4, 3] * 32, np.uint8)    # exactly 64 runs
+    assert _layout(K=64 * 32, N=64, gs=32, bits=ok).nruns == 64
+
+
+def test_layout_init_null():
+    L = dq.lib()
+    assert L.qlinear_layout_init(None, 256, 512, 32, None) == _lib.ERR_INVALID_ARGUMENT
+
+
+FAKE = 0x10000  # aligned fake device address: never dereferenced on these paths
+
+
+def _gemv(L, **kw):
+    a = dict(x=FAKE, M=1, qw=FAKE, s=FAKE, z=None, perm=None, y=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return dq.lib().qlinear_qgemv(L.ref, a["x"], a["M"], a["qw"], a["s"], a["z"], a["perm"], a["y"],
+                                  a["ws"], a["wsb"], None)
+
+
+def _gemm(L, **kw):
+    a = dict(x=FAKE, M=1, qw=FAKE, s=FAKE, z=None, perm=None, y=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return dq.lib().qlinear_qgemm(L.ref, a["x"], a["M"], a["qw"], a["s"], a["z"], a["perm"], a["y"],
+                                  a["ws"], a["wsb"], None)
+
+
+def test_qgemv_validation_before_launch():
+    L = _layout()
+    assert _gemv(L, x=None) == _lib.ERR_INVALID_ARGUMENT
+    assert _gemv(L, qw=None) == _lib.ERR_INVALID_ARGUMENT
+    assert _gemv(L, s=None) == _lib.ERR_INVALID_ARGUMENT
+    assert _gemv(L, y=None) == _lib.ERR_INVALID_ARGUMENT
+    assert _gemv(L, ws=None) == _lib.ERR_WORKSPACE
+    assert _gemv(L, M=-1) == _lib.ERR_INVALID_ARGUMENT
+    assert _gemv(L, M=17) == _lib.ERR_UNSUPPORTED
+    assert _gemv(L, x=FAKE + 2) == _lib.ERR_MISALIGNED
+    assert _gemv(L, z=FAKE + 8) == _lib.ERR_MISALIGNED
+    assert _gemv(L, perm=FAKE + 4) == _lib.ERR_MISALIGNED
+    assert _gemv(L, wsb=dq.qgemv_workspace_bytes(L) - 1) == _lib.ERR_WORKSPACE
+    assert _gemv(L, M=0) == _lib.OK   # quick return, nothing launched
+    assert _gemv(L, M=0, x=None, y=None, ws=None, wsb=0) == _lib.OK  # empty tensors may be NULL
+
+
+def test_qgemm_validation_before_launch():
+    L = _layout()
+    assert _gemm(L, qw=None) == _lib.ERR_INVALID_ARGUMENT
+    assert _gemm(L, ws=None) == _lib.ERR_WORKSPACE
+    assert _gemm(L, M=64, wsb=dq.qgemm_workspace_bytes(L, 64) - 1) == _lib.ERR_WORKSPACE
+    assert _gemm(L, y=FAKE + 1) == _lib.ERR_MISALIGNED
+    assert _gemm(L, M=0) == _lib.OK
+    assert _gemm(L, M=0, x=None, y=None, ws=None, wsb=0) == _lib.OK
+
+
+def test_tampered_layout_is_rejected():
+    L = _layout()
+    L.c.packed_rows += 1
+    assert _gemv(L) == _lib.ERR_INVALID_ARGUMENT
+    L = _layout()
+    L.c.run_bits[0] = 7
+    assert _gemv(L) == _lib.ERR_UNSUPPORTED
+    L = _layout()
+    L.c.nruns = 0
+    assert _gemm(L) == _lib.ERR_UNSUPPORTED
+
+
+def test_pack_unpack_dequant_validation():
+    L = _layout()
+    lib = dq.lib()
+    assert lib.qlinear_pack_weights(L.ref, None, FAKE, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.qlinear_pack_weights(L.ref, FAKE + 1, FAKE, None) == _lib.ERR_MISALIGNED
+    assert lib.qlinear_unpack(L.ref, FAKE, None, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.qlinear_dequant(L.ref, FAKE, None, None, FAKE, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.qlinear_dequant(L.ref, FAKE, FAKE, FAKE + 3, FAKE, None) == _lib.ERR_MISALIGNED
+
+
+def test_workspace_sizes():
+    L = _layout(N=4096, K=4096, gs=128)
+    # float32 [16][N] partial sums + one counter per 256-column strip, 256-byte rounded
+    assert dq.qgemv_workspace_bytes(L) == (16 * 4096 * 4 + 16 * 4 + 255) // 256 * 256
+    assert dq.qgemm_workspace_bytes(L, 2048) == 2048 * 4096 * 2

@@ -1,0 +1,190 @@
+"""qgemv / qgemm on the GPU against the CPU oracle.
+
+Bit-exact where one product decides the result (one-hot activations);
+otherwise relative Frobenius error <= 1e-3 and max error <= 1e-2 * max|y_ref|.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_gptq_amd as dq
+import oracle
+import workloads as wl
+from gpu_util import GpuLayer, assert_close, device, fp16_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _mixed_inputs(bits, gs, N, M, seed, zeros, act_order=True):
+    rng = np.random.default_rng(seed)
+    bits = np.asarray(bits, np.uint8)
+    K = gs * len(bits)
+    spec = wl.LayerSpec(f"mixed-{K}x{N}", K, N, gs, ((4, 1.0),), not zeros, act_order, (M,))
+    perm = rng.permutation(K).astype(np.int32) if act_order else None
+    q = np.concatenate([rng.integers(0, 1 << int(b), size=(gs, N), dtype=np.uint8) for b in bits])
+    z = rng.integers(0, 16, size=(len(bits), N), dtype=np.uint8) if zeros else None
+    s = rng.uniform(0.005, 0.02, size=(len(bits), N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    return wl.LayerInputs(spec, bits, q, z, s, perm, x)
+
+
+def _ref(inp, x=None):
+    sp = inp.spec
+    return oracle.qlinear(inp.x if x is None else x, inp.q, inp.scales, inp.zeros, inp.bits, sp.group_size, inp.perm)
+
+
+MIXED_BITS = [6, 6, 5, 5, 4, 4, 4, 3, 3, 2, 8]   # 11 blocks of 32 rows, 6 runs
+
+
+# ------------------------------------------------------------------ one-hot probes
+
+@pytest.mark.parametrize("op", ("qgemv", "qgemm"))
+@pytest.mark.parametrize("zeros", (True, False))
+def test_one_hot_rows_are_exact(op, zeros):
+    """x = e_k returns the float16 weight row holding feature k, bit for bit.
+
+    A single non-zero product is exact in float32 and the final rounding is
+    the only one, so the result must equal the oracle's RNE(s * (q - z))."""
+    say(f"one-hot {op} zeros={zeros}")
+    inp = _mixed_inputs(MIXED_BITS, 32, 520, 16, seed=5, zeros=zeros)
+    K = inp.spec.K
+    lay = GpuLayer(inp)
+    ks = np.random.default_rng(9).choice(K, 16, replace=False)
+    x = np.zeros((16, K), np.float16)
+    x[np.arange(16), ks] = 1.0
+    y = lay.qgemv(x) if op == "qgemv" else lay.qgemm(x)
+    w16 = oracle.dequant_fp16(inp.q, inp.scales, inp.zeros, inp.bits, 32)
+    inv = np.argsort(inp.perm)
+    want = w16[inv[ks]]
+    got = y.cpu().numpy()
+    # compare values (+0 and -0 are the same weight)
+    assert np.array_equal(got.astype(np.float32), want.astype(np.float32))
+
+
+# ------------------------------------------------------------------ small ragged shapes
+
+@pytest.mark.parametrize("M", (1, 2, 3, 5, 8, 13, 16))
+@pytest.mark.parametrize("zeros", (True, False))
+def test_qgemv_small_mixed(M, zeros):
+    say(f"qgemv small mixed M={M} zeros={zeros}")
+    inp = _mixed_inputs(MIXED_BITS, 32, 520, M, seed=100 + M, zeros=zeros)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv M={M}")
+
+
+@pytest.mark.parametrize("gs", (32, 64, 128))
+@pytest.mark.parametrize("b", (2, 3, 4, 5, 6, 8))
+def test_qgemv_uniform_widths(b, gs):
+    say(f"qgemv uniform b={b} gs={gs}")
+    inp = _mixed_inputs([b] * (1024 // gs), gs, 776, 4, seed=b * 31 + gs, zeros=True)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv b={b} gs={gs}")
+
+
+@pytest.mark.parametrize("M", (1, 7, 130, 257))
+@pytest.mark.parametrize("zeros", (True, False))
+def test_qgemm_small_mixed(M, zeros):
+    say(f"qgemm small mixed M={M} zeros={zeros}")
+    inp = _mixed_inputs(MIXED_BITS, 32, 520, M, seed=200 + M, zeros=zeros)
+    y = GpuLayer(inp).qgemm(inp.x)
+    assert_close(y, _ref(inp), f"qgemm M={M}")
+
+
+@pytest.mark.parametrize("gs", (32, 128))
+@pytest.mark.parametrize("b", (2, 3, 4, 5, 6, 8))
+def test_qgemm_uniform_widths(b, gs):
+    say(f"qgemm uniform b={b} gs={gs}")
+    inp = _mixed_inputs([b] * (1024 // gs), gs, 392, 100, seed=b * 17 + gs, zeros=True)
+    y = GpuLayer(inp).qgemm(inp.x)
+    assert_close(y, _ref(inp), f"qgemm b={b} gs={gs}")
+
+
+def test_no_act_order_and_single_group():
+    say("no act-order, one group")
+    inp = _mixed_inputs([4], 32, 8, 3, seed=1, zeros=True, act_order=False)
+    lay = GpuLayer(inp)
+    assert_close(lay.qgemv(inp.x), _ref(inp), "qgemv tiny")
+    assert_close(lay.qgemm(inp.x), _ref(inp), "qgemm tiny")
+
+
+def test_empty_batch():
+    inp = _mixed_inputs([4, 4], 32, 64, 1, seed=2, zeros=True)
+    lay = GpuLayer(inp)
+    x0 = np.zeros((0, inp.spec.K), np.float16)
+    assert lay.qgemv(x0).shape == (0, 64)
+    assert lay.qgemm(x0).shape == (0, 64)
+
+
+# ------------------------------------------------------------------ invariances
+
+def test_act_order_gather_invariance():
+    """(x, perm) gives the same y as (x[:, perm], identity)."""
+    say("perm invariance")
+    inp = _mixed_inputs(MIXED_BITS, 32, 520, 4, seed=7, zeros=True)
+    lay = GpuLayer(inp)
+    y1 = lay.qgemv(inp.x).float()
+    lay.perm = None
+    y2 = lay.qgemv(np.ascontiguousarray(inp.x[:, inp.perm])).float()
+    assert torch.allclose(y1, y2, rtol=1e-3, atol=1e-3 * y1.abs().max().item())
+
+
+def test_rows_are_independent():
+    """Row m of an M = 16 call equals the M = 1 call on that row."""
+    say("row independence")
+    inp = _mixed_inputs(MIXED_BITS, 32, 520, 16, seed=8, zeros=False)
+    lay = GpuLayer(inp)
+    y16 = lay.qgemv(inp.x).float()
+    for m in (0, 5, 15):
+        y1 = lay.qgemv(inp.x[m:m + 1]).float()
+        assert torch.allclose(y16[m:m + 1], y1, rtol=2e-3, atol=2e-3 * y1.abs().max().item())
+
+
+def test_workspace_returns_to_zero_and_is_reusable():
+    say("workspace reuse")
+    a = _mixed_inputs(MIXED_BITS, 32, 520, 16, seed=10, zeros=True)
+    b = _mixed_inputs([3] * 40, 32, 264, 2, seed=11, zeros=False)
+    la, lb = GpuLayer(a), GpuLayer(b)
+    assert la.ws.numel() >= dq.qgemv_workspace_bytes(lb.layout)
+    lb.ws = la.ws   # one workspace shared by calls in sequence on one stream
+    for _ in range(3):
+        assert_close(la.qgemv(a.x), _ref(a), "a")
+        assert_close(lb.qgemv(b.x), _ref(b), "b")
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(la.ws)) == 0
+    assert int(torch.count_nonzero(lb.ws)) == 0
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+DECODE_CASES = [(wl.TINY, 1)] + [(s, M) for s in wl.LLAMA7B_DECODE for M in s.Ms] + \
+    [(wl.EXL2_MIXED, M) for M in wl.EXL2_MIXED.Ms] + [(s, M) for s in wl.LLAMA70B_EXL2 for M in s.Ms]
+
+
+@pytest.mark.parametrize("spec,M", DECODE_CASES, ids=lambda v: v.name if hasattr(v, "name") else f"M{v}")
+def test_qgemv_workloads(spec, M):
+    say(f"qgemv workload {spec.name} M={M}")
+    inp = wl.generate(spec)
+    x = inp.x[:M]
+    y = GpuLayer(inp).qgemv(x)
+    assert_close(y, _ref(inp, x), f"{spec.name} M={M}")
+
+
+@pytest.mark.parametrize("spec", (wl.TINY, wl.LLAMA7B_DECODE[1], wl.EXL2_MIXED), ids=lambda s: s.name)
+def test_qgemm_decode_shapes(spec):
+    say(f"qgemm on decode shape {spec.name}")
+    inp = wl.generate(spec)
+    y = GpuLayer(inp).qgemm(inp.x)
+    assert_close(y, _ref(inp), spec.name)
+
+
+def test_qgemm_prefill_workload():
+    """Llama-2-13B MLP prefill, M = 2048: the oracle checks sampled token rows
+    (every 16th row, plus the last), computed in full float64."""
+    spec = wl.PREFILL_13B
+    say(f"qgemm workload {spec.name}")
+    inp = wl.generate(spec)
+    y = GpuLayer(inp).qgemm(inp.x)
+    rows = np.unique(np.concatenate([np.arange(0, 2048, 16), [2047]]))
+    ref = _ref(inp, inp.x[rows])
+    assert_close(y[torch.from_numpy(rows).to(y.device)], ref, spec.name)

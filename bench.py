@@ -114,7 +114,7 @@ def main():
     shapes, mats = setup_decode(torch, dq, wl, dev)
     wbytes = [wl.weight_bytes(s["spec"]) for s in shapes]
     step_bytes = sum(wbytes[m["shape"]] for m in mats)
-    ws = dq.qgemv_workspace(shapes[1]["L"], dev)  # N = 11008 covers every shape in the step
+    ws = dq.qgemv_workspace(shapes[2]["L"], dev)  # K = 11008 covers every shape in the step
     xs = [torch.from_numpy(s["inp"].x[:1].copy()).to(dev) for s in shapes]
     ys = [torch.empty((1, s["spec"].N), dtype=torch.float16, device=dev) for s in shapes]
     launches = [Launch(lib.qlinear_qgemv, shapes[m["shape"]]["L"], xs[m["shape"]], 1, m["qw"], m["sc"], m["zr"],

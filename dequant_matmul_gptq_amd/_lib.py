@@ -172,8 +172,8 @@ def qgemv_workspace_bytes(layout: Layout) -> int:
 
 
 def qgemv_workspace(layout: Layout, device) -> torch.Tensor:
-    """A zero-filled qgemv workspace (it stays zero-filled between calls)."""
-    return torch.zeros(qgemv_workspace_bytes(layout), dtype=torch.uint8, device=device)
+    """A qgemv workspace (scratch: needs no initialization)."""
+    return torch.empty(qgemv_workspace_bytes(layout), dtype=torch.uint8, device=device)
 
 
 def qgemm_workspace_bytes(layout: Layout, M: int) -> int:

@@ -155,7 +155,7 @@ int qlinear_qgemv_workspace_bytes(const qlinear_layout* layout, size_t* bytes) {
   int st = check_layout(layout);
   if (st != QLINEAR_OK) return st;
   if (!bytes) return QLINEAR_ERR_INVALID_ARGUMENT;
-  *bytes = qgemv_workspace_bytes(layout->N);
+  *bytes = qgemv_workspace_bytes(layout->K);
   return QLINEAR_OK;
 }
 
@@ -165,7 +165,7 @@ int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M, co
   int st = check_gemm_operands(layout, x, M, qweight, scales, zeros, perm, y, workspace);
   if (st != QLINEAR_OK || M == 0) return st;
   if (M > QLINEAR_GEMV_MAX_M) return QLINEAR_ERR_UNSUPPORTED;
-  if (workspace_bytes < qgemv_workspace_bytes(layout->N)) return QLINEAR_ERR_WORKSPACE;
+  if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
   return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, qweight, scales, zeros, perm, y, workspace,
                                  (hipStream_t)stream));
 }

@@ -1,10 +1,10 @@
 // Prefill-sized quantized linear layer on gfx950, bound by the matrix cores.
 //
-// 1. gather_kernel writes the act-order-gathered activations into the
-//    workspace, xq[m][32*blk + 2p + h] = x[m][perm[32*blk + row_h(p)]], where
-//    (row_0(p), row_1(p)) are the two rows that pair p of block blk unpacks
-//    to. Inside every 32-row block the K order is thus the unpacking order,
-//    and the same reordering is applied to the weights below, so the
+// 1. The shared gather kernel writes the act-order-gathered activations into
+//    the workspace, xq[m][32*blk + 2p + h] = x[m][perm[32*blk + row_h(p)]],
+//    where (row_0(p), row_1(p)) are the two rows that pair p of block blk
+//    unpacks to. Inside every 32-row block the K order is thus the unpacking
+//    order, and the same reordering is applied to the weights below, so the
 //    contraction is unchanged.
 // 2. gemm_kernel: each workgroup computes a 128 x 128 tile of y. Per K-step
 //    of 64 rows (two 32-row blocks) it copies the activation tile to LDS,
@@ -21,27 +21,6 @@ constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kPad = 8;                 // halves of padding per LDS row
 constexpr int kLdsRow = BK + kPad;      // 72 halves = 144 bytes
-
-__global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ x,
-                                                     const int32_t* __restrict__ perm,
-                                                     uint32_t* __restrict__ xq, int M, int K, Runs runs) {
-  const int pairs = (K / kBlockRows) * kPairsPerBlock;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= pairs) return;
-  const int blk = idx / kPairsPerBlock, p = idx % kPairsPerBlock;
-  int bits, row;
-  block_info(runs, blk, bits, row);
-  int lo, hi;
-  pair_rows(bits, p, lo, hi);
-  const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;
-  // perm entries are clamped into [0, K): a malformed perm cannot address outside x.
-  const int flo = perm ? (int)min((unsigned)perm[jlo], (unsigned)(K - 1)) : jlo;
-  const int fhi = perm ? (int)min((unsigned)perm[jhi], (unsigned)(K - 1)) : jhi;
-  for (int m = blockIdx.y; m < M; m += gridDim.y) {
-    const uint16_t* xr = x + (size_t)m * K;
-    xq[(size_t)m * (K / 2) + idx] = (uint32_t)xr[flo] | ((uint32_t)xr[fhi] << 16);
-  }
-}
 
 struct GemmArgs {
   const uint16_t* xq;
@@ -184,11 +163,7 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, void* ws, hipStream_t stream) {
   uint32_t* xq = reinterpret_cast<uint32_t*>(ws);
-  const int pairs = (L.K / kBlockRows) * kPairsPerBlock;
-  const int gy = M < 65535 ? M : 65535;
-  hipLaunchKernelGGL(gather_kernel, dim3((pairs + 255) / 256, gy, 1), dim3(256), 0, stream, x, perm, xq, M, L.K,
-                     runs);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, xq, nullptr, stream);
   if (e != hipSuccess) return e;
   GemmArgs a;
   a.xq = reinterpret_cast<const uint16_t*>(xq);

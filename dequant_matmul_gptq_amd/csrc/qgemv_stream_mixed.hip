@@ -1,0 +1,17 @@
+// Streaming decode kernels for mixed-width (EXL2) matrices.
+#include "qgemv_stream.hpp"
+
+namespace qlinear {
+namespace stream {
+
+constexpr unsigned kLowBits = (1u << 2) | (1u << 3);                            // ~2-3 bpw
+constexpr unsigned kMidBits = (1u << 3) | (1u << 4) | (1u << 5) | (1u << 6);   // ~3.5-5 bpw
+
+hipError_t launch_mixed(unsigned set, const StreamArgs& a, hipStream_t stream) {
+  if ((set & ~kLowBits) == 0) return launch_set_any_m<kLowBits>(a, stream);
+  if ((set & ~kMidBits) == 0) return launch_set_any_m<kMidBits>(a, stream);
+  return launch_set_any_m<kAllBits>(a, stream);
+}
+
+}  // namespace stream
+}  // namespace qlinear

@@ -85,28 +85,54 @@ struct Fmt {
 
 // Pair P of a block whose b words (one column) are w[0..B-1]; returns two
 // float16 values 1024 + code packed in a uint32 (low half = lower row).
+// `magic` is kMagic; kernels pass it in a VGPR so that a shift and one
+// v_and_or_b32 (mask in an SGPR, magic in a VGPR) expose a pair.
 template <int B, int P>
-__host__ __device__ __forceinline__ uint32_t extract_pair(const uint32_t* w) {
+__host__ __device__ __forceinline__ uint32_t extract_pair(const uint32_t* w, uint32_t magic) {
   using Fm = Fmt<B>;
   if constexpr (P < Fm::kRegular) {
     constexpr int t = P / Fm::F, i = P % Fm::F;
     if constexpr (i == 0) {
-      return (w[t] & Fm::kMask) | kMagic;
+      return (w[t] & Fm::kMask) | magic;
     } else {
-      return ((w[t] >> (B * i)) & Fm::kMask) | kMagic;
+      return ((w[t] >> (B * i)) & Fm::kMask) | magic;
     }
   } else if constexpr (B == 6) {
     constexpr int v = P - 12;
-    const uint32_t lo = (w[v] >> 12) & 0x000F000Fu;
-    const uint32_t hi = (w[4 + v / 2] >> (8 + 2 * (v % 2))) & 0x00300030u;
-    return lo | hi | kMagic;
+    const uint32_t lo = ((w[v] >> 12) & 0x000F000Fu) | magic;
+    return ((w[4 + v / 2] >> (8 + 2 * (v % 2))) & 0x00300030u) | lo;
   } else {
     static_assert(B == 3 || B == 5, "spare rows exist only for 3, 5 and 6 bits");
-    uint32_t r = kMagic | ((w[0] >> 15) & 0x00010001u);
+    uint32_t r = ((w[0] >> 15) & 0x00010001u) | magic;
 #pragma unroll
-    for (int k = 1; k < B; ++k) r |= (w[k] >> (15 - k)) & (0x00010001u << k);
+    for (int k = 1; k < B; ++k) r = ((w[k] >> (15 - k)) & (0x00010001u << k)) | r;
     return r;
   }
+}
+
+template <int B, int P>
+__host__ __device__ __forceinline__ uint32_t extract_pair(const uint32_t* w) {
+  return extract_pair<B, P>(w, kMagic);
+}
+
+// kMagic in a VGPR the compiler cannot fold back into a literal (VOP3 forms
+// such as v_and_or_b32 take no literal operand on this architecture).
+__device__ __forceinline__ uint32_t vgpr_magic() {
+  uint32_t v;
+  asm("v_mov_b32 %0, %1" : "=v"(v) : "i"(kMagic));
+  return v;
+}
+
+// Position (2 * pair + half) of block row r in the unpacking order of width b:
+// the inverse of pair_rows.
+__host__ __device__ __forceinline__ int pair_position(int b, int r) {
+  const int f = 16 / b;
+  if (r < 2 * f * b) {
+    const int t = r / (2 * f), u = r % (2 * f);
+    return 2 * (t * f + u % f) + u / f;
+  }
+  if (b == 6) return 2 * (12 + (r - 24) % 4) + (r - 24) / 4;
+  return 2 * 15 + (r - 30);
 }
 
 // Runtime-P dispatcher for the helper kernels (pack tests, dequant export).

@@ -15,8 +15,20 @@ hipError_t launch_unpack(const qlinear_layout& L, const Runs& runs, const uint32
 hipError_t launch_dequant(const qlinear_layout& L, const Runs& runs, const uint32_t* qweight,
                           const uint16_t* scales, const uint8_t* zeros, uint16_t* w, hipStream_t stream);
 
-// Decode layer (M <= 16). ws_acc: float [16][N], ws_cnt: uint32 per 256-column strip.
-size_t qgemv_workspace_bytes(int N);
+// Act-order gather into unpacking pair order: xq uint32 [M][K/32][16] (float16
+// pairs), optional xsum float [M][K/32] (sum of each block's 32 values).
+hipError_t launch_gather_pairs(const Runs& runs, const uint16_t* x, const int32_t* perm, int M, int K,
+                               uint32_t* xq, float* xsum, hipStream_t stream);
+
+// Decode layer (M <= 16). The workspace holds the gathered activations xq
+// uint32 [16][K/32][16] and the block sums xsum float [16][K/32]; it is
+// scratch (no initialization, contents not preserved).
+struct GemvWorkspace {
+  uint32_t* xq;
+  float* xsum;
+};
+size_t qgemv_workspace_bytes(int K);
+GemvWorkspace qgemv_workspace(void* ws, int K);
 hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, void* ws, hipStream_t stream);

@@ -128,12 +128,11 @@ int qlinear_dequant(const qlinear_layout* layout, const uint32_t* qweight, const
                     const uint8_t* zeros, uint16_t* w, void* stream);
 
 /*
- * Workspace of qlinear_qgemv, in bytes, for any M <= QLINEAR_GEMV_MAX_M.
- * The workspace holds float32 partial sums and per-column-strip arrival
- * counters. It must be zero-filled once before its first use; every call
- * that completes leaves it zero-filled again, so it can be reused by later
- * calls on the same stream. Calls that may overlap in time (different
- * streams) must not share one workspace.
+ * Workspace of qlinear_qgemv, in bytes, for any M <= QLINEAR_GEMV_MAX_M. It
+ * receives the act-order-gathered activations and their 32-row block sums.
+ * It is scratch: no initialization is needed and its contents are not
+ * preserved. Calls that may overlap in time (different streams) must not
+ * share one workspace.
  */
 int qlinear_qgemv_workspace_bytes(const qlinear_layout* layout, size_t* bytes);
 

@@ -39,7 +39,21 @@ static void probe(uint32_t seed, int ncols) {
   }
 }
 
+static int check_positions() {
+  const int bs[6] = {2, 3, 4, 5, 6, 8};
+  int bad = 0;
+  for (int b : bs)
+    for (int p = 0; p < kPairsPerBlock; ++p) {
+      int lo, hi;
+      pair_rows(b, p, lo, hi);
+      if (pair_position(b, lo) != 2 * p || pair_position(b, hi) != 2 * p + 1) ++bad;
+    }
+  std::printf("POSBAD %d\n", bad);
+  return bad;
+}
+
 int main() {
+  check_positions();
   probe<2>(1u, 4);
   probe<3>(2u, 4);
   probe<4>(3u, 4);

@@ -157,6 +157,6 @@ def test_pack_unpack_dequant_validation():
 
 def test_workspace_sizes():
     L = _layout(N=4096, K=4096, gs=128)
-    # float32 [16][N] partial sums + one counter per 256-column strip, 256-byte rounded
-    assert dq.qgemv_workspace_bytes(L) == (16 * 4096 * 4 + 16 * 4 + 255) // 256 * 256
+    # gathered activations float16 [16][K] + block sums float [16][K/32], 256-byte rounded
+    assert dq.qgemv_workspace_bytes(L) == 16 * 4096 * 2 + 16 * 128 * 4
     assert dq.qgemm_workspace_bytes(L, 2048) == 2048 * 4096 * 2

@@ -28,7 +28,7 @@ def probe_output(tmp_path_factory):
 
 
 def _records(text):
-    lines = text.strip().splitlines()
+    lines = [l for l in text.strip().splitlines() if not l.startswith("POSBAD")]
     for i in range(0, len(lines), 4):
         b = int(lines[i].split()[1])
         codes = np.array([int(v) for v in lines[i + 1].split()[1:]], np.uint8)
@@ -53,3 +53,8 @@ def test_kernel_pairs_cover_every_row_once(probe_output):
         for lo, hi, v in pairs:
             assert v & 0xFFFF == 0x6400 + int(q[lo]) and v >> 16 == 0x6400 + int(q[hi]), (b, lo, hi, hex(v))
             assert q[lo] == codes[lo] and q[hi] == codes[hi]
+
+
+def test_pair_position_inverts_pair_rows(probe_output):
+    line = [l for l in probe_output.splitlines() if l.startswith("POSBAD")]
+    assert line == ["POSBAD 0"]

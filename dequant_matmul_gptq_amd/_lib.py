@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libqlinear.so")
 
 MAX_RUNS = 64
 GEMV_MAX_M = 16
+PANEL = 16
 
 OK = 0
 ERR_INVALID_ARGUMENT = 1
@@ -35,6 +36,8 @@ EXPORTS = (
     "qlinear_dequant",
     "qlinear_qgemv_workspace_bytes",
     "qlinear_qgemv",
+    "qlinear_qgemv_gather",
+    "qlinear_qgemv_apply",
     "qlinear_qgemm_workspace_bytes",
     "qlinear_qgemm",
 )
@@ -57,6 +60,7 @@ class qlinear_layout(ctypes.Structure):
         ("run_group", ctypes.c_int32 * (MAX_RUNS + 1)),
         ("run_row", ctypes.c_int32 * (MAX_RUNS + 1)),
         ("run_bits", ctypes.c_int32 * MAX_RUNS),
+        ("packed_words", ctypes.c_int64),
     ]
 
 
@@ -81,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.qlinear_dequant.argtypes = [lp, vp, vp, vp, vp, vp]
         L.qlinear_qgemv_workspace_bytes.argtypes = [lp, ctypes.POINTER(sz)]
         L.qlinear_qgemv.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.qlinear_qgemv_gather.argtypes = [lp, vp, i32, vp, vp, sz, vp]
+        L.qlinear_qgemv_apply.argtypes = [lp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.qlinear_qgemm_workspace_bytes.argtypes = [lp, i32, ctypes.POINTER(sz)]
         L.qlinear_qgemm.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTS[1:]:
@@ -130,6 +136,9 @@ class Layout:
         self.groups = int(self.c.groups)
         self.packed_rows = int(self.c.packed_rows)
         self.nruns = int(self.c.nruns)
+        self.panels = (self.N + PANEL - 1) // PANEL
+        # packed words in storage order: 16-column panels of packed_rows rows
+        self.qweight_shape = (self.panels, self.packed_rows, PANEL)
 
     @property
     def ref(self):
@@ -137,17 +146,17 @@ class Layout:
 
 
 def pack_weights(layout: Layout, q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """q uint8 [K][N] (stored order) -> packed int32 [packed_rows][N] (uint32 bit patterns)."""
+    """q uint8 [K][N] (stored order) -> packed int32 [ceil(N/16)][packed_rows][16] (uint32 bit patterns)."""
     _dev(q, "q", torch.uint8, (layout.K, layout.N))
     if out is None:
-        out = torch.empty((layout.packed_rows, layout.N), dtype=torch.int32, device=q.device)
-    _dev(out, "qweight", torch.int32, (layout.packed_rows, layout.N))
+        out = torch.empty(layout.qweight_shape, dtype=torch.int32, device=q.device)
+    _dev(out, "qweight", torch.int32, layout.qweight_shape)
     _check(lib().qlinear_pack_weights(layout.ref, _ptr(q), _ptr(out), _stream(q.device)), "qlinear_pack_weights")
     return out
 
 
 def unpack(layout: Layout, qweight: torch.Tensor) -> torch.Tensor:
-    _dev(qweight, "qweight", torch.int32, (layout.packed_rows, layout.N))
+    _dev(qweight, "qweight", torch.int32, layout.qweight_shape)
     q = torch.empty((layout.K, layout.N), dtype=torch.uint8, device=qweight.device)
     _check(lib().qlinear_unpack(layout.ref, _ptr(qweight), _ptr(q), _stream(q.device)), "qlinear_unpack")
     return q
@@ -155,7 +164,7 @@ def unpack(layout: Layout, qweight: torch.Tensor) -> torch.Tensor:
 
 def dequant(layout: Layout, qweight: torch.Tensor, scales: torch.Tensor,
             zeros: torch.Tensor | None) -> torch.Tensor:
-    _dev(qweight, "qweight", torch.int32, (layout.packed_rows, layout.N))
+    _dev(qweight, "qweight", torch.int32, layout.qweight_shape)
     _dev(scales, "scales", torch.float16, (layout.groups, layout.N))
     if zeros is not None:
         _dev(zeros, "zeros", torch.uint8, (layout.groups, layout.N))
@@ -187,7 +196,7 @@ def _gemm_operands(layout, x, qweight, scales, zeros, perm, y):
         raise ValueError(f"x must be [M][{layout.K}]")
     M = int(x.shape[0])
     _dev(x, "x", torch.float16)
-    _dev(qweight, "qweight", torch.int32, (layout.packed_rows, layout.N))
+    _dev(qweight, "qweight", torch.int32, layout.qweight_shape)
     _dev(scales, "scales", torch.float16, (layout.groups, layout.N))
     if zeros is not None:
         _dev(zeros, "zeros", torch.uint8, (layout.groups, layout.N))
@@ -207,6 +216,34 @@ def qgemv(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.
     _dev(workspace, "workspace", torch.uint8)
     _check(lib().qlinear_qgemv(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
                                _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemv")
+    return y
+
+
+def qgemv_gather(layout: Layout, x: torch.Tensor, perm: torch.Tensor | None, workspace: torch.Tensor) -> None:
+    """First phase of qgemv: gather x by act-order into the workspace."""
+    if x.dim() != 2 or x.shape[1] != layout.K:
+        raise ValueError(f"x must be [M][{layout.K}]")
+    _dev(x, "x", torch.float16)
+    if perm is not None:
+        _dev(perm, "perm", torch.int32, (layout.K,))
+    _dev(workspace, "workspace", torch.uint8)
+    _check(lib().qlinear_qgemv_gather(layout.ref, _ptr(x), int(x.shape[0]), _ptr(perm), _ptr(workspace),
+                                      workspace.numel(), _stream(x.device)), "qlinear_qgemv_gather")
+
+
+def qgemv_apply(layout: Layout, M: int, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor | None,
+                workspace: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """Second phase of qgemv: y from the gathered activations in the workspace."""
+    _dev(qweight, "qweight", torch.int32, layout.qweight_shape)
+    _dev(scales, "scales", torch.float16, (layout.groups, layout.N))
+    if zeros is not None:
+        _dev(zeros, "zeros", torch.uint8, (layout.groups, layout.N))
+    _dev(workspace, "workspace", torch.uint8)
+    if y is None:
+        y = torch.empty((M, layout.N), dtype=torch.float16, device=qweight.device)
+    _dev(y, "y", torch.float16, (M, layout.N))
+    _check(lib().qlinear_qgemv_apply(layout.ref, int(M), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y),
+                                     _ptr(workspace), workspace.numel(), _stream(y.device)), "qlinear_qgemv_apply")
     return y
 
 

@@ -2,8 +2,11 @@
 // the decode and prefill paths.
 //
 //   xq[m][blk][p]  = (x[m][perm[32*blk + lo(p)]], x[m][perm[32*blk + hi(p)]])
-//   xsum[m][blk]   = sum of the 32 gathered values of block blk (optional)
+//   xsum[m][blk]   = (sum of the block's 32 values, 1024 * sum of the
+//                     scaled values) (optional, decode path)
 //
+// In scaled mode (decode path) each pair is multiplied by 2^-e, e being the
+// exponent at which the decode kernel unpacks that pair's codes.
 // where (lo(p), hi(p)) are the rows that pair p of block blk unpacks to for
 // that block's code width. Inside each 32-row block the K order is thus the
 // order in which the weights come out of the packed words, so the weights
@@ -17,8 +20,8 @@ namespace {
 
 __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __restrict__ x,
                                                            const int32_t* __restrict__ perm,
-                                                           uint32_t* __restrict__ xq, float* __restrict__ xsum,
-                                                           int M, int K, Runs runs) {
+                                                           uint32_t* __restrict__ xq, float2* __restrict__ xsum,
+                                                           int M, int K, int scaled, Runs runs) {
   const int nblk = K / kBlockRows;
   const int pairs = nblk * kPairsPerBlock;
   const int idx = blockIdx.x * 256 + threadIdx.x;
@@ -32,15 +35,28 @@ __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __res
   // perm entries are clamped into [0, K): a malformed perm cannot address outside x.
   const int flo = perm ? (int)min((unsigned)perm[jlo], (unsigned)(K - 1)) : jlo;
   const int fhi = perm ? (int)min((unsigned)perm[jhi], (unsigned)(K - 1)) : jhi;
+  // Scaled mode: the pair is multiplied by 2^-e, the scale at which the decode
+  // kernel unpacks its codes (exact unless the value becomes subnormal).
+  const float sc = scaled ? __builtin_ldexpf(1.0f, -pair_exponent(bits, p)) : 1.0f;
   for (int m = blockIdx.y; m < M; m += gridDim.y) {
     const uint16_t* xr = x + (size_t)m * K;
-    const uint16_t vl = live ? xr[flo] : (uint16_t)0, vh = live ? xr[fhi] : (uint16_t)0;
-    if (live) xq[(size_t)m * pairs + idx] = (uint32_t)vl | ((uint32_t)vh << 16);
+    const _Float16 vl = live ? __builtin_bit_cast(_Float16, xr[flo]) : (_Float16)0.0f;
+    const _Float16 vh = live ? __builtin_bit_cast(_Float16, xr[fhi]) : (_Float16)0.0f;
+    const _Float16 sl = (_Float16)((float)vl * sc), sh = (_Float16)((float)vh * sc);
+    if (live)
+      xq[(size_t)m * pairs + idx] = (uint32_t)__builtin_bit_cast(uint16_t, sl) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, sh) << 16);
     if (xsum) {
-      float s = (float)__builtin_bit_cast(_Float16, vl) + (float)__builtin_bit_cast(_Float16, vh);
+      // X = sum of the block's activations; Bsum = 1024 * sum of the scaled
+      // activations, the bias the 1024 + q * 2^e pairs add to the dot products.
+      float X = (float)vl + (float)vh;
+      float Bs = (float)sl + (float)sh;
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 16);
-      if (live && p == 0) xsum[(size_t)m * nblk + blk] = s;
+      for (int off = 8; off > 0; off >>= 1) {
+        X += __shfl_xor(X, off, 16);
+        Bs += __shfl_xor(Bs, off, 16);
+      }
+      if (live && p == 0) xsum[(size_t)m * nblk + blk] = make_float2(X, 1024.0f * Bs);
     }
   }
 }
@@ -48,11 +64,11 @@ __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __res
 }  // namespace
 
 hipError_t launch_gather_pairs(const Runs& runs, const uint16_t* x, const int32_t* perm, int M, int K,
-                               uint32_t* xq, float* xsum, hipStream_t stream) {
+                               uint32_t* xq, float2* xsum, bool scaled, hipStream_t stream) {
   const int pairs = (K / kBlockRows) * kPairsPerBlock;
   const int gy = M < 65535 ? M : 65535;
   hipLaunchKernelGGL(gather_pairs_kernel, dim3((pairs + 255) / 256, gy, 1), dim3(256), 0, stream, x, perm, xq,
-                     xsum, M, K, runs);
+                     xsum, M, K, scaled ? 1 : 0, runs);
   return hipGetLastError();
 }
 

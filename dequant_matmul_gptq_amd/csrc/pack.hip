@@ -10,30 +10,33 @@ namespace {
 
 constexpr int kColsPerCta = 256;
 
+// n may lie past N, in the padding slots of the last panel: those words are 0.
 template <int B>
-__device__ void pack_block(const uint8_t* __restrict__ q, uint32_t* __restrict__ qweight, int N,
+__device__ void pack_block(const uint8_t* __restrict__ q, uint32_t* __restrict__ qweight, int N, int R,
                            int blk, int row, int n) {
   uint32_t w[B];
 #pragma unroll
   for (int t = 0; t < B; ++t) w[t] = 0u;
-  const uint8_t* src = q + (size_t)blk * kBlockRows * N + n;
+  if (n < N) {
+    const uint8_t* src = q + (size_t)blk * kBlockRows * N + n;
 #pragma unroll
-  for (int r = 0; r < kBlockRows; ++r) place_code<B>(w, r, src[(size_t)r * N]);
+    for (int r = 0; r < kBlockRows; ++r) place_code<B>(w, r, src[(size_t)r * N]);
+  }
 #pragma unroll
-  for (int t = 0; t < B; ++t) qweight[(size_t)(row + t) * N + n] = w[t];
+  for (int t = 0; t < B; ++t) qweight[word_index(R, row + t, n)] = w[t];
 }
 
 template <int B>
-__device__ void load_block(const uint32_t* __restrict__ qweight, int N, int row, int n, uint32_t* w) {
+__device__ void load_block(const uint32_t* __restrict__ qweight, int R, int row, int n, uint32_t* w) {
 #pragma unroll
-  for (int t = 0; t < B; ++t) w[t] = qweight[(size_t)(row + t) * N + n];
+  for (int t = 0; t < B; ++t) w[t] = qweight[word_index(R, row + t, n)];
 }
 
 template <int B>
-__device__ void unpack_block(const uint32_t* __restrict__ qweight, uint8_t* __restrict__ q, int N,
+__device__ void unpack_block(const uint32_t* __restrict__ qweight, uint8_t* __restrict__ q, int N, int R,
                              int blk, int row, int n) {
   uint32_t w[B], pr[kPairsPerBlock];
-  load_block<B>(qweight, N, row, n, w);
+  load_block<B>(qweight, R, row, n, w);
   extract_all_pairs<B>(w, pr);
   uint8_t* dst = q + (size_t)blk * kBlockRows * N + n;
 #pragma unroll
@@ -47,10 +50,10 @@ __device__ void unpack_block(const uint32_t* __restrict__ qweight, uint8_t* __re
 
 template <int B>
 __device__ void dequant_block(const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
-                              const uint8_t* __restrict__ zeros, uint16_t* __restrict__ wout, int N,
+                              const uint8_t* __restrict__ zeros, uint16_t* __restrict__ wout, int N, int R,
                               int blk, int row, int g, int n) {
   uint32_t w[B], pr[kPairsPerBlock];
-  load_block<B>(qweight, N, row, n, w);
+  load_block<B>(qweight, R, row, n, w);
   extract_all_pairs<B>(w, pr);
   const uint16_t sbits = scales[(size_t)g * N + n];
   const int z = zeros ? (int)zeros[(size_t)g * N + n] : (1 << (B - 1));
@@ -73,16 +76,17 @@ __global__ __launch_bounds__(kColsPerCta) void pack_kernel(const uint8_t* __rest
                                                            Runs runs) {
   const int n = blockIdx.x * kColsPerCta + threadIdx.x;
   const int blk = blockIdx.y;
-  if (n >= N) return;
+  if (n >= (N + kPanel - 1) / kPanel * kPanel) return;
+  const int R = runs.packed_rows;
   int bits, row;
   block_info(runs, blk, bits, row);
   switch (bits) {
-    case 2: pack_block<2>(q, qweight, N, blk, row, n); break;
-    case 3: pack_block<3>(q, qweight, N, blk, row, n); break;
-    case 4: pack_block<4>(q, qweight, N, blk, row, n); break;
-    case 5: pack_block<5>(q, qweight, N, blk, row, n); break;
-    case 6: pack_block<6>(q, qweight, N, blk, row, n); break;
-    case 8: pack_block<8>(q, qweight, N, blk, row, n); break;
+    case 2: pack_block<2>(q, qweight, N, R, blk, row, n); break;
+    case 3: pack_block<3>(q, qweight, N, R, blk, row, n); break;
+    case 4: pack_block<4>(q, qweight, N, R, blk, row, n); break;
+    case 5: pack_block<5>(q, qweight, N, R, blk, row, n); break;
+    case 6: pack_block<6>(q, qweight, N, R, blk, row, n); break;
+    case 8: pack_block<8>(q, qweight, N, R, blk, row, n); break;
     default: break;
   }
 }
@@ -92,15 +96,16 @@ __global__ __launch_bounds__(kColsPerCta) void unpack_kernel(const uint32_t* __r
   const int n = blockIdx.x * kColsPerCta + threadIdx.x;
   const int blk = blockIdx.y;
   if (n >= N) return;
+  const int R = runs.packed_rows;
   int bits, row;
   block_info(runs, blk, bits, row);
   switch (bits) {
-    case 2: unpack_block<2>(qweight, q, N, blk, row, n); break;
-    case 3: unpack_block<3>(qweight, q, N, blk, row, n); break;
-    case 4: unpack_block<4>(qweight, q, N, blk, row, n); break;
-    case 5: unpack_block<5>(qweight, q, N, blk, row, n); break;
-    case 6: unpack_block<6>(qweight, q, N, blk, row, n); break;
-    case 8: unpack_block<8>(qweight, q, N, blk, row, n); break;
+    case 2: unpack_block<2>(qweight, q, N, R, blk, row, n); break;
+    case 3: unpack_block<3>(qweight, q, N, R, blk, row, n); break;
+    case 4: unpack_block<4>(qweight, q, N, R, blk, row, n); break;
+    case 5: unpack_block<5>(qweight, q, N, R, blk, row, n); break;
+    case 6: unpack_block<6>(qweight, q, N, R, blk, row, n); break;
+    case 8: unpack_block<8>(qweight, q, N, R, blk, row, n); break;
     default: break;
   }
 }
@@ -112,22 +117,24 @@ __global__ __launch_bounds__(kColsPerCta) void dequant_kernel(const uint32_t* __
   const int n = blockIdx.x * kColsPerCta + threadIdx.x;
   const int blk = blockIdx.y;
   if (n >= N) return;
+  const int R = runs.packed_rows;
   int bits, row;
   block_info(runs, blk, bits, row);
   const int g = blk / runs.blocks_per_group;
   switch (bits) {
-    case 2: dequant_block<2>(qweight, scales, zeros, w, N, blk, row, g, n); break;
-    case 3: dequant_block<3>(qweight, scales, zeros, w, N, blk, row, g, n); break;
-    case 4: dequant_block<4>(qweight, scales, zeros, w, N, blk, row, g, n); break;
-    case 5: dequant_block<5>(qweight, scales, zeros, w, N, blk, row, g, n); break;
-    case 6: dequant_block<6>(qweight, scales, zeros, w, N, blk, row, g, n); break;
-    case 8: dequant_block<8>(qweight, scales, zeros, w, N, blk, row, g, n); break;
+    case 2: dequant_block<2>(qweight, scales, zeros, w, N, R, blk, row, g, n); break;
+    case 3: dequant_block<3>(qweight, scales, zeros, w, N, R, blk, row, g, n); break;
+    case 4: dequant_block<4>(qweight, scales, zeros, w, N, R, blk, row, g, n); break;
+    case 5: dequant_block<5>(qweight, scales, zeros, w, N, R, blk, row, g, n); break;
+    case 6: dequant_block<6>(qweight, scales, zeros, w, N, R, blk, row, g, n); break;
+    case 8: dequant_block<8>(qweight, scales, zeros, w, N, R, blk, row, g, n); break;
     default: break;
   }
 }
 
 dim3 matrix_grid(const qlinear_layout& L) {
-  return dim3((unsigned)((L.N + kColsPerCta - 1) / kColsPerCta), (unsigned)(L.K / kBlockRows), 1);
+  const int n16 = (L.N + kPanel - 1) / kPanel * kPanel;   // padded columns are packed as zeros
+  return dim3((unsigned)((n16 + kColsPerCta - 1) / kColsPerCta), (unsigned)(L.K / kBlockRows), 1);
 }
 
 }  // namespace

@@ -38,7 +38,7 @@ __device__ __forceinline__ void dequant_to_lds(const GemmArgs& a, int row, int g
                                                uint32_t* dst /* 16 words */) {
   uint32_t w[B];
 #pragma unroll
-  for (int t = 0; t < B; ++t) w[t] = valid ? a.qweight[(size_t)(row + t) * a.N + n] : 0u;
+  for (int t = 0; t < B; ++t) w[t] = valid ? a.qweight[word_index(a.runs.packed_rows, row + t, n)] : 0u;
   _Float16 s = (_Float16)0.0f;
   int z = 1 << (B - 1);
   if (valid) {
@@ -163,7 +163,7 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, void* ws, hipStream_t stream) {
   uint32_t* xq = reinterpret_cast<uint32_t*>(ws);
-  hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, xq, nullptr, stream);
+  hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, xq, nullptr, false, stream);
   if (e != hipSuccess) return e;
   GemmArgs a;
   a.xq = reinterpret_cast<const uint16_t*>(xq);

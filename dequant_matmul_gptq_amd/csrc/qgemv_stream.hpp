@@ -1,29 +1,35 @@
 // Decode-sized quantized linear layer (M <= 16) on gfx950: one pass over the
 // packed weights at HBM speed, with no cross-workgroup reduction.
 //
-// Work split. A 256-thread workgroup owns a strip of 16 output columns and
-// the whole K range, so it writes its float16 outputs directly: no split-K,
-// no atomics, no workspace. Inside a wave, lane = (block slot ks, column quad
-// cq): 4 column quads x 16 block slots. Each lane unpacks whole 32-row blocks
-// of its 4 columns, streaming the block's b words with b 16-byte loads; a wave
+// Work split. A 256-thread workgroup owns a strip of 16 output columns -- one
+// storage panel, whose packed rows are contiguous in memory -- and the whole
+// K range, so it writes its float16 outputs directly: no split-K,
+// no atomics. Inside a wave, lane = (block slot ks, column quad cq):
+// 4 column quads x 16 block slots. Each lane unpacks whole 32-row blocks of
+// its 4 columns, streaming the block's b words with b 16-byte loads; a wave
 // step covers 16 consecutive blocks of one run (uniform bit width). The 4
-// waves take contiguous quarters of K, and the two steps ahead of the one
-// being computed are in flight (double buffering).
+// waves take contiguous quarters of K; the step after the one being computed
+// is in flight (double buffering), and the first step is issued before the
+// activations are staged, so its HBM latency overlaps the staging.
 //
 // Strips are assigned XCD by XCD: workgroups are dispatched round-robin over
 // the 8 XCDs, so workgroup i is given a strip from XCD (i % 8)'s contiguous
-// range. The two 16-column strips that share each 128-byte line of a packed
-// row are then read through the same L2.
+// range; neighbouring strips share the lines of the scale rows.
 //
-// Arithmetic per block and column is that of the split-K decode kernel:
-//   acc = sum_pairs dot2((1024 + q_lo, 1024 + q_hi), (x_lo, x_hi))
-//   y  += s * (acc - (1024 + z) * X_blk)
-// The activations are gathered by act-order into unpacking pair order once per
-// call by the shared gather kernel (with the block sums X_blk); each
-// workgroup copies them into LDS with 16-byte loads (in chunks when M * K is
-// large).
-// Reduction: butterfly shuffles across the 16 block slots of a wave, then
-// the 4 waves through LDS.
+// Arithmetic per block, column and activation row. The codes come out of the
+// packed words as float16 pairs 1024 + q * 2^e (mask in place; one shift per
+// word for the fields above bit 10), the activations were gathered by
+// act-order and pre-scaled by 2^-e by the gather kernel, and
+//   acc = sum_pairs dot2((1024 + q_lo 2^e, 1024 + q_hi 2^e), (x_lo 2^-e, x_hi 2^-e))
+//       = sum_j x_j q_j + 1024 * X'_blk
+//   y  += s * (acc - 1024 * X'_blk - z * X_blk)
+// where X_blk and 1024 * X'_blk are the block sums the gather kernel wrote.
+// Products of float16 values are exact in float32; accumulation is float32.
+//
+// Each wave copies the activations of its own K range from the workspace
+// into LDS (16-byte copies; in chunks when M * K is large). Reduction:
+// butterfly shuffles across the 16 block slots of a wave, then across the 4
+// waves through LDS.
 #pragma once
 
 #include "qlinear_kernels.hpp"
@@ -32,8 +38,7 @@ namespace qlinear {
 
 namespace stream {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kMaxWaves = 8;           // waves per workgroup: 4 or 8 (they split K)
 constexpr int CQ = 4;                  // column quads per strip
 constexpr int SC = 4 * CQ;             // 16 columns per workgroup
 constexpr int KS = 64 / CQ;            // 16 blocks per wave step
@@ -41,15 +46,16 @@ constexpr int kXcds = 8;
 constexpr int kStageBudget = 60 * 1024;  // bytes of LDS for staged activations
 
 struct StreamArgs {
-  const uint32_t* xq;      // gathered activations, [M][K/32][16] float16 pairs
-  const float* xsum;       // block sums, [M][K/32]
+  const uint32_t* xq;      // gathered, scaled activations, [M][K/32][16] float16 pairs
+  const float2* xsum;      // block sums (X, 1024 * X'), [M][K/32]
   const uint32_t* qweight;
   const uint16_t* scales;
   const uint8_t* zeros;
   uint16_t* y;
   int M, K, N;
   int nstrips, strips_per_xcd;
-  int chunk;                             // blocks per wave staged at a time
+  int chunk;               // blocks per wave staged at a time
+  int bpg_shift;           // log2(group_size / 32)
   Runs runs;
 };
 
@@ -71,35 +77,44 @@ __device__ __forceinline__ float half_hi(uint32_t v) {
 struct Raw {
   uint2 s;      // 4 float16 scales
   uint32_t z;   // 4 uint8 zero points
+  bool ok;      // false: the lane has no block this step (contributes nothing)
 };
 
-// One wave step: its 16 blocks start at block `blk0` and packed row `row0`
-// (blocks of one run, b rows apart); `nb` of them are real.
-struct Step {
-  int blk0, row0, nb;
-};
-
+// Loads of one lane for one step: the b words of block `blk` (packed row
+// `row`) for its 4 columns, and that block's group scales and zeros.
+// `panel` points at the lane's 4 slots in row 0 of this workgroup's panel
+// (the rows of a panel are 16 words apart); `scol` is the lane's first
+// column, clamped into the matrix for the scale and zero reads.
+// Every load is issued unconditionally, so that the compiler can count the
+// loads in flight exactly (a branch around a load makes it wait for all of
+// them). A lane without work (ok == false) reads the valid block `blk_safe`
+// at `row_safe` instead and gets a zero scale, which zeroes its contribution.
 template <int B>
-__device__ __forceinline__ void issue(const StreamArgs& a, const Step& st, int ks, int col, bool colv,
-                                      int bpg, uint4 (&W)[B], Raw& P) {
-  const bool ok = colv && ks < st.nb;
-  const int row = st.row0 + ks * B;
+__device__ __forceinline__ void issue(const StreamArgs& a, const uint32_t* panel, int blk, int row, bool ok,
+                                      int blk_safe, int row_safe, int scol, uint4 (&W)[B], Raw& P) {
+  const uint32_t* p = panel + (size_t)(ok ? row : row_safe) * kPanel;
 #pragma unroll
-  for (int t = 0; t < B; ++t)
-    W[t] = ok ? *reinterpret_cast<const uint4*>(a.qweight + (size_t)(row + t) * a.N + col)
-              : make_uint4(0u, 0u, 0u, 0u);
-  const int g = (st.blk0 + ks) / bpg;
-  P.s = ok ? *reinterpret_cast<const uint2*>(a.scales + (size_t)g * a.N + col) : make_uint2(0u, 0u);
-  P.z = (ok && a.zeros) ? *reinterpret_cast<const uint32_t*>(a.zeros + (size_t)g * a.N + col) : 0u;
+  for (int t = 0; t < B; ++t) W[t] = *reinterpret_cast<const uint4*>(p + t * kPanel);
+  const size_t g = (size_t)((ok ? blk : blk_safe) >> a.bpg_shift) * a.N + scol;
+  const uint2 sv = *reinterpret_cast<const uint2*>(a.scales + g);
+  // Without zero points, read the scales again (any valid address): the value
+  // is not used.
+  const uint8_t* zp = a.zeros ? a.zeros : reinterpret_cast<const uint8_t*>(a.scales);
+  const uint32_t zv = *reinterpret_cast<const uint32_t*>(zp + g);
+  P.s = sv;
+  P.z = zv;
+  P.ok = ok;
 }
 
 // Unpack and multiply one block (this lane's 4 columns), then fold in the
-// block's scale and zero point.
+// block's scale, zero point and bias. xs_blk points at pair 0 of the block for
+// activation row 0; rows are `row_stride` words apart. xs_sum likewise.
 template <int B, int MT>
 __device__ __forceinline__ void compute(const StreamArgs& a, const uint4 (&W)[B], const Raw& P,
-                                        const uint32_t* __restrict__ xs_blk, const float* __restrict__ xsum_blk,
-                                        uint32_t magic, float (&yacc)[4][MT]) {
-  uint32_t wc[4][B];
+                                        const uint32_t* __restrict__ xs_blk, int row_stride,
+                                        const float2* __restrict__ xsum_blk, int sum_stride, uint32_t magic,
+                                        float (&yacc)[4][MT]) {
+  uint32_t wc[4][B], wsh[4][B];
 #pragma unroll
   for (int t = 0; t < B; ++t) {
     wc[0][t] = W[t].x;
@@ -107,6 +122,10 @@ __device__ __forceinline__ void compute(const StreamArgs& a, const uint4 (&W)[B]
     wc[2][t] = W[t].z;
     wc[3][t] = W[t].w;
   }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int t = 0; t < B; ++t) wsh[c][t] = wc[c][t] >> scaled_shift(B);
   float acc[4][MT];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -117,13 +136,13 @@ __device__ __forceinline__ void compute(const StreamArgs& a, const uint4 (&W)[B]
     constexpr int q4 = decltype(Q)::value;
     uint4 xv[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) xv[m] = *reinterpret_cast<const uint4*>(xs_blk + m * kPairsPerBlock + 4 * q4);
+    for (int m = 0; m < MT; ++m) xv[m] = *reinterpret_cast<const uint4*>(xs_blk + m * row_stride + 4 * q4);
     static_for<0, 4>([&](auto R) {
       constexpr int r = decltype(R)::value;
       constexpr int Pp = 4 * q4 + r;
       uint32_t v[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] = extract_pair<B, Pp>(wc[c], magic);
+      for (int c = 0; c < 4; ++c) v[c] = extract_pair_scaled<B, Pp>(wc[c], wsh[c], magic);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const uint32_t xp = r == 0 ? xv[m].x : r == 1 ? xv[m].y : r == 2 ? xv[m].z : xv[m].w;
@@ -134,72 +153,69 @@ __device__ __forceinline__ void compute(const StreamArgs& a, const uint4 (&W)[B]
     });
   });
 
-  float s[4], zb[4];
-  s[0] = half_lo(P.s.x);
-  s[1] = half_hi(P.s.x);
-  s[2] = half_lo(P.s.y);
-  s[3] = half_hi(P.s.y);
+  float s[4], z[4];
+  s[0] = P.ok ? half_lo(P.s.x) : 0.0f;
+  s[1] = P.ok ? half_hi(P.s.x) : 0.0f;
+  s[2] = P.ok ? half_lo(P.s.y) : 0.0f;
+  s[3] = P.ok ? half_hi(P.s.y) : 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    zb[c] = 1024.0f + (a.zeros ? (float)((P.z >> (8 * c)) & 0xFFu) : (float)(1 << (B - 1)));
+  for (int c = 0; c < 4; ++c) z[c] = a.zeros ? (float)((P.z >> (8 * c)) & 0xFFu) : (float)(1 << (B - 1));
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const float X = xsum_blk[m];
+    const float2 X = xsum_blk[m * sum_stride];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) yacc[c][m] = fmaf(s[c], fmaf(-zb[c], X, acc[c][m]), yacc[c][m]);
+    for (int c = 0; c < 4; ++c) yacc[c][m] = fmaf(s[c], fmaf(-z[c], X.x, acc[c][m] - X.y), yacc[c][m]);
   }
 }
 
 // All steps of one run segment [blk0, blk1) of this wave, double-buffered
-// (8-bit runs single-buffered, to bound register use). Blocks are at LDS slot
-// (blk - lds_blk0) of this wave's staging area. With kPre, the first step's
-// words and parameters are already in Wa / Pa.
+// (8-bit runs single-buffered, to bound register use). The segment's first
+// packed row is row0. The staged activations of block blk sit at LDS slot
+// blk - lds_blk0 of this wave's area. With kPre, the first step's words and
+// parameters are already in Wa / Pa.
 template <int B, int MT, bool kPre>
-__device__ __forceinline__ void run_segment(const StreamArgs& a, int blk0, int blk1, int row0, int ks, int col,
-                                            bool colv, const uint32_t* xs_w, const float* xsum_w, int lds_blk0,
+__device__ __forceinline__ void run_segment(const StreamArgs& a, int blk0, int blk1, int row0, int ks,
+                                            const uint32_t* panel, int col, bool colv, const uint32_t* xs_w, const float2* xsum_w, int lds_blk0,
                                             uint32_t magic, float (&yacc)[4][MT], uint4 (&Wa)[B], Raw& Pa) {
-  const int bpg = a.runs.blocks_per_group;
   const int nsteps = (blk1 - blk0 + KS - 1) / KS;
-  auto step_of = [&](int i) {
-    Step st;
-    st.blk0 = blk0 + i * KS;
-    st.row0 = row0 + i * KS * B;
-    st.nb = min(KS, blk1 - st.blk0);
-    return st;
+  auto lane_issue = [&](int i, uint4 (&W)[B], Raw& P) {
+    const int blk = blk0 + i * KS + ks;
+    issue<B>(a, panel, blk, row0 + (i * KS + ks) * B, colv && blk < blk1, blk0, row0, col, W, P);
   };
-  auto lane_compute = [&](const Step& st, const uint4 (&W)[B], const Raw& P) {
-    const int bl = min(st.blk0 + ks, blk1 - 1) - lds_blk0;   // clamped: idle lanes hold zeros
-    compute<B, MT>(a, W, P, xs_w + bl * MT * kPairsPerBlock, xsum_w + bl * MT, magic, yacc);
+  auto lane_compute = [&](int i, const uint4 (&W)[B], const Raw& P) {
+    const int bl = min(blk0 + i * KS + ks, blk1 - 1) - lds_blk0;   // clamped: idle lanes hold zeros
+    compute<B, MT>(a, W, P, xs_w + bl * kPairsPerBlock, a.chunk * kPairsPerBlock, xsum_w + bl, a.chunk, magic,
+                   yacc);
   };
-  if constexpr (!kPre) issue<B>(a, step_of(0), ks, col, colv, bpg, Wa, Pa);
+  if constexpr (!kPre) lane_issue(0, Wa, Pa);
   if constexpr (B == 8) {
     for (int i = 0; i < nsteps; ++i) {
-      if (i > 0) issue<B>(a, step_of(i), ks, col, colv, bpg, Wa, Pa);
-      lane_compute(step_of(i), Wa, Pa);
+      if (i > 0) lane_issue(i, Wa, Pa);
+      lane_compute(i, Wa, Pa);
     }
   } else {
     uint4 Wb[B];
     Raw Pb;
     for (int i = 0; i < nsteps; i += 2) {
-      if (i + 1 < nsteps) issue<B>(a, step_of(i + 1), ks, col, colv, bpg, Wb, Pb);
-      lane_compute(step_of(i), Wa, Pa);
+      if (i + 1 < nsteps) lane_issue(i + 1, Wb, Pb);
+      lane_compute(i, Wa, Pa);
       if (i + 1 >= nsteps) break;
-      if (i + 2 < nsteps) issue<B>(a, step_of(i + 2), ks, col, colv, bpg, Wa, Pa);
-      lane_compute(step_of(i + 1), Wb, Pb);
+      if (i + 2 < nsteps) lane_issue(i + 2, Wa, Pa);
+      lane_compute(i + 1, Wb, Pb);
     }
   }
 }
 
 template <int MT, unsigned BS>
 __device__ __forceinline__ void any_segment(const StreamArgs& a, int bits, int blk0, int blk1, int row0, int ks,
-                                            int col, bool colv, const uint32_t* xs_w, const float* xsum_w,
+                                            const uint32_t* panel, int col, bool colv, const uint32_t* xs_w, const float2* xsum_w,
                                             int lds_blk0, uint32_t magic, float (&yacc)[4][MT]) {
 #define QLINEAR_SEGMENT(BB)                                                                                \
   case BB:                                                                                                 \
     if constexpr ((BS >> BB) & 1u) {                                                                       \
       uint4 W[BB];                                                                                         \
       Raw P;                                                                                               \
-      run_segment<BB, MT, false>(a, blk0, blk1, row0, ks, col, colv, xs_w, xsum_w, lds_blk0, magic, yacc, W, P); \
+      run_segment<BB, MT, false>(a, blk0, blk1, row0, ks, panel, col, colv, xs_w, xsum_w, lds_blk0, magic, yacc, W, P); \
     }                                                                                                      \
     break;
   switch (bits) {
@@ -214,34 +230,44 @@ __device__ __forceinline__ void any_segment(const StreamArgs& a, int bits, int b
 #undef QLINEAR_SEGMENT
 }
 
+// 32-bit words of one wave's staging area for `chunk` blocks (16-byte aligned).
+template <int MT>
+__host__ __device__ constexpr int stage_words(int chunk) {
+  return (chunk * MT * (kPairsPerBlock + 2) + 3) / 4 * 4;
+}
+
 // Kernel body, specialised on B0, the width of this wave's first run, so the
-// first step can be issued into a typed buffer before the activation staging
-// and its HBM latency overlaps the act-order gather.
-template <int MT, unsigned BS, int B0>
-__device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, float (&red)[kWaves][MT][SC],
-                                            int tid, int lane, int wave, int strip, int wb0, int wb1,
-                                            int row0) {
+// first step can be issued into a typed buffer before the activation staging.
+template <int MT, unsigned BS, int WV, int B0>
+__device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, float (&red)[WV][MT][SC],
+                                            int tid, int lane, int wave, int strip, int wb0, int wb1, int row0) {
   const int cq = lane % CQ, ks = lane / CQ;
-  const int col = strip * SC + cq * 4;
-  const bool colv = col < a.N;
+  const int col_req = strip * SC + cq * 4;
+  const bool colv = col_req < a.N;
+  const int col = colv ? col_req : a.N - 4;   // scale/zero column for lanes past N
+  // The lane's 4 word slots in row 0 of this strip's panel (padding slots of
+  // the last panel exist and hold zeros).
+  const uint32_t* panel = a.qweight + (size_t)strip * a.runs.packed_rows * kPanel + cq * 4;
   const int nblk = a.K / kBlockRows;
-  const int per_wave = (nblk + kWaves - 1) / kWaves;
+  const int per_wave = (nblk + WV - 1) / WV;
   const int nchunks = (per_wave + a.chunk - 1) / a.chunk;
   const uint32_t magic = vgpr_magic();
 
-  // LDS: per wave, `chunk` blocks of MT x 16 float16 pairs, then the block sums.
-  uint32_t* xs = lds;                                                                     // [kWaves][chunk][MT][16]
-  float* xsum = reinterpret_cast<float*>(lds + kWaves * a.chunk * MT * kPairsPerBlock);  // [kWaves][chunk][MT]
+  // This wave's LDS area: [MT][chunk][16] float16 pairs, then [MT][chunk] sums,
+  // rounded up to 16 bytes.
+  const int area = stage_words<MT>(a.chunk);
+  uint32_t* xs_w = lds + wave * area;
+  float2* xsum_w = reinterpret_cast<float2*>(xs_w + a.chunk * MT * kPairsPerBlock);
 
   uint4 W0[B0];
   Raw P0;
   const int seg0_end = wb0 < wb1 ? min(min(wb1, run_end_block(a.runs, wb0)), wb0 + a.chunk) : wb0;
-  if (wb0 < wb1) {
-    Step st;
-    st.blk0 = wb0;
-    st.row0 = row0;
-    st.nb = min(KS, seg0_end - wb0);
-    issue<B0>(a, st, ks, col, colv, a.runs.blocks_per_group, W0, P0);
+  {
+    // A wave without blocks (K < 128 rows) reads block 0 and discards it.
+    const int blk = wb0 + ks;
+    const bool any = wb0 < wb1;
+    issue<B0>(a, panel, blk, row0 + ks * B0, any && colv && blk < seg0_end, any ? wb0 : 0, any ? row0 : 0, col, W0,
+              P0);
   }
 
   float yacc[4][MT];
@@ -251,58 +277,51 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, 
     for (int m = 0; m < MT; ++m) yacc[c][m] = 0.0f;
 
   for (int ch = 0; ch < nchunks; ++ch) {
-    if (ch > 0) __syncthreads();  // every wave is done with the previous chunk
-    // Stage chunk ch of every wave from the gathered activations: contiguous
-    // 16-byte copies, eight in flight per thread.
-    {
-      const int per_w = a.chunk * MT * (kPairsPerBlock / 4);   // uint4 items per wave
-      const int items = kWaves * per_w;
-      constexpr int U = 8;
-      for (int base = tid; base < items; base += U * kThreads) {
-        uint4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int it = base + u * kThreads;
-          v[u] = make_uint4(0u, 0u, 0u, 0u);
-          if (it < items) {
-            const int w = it / per_w, rem = it % per_w;
-            const int bl = rem / (MT * 4), m = (rem / 4) % MT, q4 = rem % 4;
-            const int blk = (w * nblk) / kWaves + ch * a.chunk + bl;
-            if (m < a.M && blk < ((w + 1) * nblk) / kWaves)
-              v[u] = *reinterpret_cast<const uint4*>(a.xq + ((size_t)m * nblk + blk) * kPairsPerBlock + 4 * q4);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int it = base + u * kThreads;
-          if (it < items) *reinterpret_cast<uint4*>(xs + 4 * it) = v[u];
-        }
-      }
-      for (int it = tid; it < kWaves * a.chunk * MT; it += kThreads) {
-        const int w = it / (a.chunk * MT), rem = it % (a.chunk * MT);
-        const int bl = rem / MT, m = rem % MT;
-        const int blk = (w * nblk) / kWaves + ch * a.chunk + bl;
-        float v = 0.0f;
-        if (m < a.M && blk < ((w + 1) * nblk) / kWaves) v = a.xsum[(size_t)m * nblk + blk];
-        xsum[it] = v;
-      }
-      __syncthreads();
-    }
-
     const int c0 = wb0 + ch * a.chunk;
     const int c1 = min(wb1, c0 + a.chunk);
-    const uint32_t* xs_w = xs + wave * a.chunk * MT * kPairsPerBlock;
-    const float* xsum_w = xsum + wave * a.chunk * MT;
+    const int nb = c1 > c0 ? c1 - c0 : 0;
+    if (ch > 0) __syncthreads();  // every wave is done with its previous chunk
+    // Copy this wave's chunk of gathered activations and block sums to LDS,
+    // eight 16-byte loads in flight per lane (unconditional loads from
+    // clamped indices, wave-uniform trip count).
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m >= a.M) break;
+      const int mm = m;
+      const uint4* src = reinterpret_cast<const uint4*>(a.xq + ((size_t)mm * nblk + (nb > 0 ? c0 : 0)) * kPairsPerBlock);
+      uint4* dst = reinterpret_cast<uint4*>(xs_w + mm * a.chunk * kPairsPerBlock);
+      const int n4 = nb * (kPairsPerBlock / 4);
+      constexpr int U = 8;
+      const int iters = (n4 + U * 64 - 1) / (U * 64);
+      for (int it = 0; it < iters; ++it) {
+        const int base = it * U * 64 + lane;
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = src[min(base + u * 64, n4 - 1)];
+        // Clamped lanes rewrite the last element with its own value.
+#pragma unroll
+        for (int u = 0; u < U; ++u) dst[min(base + u * 64, n4 - 1)] = v[u];
+      }
+      const float2* ssrc = a.xsum + (size_t)mm * nblk + (nb > 0 ? c0 : 0);
+      const int siters = (nb + 63) / 64;
+      for (int it = 0; it < siters; ++it) {
+        const int i = it * 64 + lane;
+        const float2 v = ssrc[min(i, nb - 1)];
+        xsum_w[mm * a.chunk + min(i, nb - 1)] = v;
+      }
+    }
+    __syncthreads();
+
     int blk = c0;
     if (ch == 0 && blk < seg0_end) {
-      run_segment<B0, MT, true>(a, blk, seg0_end, row0, ks, col, colv, xs_w, xsum_w, c0, magic, yacc, W0, P0);
+      run_segment<B0, MT, true>(a, blk, seg0_end, row0, ks, panel, col, colv, xs_w, xsum_w, c0, magic, yacc, W0, P0);
       blk = seg0_end;
     }
     while (blk < c1) {
       int bits, row;
       block_info(a.runs, blk, bits, row);
       const int seg_end = min(c1, run_end_block(a.runs, blk));
-      any_segment<MT, BS>(a, bits, blk, seg_end, row, ks, col, colv, xs_w, xsum_w, c0, magic, yacc);
+      any_segment<MT, BS>(a, bits, blk, seg_end, row, ks, panel, col, colv, xs_w, xsum_w, c0, magic, yacc);
       blk = seg_end;
     }
   }
@@ -330,7 +349,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, 
     if (m < a.M && n < a.N) {
       float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red[w][m][c];
+      for (int w = 0; w < WV; ++w) v += red[w][m][c];
       a.y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
     }
   }
@@ -340,10 +359,10 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, 
 // for every width b the matrix may contain; the host picks the smallest
 // instantiated set that covers the layout's runs, which keeps the register
 // budget of the common formats low.
-template <int MT, unsigned BS>
-__global__ __launch_bounds__(kThreads) void qgemv_stream_kernel(StreamArgs a) {
+template <int MT, unsigned BS, int WV>
+__global__ __launch_bounds__(WV * 64) void qgemv_stream_kernel(StreamArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
-  __shared__ float red[kWaves][MT][SC];
+  __shared__ float red[WV][MT][SC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -353,12 +372,12 @@ __global__ __launch_bounds__(kThreads) void qgemv_stream_kernel(StreamArgs a) {
   if (strip >= a.nstrips) return;  // the whole workgroup leaves together
 
   const int nblk = a.K / kBlockRows;
-  const int wb0 = (wave * nblk) / kWaves, wb1 = ((wave + 1) * nblk) / kWaves;
+  const int wb0 = (wave * nblk) / WV, wb1 = ((wave + 1) * nblk) / WV;
   int bits0 = 0, row0 = 0;
   if (wb0 < wb1) block_info(a.runs, wb0, bits0, row0);
 #define QLINEAR_BODY(BB)                                                                     \
   case BB:                                                                                   \
-    if constexpr ((BS >> BB) & 1u) stream_body<MT, BS, BB>(a, lds, red, tid, lane, wave, strip, wb0, wb1, row0); \
+    if constexpr ((BS >> BB) & 1u) stream_body<MT, BS, WV, BB>(a, lds, red, tid, lane, wave, strip, wb0, wb1, row0); \
     return;
   switch (bits0) {
     QLINEAR_BODY(2)
@@ -370,32 +389,46 @@ __global__ __launch_bounds__(kThreads) void qgemv_stream_kernel(StreamArgs a) {
     default: break;
   }
 #undef QLINEAR_BODY
-  // This wave has no blocks (K < 128 rows): it still joins the barriers of
-  // the staging and the final reduction, which stream_body's other waves run.
-  stream_body<MT, BS, (BS & 16u) ? 4 : (BS & 4u) ? 2 : (BS & 8u) ? 3 : (BS & 32u) ? 5 : (BS & 64u) ? 6 : 8>(
+  // This wave has no blocks (K too small for every wave): it still joins the
+  // barriers of the staging and the final reduction, which the other waves run.
+  stream_body<MT, BS, WV, (BS & 16u) ? 4 : (BS & 4u) ? 2 : (BS & 8u) ? 3 : (BS & 32u) ? 5 : (BS & 64u) ? 6 : 8>(
       a, lds, red, tid, lane, wave, strip, wb0, wb1, row0);
 }
 
-template <int MT, unsigned BS>
+template <int MT, unsigned BS, int WV>
 hipError_t launch_set(StreamArgs a, hipStream_t stream) {
   const int nblk = a.K / kBlockRows;
-  const int per_wave = (nblk + kWaves - 1) / kWaves;
-  const int per_block_bytes = MT * (kPairsPerBlock * 4 + 4);
-  const int max_chunk = kStageBudget / (kWaves * per_block_bytes);
+  const int per_wave = (nblk + WV - 1) / WV;
+  const int max_chunk = (kStageBudget / (WV * 4) - 3) / (MT * (kPairsPerBlock + 2));
   a.chunk = per_wave < max_chunk ? per_wave : max_chunk;
   if (a.chunk < 1) a.chunk = 1;
   a.nstrips = (a.N + SC - 1) / SC;
   a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
-  const size_t lds = (size_t)kWaves * a.chunk * per_block_bytes;
-  hipLaunchKernelGGL((qgemv_stream_kernel<MT, BS>), dim3(kXcds * a.strips_per_xcd), dim3(kThreads), lds, stream, a);
+  const size_t lds = (size_t)WV * stage_words<MT>(a.chunk) * 4;
+  hipLaunchKernelGGL((qgemv_stream_kernel<MT, BS, WV>), dim3(kXcds * a.strips_per_xcd), dim3(WV * 64), lds, stream,
+                     a);
   return hipGetLastError();
 }
 
-template <unsigned BS>
+// Waves per workgroup for M = 1 (they split K). Measured on MI355X: 8 waves
+// pay off only when there are few 16-column strips and K is long; 4 otherwise.
+inline int waves_for(int N, int K) {
+  const int nstrips = (N + SC - 1) / SC;
+  return (nstrips <= 512 && K / kBlockRows >= 256) ? 8 : 4;
+}
+
+// kMaxWv: the most waves per workgroup instantiated for M = 1 for this width set.
+template <unsigned BS, int kMaxWv>
 hipError_t launch_set_any_m(const StreamArgs& a, hipStream_t stream) {
-  if (a.M <= 1) return launch_set<1, BS>(a, stream);
-  if (a.M <= 2) return launch_set<2, BS>(a, stream);
-  return launch_set<4, BS>(a, stream);
+  if (a.M <= 1) {
+    const int wv = waves_for(a.N, a.K);
+    if constexpr (kMaxWv >= 8) {
+      if (wv >= 8) return launch_set<1, BS, 8>(a, stream);
+    }
+    return launch_set<1, BS, 4>(a, stream);
+  }
+  if (a.M <= 2) return launch_set<2, BS, 4>(a, stream);
+  return launch_set<4, BS, 4>(a, stream);
 }
 
 constexpr unsigned kAllBits = (1u << 2) | (1u << 3) | (1u << 4) | (1u << 5) | (1u << 6) | (1u << 8);

@@ -14,6 +14,7 @@
 namespace qlinear {
 
 constexpr int kBlockRows = 32;          // rows per packing block (b words per block and column)
+constexpr int kPanel = 16;              // output columns per storage panel
 constexpr int kPairsPerBlock = 16;      // a block unpacks into 16 float16 pairs
 constexpr uint32_t kMagic = 0x64006400u;  // float16 1024.0 in both halves
 
@@ -25,10 +26,17 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 struct Runs {
   int nruns;
   int blocks_per_group;                   // group_size / 32
+  int packed_rows;                        // R
   int run_block[QLINEAR_MAX_RUNS + 1];    // first block of run r; [nruns] = K / 32
   int run_row[QLINEAR_MAX_RUNS + 1];      // first packed row of run r
   int run_bits[QLINEAR_MAX_RUNS];
 };
+
+// Storage index of word (packed row r, column n): 16-column panels, each
+// holding its R rows contiguously, [ceil(N/16)][R][16].
+__host__ __device__ __forceinline__ size_t word_index(int R, int r, int n) {
+  return ((size_t)(n / kPanel) * R + r) * kPanel + (n % kPanel);
+}
 
 // Bit width and first packed row of 32-row block `blk`.
 __device__ __forceinline__ void block_info(const Runs& R, int blk, int& bits, int& row) {
@@ -121,6 +129,40 @@ __device__ __forceinline__ uint32_t vgpr_magic() {
   uint32_t v;
   asm("v_mov_b32 %0, %1" : "=v"(v) : "i"(kMagic));
   return v;
+}
+
+// Scaled unpacking (decode path). A code whose field lies below bit 10 of its
+// half is masked in place: (w & (mask << pos)) | 0x6400 is the float16 value
+// 1024 + q * 2^pos, exactly. The activation paired with it is pre-scaled by
+// 2^-pos, so the product keeps its value up to the known bias 1024 * x'.
+// Fields at or above scaled_shift(b) are first moved down by one shift of the
+// whole word, shared by all such fields of the word.
+__host__ __device__ constexpr int scaled_shift(int b) { return b * ((10 - b) / b + 1); }
+
+// Exponent e with pair p exposing 1024 + q * 2^e (0 for the spare pairs).
+__host__ __device__ constexpr int pair_exponent(int b, int p) {
+  const int f = 16 / b;
+  if (p >= b * f) return 0;
+  const int pos = b * (p % f);
+  return pos + b <= 10 ? pos : pos - scaled_shift(b);
+}
+
+// Pair P from the block's words w[] and the same words shifted right by
+// scaled_shift(B), wsh[] (only read for fields above the first 10 bits).
+template <int B, int P>
+__host__ __device__ __forceinline__ uint32_t extract_pair_scaled(const uint32_t* w, const uint32_t* wsh,
+                                                                 uint32_t magic) {
+  using Fm = Fmt<B>;
+  if constexpr (P < Fm::kRegular) {
+    constexpr int t = P / Fm::F, pos = B * (P % Fm::F);
+    if constexpr (pos + B <= 10) {
+      return (w[t] & (Fm::kMask << pos)) | magic;
+    } else {
+      return (wsh[t] & (Fm::kMask << (pos - scaled_shift(B)))) | magic;
+    }
+  } else {
+    return extract_pair<B, P>(w, magic);
+  }
 }
 
 // Position (2 * pair + half) of block row r in the unpacking order of width b:

@@ -16,22 +16,27 @@ hipError_t launch_dequant(const qlinear_layout& L, const Runs& runs, const uint3
                           const uint16_t* scales, const uint8_t* zeros, uint16_t* w, hipStream_t stream);
 
 // Act-order gather into unpacking pair order: xq uint32 [M][K/32][16] (float16
-// pairs), optional xsum float [M][K/32] (sum of each block's 32 values).
+// pairs, optionally pre-scaled by 2^-pair_exponent), optional block sums
+// xsum float2 [M][K/32] = (sum x, 1024 * sum of the scaled x).
 hipError_t launch_gather_pairs(const Runs& runs, const uint16_t* x, const int32_t* perm, int M, int K,
-                               uint32_t* xq, float* xsum, hipStream_t stream);
+                               uint32_t* xq, float2* xsum, bool scaled, hipStream_t stream);
 
 // Decode layer (M <= 16). The workspace holds the gathered activations xq
-// uint32 [16][K/32][16] and the block sums xsum float [16][K/32]; it is
+// uint32 [16][K/32][16] and the block sums xsum float2 [16][K/32]; it is
 // scratch (no initialization, contents not preserved).
 struct GemvWorkspace {
   uint32_t* xq;
-  float* xsum;
+  float2* xsum;
 };
 size_t qgemv_workspace_bytes(int K);
 GemvWorkspace qgemv_workspace(void* ws, int K);
-hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
-                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
-                        const int32_t* perm, uint16_t* y, void* ws, hipStream_t stream);
+// The two phases: the act-order gather of x into the workspace, then the
+// streaming kernel over the packed weights.
+hipError_t launch_qgemv_gather(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
+                               const int32_t* perm, void* ws, hipStream_t stream);
+hipError_t launch_qgemv_apply(const qlinear_layout& L, const Runs& runs, int M, const uint32_t* qweight,
+                              const uint16_t* scales, const uint8_t* zeros, uint16_t* y, void* ws,
+                              hipStream_t stream);
 
 // Prefill layer. ws holds the gathered activations, float16 [M][K].
 size_t qgemm_workspace_bytes(int M, int K);

@@ -60,13 +60,13 @@ extern "C" {
  * row-group -> bit-width map, run-length encoded. Filled on the host by
  * qlinear_layout_init and passed by pointer (host memory) to every call.
  *
- * Packed format. The packed matrix is uint32 [packed_rows][N]. Each group is
- * cut into 32-row blocks; a block of b-bit codes for one output column is b
- * words, stored in consecutive packed rows of that column. Group g starts at
- * packed row goff[g] = sum_{g'<g} gs * b_g' / 32, its block c at
- * goff[g] + c * b_g. Inside a block each word is two 16-bit halves
- * (h = 0: bits 0..15, h = 1: bits 16..31) and every code lies inside one half.
- * With f = floor(16 / b) codes per half:
+ * Packed format. Codes are packed into a word matrix of packed_rows x N
+ * uint32 words. Each group is cut into 32-row blocks; a block of b-bit codes
+ * for one output column is b words, in consecutive packed rows of that
+ * column. Group g starts at packed row goff[g] = sum_{g'<g} gs * b_g' / 32,
+ * its block c at goff[g] + c * b_g. Inside a block each word is two 16-bit
+ * halves (h = 0: bits 0..15, h = 1: bits 16..31) and every code lies inside
+ * one half. With f = floor(16 / b) codes per half:
  *   - row r < 2*f*b: word r / (2f); u = r % (2f); half u / f; slot u % f;
  *     code bits at 16*h + b*(u % f) upward. For b = 2, 4, 8 this covers all
  *     32 rows and is the plain least-significant-first order (4-bit: row i of
@@ -75,17 +75,22 @@ extern "C" {
  *   - b = 6: rows 24 + 4*h + v (v < 4) keep code bits 0..3 in word v at
  *     bits 16*h + 12..15, and code bits 4, 5 in word 4 + v/2 at bits
  *     16*h + 12 + 2*(v % 2) and the bit above it.
+ * Storage order: 16-column panels, one after another, each holding its
+ * packed rows contiguously: word (r, n) is element ((n/16) * packed_rows + r)
+ * * 16 + n % 16 of the uint32 buffer, which holds packed_words =
+ * ceil(N/16) * packed_rows * 16 words (panel slots past N are zero).
  */
 typedef struct qlinear_layout {
   int32_t K;            /* input features (rows of the weight matrix) */
   int32_t N;            /* output features (columns) */
   int32_t group_size;   /* rows per scale group: 32, 64 or 128 */
   int32_t groups;       /* G = K / group_size */
-  int32_t packed_rows;  /* R: rows of the uint32 [R][N] packed matrix */
+  int32_t packed_rows;  /* R: rows of the packed word matrix (R x N words) */
   int32_t nruns;        /* number of runs, 1..QLINEAR_MAX_RUNS */
   int32_t run_group[QLINEAR_MAX_RUNS + 1]; /* first group of run r; [nruns] = groups */
   int32_t run_row[QLINEAR_MAX_RUNS + 1];   /* first packed row of run r; [nruns] = packed_rows */
   int32_t run_bits[QLINEAR_MAX_RUNS];      /* code width of run r: 2, 3, 4, 5, 6 or 8 */
+  int64_t packed_words;  /* uint32 words of the packed buffer: ceil(N/16) * packed_rows * 16 */
 } qlinear_layout;
 
 /* Static, human-readable name of a status code. Never NULL. */
@@ -106,7 +111,7 @@ int qlinear_layout_init(qlinear_layout* layout, int32_t K, int32_t N, int32_t gr
  * Pack codes into the format above.
  *   q       : uint8 [K][N], stored row order, each code < 2^b of its group
  *             (larger codes are truncated to their low b bits).
- *   qweight : uint32 [packed_rows][N], written entirely.
+ *   qweight : uint32 [packed_words] in panel order, written entirely.
  */
 int qlinear_pack_weights(const qlinear_layout* layout, const uint8_t* q, uint32_t* qweight,
                          void* stream);
@@ -140,7 +145,7 @@ int qlinear_qgemv_workspace_bytes(const qlinear_layout* layout, size_t* bytes);
  * Decode-sized layer, 1 <= M <= QLINEAR_GEMV_MAX_M. M == 0 returns OK after
  * checking the layout only, and launches nothing (operands may then be NULL).
  *   x       : float16 [M][K], original feature order
- *   qweight : uint32 [packed_rows][N] from qlinear_pack_weights
+ *   qweight : uint32 [packed_words] from qlinear_pack_weights
  *   scales  : float16 [G][N]
  *   zeros   : uint8 [G][N] or NULL (symmetric)
  *   perm    : int32 [K], stored row j holds feature perm[j]; NULL = identity.
@@ -152,6 +157,22 @@ int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M,
                   const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                   const int32_t* perm, uint16_t* y, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * The two phases of qlinear_qgemv, for callers that schedule them separately
+ * (for example, the gather of one layer on a second stream while the previous
+ * layer's apply runs; the two then need separate workspaces).
+ * qlinear_qgemv_gather writes the act-order-gathered activations x[:, perm]
+ * (in the order the packed words unpack to) and their 32-row block sums into
+ * the workspace. qlinear_qgemv_apply reads them and computes y; it must run
+ * after a gather with the same layout, M and workspace (stream order).
+ * Arguments and errors as for qlinear_qgemv; M == 0 returns OK.
+ */
+int qlinear_qgemv_gather(const qlinear_layout* layout, const uint16_t* x, int32_t M, const int32_t* perm,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int qlinear_qgemv_apply(const qlinear_layout* layout, int32_t M, const uint32_t* qweight,
+                        const uint16_t* scales, const uint8_t* zeros, uint16_t* y, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* Workspace of qlinear_qgemm for M tokens, in bytes (no initialization needed). */
 int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes);

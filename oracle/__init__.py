@@ -24,6 +24,9 @@ from .qlinear_oracle import (  # noqa: F401
     packed_rows,
     pack,
     unpack,
+    panel_layout,
+    panel_unlayout,
+    PANEL,
     zero_points,
     dequant,
     dequant_fp16,

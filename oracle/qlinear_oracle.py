@@ -35,6 +35,7 @@ import numpy as np
 BITS_SUPPORTED = (2, 3, 4, 5, 6, 8)
 GROUP_SIZES_SUPPORTED = (32, 64, 128)
 BLOCK_ROWS = 32  # rows per packing block; a block of b-bit codes is exactly b words
+PANEL = 16       # output columns per storage panel
 
 
 # --------------------------------------------------------------------------
@@ -176,6 +177,33 @@ def unpack(packed: np.ndarray, bits, gs: int, K: int) -> np.ndarray:
                     code |= ((packed[base + t] >> np.uint32(pos)) & np.uint32(1)) << np.uint32(k)
                 q[g * gs + c * BLOCK_ROWS + r] = code.astype(np.uint8)
     return q
+
+
+def panel_layout(words: np.ndarray) -> np.ndarray:
+    """Storage order of the packed words: 16-column panels, one after another.
+
+    ``words`` is the word matrix [R][N] of :func:`pack`. The stored array is
+    [ceil(N/16)][R][16]: word (r, n) sits at panel n // 16, row r, slot
+    n % 16, and panel columns past N are zero. Each panel's R rows are thus
+    contiguous (a reader of 16 columns streams one contiguous region).
+    """
+    words = np.asarray(words, dtype=np.uint32)
+    R, N = words.shape
+    npan = (N + PANEL - 1) // PANEL
+    out = np.zeros((npan, R, PANEL), dtype=np.uint32)
+    for n in range(N):
+        out[n // PANEL, :, n % PANEL] = words[:, n]
+    return out
+
+
+def panel_unlayout(panels: np.ndarray, N: int) -> np.ndarray:
+    """Inverse of :func:`panel_layout`: [ceil(N/16)][R][16] -> [R][N]."""
+    panels = np.asarray(panels, dtype=np.uint32)
+    R = panels.shape[1]
+    words = np.zeros((R, N), dtype=np.uint32)
+    for n in range(N):
+        words[:, n] = panels[n // PANEL, :, n % PANEL]
+    return words
 
 
 # --------------------------------------------------------------------------

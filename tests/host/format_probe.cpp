@@ -23,8 +23,12 @@ static void probe(uint32_t seed, int ncols) {
       for (int r = 0; r < kBlockRows; ++r) codes[r] = (1u << B) - 1u;  // all ones
     uint32_t w[B] = {};
     for (int r = 0; r < kBlockRows; ++r) place_code<B>(w, r, codes[r]);
-    uint32_t pr[kPairsPerBlock];
+    uint32_t pr[kPairsPerBlock], ps[kPairsPerBlock], wsh[B];
     extract_all_pairs<B>(w, pr);
+    for (int t = 0; t < B; ++t) wsh[t] = w[t] >> scaled_shift(B);
+    [&]<int... P>(std::integer_sequence<int, P...>) {
+      ((ps[P] = extract_pair_scaled<B, P>(w, wsh, kMagic)), ...);
+    }(std::make_integer_sequence<int, kPairsPerBlock>{});
     std::printf("B %d\nC", B);
     for (int r = 0; r < kBlockRows; ++r) std::printf(" %u", codes[r]);
     std::printf("\nW");
@@ -33,7 +37,7 @@ static void probe(uint32_t seed, int ncols) {
     for (int p = 0; p < kPairsPerBlock; ++p) {
       int lo, hi;
       pair_rows(B, p, lo, hi);
-      std::printf(" %d:%d:%u", lo, hi, pr[p]);
+      std::printf(" %d:%d:%u:%u:%d", lo, hi, pr[p], ps[p], pair_exponent(B, p));
     }
     std::printf("\n");
   }

@@ -24,15 +24,15 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = dq.lib()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     assert sorted(names) == sorted(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_struct_size_matches_header():
-    # 6 scalars + 2 * (MAX_RUNS + 1) + MAX_RUNS int32
-    assert ctypes.sizeof(_lib.qlinear_layout) == 4 * (6 + 2 * 65 + 64)
+    # 6 scalars + 2 * (MAX_RUNS + 1) + MAX_RUNS int32, then the int64 word count
+    assert ctypes.sizeof(_lib.qlinear_layout) == 4 * (6 + 2 * 65 + 64) + 8
 
 
 def test_status_strings():
@@ -56,6 +56,9 @@ def test_layout_runs_and_rows():
     # 2 blocks per group, b words per block
     assert list(c.run_row)[:5] == [0, 36, 56, 96, 120]
     assert L.packed_rows == 120
+    assert c.packed_words == 4 * 120 * 16       # N = 64: four 16-column panels
+    L2 = _layout(K=64, N=24, gs=32, bits=np.array([3, 3], np.uint8))
+    assert L2.c.packed_words == 2 * 6 * 16       # N = 24: last panel half padding
 
 
 @pytest.mark.parametrize("args,status", [
@@ -123,6 +126,21 @@ def test_qgemv_validation_before_launch():
     assert _gemv(L, M=0, x=None, y=None, ws=None, wsb=0) == _lib.OK  # empty tensors may be NULL
 
 
+def test_qgemv_phase_validation_before_launch():
+    L = _layout()
+    lib = dq.lib()
+    big = 1 << 30
+    assert lib.qlinear_qgemv_gather(L.ref, None, 1, None, FAKE, big, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.qlinear_qgemv_gather(L.ref, FAKE, 17, None, FAKE, big, None) == _lib.ERR_UNSUPPORTED
+    assert lib.qlinear_qgemv_gather(L.ref, FAKE, 1, None, FAKE, 16, None) == _lib.ERR_WORKSPACE
+    assert lib.qlinear_qgemv_gather(L.ref, FAKE + 2, 1, None, FAKE, big, None) == _lib.ERR_MISALIGNED
+    assert lib.qlinear_qgemv_gather(L.ref, None, 0, None, None, 0, None) == _lib.OK
+    assert lib.qlinear_qgemv_apply(L.ref, 1, None, FAKE, None, FAKE, FAKE, big, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.qlinear_qgemv_apply(L.ref, 1, FAKE, FAKE, None, FAKE, None, big, None) == _lib.ERR_WORKSPACE
+    assert lib.qlinear_qgemv_apply(L.ref, 1, FAKE, FAKE, FAKE + 4, FAKE, FAKE, big, None) == _lib.ERR_MISALIGNED
+    assert lib.qlinear_qgemv_apply(L.ref, -1, FAKE, FAKE, None, FAKE, FAKE, big, None) == _lib.ERR_INVALID_ARGUMENT
+
+
 def test_qgemm_validation_before_launch():
     L = _layout()
     assert _gemm(L, qw=None) == _lib.ERR_INVALID_ARGUMENT
@@ -141,6 +159,9 @@ def test_tampered_layout_is_rejected():
     L.c.run_bits[0] = 7
     assert _gemv(L) == _lib.ERR_UNSUPPORTED
     L = _layout()
+    L.c.packed_words -= 16
+    assert _gemv(L) == _lib.ERR_INVALID_ARGUMENT
+    L = _layout()
     L.c.nruns = 0
     assert _gemm(L) == _lib.ERR_UNSUPPORTED
 
@@ -157,6 +178,6 @@ def test_pack_unpack_dequant_validation():
 
 def test_workspace_sizes():
     L = _layout(N=4096, K=4096, gs=128)
-    # gathered activations float16 [16][K] + block sums float [16][K/32], 256-byte rounded
-    assert dq.qgemv_workspace_bytes(L) == 16 * 4096 * 2 + 16 * 128 * 4
+    # gathered activations float16 [16][K] + block sums float2 [16][K/32], 256-byte rounded
+    assert dq.qgemv_workspace_bytes(L) == 16 * 4096 * 2 + 16 * 128 * 8
     assert dq.qgemm_workspace_bytes(L, 2048) == 2048 * 4096 * 2

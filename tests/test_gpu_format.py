@@ -37,6 +37,10 @@ def _run(K, N, gs, bits, q, s, z):
     return packed.cpu().numpy().view(np.uint32), un.cpu().numpy(), fp16_bits(w)
 
 
+def _oracle_storage(q, bits, gs):
+    return oracle.panel_layout(oracle.pack(q, bits, gs))
+
+
 @pytest.mark.parametrize("b", BITS)
 @pytest.mark.parametrize("gs", (32, 64, 128))
 def test_small_uniform(b, gs):
@@ -44,7 +48,7 @@ def test_small_uniform(b, gs):
     N = 264  # one full 256-column strip plus a ragged one
     K, bits, q, s, z = _small([b] * 3, gs, N, seed=b * 7 + gs)
     packed, un, w = _run(K, N, gs, bits, q, s, z)
-    assert np.array_equal(packed, oracle.pack(q, bits, gs))
+    assert np.array_equal(packed, _oracle_storage(q, bits, gs))
     assert np.array_equal(un, q)
     assert np.array_equal(w, oracle.dequant_fp16(q, s, z, bits, gs).view(np.uint16))
 
@@ -55,7 +59,7 @@ def test_small_mixed_runs(zeros):
     say(f"format mixed zeros={zeros}")
     K, bits, q, s, z = _small(bits, 32, 40, seed=3, zeros=zeros)
     packed, un, w = _run(K, 40, 32, bits, q, s, z)
-    assert np.array_equal(packed, oracle.pack(q, bits, 32))
+    assert np.array_equal(packed, _oracle_storage(q, bits, 32))
     assert np.array_equal(un, q)
     assert np.array_equal(w, oracle.dequant_fp16(q, s, z, bits, 32).view(np.uint16))
 
@@ -69,7 +73,7 @@ def test_extreme_codes():
                    (np.indices((gs, N)).sum(0) % 2 * ((1 << b) - 1)).astype(np.uint8)):
             s = np.full((1, N), 1.0, np.float16)
             packed, un, w = _run(gs, N, gs, np.array([b], np.uint8), q1, s, None)
-            assert np.array_equal(packed, oracle.pack(q1, [b], gs))
+            assert np.array_equal(packed, _oracle_storage(q1, [b], gs))
             assert np.array_equal(un, q1)
             assert np.array_equal(w, oracle.dequant_fp16(q1, s, None, [b], gs).view(np.uint16))
 
@@ -87,7 +91,8 @@ def test_full_size_layers(spec):
     rng = np.random.default_rng(1)
     cols = np.unique(np.concatenate([rng.choice(spec.N, 24, replace=False), [0, spec.N - 1]]))
     ci = torch.from_numpy(cols).to(lay.dev)
-    packed = lay.qweight.index_select(1, ci).cpu().numpy().view(np.uint32)
+    panels = lay.qweight.cpu().numpy().view(np.uint32)
+    packed = np.stack([panels[n // 16, :, n % 16] for n in cols], axis=1)   # word matrix columns
     assert np.array_equal(packed, oracle.pack(inp.q[:, cols], inp.bits, spec.group_size))
     zc = None if inp.zeros is None else inp.zeros[:, cols]
     want = oracle.dequant_fp16(inp.q[:, cols], inp.scales[:, cols], zc, inp.bits, spec.group_size)

@@ -156,6 +156,19 @@ def test_workspace_is_scratch_and_shareable():
         assert_close(lb.qgemv(b.x[:1]), _ref(b, b.x[:1]), "b M=1")
 
 
+def test_two_phase_qgemv_matches_one_call():
+    """gather + apply on their own give the same y as qlinear_qgemv."""
+    say("two-phase qgemv")
+    inp = _mixed_inputs(MIXED_BITS, 32, 520, 3, seed=12, zeros=True)
+    lay = GpuLayer(inp)
+    x = lay.x(inp.x)
+    y1 = lay.qgemv(inp.x)
+    dq.qgemv_gather(lay.layout, x, lay.perm, lay.ws)
+    y2 = dq.qgemv_apply(lay.layout, 3, lay.qweight, lay.scales, lay.zeros, lay.ws)
+    assert torch.equal(y1, y2)
+    assert_close(y2, _ref(inp), "two-phase")
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 DECODE_CASES = [(wl.TINY, 1)] + [(s, M) for s in wl.LLAMA7B_DECODE for M in s.Ms] + \

@@ -50,9 +50,14 @@ def test_kernel_pairs_cover_every_row_once(probe_output):
         rows = sorted([p[0] for p in pairs] + [p[1] for p in pairs])
         assert rows == list(range(32)), b
         q = oracle.unpack(words[:, None], [b], 32, 32)[:, 0]
-        for lo, hi, v in pairs:
+        for lo, hi, v, vs, e in pairs:
             assert v & 0xFFFF == 0x6400 + int(q[lo]) and v >> 16 == 0x6400 + int(q[hi]), (b, lo, hi, hex(v))
             assert q[lo] == codes[lo] and q[hi] == codes[hi]
+            # scaled unpacking: the float16 halves are exactly 1024 + q * 2^e
+            assert 0 <= e and e + b <= 10
+            for half, row in ((vs & 0xFFFF, lo), (vs >> 16, hi)):
+                val = float(np.array([half], np.uint16).view(np.float16)[0])
+                assert val == 1024.0 + int(q[row]) * 2.0 ** e, (b, row, e, hex(vs))
 
 
 def test_pair_position_inverts_pair_rows(probe_output):

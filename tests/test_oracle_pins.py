@@ -126,6 +126,20 @@ def test_mixed_bits_group_offsets():
         assert np.array_equal((packed[34] >> (4 * i)) & 0xF, q[192 + i])
 
 
+def test_panel_layout_hand_example():
+    # words[r][n] = 100 r + n, N = 24: panel 0 holds columns 0..15, panel 1
+    # columns 16..23 followed by 8 zero slots; rows are contiguous per panel.
+    R, N = 3, 24
+    words = (100 * np.arange(R)[:, None] + np.arange(N)[None, :]).astype(np.uint32)
+    P = oracle.panel_layout(words)
+    assert P.shape == (2, 3, 16)
+    flat = P.reshape(-1)
+    assert flat[0] == 0 and flat[15] == 15 and flat[16] == 100 and flat[47] == 215
+    assert flat[48] == 16 and flat[55] == 23 and flat[56] == 0 and flat[63] == 0
+    assert flat[64] == 116 and flat[48 + 2 * 16 + 7] == 223
+    assert np.array_equal(oracle.panel_unlayout(P, N), words)
+
+
 def test_pack_rejects_out_of_range_codes():
     q = np.full((32, 3), 8, dtype=np.uint8)
     with pytest.raises(ValueError):

@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the M = 2048 qgemm measurement")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy a MIB-MiB buffer 3 times (a known-size kernel for HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -49,20 +52,93 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-class Launch:
-    """Pre-marshalled arguments of one qlinear_qgemv / qlinear_qgemm call."""
+class Call:
+    """One C entry point with its arguments marshalled once: layouts become
+    struct pointers, tensors device pointers (workspaces add their size)."""
 
-    def __init__(self, fn, layout, x, M, qweight, scales, zeros, perm, y, ws, stream):
+    def __init__(self, fn, *args, ws_last=True):
         self.fn = fn
-        self.layout = layout  # keeps the ctypes struct alive
-        self.args = (layout.ref, x.data_ptr(), M, qweight.data_ptr(), scales.data_ptr(),
-                     None if zeros is None else zeros.data_ptr(), None if perm is None else perm.data_ptr(),
-                     y.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        self.keep = args  # keeps layouts and tensors alive
+        out = []
+        for a in args:
+            if hasattr(a, "ref"):
+                out.append(a.ref)
+            elif hasattr(a, "data_ptr"):
+                out.append(a.data_ptr())
+            else:
+                out.append(a)
+        if ws_last:  # (..., workspace, stream) -> (..., workspace, workspace bytes, stream)
+            out.insert(len(out) - 1, args[-2].numel())
+        self.args = tuple(out)
 
     def __call__(self):
         st = self.fn(*self.args)
         if st != 0:
             raise RuntimeError(f"launch failed with status {st}")
+
+
+def Launch(fn, layout, x, M, qweight, scales, zeros, perm, y, ws, stream):
+    """A qlinear_qgemv / qlinear_qgemm call."""
+    return Call(fn, layout, x, M, qweight, scales, zeros, perm, y, ws, stream)
+
+
+def spin_cycles(torch, stream, ms):
+    """Argument of torch.cuda._sleep that keeps the GPU busy for about `ms`."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    probe = 1 << 22
+    torch.cuda._sleep(probe)  # first launch loads the kernel
+    torch.cuda.synchronize()
+    a.record(stream)
+    torch.cuda._sleep(probe)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return int(probe * ms / max(a.elapsed_time(b), 1e-3))
+
+
+def apply_bytes(layout, M, zeros=True):
+    """Algorithmic HBM bytes of one qgemv apply launch: every operand byte read
+    once and the output written once. Packed codes at b bits per weight,
+    float16 scales, uint8 zero points, the gathered float16 activations, their
+    float32 block sums (two per 32-row block), the float16 result."""
+    bits = layout.bits.astype(np.int64)
+    K, N, G = layout.K, layout.N, layout.groups
+    codes = int((bits * layout.group_size).sum()) * N // 8
+    return codes + G * N * 2 + (G * N if zeros else 0) + M * K * 2 + M * (K // 32) * 8 + M * N * 2
+
+
+# Files whose code makes up the qgemv apply kernel; recorded counter data is
+# valid only for the exact sources it was taken on.
+STREAM_KERNEL_SOURCES = ("qgemv_stream.hpp", "qgemv_stream.hip", "qgemv_stream_uniform.hip", "qlinear_device.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemv_stream_llama7b_decode_traffic.txt")
+
+
+def stream_kernel_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in STREAM_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dequant_matmul_gptq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per apply launch measured with FETCH_SIZE and WRITE_SIZE
+    (scaled by the copy-kernel calibration), averaged over the step's
+    launches, from the committed counter summary; None when it is missing or
+    was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256_16") != stream_kernel_digest():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def setup_decode(torch, dq, wl, dev):
@@ -108,6 +184,16 @@ def main():
     stream = torch.cuda.Stream(dev)
     torch.cuda.set_stream(stream)
     sh = stream.cuda_stream
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {n} bytes read and written")
+        del src, dst
 
     # ---------------------------------------------------------------- decode setup
     t0 = time.time()
@@ -164,34 +250,108 @@ def main():
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"decode step {ms_step * 1e3:.1f} us -> {value:.0f} GB/s ({value / HBM_PEAK_GBS:.1%} of HBM peak)")
 
-    # per-launch durations with HIP events on the launch stream (eager)
-    n_ev = len(launches)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
-    dur = {0: [], 1: [], 2: []}
-    reps = max(1, min(args.steps, 10))
-    for _ in range(reps):
-        for ln, (a, b) in zip(launches, evs):
-            a.record(stream)
-            ln()
-            b.record(stream)
-        torch.cuda.synchronize()
-        for m, (a, b) in zip(mats, evs):
-            dur[m["shape"]].append(a.elapsed_time(b) * 1e3)
+    # Per-launch durations of the two kernels of a call, with HIP events on the
+    # launch stream: for each shape, >= 256 launches back to back (cycling
+    # through that shape's distinct matrices, so weights come from HBM)
+    # between two events, issued through the two phase entry points so that
+    # each batch holds one kernel. A spin kernel queued first keeps the GPU
+    # behind the host: the events then time the kernels, not host launch
+    # latency.
+    spin = spin_cycles(torch, stream, 50.0)
     per_shape = []
-    tot_bytes, tot_us = 0, 0.0
+    tot_bytes, tot_us, g_tot_us, n_step = 0, 0.0, 0.0, 0
     for si, s in enumerate(shapes):
-        us = float(np.mean(dur[si]))
-        gbs = wbytes[si] / (us * 1e-6) / 1e9
-        per_shape.append(dict(shape=f"{s['spec'].K}x{s['spec'].N}", weight_bytes=wbytes[si], avg_us=round(us, 3),
-                              gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4)))
-        tot_bytes += wbytes[si] * len(dur[si])
-        tot_us += float(np.sum(dur[si]))
+        mine = [m for m in mats if m["shape"] == si]
+        rounds = -(-256 // len(mine))
+        L = s["L"]
+        gathers = [Call(lib.qlinear_qgemv_gather, L, xs[si], 1, m["pm"], ws, sh) for m in mine]
+        applies = [Call(lib.qlinear_qgemv_apply, L, 1, m["qw"], m["sc"], m["zr"], ys[si], ws, sh) for m in mine]
+        g0_, g1_, a1_ = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        torch.cuda._sleep(spin)
+        g0_.record(stream)
+        for _ in range(rounds):
+            for g in gathers:
+                g()
+        g1_.record(stream)
+        for _ in range(rounds):
+            for ap in applies:
+                ap()
+        a1_.record(stream)
+        torch.cuda.synchronize()
+        n = rounds * len(mine)
+        g_us = g0_.elapsed_time(g1_) * 1e3 / n
+        a_us = g1_.elapsed_time(a1_) * 1e3 / n
+        ab = apply_bytes(L, 1)
+        gbs = ab / (a_us * 1e-6) / 1e9
+        per_shape.append(dict(shape=f"{s['spec'].K}x{s['spec'].N}", algorithmic_bytes=ab, launches=n,
+                              avg_us=round(a_us, 3), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
+                              gather_avg_us=round(g_us, 3)))
+        # weight the shapes as the step does
+        tot_bytes += ab * len(mine)
+        tot_us += a_us * len(mine)
+        g_tot_us += g_us * len(mine)
+        n_step += len(mine)
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
-    n_launch = sum(len(v) for v in dur.values())
-    log(f"qgemv per launch: avg {tot_us / n_launch:.2f} us, {achieved:.0f} GB/s; " +
+    log(f"qgemv_stream_kernel per launch: avg {tot_us / n_step:.2f} us, {achieved:.0f} GB/s; gather avg "
+        f"{g_tot_us / n_step:.2f} us; " +
         ", ".join(f"{p['shape']}: {p['avg_us']} us {p['gbs']} GB/s" for p in per_shape))
+    traffic = recorded_traffic()
 
-    # ---------------------------------------------------------------- prefill
+    gemm = None if args.no_gemm else bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream)
+
+    # ---------------------------------------------------------------- oracle on the host
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(shapes[1]["inp"], wbytes[1])
+        log(f"oracle on host: {cpu['value']} GB/s with {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-2-7B-shaped decode, GPTQ 4-bit g128 act-order, M=1: 32 layers x "
+                        "(4 x 4096->4096, 2 x 4096->11008, 1 x 11008->4096), weights resident in HBM",
+            "M": 1,
+            "matrices_per_step": len(mats),
+            "weight_bytes_per_step": step_bytes,
+            "hbm_peak_gbs": HBM_PEAK_GBS,
+            "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+            "launch": "hip_graph" if graph is not None else "eager",
+            "accumulate": "fp32",
+        },
+        "roofline": {
+            "kernel": "qgemv_stream_kernel (M=1, 4-bit)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(tot_us / n_step, 3),
+            "algorithmic_bytes_per_launch": round(tot_bytes / n_step),
+            "gather_avg_launch_us": round(g_tot_us / n_step, 3),
+            "per_shape": per_shape,
+        },
+        "cpu_baseline": cpu,
+        "qgemm": gemm,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream):
+    """qgemm on the Llama-2-13B MLP prefill shape, M = 2048, checked against
+    the oracle on sampled rows, then timed over --gemm-iters calls."""
+    sh = stream.cuda_stream
     spec = wl.PREFILL_13B
     inp = wl.generate(spec)
     L = dq.Layout(spec.K, spec.N, spec.group_size, inp.bits)
@@ -227,65 +387,20 @@ def main():
     tflops = flops / (gemm_ms * 1e-3) / 1e12
     log(f"qgemm M={M}: {gemm_ms * 1e3:.1f} us per call -> {tflops:.1f} TFLOP/s "
         f"({tflops / MFMA_F16_PEAK_TFLOPS:.1%} of fp16 MFMA peak), rel_fro={rel:.1e}")
-
-    # ---------------------------------------------------------------- oracle on the host
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(shapes[1]["inp"], wbytes[1])
-        log(f"oracle on host: {cpu['value']} GB/s with {cpu['cores']} threads")
-
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp16",
-        "data": "synthetic",
-        "config": {
-            "workload": "Llama-2-7B-shaped decode, GPTQ 4-bit g128 act-order, M=1: 32 layers x "
-                        "(4 x 4096->4096, 2 x 4096->11008, 1 x 11008->4096), weights resident in HBM",
-            "M": 1,
-            "matrices_per_step": len(mats),
-            "weight_bytes_per_step": step_bytes,
-            "hbm_peak_gbs": HBM_PEAK_GBS,
-            "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-            "launch": "hip_graph" if graph is not None else "eager",
-            "accumulate": "fp32",
-        },
+    return {
+        "workload": "Llama-2-13B MLP prefill 5120->13824, GPTQ 4-bit g128 act-order, M=2048",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "ms_per_call": round(gemm_ms, 5),
         "roofline": {
-            "kernel": "qgemv_kernel<1>",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "avg_launch_us": round(tot_us / n_launch, 3),
-            "per_shape": per_shape,
-        },
-        "cpu_baseline": cpu,
-        "qgemm": {
-            "workload": "Llama-2-13B MLP prefill 5120->13824, GPTQ 4-bit g128 act-order, M=2048",
-            "value": round(tflops, 2),
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "ms_per_call": round(gemm_ms, 5),
-            "roofline": {
-                "bound": "mfma",
-                "achieved": round(tflops, 2),
-                "peak": MFMA_F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s",
-                "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                "traffic": None,
-            },
+            "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": None,
         },
     }
-    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(inp, wbytes):

@@ -95,34 +95,34 @@ def spin_cycles(torch, stream, ms):
     return int(probe * ms / max(a.elapsed_time(b), 1e-3))
 
 
-def apply_bytes(layout, M, zeros=True):
-    """Algorithmic HBM bytes of one qgemv apply launch: every operand byte read
-    once and the output written once. Packed codes at b bits per weight,
-    float16 scales, uint8 zero points, the gathered float16 activations, their
-    float32 block sums (two per 32-row block), the float16 result."""
+def row_kernel_bytes(layout, M, zeros=True, perm=True):
+    """Algorithmic HBM bytes of one single-row qgemv launch: every operand
+    byte read once and the output written once. Packed codes at b bits per
+    weight, float16 scales, uint8 zero points, the float16 activations, the
+    int32 act-order permutation, the float16 result."""
     bits = layout.bits.astype(np.int64)
     K, N, G = layout.K, layout.N, layout.groups
     codes = int((bits * layout.group_size).sum()) * N // 8
-    return codes + G * N * 2 + (G * N if zeros else 0) + M * K * 2 + M * (K // 32) * 8 + M * N * 2
+    return codes + G * N * 2 + (G * N if zeros else 0) + M * K * 2 + (K * 4 if perm else 0) + M * N * 2
 
 
-# Files whose code makes up the qgemv apply kernel; recorded counter data is
-# valid only for the exact sources it was taken on.
-STREAM_KERNEL_SOURCES = ("qgemv_stream.hpp", "qgemv_stream.hip", "qgemv_stream_uniform.hip", "qlinear_device.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemv_stream_llama7b_decode_traffic.txt")
+# Files whose code makes up the single-row qgemv kernel; recorded counter
+# data is valid only for the exact sources it was taken on.
+ROW_KERNEL_SOURCES = ("qgemv_m1.hpp", "qgemv_row.hip", "qgemv_stream.hpp", "qgemv_stream.hip", "qlinear_device.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemv_row_llama7b_decode_traffic.txt")
 
 
-def stream_kernel_digest():
+def row_kernel_digest():
     import hashlib
     h = hashlib.sha256()
-    for f in STREAM_KERNEL_SOURCES:
+    for f in ROW_KERNEL_SOURCES:
         with open(os.path.join(ROOT, "dequant_matmul_gptq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def recorded_traffic():
-    """HBM bytes per apply launch measured with FETCH_SIZE and WRITE_SIZE
+    """HBM bytes per single-row launch measured with FETCH_SIZE and WRITE_SIZE
     (scaled by the copy-kernel calibration), averaged over the step's
     launches, from the committed counter summary; None when it is missing or
     was taken on other kernel sources."""
@@ -133,7 +133,7 @@ def recorded_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_sources_sha256_16") != stream_kernel_digest():
+    if kv.get("kernel_sources_sha256_16") != row_kernel_digest():
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -250,50 +250,41 @@ def main():
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"decode step {ms_step * 1e3:.1f} us -> {value:.0f} GB/s ({value / HBM_PEAK_GBS:.1%} of HBM peak)")
 
-    # Per-launch durations of the two kernels of a call, with HIP events on the
-    # launch stream: for each shape, >= 256 launches back to back (cycling
-    # through that shape's distinct matrices, so weights come from HBM)
-    # between two events, issued through the two phase entry points so that
-    # each batch holds one kernel. A spin kernel queued first keeps the GPU
-    # behind the host: the events then time the kernels, not host launch
-    # latency.
+    # Per-launch duration of the single-row kernel (one kernel per call at
+    # M = 1 with one code width), with HIP events on the launch stream: for
+    # each shape, >= 256 calls back to back (cycling through that shape's
+    # distinct matrices, so weights come from HBM) between two events. A spin
+    # kernel queued first keeps the GPU behind the host: the events then time
+    # the kernels, not host launch latency.
     spin = spin_cycles(torch, stream, 50.0)
     per_shape = []
-    tot_bytes, tot_us, g_tot_us, n_step = 0, 0.0, 0.0, 0
+    tot_bytes, tot_us, n_step = 0, 0.0, 0
     for si, s in enumerate(shapes):
         mine = [m for m in mats if m["shape"] == si]
         rounds = -(-256 // len(mine))
         L = s["L"]
-        gathers = [Call(lib.qlinear_qgemv_gather, L, xs[si], 1, m["pm"], ws, sh) for m in mine]
-        applies = [Call(lib.qlinear_qgemv_apply, L, 1, m["qw"], m["sc"], m["zr"], ys[si], ws, sh) for m in mine]
-        g0_, g1_, a1_ = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        calls = [Call(lib.qlinear_qgemv, L, xs[si], 1, m["qw"], m["sc"], m["zr"], m["pm"], ys[si], ws, sh)
+                 for m in mine]
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda._sleep(spin)
-        g0_.record(stream)
+        ev0.record(stream)
         for _ in range(rounds):
-            for g in gathers:
-                g()
-        g1_.record(stream)
-        for _ in range(rounds):
-            for ap in applies:
-                ap()
-        a1_.record(stream)
+            for c in calls:
+                c()
+        ev1.record(stream)
         torch.cuda.synchronize()
         n = rounds * len(mine)
-        g_us = g0_.elapsed_time(g1_) * 1e3 / n
-        a_us = g1_.elapsed_time(a1_) * 1e3 / n
-        ab = apply_bytes(L, 1)
-        gbs = ab / (a_us * 1e-6) / 1e9
+        us = ev0.elapsed_time(ev1) * 1e3 / n
+        ab = row_kernel_bytes(L, 1)
+        gbs = ab / (us * 1e-6) / 1e9
         per_shape.append(dict(shape=f"{s['spec'].K}x{s['spec'].N}", algorithmic_bytes=ab, launches=n,
-                              avg_us=round(a_us, 3), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
-                              gather_avg_us=round(g_us, 3)))
+                              avg_us=round(us, 3), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4)))
         # weight the shapes as the step does
         tot_bytes += ab * len(mine)
-        tot_us += a_us * len(mine)
-        g_tot_us += g_us * len(mine)
+        tot_us += us * len(mine)
         n_step += len(mine)
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
-    log(f"qgemv_stream_kernel per launch: avg {tot_us / n_step:.2f} us, {achieved:.0f} GB/s; gather avg "
-        f"{g_tot_us / n_step:.2f} us; " +
+    log(f"qgemv_row_kernel per launch: avg {tot_us / n_step:.2f} us, {achieved:.0f} GB/s; " +
         ", ".join(f"{p['shape']}: {p['avg_us']} us {p['gbs']} GB/s" for p in per_shape))
     traffic = recorded_traffic()
 
@@ -330,7 +321,7 @@ def main():
             "accumulate": "fp32",
         },
         "roofline": {
-            "kernel": "qgemv_stream_kernel (M=1, 4-bit)",
+            "kernel": "qgemv_row_kernel (M=1, 4-bit)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -339,7 +330,6 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(tot_us / n_step, 3),
             "algorithmic_bytes_per_launch": round(tot_bytes / n_step),
-            "gather_avg_launch_us": round(g_tot_us / n_step, 3),
             "per_shape": per_shape,
         },
         "cpu_baseline": cpu,

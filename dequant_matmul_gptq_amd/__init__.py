@@ -19,8 +19,6 @@ from ._lib import (  # noqa: F401
     qgemm,
     qgemm_workspace_bytes,
     qgemv,
-    qgemv_apply,
-    qgemv_gather,
     qgemv_workspace,
     qgemv_workspace_bytes,
     status_string,

@@ -36,8 +36,6 @@ EXPORTS = (
     "qlinear_dequant",
     "qlinear_qgemv_workspace_bytes",
     "qlinear_qgemv",
-    "qlinear_qgemv_gather",
-    "qlinear_qgemv_apply",
     "qlinear_qgemm_workspace_bytes",
     "qlinear_qgemm",
 )
@@ -85,8 +83,6 @@ def lib() -> ctypes.CDLL:
         L.qlinear_dequant.argtypes = [lp, vp, vp, vp, vp, vp]
         L.qlinear_qgemv_workspace_bytes.argtypes = [lp, ctypes.POINTER(sz)]
         L.qlinear_qgemv.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.qlinear_qgemv_gather.argtypes = [lp, vp, i32, vp, vp, sz, vp]
-        L.qlinear_qgemv_apply.argtypes = [lp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.qlinear_qgemm_workspace_bytes.argtypes = [lp, i32, ctypes.POINTER(sz)]
         L.qlinear_qgemm.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTS[1:]:
@@ -216,34 +212,6 @@ def qgemv(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.
     _dev(workspace, "workspace", torch.uint8)
     _check(lib().qlinear_qgemv(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
                                _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemv")
-    return y
-
-
-def qgemv_gather(layout: Layout, x: torch.Tensor, perm: torch.Tensor | None, workspace: torch.Tensor) -> None:
-    """First phase of qgemv: gather x by act-order into the workspace."""
-    if x.dim() != 2 or x.shape[1] != layout.K:
-        raise ValueError(f"x must be [M][{layout.K}]")
-    _dev(x, "x", torch.float16)
-    if perm is not None:
-        _dev(perm, "perm", torch.int32, (layout.K,))
-    _dev(workspace, "workspace", torch.uint8)
-    _check(lib().qlinear_qgemv_gather(layout.ref, _ptr(x), int(x.shape[0]), _ptr(perm), _ptr(workspace),
-                                      workspace.numel(), _stream(x.device)), "qlinear_qgemv_gather")
-
-
-def qgemv_apply(layout: Layout, M: int, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor | None,
-                workspace: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
-    """Second phase of qgemv: y from the gathered activations in the workspace."""
-    _dev(qweight, "qweight", torch.int32, layout.qweight_shape)
-    _dev(scales, "scales", torch.float16, (layout.groups, layout.N))
-    if zeros is not None:
-        _dev(zeros, "zeros", torch.uint8, (layout.groups, layout.N))
-    _dev(workspace, "workspace", torch.uint8)
-    if y is None:
-        y = torch.empty((M, layout.N), dtype=torch.float16, device=qweight.device)
-    _dev(y, "y", torch.float16, (M, layout.N))
-    _check(lib().qlinear_qgemv_apply(layout.ref, int(M), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y),
-                                     _ptr(workspace), workspace.numel(), _stream(y.device)), "qlinear_qgemv_apply")
     return y
 
 

@@ -170,39 +170,8 @@ int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M, co
   if (st != QLINEAR_OK || M == 0) return st;
   if (M > QLINEAR_GEMV_MAX_M) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
-  const Runs runs = make_runs(*layout);
-  st = hip_status(launch_qgemv_gather(*layout, runs, x, M, perm, workspace, (hipStream_t)stream));
-  if (st != QLINEAR_OK) return st;
-  return hip_status(launch_qgemv_apply(*layout, runs, M, qweight, scales, zeros, y, workspace, (hipStream_t)stream));
-}
-
-int qlinear_qgemv_gather(const qlinear_layout* layout, const uint16_t* x, int32_t M, const int32_t* perm,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_layout(layout);
-  if (st != QLINEAR_OK) return st;
-  if (M < 0) return QLINEAR_ERR_INVALID_ARGUMENT;
-  if (M == 0) return QLINEAR_OK;
-  if (M > QLINEAR_GEMV_MAX_M) return QLINEAR_ERR_UNSUPPORTED;
-  if (!x) return QLINEAR_ERR_INVALID_ARGUMENT;
-  if (!workspace || workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
-  if (!aligned16(x) || !aligned16(workspace) || (perm && !aligned16(perm))) return QLINEAR_ERR_MISALIGNED;
-  return hip_status(launch_qgemv_gather(*layout, make_runs(*layout), x, M, perm, workspace, (hipStream_t)stream));
-}
-
-int qlinear_qgemv_apply(const qlinear_layout* layout, int32_t M, const uint32_t* qweight, const uint16_t* scales,
-                        const uint8_t* zeros, uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_layout(layout);
-  if (st != QLINEAR_OK) return st;
-  if (M < 0) return QLINEAR_ERR_INVALID_ARGUMENT;
-  if (M == 0) return QLINEAR_OK;
-  if (M > QLINEAR_GEMV_MAX_M) return QLINEAR_ERR_UNSUPPORTED;
-  if (!qweight || !scales || !y) return QLINEAR_ERR_INVALID_ARGUMENT;
-  if (!workspace || workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
-  if (!aligned16(qweight) || !aligned16(scales) || !aligned16(y) || !aligned16(workspace) ||
-      (zeros && !aligned16(zeros)))
-    return QLINEAR_ERR_MISALIGNED;
-  return hip_status(launch_qgemv_apply(*layout, make_runs(*layout), M, qweight, scales, zeros, y, workspace,
-                                       (hipStream_t)stream));
+  return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, qweight, scales, zeros, y, workspace,
+                                 (hipStream_t)stream));
 }
 
 int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes) {

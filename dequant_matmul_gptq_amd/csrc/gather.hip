@@ -27,8 +27,7 @@ __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __res
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const bool live = idx < pairs;
   const int blk = live ? idx / kPairsPerBlock : 0, p = idx % kPairsPerBlock;
-  int bits, row;
-  block_info(runs, blk, bits, row);
+  const int bits = block_bits_scan(runs, blk);
   int lo, hi;
   pair_rows(bits, p, lo, hi);
   const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;

@@ -1,0 +1,301 @@
+// Single-row decode kernel (M = 1) on gfx950: the act-order gather happens
+// inside the kernel, so a call is one launch.
+//
+// Work split as in the multi-row kernel: a workgroup of 4 or 8 waves owns a
+// 16-column panel and the whole K range; lane = (block slot ks, column quad
+// cq); a wave step is 16 consecutive blocks of one run, two steps in flight.
+//
+// Activations. The workgroup copies the x row (float16, original order) into
+// LDS; its loads are issued first, before any weight load (vector loads
+// complete in issue order, so a load issued after the weights would wait for
+// them). For its block, each lane of a column quad gathers 4 of the block's
+// 16 pairs: the perm entries of those 8 rows are loaded with the step's
+// weights, the values read from the LDS row and scaled by 2^-e (the exponent
+// at which the pair's codes are unpacked), and the four lanes of the quad
+// exchange their pairs with DPP broadcasts. The block sums X (activations)
+// and X' (scaled activations) are reduced over the quad the same way.
+// Arithmetic per block and column is that of the multi-row kernel:
+//   acc = sum_pairs dot2((1024 + q_lo 2^e, 1024 + q_hi 2^e), (x_lo 2^-e, x_hi 2^-e))
+//   y  += s * (acc - 1024 * X' - z * X)
+#pragma once
+
+#include "qgemv_stream.hpp"
+
+namespace qlinear {
+
+namespace stream {
+
+constexpr int kRowLdsBudget = 62 * 1024;  // bytes of LDS for the x row
+
+// LDS words of the x row (K float16, rounded up to 16 bytes).
+__host__ __device__ constexpr int row_words(int K) { return (K / 2 + 3) / 4 * 4; }
+
+// Whether a single-row call runs the single-row kernel: the x row must fit
+// in LDS, and the matrix must have a single code width. (Measured on MI355X:
+// with several widths, the short run segments of each wave and the perm
+// loads at 2-3 bits make the gather kernel plus the multi-row kernel faster.)
+inline bool single_row(int M, int K, unsigned set) {
+  return M == 1 && (size_t)row_words(K) * 4 <= kRowLdsBudget && (set & (set - 1)) == 0;
+}
+
+// Loads of one lane for one step: the block's weights, scale and zero point
+// (as in the multi-row kernel) and the perm entries of the lane's 4 pairs.
+struct StepRegs {
+  uint4 W[8];   // entries 0 .. B-1 used
+  Raw P;
+  int pl[4], ph[4];
+};
+
+// The lane's 4 pairs 4 cq + r of a block of width B: their rows in the block
+// and the scale 2^-e of their activations.
+template <int B>
+__device__ __forceinline__ void lane_pairs(int cq, int (&rlo)[4], int (&rhi)[4], float (&sc)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int p = 4 * cq + r;
+    pair_rows(B, p, rlo[r], rhi[r]);
+    sc[r] = __builtin_ldexpf(1.0f, -pair_exponent(B, p));
+  }
+}
+
+// The perm entries follow the block alone (blk_ok), not the lane's columns:
+// the four lanes of a quad exchange the pairs of one block, so a lane whose
+// columns lie past N must still gather its quad's block.
+template <int B>
+__device__ __forceinline__ void issue_step(const StreamArgs& a, const uint32_t* panel, const int32_t* psrc, int blk,
+                                           int row, bool blk_ok, bool ok, int blk_safe, int row_safe, int col,
+                                           const int (&rlo)[4], const int (&rhi)[4], StepRegs& S) {
+  issue<B>(a, panel, blk, row, ok, blk_safe, row_safe, col, reinterpret_cast<uint4(&)[B]>(S.W), S.P);
+  const int32_t* pb = psrc + (size_t)(blk_ok ? blk : blk_safe) * kBlockRows;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    S.pl[r] = pb[rlo[r]];
+    S.ph[r] = pb[rhi[r]];
+  }
+}
+
+__device__ __forceinline__ float quad_sum(float v) {
+  // quad_perm [1,0,3,2] then [2,3,0,1]
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  return v;
+}
+
+// Gather the lane's 4 pairs of block blk from the LDS row, exchange them over
+// the quad, then unpack and multiply the block for the lane's 4 columns.
+template <int B>
+__device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs& S, const _Float16* xrow, int blk,
+                                             const int (&rlo)[4], const int (&rhi)[4], const float (&sc)[4],
+                                             uint32_t magic, float (&yacc)[4]) {
+  uint32_t own[4];
+  float xs = 0.0f, xss = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
+    const int flo = a.perm ? (int)min((unsigned)S.pl[r], (unsigned)(a.K - 1)) : blk * kBlockRows + rlo[r];
+    const int fhi = a.perm ? (int)min((unsigned)S.ph[r], (unsigned)(a.K - 1)) : blk * kBlockRows + rhi[r];
+    const float vl = (float)xrow[flo], vh = (float)xrow[fhi];
+    const _Float16 sl = (_Float16)(vl * sc[r]), sh = (_Float16)(vh * sc[r]);
+    own[r] = (uint32_t)__builtin_bit_cast(uint16_t, sl) | ((uint32_t)__builtin_bit_cast(uint16_t, sh) << 16);
+    xs += vl + vh;
+    xss += (float)sl + (float)sh;
+  }
+  const float X = quad_sum(xs), Xs = quad_sum(xss);
+
+  const uint4* W = S.W;
+  uint32_t wc[4][B], wsh[4][B];
+#pragma unroll
+  for (int t = 0; t < B; ++t) {
+    wc[0][t] = W[t].x;
+    wc[1][t] = W[t].y;
+    wc[2][t] = W[t].z;
+    wc[3][t] = W[t].w;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int t = 0; t < B; ++t) wsh[c][t] = wc[c][t] >> scaled_shift(B);
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  static_for<0, kPairsPerBlock>([&](auto Q) {
+    constexpr int Pp = decltype(Q)::value;
+    const uint32_t xp = (uint32_t)__builtin_amdgcn_mov_dpp((int)own[Pp % 4], (Pp / 4) * 0x55, 0xF, 0xF, false);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t v = extract_pair_scaled<B, Pp>(wc[c], wsh[c], magic);
+      acc[c] = __builtin_amdgcn_fdot2(as_half2(v), as_half2(xp), acc[c], false);
+    }
+  });
+  float s[4], z[4];
+  s[0] = S.P.ok ? half_lo(S.P.s.x) : 0.0f;
+  s[1] = S.P.ok ? half_hi(S.P.s.x) : 0.0f;
+  s[2] = S.P.ok ? half_lo(S.P.s.y) : 0.0f;
+  s[3] = S.P.ok ? half_hi(S.P.s.y) : 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) z[c] = a.zeros ? (float)((S.P.z >> (8 * c)) & 0xFFu) : (float)(1 << (B - 1));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) yacc[c] = fmaf(s[c], fmaf(-z[c], X, acc[c] - 1024.0f * Xs), yacc[c]);
+}
+
+// Lane context shared by the steps of a wave.
+struct RowLane {
+  const uint32_t* panel;
+  const int32_t* psrc;
+  const _Float16* xrow;
+  int ks, cq, col;
+  bool colv;
+  uint32_t magic;
+};
+
+// Step i of the segment [blk0, blk1) starting at packed row row0.
+template <int B>
+__device__ __forceinline__ void seg_issue(const StreamArgs& a, const RowLane& L, int blk0, int blk1, int row0, int i,
+                                          const int (&rlo)[4], const int (&rhi)[4], StepRegs& S) {
+  const int blk = blk0 + i * KS + L.ks;
+  const bool blk_ok = blk < blk1;
+  issue_step<B>(a, L.panel, L.psrc, blk, row0 + (i * KS + L.ks) * B, blk_ok, L.colv && blk_ok, blk0, row0, L.col,
+                rlo, rhi, S);
+}
+
+// All steps of one run segment of this wave, two in flight. With kPre the
+// first two steps were issued already into S0 and S1.
+template <int B, bool kPre>
+__device__ __forceinline__ void row_segment(const StreamArgs& a, const RowLane& L, int blk0, int blk1, int row0,
+                                            float (&yacc)[4], StepRegs& S0, StepRegs& S1) {
+  int rlo[4], rhi[4];
+  float sc[4];
+  lane_pairs<B>(L.cq, rlo, rhi, sc);
+  const int nsteps = (blk1 - blk0 + KS - 1) / KS;
+  auto comp = [&](int i, const StepRegs& S) {
+    // Past the segment the whole quad is idle (zero scale); its pairs come
+    // from block blk0 (as its perm entries did).
+    const int blk = blk0 + i * KS + L.ks < blk1 ? blk0 + i * KS + L.ks : blk0;
+    compute_step<B>(a, S, L.xrow, blk, rlo, rhi, sc, L.magic, yacc);
+  };
+  if constexpr (!kPre) {
+    seg_issue<B>(a, L, blk0, blk1, row0, 0, rlo, rhi, S0);
+    seg_issue<B>(a, L, blk0, blk1, row0, 1, rlo, rhi, S1);   // past the end: a duplicate read, zero scale
+  }
+  for (int i = 0; i < nsteps; i += 2) {
+    comp(i, S0);
+    if (i + 2 < nsteps) seg_issue<B>(a, L, blk0, blk1, row0, i + 2, rlo, rhi, S0);
+    if (i + 1 >= nsteps) break;
+    comp(i + 1, S1);
+    if (i + 3 < nsteps) seg_issue<B>(a, L, blk0, blk1, row0, i + 3, rlo, rhi, S1);
+  }
+}
+
+// Dispatch on a run's width (only widths in BS are instantiated).
+template <unsigned BS, class F>
+__device__ __forceinline__ void with_width(int bits, F&& f) {
+  switch (bits) {
+    case 2: if constexpr ((BS >> 2) & 1u) f(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr ((BS >> 3) & 1u) f(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr ((BS >> 4) & 1u) f(std::integral_constant<int, 4>{}); break;
+    case 5: if constexpr ((BS >> 5) & 1u) f(std::integral_constant<int, 5>{}); break;
+    case 6: if constexpr ((BS >> 6) & 1u) f(std::integral_constant<int, 6>{}); break;
+    case 8: if constexpr ((BS >> 8) & 1u) f(std::integral_constant<int, 8>{}); break;
+    default: break;
+  }
+}
+
+// Sixteen-byte pieces of the x row per thread issued before the weights.
+constexpr int kRowPieces = 8;
+
+template <unsigned BS, int WV>
+__global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  __shared__ float red[WV][1][SC];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = blockIdx.x;
+  const int strip = (bid % kXcds) * a.strips_per_xcd + bid / kXcds;
+  if (strip >= a.nstrips) return;  // the whole workgroup leaves together
+
+  // 1. The x row: every piece this thread copies, loaded before anything else.
+  constexpr int nthr = WV * 64;
+  const int n16 = a.K / 8;
+  const uint4* xg = reinterpret_cast<const uint4*>(a.x);
+#define QLINEAR_PIECE(u) const uint4 xr##u = xg[min((u) * nthr + tid, n16 - 1)];
+  QLINEAR_PIECE(0) QLINEAR_PIECE(1) QLINEAR_PIECE(2) QLINEAR_PIECE(3)
+  QLINEAR_PIECE(4) QLINEAR_PIECE(5) QLINEAR_PIECE(6) QLINEAR_PIECE(7)
+#undef QLINEAR_PIECE
+  static_assert(kRowPieces == 8, "the row prefetch is written out for eight pieces");
+  asm volatile("" ::: "memory");   // keep the row loads ahead of the weight loads
+
+  // 2. The first two steps of the wave's first run segment.
+  const int nblk = a.K / kBlockRows;
+  const int wb0 = (wave * nblk) / WV, wb1 = ((wave + 1) * nblk) / WV;
+  int b0 = 0, row0 = 0;
+  if (wb0 < wb1) block_info(a.runs, wb0, b0, row0);
+  const int seg0_end = wb0 < wb1 ? min(wb1, run_end_block(a.runs, wb0)) : wb0;
+  RowLane L;
+  L.cq = lane % CQ;
+  L.ks = lane / CQ;
+  const int col_req = strip * SC + L.cq * 4;
+  L.colv = col_req < a.N;
+  L.col = L.colv ? col_req : a.N - 4;   // scale/zero column for lanes past N
+  L.panel = a.qweight + (size_t)strip * a.runs.packed_rows * kPanel + L.cq * 4;
+  L.psrc = a.perm ? a.perm : reinterpret_cast<const int32_t*>(a.qweight);   // >= K readable words
+  L.xrow = reinterpret_cast<const _Float16*>(lds);
+  L.magic = vgpr_magic();
+  StepRegs S0, S1;
+  with_width<BS>(b0, [&](auto BB) {
+    constexpr int B = decltype(BB)::value;
+    int rlo[4], rhi[4];
+    float sc[4];
+    lane_pairs<B>(L.cq, rlo, rhi, sc);
+    seg_issue<B>(a, L, wb0, seg0_end, row0, 0, rlo, rhi, S0);
+    seg_issue<B>(a, L, wb0, seg0_end, row0, 1, rlo, rhi, S1);
+  });
+
+  // 3. The row into LDS (clamped threads rewrite the last piece with its own value).
+  uint4* xl = reinterpret_cast<uint4*>(lds);
+#define QLINEAR_STORE(u) xl[min((u) * nthr + tid, n16 - 1)] = xr##u;
+  QLINEAR_STORE(0) QLINEAR_STORE(1) QLINEAR_STORE(2) QLINEAR_STORE(3)
+  QLINEAR_STORE(4) QLINEAR_STORE(5) QLINEAR_STORE(6) QLINEAR_STORE(7)
+#undef QLINEAR_STORE
+  for (int i = kRowPieces * nthr + tid; i < n16; i += nthr) xl[i] = xg[i];
+  __syncthreads();
+
+  // 4. Stream the wave's blocks, run segment by run segment.
+  float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  with_width<BS>(b0, [&](auto BB) { row_segment<decltype(BB)::value, true>(a, L, wb0, seg0_end, row0, yacc, S0, S1); });
+  for (int blk = seg0_end; blk < wb1;) {
+    int bits, row;
+    block_info(a.runs, blk, bits, row);
+    const int seg_end = min(wb1, run_end_block(a.runs, blk));
+    with_width<BS>(bits, [&](auto BB) { row_segment<decltype(BB)::value, false>(a, L, blk, seg_end, row, yacc, S0, S1); });
+    blk = seg_end;
+  }
+
+  float y4[4][1] = {{yacc[0]}, {yacc[1]}, {yacc[2]}, {yacc[3]}};
+  reduce_store<1, WV>(a, red, y4, tid, lane, wave, strip);
+}
+
+template <unsigned BS, int WV>
+hipError_t launch_row(StreamArgs a, hipStream_t stream) {
+  a.nstrips = (a.N + SC - 1) / SC;
+  a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
+  a.xrow_words = row_words(a.K);
+  const size_t lds = (size_t)a.xrow_words * 4;
+  hipLaunchKernelGGL((qgemv_row_kernel<BS, WV>), dim3(kXcds * a.strips_per_xcd), dim3(WV * 64), lds, stream, a);
+  return hipGetLastError();
+}
+
+// kMaxWv: the most waves per workgroup instantiated for this width set.
+template <unsigned BS, int kMaxWv>
+hipError_t launch_row_any(const StreamArgs& a, hipStream_t stream) {
+  if constexpr (kMaxWv >= 8) {
+    if (waves_for(a.N, a.K) >= 8) return launch_row<BS, 8>(a, stream);
+  }
+  return launch_row<BS, 4>(a, stream);
+}
+
+// Instantiated in qgemv_row.hip.
+hipError_t launch_row_set(unsigned set, const StreamArgs& a, hipStream_t stream);
+
+}  // namespace stream
+
+}  // namespace qlinear

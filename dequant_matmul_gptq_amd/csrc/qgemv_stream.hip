@@ -1,7 +1,7 @@
-// Host side of the decode path: workspace layout, the act-order gather, and
-// the choice of the streaming kernel instantiated for the smallest set of code
-// widths covering the layout.
-#include "qgemv_stream.hpp"
+// Host side of the decode path: the single-row kernel for M = 1, otherwise
+// the act-order gather into the workspace and the multi-row kernel
+// instantiated for the smallest set of code widths covering the layout.
+#include "qgemv_m1.hpp"
 
 namespace qlinear {
 
@@ -22,19 +22,14 @@ GemvWorkspace qgemv_workspace(void* ws, int K) {
   return w;
 }
 
-hipError_t launch_qgemv_gather(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
-                               const int32_t* perm, void* ws, hipStream_t stream) {
-  const GemvWorkspace w = qgemv_workspace(ws, L.K);
-  return launch_gather_pairs(runs, x, perm, M, L.K, w.xq, w.xsum, true, stream);
-}
-
-hipError_t launch_qgemv_apply(const qlinear_layout& L, const Runs& runs, int M, const uint32_t* qweight,
-                              const uint16_t* scales, const uint8_t* zeros, uint16_t* y, void* ws,
-                              hipStream_t stream) {
-  const GemvWorkspace w = qgemv_workspace(ws, L.K);
+hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M, const int32_t* perm,
+                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y, void* ws,
+                        hipStream_t stream) {
   stream::StreamArgs a;
-  a.xq = w.xq;
-  a.xsum = w.xsum;
+  a.x = x;
+  a.perm = perm;
+  a.xq = nullptr;
+  a.xsum = nullptr;
   a.qweight = qweight;
   a.scales = scales;
   a.zeros = zeros;
@@ -45,11 +40,19 @@ hipError_t launch_qgemv_apply(const qlinear_layout& L, const Runs& runs, int M, 
   a.nstrips = 0;
   a.strips_per_xcd = 0;
   a.chunk = 1;
+  a.xrow_words = 0;
   a.bpg_shift = L.group_size == 128 ? 2 : L.group_size == 64 ? 1 : 0;
   a.runs = runs;
-  if (M > 4) return stream::launch_wide(a, stream);
   unsigned set = 0;
   for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
+  if (stream::single_row(M, L.K, set)) return stream::launch_row_set(set, a, stream);
+  // The activations are gathered into the workspace by a kernel of their own.
+  const GemvWorkspace w = qgemv_workspace(ws, L.K);
+  const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, w.xsum, true, stream);
+  if (e != hipSuccess) return e;
+  a.xq = w.xq;
+  a.xsum = w.xsum;
+  if (M > 4) return stream::launch_wide(a, stream);
   if ((set & (set - 1)) == 0) return stream::launch_uniform(set, a, stream);
   return stream::launch_mixed(set, a, stream);
 }

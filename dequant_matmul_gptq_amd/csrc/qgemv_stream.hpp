@@ -1,16 +1,24 @@
 // Decode-sized quantized linear layer (M <= 16) on gfx950: one pass over the
 // packed weights at HBM speed, with no cross-workgroup reduction.
 //
-// Work split. A 256-thread workgroup owns a strip of 16 output columns -- one
-// storage panel, whose packed rows are contiguous in memory -- and the whole
-// K range, so it writes its float16 outputs directly: no split-K,
-// no atomics. Inside a wave, lane = (block slot ks, column quad cq):
-// 4 column quads x 16 block slots. Each lane unpacks whole 32-row blocks of
-// its 4 columns, streaming the block's b words with b 16-byte loads; a wave
-// step covers 16 consecutive blocks of one run (uniform bit width). The 4
-// waves take contiguous quarters of K; the step after the one being computed
-// is in flight (double buffering), and the first step is issued before the
-// activations are staged, so its HBM latency overlaps the staging.
+// Work split. A workgroup of 4 or 8 waves owns a strip of 16 output columns
+// -- one storage panel, whose packed rows are contiguous in memory -- and the
+// whole K range, so it writes its float16 outputs directly: no split-K, no
+// atomics. Inside a wave, lane = (block slot ks, column quad cq): 4 column
+// quads x 16 block slots. Each lane unpacks whole 32-row blocks of its 4
+// columns, streaming the block's b words with b 16-byte loads; a wave step
+// covers 16 consecutive blocks of one run (uniform bit width). The waves take
+// contiguous parts of K; the step after the one being computed is in flight
+// (double buffering), and the first step is issued before the activations
+// are staged, so its HBM latency overlaps the staging.
+//
+// Activations. For M = 1 the kernel gathers them itself: the perm entries of
+// the wave's first blocks and the whole x row are loaded first, before the
+// weights (vector loads complete in issue order, so anything issued after the
+// weights would wait for them), the x row goes to LDS, and each wave builds
+// its own act-order-gathered, pair-ordered copy from there. For M > 1 a
+// separate gather kernel writes that copy to the workspace and each wave
+// copies its part into LDS.
 //
 // Strips are assigned XCD by XCD: workgroups are dispatched round-robin over
 // the 8 XCDs, so workgroup i is given a strip from XCD (i % 8)'s contiguous
@@ -18,18 +26,17 @@
 //
 // Arithmetic per block, column and activation row. The codes come out of the
 // packed words as float16 pairs 1024 + q * 2^e (mask in place; one shift per
-// word for the fields above bit 10), the activations were gathered by
-// act-order and pre-scaled by 2^-e by the gather kernel, and
+// word for the fields above bit 10), the activations are gathered by
+// act-order and pre-scaled by 2^-e, and
 //   acc = sum_pairs dot2((1024 + q_lo 2^e, 1024 + q_hi 2^e), (x_lo 2^-e, x_hi 2^-e))
 //       = sum_j x_j q_j + 1024 * X'_blk
 //   y  += s * (acc - 1024 * X'_blk - z * X_blk)
-// where X_blk and 1024 * X'_blk are the block sums the gather kernel wrote.
-// Products of float16 values are exact in float32; accumulation is float32.
+// where X_blk is the block's sum of activations and X'_blk that of the
+// scaled ones. Products of float16 values are exact in float32; accumulation
+// is float32.
 //
-// Each wave copies the activations of its own K range from the workspace
-// into LDS (16-byte copies; in chunks when M * K is large). Reduction:
-// butterfly shuffles across the 16 block slots of a wave, then across the 4
-// waves through LDS.
+// Reduction: butterfly shuffles across the 16 block slots of a wave, then
+// across the waves through LDS.
 #pragma once
 
 #include "qlinear_kernels.hpp"
@@ -46,6 +53,8 @@ constexpr int kXcds = 8;
 constexpr int kStageBudget = 60 * 1024;  // bytes of LDS for staged activations
 
 struct StreamArgs {
+  const uint16_t* x;       // single-row kernel: the activations, float16 [K], original order
+  const int32_t* perm;     // single-row kernel: act-order permutation or NULL
   const uint32_t* xq;      // gathered, scaled activations, [M][K/32][16] float16 pairs
   const float2* xsum;      // block sums (X, 1024 * X'), [M][K/32]
   const uint32_t* qweight;
@@ -55,6 +64,7 @@ struct StreamArgs {
   int M, K, N;
   int nstrips, strips_per_xcd;
   int chunk;               // blocks per wave staged at a time
+  int xrow_words;          // single-row kernel: LDS words holding the x row
   int bpg_shift;           // log2(group_size / 32)
   Runs runs;
 };
@@ -236,6 +246,40 @@ __host__ __device__ constexpr int stage_words(int chunk) {
   return (chunk * MT * (kPairsPerBlock + 2) + 3) / 4 * 4;
 }
 
+// Reduce the lane sums over the 16 block slots of each wave (lanes cq,
+// cq + 4, ..., cq + 60), then over the waves through LDS, and store y.
+template <int MT, int WV>
+__device__ __forceinline__ void reduce_store(const StreamArgs& a, float (&red)[WV][MT][SC], float (&yacc)[4][MT],
+                                             int tid, int lane, int wave, int strip) {
+  const int cq = lane % CQ, ks = lane / CQ;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float v = yacc[c][m];
+#pragma unroll
+      for (int off = CQ; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+      yacc[c][m] = v;
+    }
+  if (ks == 0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) red[wave][m][cq * 4 + c] = yacc[c][m];
+  }
+  __syncthreads();
+  if (tid < SC * MT) {
+    const int m = tid / SC, c = tid % SC;
+    const int n = strip * SC + c;
+    if (m < a.M && n < a.N) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WV; ++w) v += red[w][m][c];
+      a.y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
+  }
+}
+
 // Kernel body, specialised on B0, the width of this wave's first run, so the
 // first step can be issued into a typed buffer before the activation staging.
 template <int MT, unsigned BS, int WV, int B0>
@@ -263,7 +307,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, 
   Raw P0;
   const int seg0_end = wb0 < wb1 ? min(min(wb1, run_end_block(a.runs, wb0)), wb0 + a.chunk) : wb0;
   {
-    // A wave without blocks (K < 128 rows) reads block 0 and discards it.
+    // A wave without blocks (K < 32 * waves) reads block 0 and discards it.
     const int blk = wb0 + ks;
     const bool any = wb0 < wb1;
     issue<B0>(a, panel, blk, row0 + ks * B0, any && colv && blk < seg0_end, any ? wb0 : 0, any ? row0 : 0, col, W0,
@@ -326,33 +370,13 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, 
     }
   }
 
-  // Reduce over the 16 block slots of the wave (lanes cq, cq + 4, ..., cq + 60).
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float v = yacc[c][m];
-#pragma unroll
-      for (int off = CQ; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-      yacc[c][m] = v;
-    }
-  if (ks == 0) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) red[wave][m][cq * 4 + c] = yacc[c][m];
-  }
-  __syncthreads();
-  if (tid < SC * MT) {
-    const int m = tid / SC, c = tid % SC;
-    const int n = strip * SC + c;
-    if (m < a.M && n < a.N) {
-      float v = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WV; ++w) v += red[w][m][c];
-      a.y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
-    }
-  }
+  reduce_store<MT, WV>(a, red, yacc, tid, lane, wave, strip);
+}
+
+template <int MT, unsigned BS, int WV, int B0>
+__device__ __forceinline__ void dispatch_body(const StreamArgs& a, uint32_t* lds, float (&red)[WV][MT][SC], int tid,
+                                              int lane, int wave, int strip, int wb0, int wb1, int row0) {
+  stream_body<MT, BS, WV, B0>(a, lds, red, tid, lane, wave, strip, wb0, wb1, row0);
 }
 
 // One kernel per (MT, set of code widths that may occur). BS has bit b set
@@ -375,9 +399,10 @@ __global__ __launch_bounds__(WV * 64) void qgemv_stream_kernel(StreamArgs a) {
   const int wb0 = (wave * nblk) / WV, wb1 = ((wave + 1) * nblk) / WV;
   int bits0 = 0, row0 = 0;
   if (wb0 < wb1) block_info(a.runs, wb0, bits0, row0);
+
 #define QLINEAR_BODY(BB)                                                                     \
   case BB:                                                                                   \
-    if constexpr ((BS >> BB) & 1u) stream_body<MT, BS, WV, BB>(a, lds, red, tid, lane, wave, strip, wb0, wb1, row0); \
+    if constexpr ((BS >> BB) & 1u) dispatch_body<MT, BS, WV, BB>(a, lds, red, tid, lane, wave, strip, wb0, wb1, row0);                                              \
     return;
   switch (bits0) {
     QLINEAR_BODY(2)
@@ -391,8 +416,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_stream_kernel(StreamArgs a) {
 #undef QLINEAR_BODY
   // This wave has no blocks (K too small for every wave): it still joins the
   // barriers of the staging and the final reduction, which the other waves run.
-  stream_body<MT, BS, WV, (BS & 16u) ? 4 : (BS & 4u) ? 2 : (BS & 8u) ? 3 : (BS & 32u) ? 5 : (BS & 64u) ? 6 : 8>(
-      a, lds, red, tid, lane, wave, strip, wb0, wb1, row0);
+  dispatch_body<MT, BS, WV, (BS & 16u) ? 4 : (BS & 4u) ? 2 : (BS & 8u) ? 3 : (BS & 32u) ? 5 : (BS & 64u) ? 6 : 8>(a, lds, red, tid, lane, wave, strip, wb0, wb1, row0);
 }
 
 template <int MT, unsigned BS, int WV>
@@ -402,9 +426,9 @@ hipError_t launch_set(StreamArgs a, hipStream_t stream) {
   const int max_chunk = (kStageBudget / (WV * 4) - 3) / (MT * (kPairsPerBlock + 2));
   a.chunk = per_wave < max_chunk ? per_wave : max_chunk;
   if (a.chunk < 1) a.chunk = 1;
+  const size_t lds = (size_t)WV * stage_words<MT>(a.chunk) * 4;
   a.nstrips = (a.N + SC - 1) / SC;
   a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
-  const size_t lds = (size_t)WV * stage_words<MT>(a.chunk) * 4;
   hipLaunchKernelGGL((qgemv_stream_kernel<MT, BS, WV>), dim3(kXcds * a.strips_per_xcd), dim3(WV * 64), lds, stream,
                      a);
   return hipGetLastError();
@@ -417,14 +441,11 @@ inline int waves_for(int N, int K) {
   return (nstrips <= 512 && K / kBlockRows >= 256) ? 8 : 4;
 }
 
-// kMaxWv: the most waves per workgroup instantiated for M = 1 for this width set.
-template <unsigned BS, int kMaxWv>
-hipError_t launch_set_any_m(const StreamArgs& a, hipStream_t stream) {
+// Kernels for M <= 4 with the activations gathered by the gather kernel.
+template <unsigned BS>
+hipError_t launch_set_small_m(const StreamArgs& a, hipStream_t stream) {
   if (a.M <= 1) {
-    const int wv = waves_for(a.N, a.K);
-    if constexpr (kMaxWv >= 8) {
-      if (wv >= 8) return launch_set<1, BS, 8>(a, stream);
-    }
+    if (waves_for(a.N, a.K) >= 8) return launch_set<1, BS, 8>(a, stream);
     return launch_set<1, BS, 4>(a, stream);
   }
   if (a.M <= 2) return launch_set<2, BS, 4>(a, stream);

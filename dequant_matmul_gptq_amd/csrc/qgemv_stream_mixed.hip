@@ -1,4 +1,4 @@
-// Streaming decode kernels for mixed-width (EXL2) matrices.
+// Multi-row (2 <= M <= 4) decode kernels for mixed-width (EXL2) matrices.
 #include "qgemv_stream.hpp"
 
 namespace qlinear {
@@ -8,9 +8,9 @@ constexpr unsigned kLowBits = (1u << 2) | (1u << 3);                            
 constexpr unsigned kMidBits = (1u << 3) | (1u << 4) | (1u << 5) | (1u << 6);   // ~3.5-5 bpw
 
 hipError_t launch_mixed(unsigned set, const StreamArgs& a, hipStream_t stream) {
-  if ((set & ~kLowBits) == 0) return launch_set_any_m<kLowBits, 8>(a, stream);
-  if ((set & ~kMidBits) == 0) return launch_set_any_m<kMidBits, 8>(a, stream);
-  return launch_set_any_m<kAllBits, 4>(a, stream);
+  if ((set & ~kLowBits) == 0) return launch_set_small_m<kLowBits>(a, stream);
+  if ((set & ~kMidBits) == 0) return launch_set_small_m<kMidBits>(a, stream);
+  return launch_set_small_m<kAllBits>(a, stream);
 }
 
 }  // namespace stream

@@ -1,4 +1,4 @@
-// Streaming decode kernels for matrices with a single code width.
+// Multi-row (2 <= M <= 4) decode kernels for matrices with a single code width.
 #include "qgemv_stream.hpp"
 
 namespace qlinear {
@@ -6,12 +6,12 @@ namespace stream {
 
 hipError_t launch_uniform(unsigned set, const StreamArgs& a, hipStream_t stream) {
   switch (set) {
-    case 1u << 2: return launch_set_any_m<1u << 2, 4>(a, stream);
-    case 1u << 3: return launch_set_any_m<1u << 3, 4>(a, stream);
-    case 1u << 4: return launch_set_any_m<1u << 4, 8>(a, stream);
-    case 1u << 5: return launch_set_any_m<1u << 5, 4>(a, stream);
-    case 1u << 6: return launch_set_any_m<1u << 6, 4>(a, stream);
-    default: return launch_set_any_m<1u << 8, 4>(a, stream);
+    case 1u << 2: return launch_set_small_m<1u << 2>(a, stream);
+    case 1u << 3: return launch_set_small_m<1u << 3>(a, stream);
+    case 1u << 4: return launch_set_small_m<1u << 4>(a, stream);
+    case 1u << 5: return launch_set_small_m<1u << 5>(a, stream);
+    case 1u << 6: return launch_set_small_m<1u << 6>(a, stream);
+    default: return launch_set_small_m<1u << 8>(a, stream);
   }
 }
 

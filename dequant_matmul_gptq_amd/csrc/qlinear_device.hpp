@@ -46,6 +46,16 @@ __device__ __forceinline__ void block_info(const Runs& R, int blk, int& bits, in
   row = R.run_row[r] + (blk - R.run_block[r]) * bits;
 }
 
+// Bit width of block `blk` when blk differs between lanes: a scan over the
+// runs with wave-uniform indices, so the table is read with scalar loads
+// (a lane-dependent index into the kernel arguments becomes a vector load,
+// and waiting for it waits for every vector load issued before it).
+__device__ __forceinline__ int block_bits_scan(const Runs& R, int blk) {
+  int bits = R.run_bits[0];
+  for (int r = 1; r < R.nruns; ++r) bits = blk >= R.run_block[r] ? R.run_bits[r] : bits;
+  return bits;
+}
+
 // Last block (exclusive) of the run that contains `blk`.
 __device__ __forceinline__ int run_end_block(const Runs& R, int blk) {
   int r = 0;

@@ -21,22 +21,19 @@ hipError_t launch_dequant(const qlinear_layout& L, const Runs& runs, const uint3
 hipError_t launch_gather_pairs(const Runs& runs, const uint16_t* x, const int32_t* perm, int M, int K,
                                uint32_t* xq, float2* xsum, bool scaled, hipStream_t stream);
 
-// Decode layer (M <= 16). The workspace holds the gathered activations xq
-// uint32 [16][K/32][16] and the block sums xsum float2 [16][K/32]; it is
-// scratch (no initialization, contents not preserved).
+// Decode layer (M <= 16). For M > 1 (and for rows too long for the fused
+// M = 1 kernel) the workspace receives the gathered activations xq uint32
+// [M][K/32][16] and the block sums xsum float2 [M][K/32]; it is scratch (no
+// initialization, contents not preserved).
 struct GemvWorkspace {
   uint32_t* xq;
   float2* xsum;
 };
 size_t qgemv_workspace_bytes(int K);
 GemvWorkspace qgemv_workspace(void* ws, int K);
-// The two phases: the act-order gather of x into the workspace, then the
-// streaming kernel over the packed weights.
-hipError_t launch_qgemv_gather(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
-                               const int32_t* perm, void* ws, hipStream_t stream);
-hipError_t launch_qgemv_apply(const qlinear_layout& L, const Runs& runs, int M, const uint32_t* qweight,
-                              const uint16_t* scales, const uint8_t* zeros, uint16_t* y, void* ws,
-                              hipStream_t stream);
+hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M, const int32_t* perm,
+                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y, void* ws,
+                        hipStream_t stream);
 
 // Prefill layer. ws holds the gathered activations, float16 [M][K].
 size_t qgemm_workspace_bytes(int M, int K);

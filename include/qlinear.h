@@ -133,8 +133,9 @@ int qlinear_dequant(const qlinear_layout* layout, const uint32_t* qweight, const
                     const uint8_t* zeros, uint16_t* w, void* stream);
 
 /*
- * Workspace of qlinear_qgemv, in bytes, for any M <= QLINEAR_GEMV_MAX_M. It
- * receives the act-order-gathered activations and their 32-row block sums.
+ * Workspace of qlinear_qgemv, in bytes, for any M <= QLINEAR_GEMV_MAX_M. For
+ * M > 1 it receives the act-order-gathered activations and their 32-row
+ * block sums (M = 1 gathers inside the kernel's LDS unless K is very large).
  * It is scratch: no initialization is needed and its contents are not
  * preserved. Calls that may overlap in time (different streams) must not
  * share one workspace.
@@ -157,22 +158,6 @@ int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M,
                   const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                   const int32_t* perm, uint16_t* y, void* workspace, size_t workspace_bytes,
                   void* stream);
-
-/*
- * The two phases of qlinear_qgemv, for callers that schedule them separately
- * (for example, the gather of one layer on a second stream while the previous
- * layer's apply runs; the two then need separate workspaces).
- * qlinear_qgemv_gather writes the act-order-gathered activations x[:, perm]
- * (in the order the packed words unpack to) and their 32-row block sums into
- * the workspace. qlinear_qgemv_apply reads them and computes y; it must run
- * after a gather with the same layout, M and workspace (stream order).
- * Arguments and errors as for qlinear_qgemv; M == 0 returns OK.
- */
-int qlinear_qgemv_gather(const qlinear_layout* layout, const uint16_t* x, int32_t M, const int32_t* perm,
-                         void* workspace, size_t workspace_bytes, void* stream);
-int qlinear_qgemv_apply(const qlinear_layout* layout, int32_t M, const uint32_t* qweight,
-                        const uint16_t* scales, const uint8_t* zeros, uint16_t* y, void* workspace,
-                        size_t workspace_bytes, void* stream);
 
 /* Workspace of qlinear_qgemm for M tokens, in bytes (no initialization needed). */
 int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes);

@@ -20,15 +20,16 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
-def test_apply_bytes_counts_each_operand_once():
+def test_row_kernel_bytes_count_each_operand_once():
     spec = wl.LLAMA7B_DECODE[0]                     # 4096 -> 4096, 4-bit, g128
     L = dq.Layout(spec.K, spec.N, spec.group_size, wl.bit_map(spec))
     codes = 4096 * 4096 // 2
     scales = 32 * 4096 * 2
     zeros = 32 * 4096                               # uint8 zero points
-    act = 4096 * 2 + 128 * 8 + 4096 * 2             # gathered x, block sums, y
-    assert bench.apply_bytes(L, 1) == codes + scales + zeros + act
-    assert bench.apply_bytes(L, 1, zeros=False) == codes + scales + act
+    act = 4096 * 2 + 4096 * 4 + 4096 * 2            # x, perm, y
+    assert bench.row_kernel_bytes(L, 1) == codes + scales + zeros + act
+    assert bench.row_kernel_bytes(L, 1, zeros=False) == codes + scales + act
+    assert bench.row_kernel_bytes(L, 1, perm=False) == codes + scales + zeros + act - 4096 * 4
     # the nominal weight bytes count zeros at 4 bits
     assert wl.weight_bytes(spec) == codes + scales + zeros // 2
 
@@ -37,12 +38,12 @@ def test_mixed_width_codes_bytes():
     bits = np.array([6, 5, 4, 3, 2, 8], np.uint8)
     L = dq.Layout(6 * 32, 64, 32, bits)
     codes = int(sum(int(b) * 32 * 64 for b in bits)) // 8
-    assert bench.apply_bytes(L, 2, zeros=False) == codes + 6 * 64 * 2 + 2 * 192 * 2 + 2 * 6 * 8 + 2 * 64 * 2
+    assert bench.row_kernel_bytes(L, 1, zeros=False) == codes + 6 * 64 * 2 + 192 * 2 + 192 * 4 + 64 * 2
 
 
 def test_recorded_traffic_is_tied_to_the_kernel_sources(tmp_path, monkeypatch):
     f = tmp_path / "t.txt"
-    f.write_text(f"# comment\nkernel_sources_sha256_16: {bench.stream_kernel_digest()}\nhbm_bytes_per_launch: 123.0\n")
+    f.write_text(f"# comment\nkernel_sources_sha256_16: {bench.row_kernel_digest()}\nhbm_bytes_per_launch: 123.0\n")
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.recorded_traffic() == 123
     f.write_text("kernel_sources_sha256_16: 0000000000000000\nhbm_bytes_per_launch: 123\n")

@@ -100,6 +100,17 @@ def test_qgemm_uniform_widths(b, gs):
     assert_close(y, _ref(inp), f"qgemm b={b} gs={gs}")
 
 
+@pytest.mark.parametrize("K", (31744, 33792))
+def test_qgemv_long_rows(K):
+    """M = 1 rows near and past the LDS capacity of the single-row kernel (the
+    longer one runs the multi-row path)."""
+    say(f"qgemv long row K={K}")
+    bits = [3] * (K // 64) + [2] * (K // 64)
+    inp = _mixed_inputs(bits, 32, 48, 1, seed=K % 97, zeros=False)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv K={K}")
+
+
 def test_no_act_order_and_single_group():
     say("no act-order, one group")
     inp = _mixed_inputs([4], 32, 8, 3, seed=1, zeros=True, act_order=False)
@@ -154,19 +165,6 @@ def test_workspace_is_scratch_and_shareable():
         assert_close(la.qgemv(a.x), _ref(a), "a")
         assert_close(lb.qgemv(b.x), _ref(b), "b")
         assert_close(lb.qgemv(b.x[:1]), _ref(b, b.x[:1]), "b M=1")
-
-
-def test_two_phase_qgemv_matches_one_call():
-    """gather + apply on their own give the same y as qlinear_qgemv."""
-    say("two-phase qgemv")
-    inp = _mixed_inputs(MIXED_BITS, 32, 520, 3, seed=12, zeros=True)
-    lay = GpuLayer(inp)
-    x = lay.x(inp.x)
-    y1 = lay.qgemv(inp.x)
-    dq.qgemv_gather(lay.layout, x, lay.perm, lay.ws)
-    y2 = dq.qgemv_apply(lay.layout, 3, lay.qweight, lay.scales, lay.zeros, lay.ws)
-    assert torch.equal(y1, y2)
-    assert_close(y2, _ref(inp), "two-phase")
 
 
 # ------------------------------------------------------------------ full-size workloads

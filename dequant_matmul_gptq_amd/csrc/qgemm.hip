@@ -4,13 +4,27 @@
 //    the workspace, xq[m][32*blk + 2p + h] = x[m][perm[32*blk + row_h(p)]],
 //    where (row_0(p), row_1(p)) are the two rows that pair p of block blk
 //    unpacks to. Inside every 32-row block the K order is thus the unpacking
-//    order, and the same reordering is applied to the weights below, so the
+//    order, and the weights below are used in that same order, so the
 //    contraction is unchanged.
-// 2. gemm_kernel: each workgroup computes a 128 x 128 tile of y. Per K-step
-//    of 64 rows (two 32-row blocks) it copies the activation tile to LDS,
-//    unpacks and dequantizes the weight tile exactly to float16 in LDS
-//    (w = RNE(s * (q - z)), one rounding) and runs v_mfma_f32_16x16x32_f16
-//    on it, accumulating in float32; the epilogue rounds to float16.
+// 2. gemm_kernel (one code width; several widths go to the kernel in
+//    qgemm_lds.hip): a workgroup of 4 waves computes a 256 x 128 tile of y,
+//    each wave a 128 x 64 quarter as 8 x 4 fragments of
+//    v_mfma_f32_16x16x32_f16 (one 32-row block is one MFMA K step).
+//      - B (weights): no LDS. The B operand of a 16 x 16 x 32 MFMA gives
+//        lane l column l % 16 of the fragment and rows 8 (l / 16) .. + 7 of
+//        the block, i.e. pairs 4g .. 4g + 3 (g = l / 16); for 4-bit codes
+//        those are exactly packed word g of the column. A lane's 4 fragments
+//        take 4 adjacent columns, so one 16-byte load brings word g of all
+//        four. Each wave dequantizes its fragments exactly to float16 in
+//        registers (w = RNE(s * (q - z)), one rounding); each fragment feeds
+//        8 MFMAs. The packed words run two blocks ahead in a register ring.
+//      - A (activations): two LDS stages; block kb + 1's tile is loaded into
+//        registers during block kb and stored after its MFMAs; one barrier
+//        per block.
+//    Buffer loads take their per-block offsets in scalars. Two workgroups
+//    per CU (256 registers per lane): while one wave unpacks, another
+//    wave's MFMAs keep the matrix core busy.
+//    Accumulation is float32; the epilogue rounds to float16.
 #include "qlinear_kernels.hpp"
 
 namespace qlinear {
@@ -18,9 +32,16 @@ namespace qlinear {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kPad = 8;                 // halves of padding per LDS row
-constexpr int kLdsRow = BK + kPad;      // 72 halves = 144 bytes
+constexpr int BM = 256, BN = 128;
+constexpr int WM = 128, WN = 64;             // wave tile: 2 x 2 waves
+constexpr int FM = WM / 16, FN = WN / 16;    // 8 x 4 fragments per wave
+constexpr int kPad = 8;                      // halves of padding per LDS row
+constexpr int kLdsRow = kBlockRows + kPad;   // 40 halves = 80 bytes
+constexpr int kAPieces = BM * kBlockRows / 8 / kThreads;  // 16-byte pieces of an A block per thread
+constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, 32-bit data
+
+// Native vector type: arrays of HIP's uint4 struct are kept in scratch memory.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   const uint16_t* xq;
@@ -29,135 +50,313 @@ struct GemmArgs {
   const uint8_t* zeros;
   uint16_t* y;
   int M, K, N;
+  int xq_bytes, qweight_bytes, scale_bytes;
   Runs runs;
 };
 
-// Unpack + dequantize one (block, column) into 16 float16 pairs in LDS.
-template <int B>
-__device__ __forceinline__ void dequant_to_lds(const GemmArgs& a, int row, int g, int n, bool valid,
-                                               uint32_t* dst /* 16 words */) {
-  uint32_t w[B];
-#pragma unroll
-  for (int t = 0; t < B; ++t) w[t] = valid ? a.qweight[word_index(a.runs.packed_rows, row + t, n)] : 0u;
-  _Float16 s = (_Float16)0.0f;
-  int z = 1 << (B - 1);
-  if (valid) {
-    s = __builtin_bit_cast(_Float16, a.scales[(size_t)g * a.N + n]);
-    if (a.zeros) z = a.zeros[(size_t)g * a.N + n];
-  }
-  const _Float16 nb = (_Float16)(-(1024 + z));
-  const half2_t scale = {s, s}, neg_bias = {nb, nb};
-  uint32_t pr[kPairsPerBlock];
-  extract_all_pairs<B>(w, pr);
-#pragma unroll
-  for (int q4 = 0; q4 < kPairsPerBlock / 4; ++q4) {
-    uint4 v;
-    v.x = as_u32(dequant_pair(pr[4 * q4 + 0], neg_bias, scale));
-    v.y = as_u32(dequant_pair(pr[4 * q4 + 1], neg_bias, scale));
-    v.z = as_u32(dequant_pair(pr[4 * q4 + 2], neg_bias, scale));
-    v.w = as_u32(dequant_pair(pr[4 * q4 + 3], neg_bias, scale));
-    *reinterpret_cast<uint4*>(dst + 4 * q4) = v;
+template <int I, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, E>(f);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint16_t As[BM * kLdsRow];
-  __shared__ __align__(16) uint16_t Bs[BN * kLdsRow];
+// Packed words of one (block, column) that the lanes of k-group g read, and
+// the first of them (relative to the block's first packed row). Widths 2, 4
+// and 8 keep a k-group's four pairs in one or two words; 3, 5 and 6 spread
+// them, and all b words are read.
+template <int B>
+constexpr int frag_words() {
+  return (B == 2 || B == 4) ? 1 : B == 8 ? 2 : B;
+}
+template <int B>
+__device__ __forceinline__ int frag_first_word(int g) {
+  return B == 4 ? g : B == 2 ? g / 2 : B == 8 ? 2 * g : 0;
+}
+template <unsigned BS>
+constexpr int max_frag_words() {
+  int m = 1;
+  if ((BS >> 3) & 1u) m = m > 3 ? m : 3;
+  if ((BS >> 5) & 1u) m = m > 5 ? m : 5;
+  if ((BS >> 6) & 1u) m = m > 6 ? m : 6;
+  if ((BS >> 8) & 1u) m = m > 2 ? m : 2;
+  return m;
+}
+
+constexpr int kRing = 2;   // blocks of B loads in flight; also LDS stages of the A tile
+
+template <unsigned BS, class F>
+__device__ __forceinline__ void with_width(int bits, F&& f) {
+  switch (bits) {
+    case 2: if constexpr ((BS >> 2) & 1u) f(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr ((BS >> 3) & 1u) f(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr ((BS >> 4) & 1u) f(std::integral_constant<int, 4>{}); break;
+    case 5: if constexpr ((BS >> 5) & 1u) f(std::integral_constant<int, 5>{}); break;
+    case 6: if constexpr ((BS >> 6) & 1u) f(std::integral_constant<int, 6>{}); break;
+    case 8: if constexpr ((BS >> 8) & 1u) f(std::integral_constant<int, 8>{}); break;
+    default: break;
+  }
+}
+
+// The B fragment of k-group g from the words read for it: pairs 4g .. 4g + 3
+// as 1024 + q, then (1024 + q) - (1024 + z) exactly and one rounding of s * d.
+template <int B, int kW>
+__device__ __forceinline__ half8_t dequant_frag(const uint32_t (&w)[kW], int g, half2_t neg_bias, half2_t scale,
+                                               uint32_t magic) {
+  uint32_t pr[4];
+  if constexpr (B == 4 || B == 8) {
+    pr[0] = extract_pair<B, 0>(w, magic);
+    pr[1] = extract_pair<B, 1>(w, magic);
+    pr[2] = extract_pair<B, 2>(w, magic);
+    pr[3] = extract_pair<B, 3>(w, magic);
+  } else if constexpr (B == 2) {
+    const uint32_t ws[1] = {w[0] >> (8 * (g & 1))};
+    pr[0] = extract_pair<2, 0>(ws, magic);
+    pr[1] = extract_pair<2, 1>(ws, magic);
+    pr[2] = extract_pair<2, 2>(ws, magic);
+    pr[3] = extract_pair<2, 3>(ws, magic);
+  } else {
+    uint32_t all[kPairsPerBlock];
+#pragma unroll
+    for (int p = 0; p < kPairsPerBlock; ++p) all[p] = 0;
+    static_for<0, kPairsPerBlock>([&](auto P) { all[decltype(P)::value] = extract_pair<B, decltype(P)::value>(w, magic); });
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      pr[r] = g == 0 ? all[r] : g == 1 ? all[4 + r] : g == 2 ? all[8 + r] : all[12 + r];
+  }
+  half8_t f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const half2_t d = dequant_pair(pr[r], neg_bias, scale);
+    f[2 * r] = d[0];
+    f[2 * r + 1] = d[1];
+  }
+  return f;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Register ring of the global loads of D blocks. A lane's 4 column
+// fragments take 4 adjacent columns (its column quad), so each packed-word
+// row, the 4 scales and the 4 zero points are one load each.
+template <int kW, int D>
+struct Ring {
+  u32x4 w[D][kW];         // packed-word rows t of the quad's 4 columns
+  u32x2 s[D];             // 4 float16 scales
+  uint32_t z[D];          // 4 uint8 zero points
+  int bits[D];
+};
+
+// Per-lane byte offsets that do not change along K.
+struct LaneOffsets {
+  uint32_t a[kAPieces];   // A piece (row, 16-byte chunk) at K = 0
+  uint32_t w;             // packed row 0 of the quad's first column
+  uint32_t col;           // the quad's first column
+};
+
+template <unsigned BS, int kW, int D, int S>
+__device__ __forceinline__ void load_block(const GemmArgs& a, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
+                                           __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz, int g,
+                                           const LaneOffsets& off, int blk, Ring<kW, D>& R) {
+  int bits, row;
+  if constexpr ((BS & (BS - 1)) == 0) {
+    bits = __builtin_ctz(BS);   // one width: block blk starts at packed row blk * b
+    row = blk * bits;
+  } else {
+    block_info(a.runs, blk, bits, row);
+  }
+  R.bits[S] = bits;
+  with_width<BS>(bits, [&](auto BB) {
+    constexpr int B = decltype(BB)::value;
+    const uint32_t v = off.w + (uint32_t)frag_first_word<B>(g) * kPanel * 4;   // g differs between lanes
+#pragma unroll
+    for (int t = 0; t < frag_words<B>(); ++t)
+      R.w[S][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, v, (row + t) * kPanel * 4, 0));
+  });
+  const int grp = blk / a.runs.blocks_per_group;
+  R.s[S] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off.col * 2, grp * a.N * 2, 0));
+  R.z[S] = __builtin_amdgcn_raw_buffer_load_b32(rz, off.col, a.zeros ? grp * a.N : 0, 0);
+}
+
+__device__ __forceinline__ void store_a(uint16_t* stage, int tid, const u32x4 (&pieces)[kAPieces]) {
+#pragma unroll
+  for (int i = 0; i < kAPieces; ++i) {
+    const int lin = tid + i * kThreads;
+    const int r = lin / 4, ch = lin % 4;
+    *reinterpret_cast<u32x4*>(&stage[r * kLdsRow + ch * 8]) = pieces[i];
+  }
+}
+
+// The B fragments of the block in ring slot S, exactly dequantized.
+// Zero point and scale come as float16 bit patterns: -(1024 + z) is 0xE400 | z
+// (z < 1024), and the scale is splatted into both halves with a byte permute.
+template <unsigned BS, int kW, int D, int S>
+__device__ __forceinline__ void dequant_block(const GemmArgs& a, const Ring<kW, D>& R, int g, uint32_t magic,
+                                              half8_t (&bf)[FN]) {
+  with_width<BS>(R.bits[S], [&](auto BB) {
+    constexpr int B = decltype(BB)::value;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      // byte j of the zero points into the low byte of both halves
+      const uint32_t zsel = 0x0C000C00u | ((uint32_t)j << 16) | (uint32_t)j;
+      const uint32_t zz = a.zeros ? __builtin_amdgcn_perm(0u, R.z[S], zsel) : (uint32_t)(1 << (B - 1)) * 0x10001u;
+      const uint32_t nb = zz | 0xE400E400u;
+      const uint32_t ssel = (j % 2) ? 0x03020302u : 0x01000100u;
+      const uint32_t sv = __builtin_amdgcn_perm(R.s[S][j / 2], R.s[S][j / 2], ssel);
+      uint32_t w[kW];
+#pragma unroll
+      for (int t = 0; t < kW; ++t) w[t] = R.w[S][t][j];
+      bf[j] = dequant_frag<B, kW>(w, g, as_half2(nb), as_half2(sv), magic);
+    }
+  });
+}
+
+__device__ __forceinline__ void read_a(const uint16_t* stage, int lane, int g, int wr, half8_t (&af)[FM]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    af[i] = *reinterpret_cast<const half8_t*>(&stage[(wr * WM + i * 16 + (lane & 15)) * kLdsRow + 8 * g]);
+}
+
+// Block kb = kb0 + S (its A tile is in LDS stage S, its B words in ring slot
+// S): load block kb + 1's A pieces and block kb + 2's B words (clamped to the
+// last block), dequantize block kb's B fragments, read its A fragments, run
+// its MFMAs, then store block kb + 1's A pieces into stage S + 1.
+template <unsigned BS, int kW, int S>
+__device__ __forceinline__ void block_step(const GemmArgs& a, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
+                                           __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz, int tid, int lane,
+                                           int g, int wr, uint32_t magic, const LaneOffsets& off, int kb, int nblk,
+                                           uint16_t* As, Ring<kW, kRing>& R, float4_t (&acc)[FM][FN]) {
+  constexpr int kStage = BM * kLdsRow;
+  u32x4 an[kAPieces];
+  const int nb1 = min(kb + 1, nblk - 1);
+#pragma unroll
+  for (int i = 0; i < kAPieces; ++i)
+    an[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off.a[i], nb1 * kBlockRows * 2, 0));
+  half8_t bf[FN];
+  dequant_block<BS, kW, kRing, S>(a, R, g, magic, bf);
+  load_block<BS, kW, kRing, S>(a, rx, rw, rs, rz, g, off, min(kb + kRing, nblk - 1), R);
+  half8_t af[FM];
+  read_a(As + S * kStage, lane, g, wr, af);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  store_a(As + ((S + 1) % kRing) * kStage, tid, an);
+  __syncthreads();
+}
+
+template <unsigned BS>
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
+  constexpr int kW = max_frag_words<BS>();
+  constexpr int D = kRing;
+  __shared__ __align__(16) uint16_t As[kRing * BM * kLdsRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;   // 2 x 2 waves of 64 x 64
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
   const int n0 = blockIdx.x * BN;
   const int m0 = blockIdx.y * BM;
   const int nblk = a.K / kBlockRows;
+  const int g = lane >> 4;   // k-group of the lane's B fragments
 
-  float4_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = {0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, 0, a.xq_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.qweight, 0, a.qweight_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)a.scales, 0, a.scale_bytes, kRsrcWord3);
+  // Without zero points the zero loads read the scale buffer (not used).
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+      a.zeros ? (void*)a.zeros : (void*)a.scales, 0, a.zeros ? a.scale_bytes / 2 : a.scale_bytes, kRsrcWord3);
 
-  // B-tile work item of this thread: block (tid / 128) of the step, column tid % 128.
-  const int bsub = tid / BN;
-  const int bn = tid % BN;
-  const int ncol = n0 + bn;
-  const bool nvalid = ncol < a.N;
-
-  for (int kb = 0; kb < nblk; kb += BK / kBlockRows) {
-    // A tile: 128 rows x 64 halves, 16 bytes per thread per pass.
+  LaneOffsets off;
 #pragma unroll
-    for (int i = 0; i < (BM * BK / 8) / kThreads; ++i) {
-      const int lin = tid + i * kThreads;
-      const int r = lin / (BK / 8), ch = lin % (BK / 8);
-      const int m = m0 + r;
-      const int k = kb * kBlockRows + ch * 8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (m < a.M && k < a.K) v = *reinterpret_cast<const uint4*>(a.xq + (size_t)m * a.K + k);
-      *reinterpret_cast<uint4*>(As + r * kLdsRow + ch * 8) = v;
-    }
-    // B tile: dequantize block kb + bsub for column ncol.
-    {
-      const int blk = kb + bsub;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(Bs + bn * kLdsRow + bsub * kBlockRows);
-      if (blk < nblk) {
-        int bits, row;
-        block_info(a.runs, blk, bits, row);
-        const int g = blk / a.runs.blocks_per_group;
-        switch (bits) {
-          case 2: dequant_to_lds<2>(a, row, g, ncol, nvalid, dst); break;
-          case 3: dequant_to_lds<3>(a, row, g, ncol, nvalid, dst); break;
-          case 4: dequant_to_lds<4>(a, row, g, ncol, nvalid, dst); break;
-          case 5: dequant_to_lds<5>(a, row, g, ncol, nvalid, dst); break;
-          case 6: dequant_to_lds<6>(a, row, g, ncol, nvalid, dst); break;
-          case 8: dequant_to_lds<8>(a, row, g, ncol, nvalid, dst); break;
-          default: break;
-        }
-      } else {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<uint4*>(dst + 4 * q4) = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      half8_t af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(As + (wr * 64 + i * 16 + (lane & 15)) * kLdsRow + kk +
-                                                  8 * (lane >> 4));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(Bs + (wc * 64 + j * 16 + (lane & 15)) * kLdsRow + kk +
-                                                  8 * (lane >> 4));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
+  for (int i = 0; i < kAPieces; ++i) {
+    const int lin = tid + i * kThreads;
+    const int m = min(m0 + lin / 4, a.M - 1);   // rows past M repeat row M - 1 (not stored)
+    off.a[i] = ((uint32_t)m * (uint32_t)a.K + (uint32_t)(lin % 4) * 8) * 2;
   }
+  // The lane's column quad; N is a multiple of 8, so a quad is in or out as a
+  // whole. A quad past N reads at offsets beyond every buffer: the buffer
+  // loads return zeros (zero scales), and it is not stored.
+  const int nq = n0 + wc * WN + (lane & 15) * 4;
+  const bool nok = nq < a.N;
+  off.w = nok ? ((uint32_t)(nq / kPanel) * (uint32_t)a.runs.packed_rows * kPanel + nq % kPanel) * 4 : 0x80000000u;
+  off.col = nok ? (uint32_t)nq : 0x40000000u;
 
-  // Epilogue: lane holds C[4*(lane/16) + r][lane % 16] of each 16 x 16 tile.
+  Ring<kW, D> R;
+  const uint32_t magic = vgpr_magic();
+  float4_t acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wc * 64 + j * 16 + (lane & 15);
-      if (n >= a.N) continue;
+    for (int j = 0; j < FN; ++j) acc[i][j] = {0.f, 0.f, 0.f, 0.f};
+
+  // Prologue: blocks 0 .. 3 in flight, A tiles of blocks 0 and 1 in stages 0
+  // and 1, block 0's fragments in registers.
+  static_for<0, D>([&](auto SS) {
+    constexpr int S = decltype(SS)::value;
+    load_block<BS, kW, D, S>(a, rx, rw, rs, rz, g, off, min(S, nblk - 1), R);
+  });
+  {
+    u32x4 a0[kAPieces];
+#pragma unroll
+    for (int i = 0; i < kAPieces; ++i)
+      a0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off.a[i], 0, 0));
+    store_a(As, tid, a0);
+  }
+  __syncthreads();
+
+  // Whole rounds of D blocks without conditions (static ring slots, exact
+  // load counts), then the remaining blocks.
+  const int nfull = nblk / D * D;
+  for (int kb0 = 0; kb0 < nfull; kb0 += D) {
+    static_for<0, D>([&](auto SS) {
+      constexpr int S = decltype(SS)::value;
+      block_step<BS, kW, S>(a, rx, rw, rs, rz, tid, lane, g, wr, magic, off, kb0 + S, nblk, As, R, acc);
+    });
+  }
+  static_for<0, D - 1>([&](auto SS) {
+    constexpr int S = decltype(SS)::value;
+    if (nfull + S < nblk) block_step<BS, kW, S>(a, rx, rw, rs, rz, tid, lane, g, wr, magic, off, nfull + S, nblk, As, R, acc);
+  });
+
+  // Epilogue: lane holds C[4*(lane/16) + r][lane % 16] of each 16 x 16 tile;
+  // fragment j's column c is column 4c + j of the wave's 64, so a lane's 4
+  // fragments give 4 adjacent columns of a row: one 8-byte store.
+  if (nok) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wr * 64 + i * 16 + 4 * (lane >> 4) + r;
-        if (m < a.M) a.y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
+        const int m = m0 + wr * WM + i * 16 + 4 * (lane >> 4) + r;
+        if (m < a.M) {
+          u32x2 v;
+          v[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[i][0][r]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[i][1][r]) << 16);
+          v[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[i][2][r]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[i][3][r]) << 16);
+          *reinterpret_cast<u32x2*>(a.y + (size_t)m * a.N + nq) = v;
+        }
       }
     }
   }
+}
+
+template <unsigned BS>
+void launch_set(const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_kernel<BS>), grid, dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace
 
 size_t qgemm_workspace_bytes(int M, int K) { return ((size_t)M * K * 2 + 255) / 256 * 256; }
+
+bool qgemm_fits(const qlinear_layout& L, int M) {
+  // Buffer offsets and sizes are 32-bit: every operand must stay below 2^31 bytes.
+  const size_t lim = (size_t)1 << 31;
+  return (size_t)M * L.K * 2 < lim && (size_t)L.packed_words * 4 < lim && (size_t)L.groups * L.N * 2 < lim;
+}
 
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
@@ -174,9 +373,23 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
   a.M = M;
   a.K = L.K;
   a.N = L.N;
+  a.xq_bytes = (int)((size_t)M * L.K * 2);
+  a.qweight_bytes = (int)((size_t)L.packed_words * 4);
+  a.scale_bytes = (int)((size_t)L.groups * L.N * 2);
   a.runs = runs;
-  const int gmy = (M + BM - 1) / BM;
-  hipLaunchKernelGGL(gemm_kernel, dim3((L.N + BN - 1) / BN, gmy, 1), dim3(kThreads), 0, stream, a);
+  unsigned set = 0;
+  for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
+  // Several code widths: the kernel that dequantizes into LDS block by block.
+  if ((set & (set - 1)) != 0) return launch_qgemm_lds(L, runs, a.xq, M, qweight, scales, zeros, y, stream);
+  const dim3 grid((L.N + BN - 1) / BN, (M + BM - 1) / BM, 1);
+  switch (set) {
+    case 1u << 2: launch_set<1u << 2>(a, grid, stream); break;
+    case 1u << 3: launch_set<1u << 3>(a, grid, stream); break;
+    case 1u << 4: launch_set<1u << 4>(a, grid, stream); break;
+    case 1u << 5: launch_set<1u << 5>(a, grid, stream); break;
+    case 1u << 6: launch_set<1u << 6>(a, grid, stream); break;
+    default: launch_set<1u << 8>(a, grid, stream); break;
+  }
   return hipGetLastError();
 }
 

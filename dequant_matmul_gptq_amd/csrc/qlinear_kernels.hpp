@@ -36,6 +36,11 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
                         hipStream_t stream);
 
 // Prefill layer. ws holds the gathered activations, float16 [M][K].
+// launch_qgemm_lds: the multiplication for layouts with several code widths,
+// from activations already gathered (xq, float16 [M][K]).
+hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uint16_t* xq, int M,
+                            const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y,
+                            hipStream_t stream);
 size_t qgemm_workspace_bytes(int M, int K);
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,

@@ -5,7 +5,10 @@ step, GPTQ 4-bit, group size 128, act-order. One step = one token through the
 linear layers of 32 decoder layers; each layer has q, k, v, o (4096 -> 4096),
 gate, up (4096 -> 11008) and down (11008 -> 4096). All 224 packed matrices are
 distinct buffers resident in HBM (3.36 GB), so the 256 MB Infinity Cache cannot
-serve repeated weights. The step is captured in a HIP graph and replayed.
+serve repeated weights. q, k, v read the same input and so do gate and up
+(quantized against the same input, they share the act-order permutation):
+each of those sets is one grouped launch, 4 launches per layer (--no-group: 7).
+The step is captured in a HIP graph and replayed.
 
 Secondary (qgemm): dequant-GEMM TFLOP/s at M = 2048 on the Llama-2-13B MLP
 shape 5120 -> 13824, GPTQ 4-bit, group size 128, act-order.
@@ -42,6 +45,7 @@ def parse():
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-group", action="store_true", help="one qgemv launch per matrix (no grouped q/k/v, gate/up)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the M = 2048 qgemm measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy a MIB-MiB buffer 3 times (a known-size kernel for HBM counter calibration)")
@@ -82,6 +86,35 @@ def Launch(fn, layout, x, M, qweight, scales, zeros, perm, y, ws, stream):
     return Call(fn, layout, x, M, qweight, scales, zeros, perm, y, ws, stream)
 
 
+def decode_groups(mats, grouped):
+    """The step's launches in layer order: per layer [q, k, v], [o], [gate,
+    up], [down] when grouped (the matrices of a launch share x and perm),
+    else one launch per matrix."""
+    out, i = [], 0
+    per_layer = sum(c for _, c in LAYER_MIX)
+    while i < len(mats):
+        layer = mats[i:i + per_layer]
+        parts = [layer[0:3], layer[3:4], layer[4:6], layer[6:7]] if grouped else [[m] for m in layer]
+        out += [dict(shape=p[0]["shape"], mats=p) for p in parts]
+        i += per_layer
+    return out
+
+
+def group_call(lib, dq, shapes, xs, ys, g, ws, sh):
+    """A qlinear_qgemv call for one matrix, a qlinear_qgemv_grouped call for several."""
+    import ctypes
+    si, ms = g["shape"], g["mats"]
+    L = shapes[si]["L"]
+    if len(ms) == 1:
+        m = ms[0]
+        return Call(lib.qlinear_qgemv, L, xs[si], 1, m["qw"], m["sc"], m["zr"], m["pm"], ys[si][0], ws, sh)
+    arr = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+    call = Call(lib.qlinear_qgemv_grouped, L, xs[si], 1, len(ms), arr([m["qw"] for m in ms]),
+                arr([m["sc"] for m in ms]), arr([m["zr"] for m in ms]), ms[0]["pm"], arr(ys[si][:len(ms)]), ws, sh)
+    call.hold = ms
+    return call
+
+
 def spin_cycles(torch, stream, ms):
     """Argument of torch.cuda._sleep that keeps the GPU busy for about `ms`."""
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -95,15 +128,17 @@ def spin_cycles(torch, stream, ms):
     return int(probe * ms / max(a.elapsed_time(b), 1e-3))
 
 
-def row_kernel_bytes(layout, M, zeros=True, perm=True):
-    """Algorithmic HBM bytes of one single-row qgemv launch: every operand
-    byte read once and the output written once. Packed codes at b bits per
-    weight, float16 scales, uint8 zero points, the float16 activations, the
-    int32 act-order permutation, the float16 result."""
+def row_kernel_bytes(layout, M, zeros=True, perm=True, count=1):
+    """Algorithmic HBM bytes of one single-row qgemv launch over `count`
+    matrices of one layout: every operand byte read once and the outputs
+    written once. Per matrix: packed codes at b bits per weight, float16
+    scales, uint8 zero points, the float16 result; shared: the float16
+    activations and the int32 act-order permutation."""
     bits = layout.bits.astype(np.int64)
     K, N, G = layout.K, layout.N, layout.groups
     codes = int((bits * layout.group_size).sum()) * N // 8
-    return codes + G * N * 2 + (G * N if zeros else 0) + M * K * 2 + (K * 4 if perm else 0) + M * N * 2
+    per = codes + G * N * 2 + (G * N if zeros else 0) + M * N * 2
+    return count * per + M * K * 2 + (K * 4 if perm else 0)
 
 
 # Files whose code makes up the single-row qgemv kernel; recorded counter
@@ -202,10 +237,11 @@ def main():
     step_bytes = sum(wbytes[m["shape"]] for m in mats)
     ws = dq.qgemv_workspace(shapes[2]["L"], dev)  # K = 11008 covers every shape in the step
     xs = [torch.from_numpy(s["inp"].x[:1].copy()).to(dev) for s in shapes]
-    ys = [torch.empty((1, s["spec"].N), dtype=torch.float16, device=dev) for s in shapes]
-    launches = [Launch(lib.qlinear_qgemv, shapes[m["shape"]]["L"], xs[m["shape"]], 1, m["qw"], m["sc"], m["zr"],
-                       m["pm"], ys[m["shape"]], ws, sh) for m in mats]
-    log(f"decode setup {time.time() - t0:.1f}s: {len(mats)} matrices, {step_bytes / 1e9:.3f} GB per step")
+    ys = [[torch.empty((1, s["spec"].N), dtype=torch.float16, device=dev) for _ in range(3)] for s in shapes]
+    groups = decode_groups(mats, not args.no_group)
+    launches = [group_call(lib, dq, shapes, xs, ys, g, ws, sh) for g in groups]
+    log(f"decode setup {time.time() - t0:.1f}s: {len(mats)} matrices in {len(launches)} launches, "
+        f"{step_bytes / 1e9:.3f} GB per step")
 
     def step():
         for ln in launches:
@@ -252,19 +288,18 @@ def main():
 
     # Per-launch duration of the single-row kernel (one kernel per call at
     # M = 1 with one code width), with HIP events on the launch stream: for
-    # each shape, >= 256 calls back to back (cycling through that shape's
-    # distinct matrices, so weights come from HBM) between two events. A spin
-    # kernel queued first keeps the GPU behind the host: the events then time
-    # the kernels, not host launch latency.
+    # each kind of launch in the step, >= 256 launches back to back (cycling
+    # through that kind's distinct matrices, so weights come from HBM)
+    # between two events. A spin kernel queued first keeps the GPU behind the
+    # host: the events then time the kernels, not host launch latency.
     spin = spin_cycles(torch, stream, 50.0)
-    per_shape = []
+    per_kind = []
     tot_bytes, tot_us, n_step = 0, 0.0, 0
-    for si, s in enumerate(shapes):
-        mine = [m for m in mats if m["shape"] == si]
-        rounds = -(-256 // len(mine))
-        L = s["L"]
-        calls = [Call(lib.qlinear_qgemv, L, xs[si], 1, m["qw"], m["sc"], m["zr"], m["pm"], ys[si], ws, sh)
-                 for m in mine]
+    kinds = {}
+    for g, ln in zip(groups, launches):
+        kinds.setdefault((g["shape"], len(g["mats"])), []).append(ln)
+    for (si, cnt), calls in kinds.items():
+        rounds = -(-256 // len(calls))
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda._sleep(spin)
         ev0.record(stream)
@@ -273,19 +308,20 @@ def main():
                 c()
         ev1.record(stream)
         torch.cuda.synchronize()
-        n = rounds * len(mine)
+        n = rounds * len(calls)
         us = ev0.elapsed_time(ev1) * 1e3 / n
-        ab = row_kernel_bytes(L, 1)
+        ab = row_kernel_bytes(shapes[si]["L"], 1, count=cnt)
         gbs = ab / (us * 1e-6) / 1e9
-        per_shape.append(dict(shape=f"{s['spec'].K}x{s['spec'].N}", algorithmic_bytes=ab, launches=n,
-                              avg_us=round(us, 3), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4)))
-        # weight the shapes as the step does
-        tot_bytes += ab * len(mine)
-        tot_us += us * len(mine)
-        n_step += len(mine)
+        sp = shapes[si]["spec"]
+        per_kind.append(dict(launch=f"{cnt} x {sp.K}x{sp.N}", algorithmic_bytes=ab, launches=n,
+                             avg_us=round(us, 3), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4)))
+        # weight the kinds as the step does
+        tot_bytes += ab * len(calls)
+        tot_us += us * len(calls)
+        n_step += len(calls)
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
     log(f"qgemv_row_kernel per launch: avg {tot_us / n_step:.2f} us, {achieved:.0f} GB/s; " +
-        ", ".join(f"{p['shape']}: {p['avg_us']} us {p['gbs']} GB/s" for p in per_shape))
+        ", ".join(f"{p['launch']}: {p['avg_us']} us {p['gbs']} GB/s" for p in per_kind))
     traffic = recorded_traffic()
 
     gemm = None if args.no_gemm else bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream)
@@ -311,9 +347,11 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "Llama-2-7B-shaped decode, GPTQ 4-bit g128 act-order, M=1: 32 layers x "
-                        "(4 x 4096->4096, 2 x 4096->11008, 1 x 11008->4096), weights resident in HBM",
+                        "(4 x 4096->4096, 2 x 4096->11008, 1 x 11008->4096), weights resident in HBM; "
+                        + ("q/k/v and gate/up as grouped launches" if not args.no_group else "one launch per matrix"),
             "M": 1,
             "matrices_per_step": len(mats),
+            "launches_per_step": len(launches),
             "weight_bytes_per_step": step_bytes,
             "hbm_peak_gbs": HBM_PEAK_GBS,
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
@@ -330,7 +368,7 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(tot_us / n_step, 3),
             "algorithmic_bytes_per_launch": round(tot_bytes / n_step),
-            "per_shape": per_shape,
+            "per_launch_kind": per_kind,
         },
         "cpu_baseline": cpu,
         "qgemm": gemm,

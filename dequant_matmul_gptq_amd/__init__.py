@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     GEMV_MAX_M,
     LIB_PATH,
+    MAX_GROUP,
     MAX_RUNS,
     Layout,
     QlinearError,
@@ -19,6 +20,7 @@ from ._lib import (  # noqa: F401
     qgemm,
     qgemm_workspace_bytes,
     qgemv,
+    qgemv_grouped,
     qgemv_workspace,
     qgemv_workspace_bytes,
     status_string,

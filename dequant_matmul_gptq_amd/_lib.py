@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libqlinear.so")
 
 MAX_RUNS = 64
 GEMV_MAX_M = 16
+MAX_GROUP = 8
 PANEL = 16
 
 OK = 0
@@ -36,6 +37,7 @@ EXPORTS = (
     "qlinear_dequant",
     "qlinear_qgemv_workspace_bytes",
     "qlinear_qgemv",
+    "qlinear_qgemv_grouped",
     "qlinear_qgemm_workspace_bytes",
     "qlinear_qgemm",
 )
@@ -83,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.qlinear_dequant.argtypes = [lp, vp, vp, vp, vp, vp]
         L.qlinear_qgemv_workspace_bytes.argtypes = [lp, ctypes.POINTER(sz)]
         L.qlinear_qgemv.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        pp = ctypes.POINTER(vp)
+        L.qlinear_qgemv_grouped.argtypes = [lp, vp, i32, i32, pp, pp, pp, vp, pp, vp, sz, vp]
         L.qlinear_qgemm_workspace_bytes.argtypes = [lp, i32, ctypes.POINTER(sz)]
         L.qlinear_qgemm.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in EXPORTS[1:]:
@@ -213,6 +217,32 @@ def qgemv(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.
     _check(lib().qlinear_qgemv(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
                                _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemv")
     return y
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def qgemv_grouped(layout: Layout, x: torch.Tensor, qweights, scales, zeros, perm: torch.Tensor | None,
+                  workspace: torch.Tensor, ys=None) -> list:
+    """Decode layer for several matrices that share the layout, x and perm
+    (e.g. q, k, v). zeros: None or a list (one per matrix). Returns the list
+    of outputs y_i float16 [M][N]."""
+    count = len(qweights)
+    if len(scales) != count or (zeros is not None and len(zeros) != count):
+        raise ValueError("one scales (and zeros) tensor per matrix")
+    outs = []
+    for i in range(count):
+        M, y = _gemm_operands(layout, x, qweights[i], scales[i], None if zeros is None else zeros[i], perm,
+                              None if ys is None else ys[i])
+        outs.append(y)
+    _dev(workspace, "workspace", torch.uint8)
+    qa, sa, ya = _ptr_array(qweights), _ptr_array(scales), _ptr_array(outs)
+    za = None if zeros is None else _ptr_array(zeros)
+    _check(lib().qlinear_qgemv_grouped(layout.ref, _ptr(x), int(x.shape[0]), count, qa, sa, za, _ptr(perm), ya,
+                                       _ptr(workspace), workspace.numel(), _stream(x.device)),
+           "qlinear_qgemv_grouped")
+    return outs
 
 
 def qgemm(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,

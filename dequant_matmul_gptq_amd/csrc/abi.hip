@@ -170,8 +170,32 @@ int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M, co
   if (st != QLINEAR_OK || M == 0) return st;
   if (M > QLINEAR_GEMV_MAX_M) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
-  return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, qweight, scales, zeros, y, workspace,
-                                 (hipStream_t)stream));
+  return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, 1, &qweight, &scales,
+                                 zeros ? &zeros : nullptr, &y, workspace, (hipStream_t)stream));
+}
+
+int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32_t M, int32_t count,
+                          const uint32_t* const* qweights_host, const uint16_t* const* scales_host,
+                          const uint8_t* const* zeros_host, const int32_t* perm, uint16_t* const* y_host,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_layout(layout);
+  if (st != QLINEAR_OK) return st;
+  if (M < 0 || count < 1) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (count > QLINEAR_MAX_GROUP) return QLINEAR_ERR_UNSUPPORTED;
+  if (!qweights_host || !scales_host || !y_host) return QLINEAR_ERR_INVALID_ARGUMENT;
+  const bool zeros = zeros_host && zeros_host[0];
+  for (int i = 0; i < count; ++i) {
+    // every matrix is checked like the operands of qlinear_qgemv
+    st = check_gemm_operands(layout, x, M, qweights_host[i], scales_host[i], zeros ? zeros_host[i] : nullptr, perm,
+                             y_host[i], workspace);
+    if (st != QLINEAR_OK) return st;
+    if (zeros_host && (zeros_host[i] != nullptr) != zeros) return QLINEAR_ERR_INVALID_ARGUMENT;
+  }
+  if (M == 0) return QLINEAR_OK;
+  if (M > QLINEAR_GEMV_MAX_M) return QLINEAR_ERR_UNSUPPORTED;
+  if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
+  return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, count, qweights_host, scales_host,
+                                 zeros ? zeros_host : nullptr, y_host, workspace, (hipStream_t)stream));
 }
 
 int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes) {

@@ -62,10 +62,11 @@ __device__ __forceinline__ void lane_pairs(int cq, int (&rlo)[4], int (&rhi)[4],
 // the four lanes of a quad exchange the pairs of one block, so a lane whose
 // columns lie past N must still gather its quad's block.
 template <int B>
-__device__ __forceinline__ void issue_step(const StreamArgs& a, const uint32_t* panel, const int32_t* psrc, int blk,
+__device__ __forceinline__ void issue_step(const StreamArgs& a, const MatPtrs& mp, const uint32_t* panel,
+                                           const int32_t* psrc, int blk,
                                            int row, bool blk_ok, bool ok, int blk_safe, int row_safe, int col,
                                            const int (&rlo)[4], const int (&rhi)[4], StepRegs& S) {
-  issue<B>(a, panel, blk, row, ok, blk_safe, row_safe, col, reinterpret_cast<uint4(&)[B]>(S.W), S.P);
+  issue<B>(a, mp, panel, blk, row, ok, blk_safe, row_safe, col, reinterpret_cast<uint4(&)[B]>(S.W), S.P);
   const int32_t* pb = psrc + (size_t)(blk_ok ? blk : blk_safe) * kBlockRows;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -131,13 +132,14 @@ __device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs
   s[2] = S.P.ok ? half_lo(S.P.s.y) : 0.0f;
   s[3] = S.P.ok ? half_hi(S.P.s.y) : 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) z[c] = a.zeros ? (float)((S.P.z >> (8 * c)) & 0xFFu) : (float)(1 << (B - 1));
+  for (int c = 0; c < 4; ++c) z[c] = a.has_zeros ? (float)((S.P.z >> (8 * c)) & 0xFFu) : (float)(1 << (B - 1));
 #pragma unroll
   for (int c = 0; c < 4; ++c) yacc[c] = fmaf(s[c], fmaf(-z[c], X, acc[c] - 1024.0f * Xs), yacc[c]);
 }
 
 // Lane context shared by the steps of a wave.
 struct RowLane {
+  MatPtrs mp;
   const uint32_t* panel;
   const int32_t* psrc;
   const _Float16* xrow;
@@ -152,8 +154,8 @@ __device__ __forceinline__ void seg_issue(const StreamArgs& a, const RowLane& L,
                                           const int (&rlo)[4], const int (&rhi)[4], StepRegs& S) {
   const int blk = blk0 + i * KS + L.ks;
   const bool blk_ok = blk < blk1;
-  issue_step<B>(a, L.panel, L.psrc, blk, row0 + (i * KS + L.ks) * B, blk_ok, L.colv && blk_ok, blk0, row0, L.col,
-                rlo, rhi, S);
+  issue_step<B>(a, L.mp, L.panel, L.psrc, blk, row0 + (i * KS + L.ks) * B, blk_ok, L.colv && blk_ok, blk0, row0,
+                L.col, rlo, rhi, S);
 }
 
 // All steps of one run segment of this wave, two in flight. With kPre the
@@ -210,8 +212,10 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
-  const int strip = (bid % kXcds) * a.strips_per_xcd + bid / kXcds;
-  if (strip >= a.nstrips) return;  // the whole workgroup leaves together
+  const int gstrip = (bid % kXcds) * a.strips_per_xcd + bid / kXcds;
+  if (gstrip >= a.mats * a.nstrips) return;  // the whole workgroup leaves together
+  const int mi = gstrip / a.nstrips;         // matrix of the group
+  const int strip = gstrip - mi * a.nstrips;
 
   // 1. The x row: every piece this thread copies, loaded before anything else.
   constexpr int nthr = WV * 64;
@@ -231,13 +235,14 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   if (wb0 < wb1) block_info(a.runs, wb0, b0, row0);
   const int seg0_end = wb0 < wb1 ? min(wb1, run_end_block(a.runs, wb0)) : wb0;
   RowLane L;
+  L.mp = a.mat[mi];
   L.cq = lane % CQ;
   L.ks = lane / CQ;
   const int col_req = strip * SC + L.cq * 4;
   L.colv = col_req < a.N;
   L.col = L.colv ? col_req : a.N - 4;   // scale/zero column for lanes past N
-  L.panel = a.qweight + (size_t)strip * a.runs.packed_rows * kPanel + L.cq * 4;
-  L.psrc = a.perm ? a.perm : reinterpret_cast<const int32_t*>(a.qweight);   // >= K readable words
+  L.panel = L.mp.qweight + (size_t)strip * a.runs.packed_rows * kPanel + L.cq * 4;
+  L.psrc = a.perm ? a.perm : reinterpret_cast<const int32_t*>(L.mp.qweight);   // >= K readable words
   L.xrow = reinterpret_cast<const _Float16*>(lds);
   L.magic = vgpr_magic();
   StepRegs S0, S1;
@@ -271,13 +276,13 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   }
 
   float y4[4][1] = {{yacc[0]}, {yacc[1]}, {yacc[2]}, {yacc[3]}};
-  reduce_store<1, WV>(a, red, y4, tid, lane, wave, strip);
+  reduce_store<1, WV>(a, L.mp.y, red, y4, tid, lane, wave, strip);
 }
 
 template <unsigned BS, int WV>
 hipError_t launch_row(StreamArgs a, hipStream_t stream) {
   a.nstrips = (a.N + SC - 1) / SC;
-  a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
+  a.strips_per_xcd = (a.mats * a.nstrips + kXcds - 1) / kXcds;
   a.xrow_words = row_words(a.K);
   const size_t lds = (size_t)a.xrow_words * 4;
   hipLaunchKernelGGL((qgemv_row_kernel<BS, WV>), dim3(kXcds * a.strips_per_xcd), dim3(WV * 64), lds, stream, a);

@@ -23,17 +23,22 @@ GemvWorkspace qgemv_workspace(void* ws, int K) {
 }
 
 hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M, const int32_t* perm,
-                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y, void* ws,
-                        hipStream_t stream) {
+                        int mats, const uint32_t* const* qweights, const uint16_t* const* scales,
+                        const uint8_t* const* zeros, uint16_t* const* ys, void* ws, hipStream_t stream) {
   stream::StreamArgs a;
   a.x = x;
   a.perm = perm;
   a.xq = nullptr;
   a.xsum = nullptr;
-  a.qweight = qweight;
-  a.scales = scales;
-  a.zeros = zeros;
-  a.y = y;
+  a.mats = mats;
+  a.has_zeros = zeros != nullptr && zeros[0] != nullptr;
+  for (int i = 0; i < stream::kMaxMats; ++i) {
+    const int j = i < mats ? i : 0;   // unused entries repeat matrix 0
+    a.mat[i].qweight = qweights[j];
+    a.mat[i].scales = scales[j];
+    a.mat[i].zeros = a.has_zeros ? zeros[j] : nullptr;
+    a.mat[i].y = ys[j];
+  }
   a.M = M;
   a.K = L.K;
   a.N = L.N;

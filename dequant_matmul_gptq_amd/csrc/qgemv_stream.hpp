@@ -52,17 +52,27 @@ constexpr int KS = 64 / CQ;            // 16 blocks per wave step
 constexpr int kXcds = 8;
 constexpr int kStageBudget = 60 * 1024;  // bytes of LDS for staged activations
 
+constexpr int kMaxMats = 8;   // matrices of one grouped call
+
+// One matrix of a call: the matrices of a grouped call share the layout, the
+// activations and the permutation, and have their own weights and output.
+struct MatPtrs {
+  const uint32_t* qweight;
+  const uint16_t* scales;
+  const uint8_t* zeros;   // NULL for every matrix of the call, or for none
+  uint16_t* y;
+};
+
 struct StreamArgs {
   const uint16_t* x;       // single-row kernel: the activations, float16 [K], original order
   const int32_t* perm;     // single-row kernel: act-order permutation or NULL
   const uint32_t* xq;      // gathered, scaled activations, [M][K/32][16] float16 pairs
   const float2* xsum;      // block sums (X, 1024 * X'), [M][K/32]
-  const uint32_t* qweight;
-  const uint16_t* scales;
-  const uint8_t* zeros;
-  uint16_t* y;
+  int mats;                // matrices in this call, 1 .. kMaxMats
+  int has_zeros;
+  MatPtrs mat[kMaxMats];
   int M, K, N;
-  int nstrips, strips_per_xcd;
+  int nstrips, strips_per_xcd;  // 16-column strips per matrix; workgroups per XCD over all matrices
   int chunk;               // blocks per wave staged at a time
   int xrow_words;          // single-row kernel: LDS words holding the x row
   int bpg_shift;           // log2(group_size / 32)
@@ -100,16 +110,16 @@ struct Raw {
 // them). A lane without work (ok == false) reads the valid block `blk_safe`
 // at `row_safe` instead and gets a zero scale, which zeroes its contribution.
 template <int B>
-__device__ __forceinline__ void issue(const StreamArgs& a, const uint32_t* panel, int blk, int row, bool ok,
-                                      int blk_safe, int row_safe, int scol, uint4 (&W)[B], Raw& P) {
+__device__ __forceinline__ void issue(const StreamArgs& a, const MatPtrs& mp, const uint32_t* panel, int blk,
+                                      int row, bool ok, int blk_safe, int row_safe, int scol, uint4 (&W)[B], Raw& P) {
   const uint32_t* p = panel + (size_t)(ok ? row : row_safe) * kPanel;
 #pragma unroll
   for (int t = 0; t < B; ++t) W[t] = *reinterpret_cast<const uint4*>(p + t * kPanel);
   const size_t g = (size_t)((ok ? blk : blk_safe) >> a.bpg_shift) * a.N + scol;
-  const uint2 sv = *reinterpret_cast<const uint2*>(a.scales + g);
+  const uint2 sv = *reinterpret_cast<const uint2*>(mp.scales + g);
   // Without zero points, read the scales again (any valid address): the value
   // is not used.
-  const uint8_t* zp = a.zeros ? a.zeros : reinterpret_cast<const uint8_t*>(a.scales);
+  const uint8_t* zp = a.has_zeros ? mp.zeros : reinterpret_cast<const uint8_t*>(mp.scales);
   const uint32_t zv = *reinterpret_cast<const uint32_t*>(zp + g);
   P.s = sv;
   P.z = zv;
@@ -169,7 +179,7 @@ __device__ __forceinline__ void compute(const StreamArgs& a, const uint4 (&W)[B]
   s[2] = P.ok ? half_lo(P.s.y) : 0.0f;
   s[3] = P.ok ? half_hi(P.s.y) : 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) z[c] = a.zeros ? (float)((P.z >> (8 * c)) & 0xFFu) : (float)(1 << (B - 1));
+  for (int c = 0; c < 4; ++c) z[c] = a.has_zeros ? (float)((P.z >> (8 * c)) & 0xFFu) : (float)(1 << (B - 1));
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const float2 X = xsum_blk[m * sum_stride];
@@ -184,13 +194,13 @@ __device__ __forceinline__ void compute(const StreamArgs& a, const uint4 (&W)[B]
 // blk - lds_blk0 of this wave's area. With kPre, the first step's words and
 // parameters are already in Wa / Pa.
 template <int B, int MT, bool kPre>
-__device__ __forceinline__ void run_segment(const StreamArgs& a, int blk0, int blk1, int row0, int ks,
+__device__ __forceinline__ void run_segment(const StreamArgs& a, const MatPtrs& mp, int blk0, int blk1, int row0, int ks,
                                             const uint32_t* panel, int col, bool colv, const uint32_t* xs_w, const float2* xsum_w, int lds_blk0,
                                             uint32_t magic, float (&yacc)[4][MT], uint4 (&Wa)[B], Raw& Pa) {
   const int nsteps = (blk1 - blk0 + KS - 1) / KS;
   auto lane_issue = [&](int i, uint4 (&W)[B], Raw& P) {
     const int blk = blk0 + i * KS + ks;
-    issue<B>(a, panel, blk, row0 + (i * KS + ks) * B, colv && blk < blk1, blk0, row0, col, W, P);
+    issue<B>(a, mp, panel, blk, row0 + (i * KS + ks) * B, colv && blk < blk1, blk0, row0, col, W, P);
   };
   auto lane_compute = [&](int i, const uint4 (&W)[B], const Raw& P) {
     const int bl = min(blk0 + i * KS + ks, blk1 - 1) - lds_blk0;   // clamped: idle lanes hold zeros
@@ -217,7 +227,7 @@ __device__ __forceinline__ void run_segment(const StreamArgs& a, int blk0, int b
 }
 
 template <int MT, unsigned BS>
-__device__ __forceinline__ void any_segment(const StreamArgs& a, int bits, int blk0, int blk1, int row0, int ks,
+__device__ __forceinline__ void any_segment(const StreamArgs& a, const MatPtrs& mp, int bits, int blk0, int blk1, int row0, int ks,
                                             const uint32_t* panel, int col, bool colv, const uint32_t* xs_w, const float2* xsum_w,
                                             int lds_blk0, uint32_t magic, float (&yacc)[4][MT]) {
 #define QLINEAR_SEGMENT(BB)                                                                                \
@@ -225,7 +235,7 @@ __device__ __forceinline__ void any_segment(const StreamArgs& a, int bits, int b
     if constexpr ((BS >> BB) & 1u) {                                                                       \
       uint4 W[BB];                                                                                         \
       Raw P;                                                                                               \
-      run_segment<BB, MT, false>(a, blk0, blk1, row0, ks, panel, col, colv, xs_w, xsum_w, lds_blk0, magic, yacc, W, P); \
+      run_segment<BB, MT, false>(a, mp, blk0, blk1, row0, ks, panel, col, colv, xs_w, xsum_w, lds_blk0, magic, yacc, W, P); \
     }                                                                                                      \
     break;
   switch (bits) {
@@ -249,7 +259,7 @@ __host__ __device__ constexpr int stage_words(int chunk) {
 // Reduce the lane sums over the 16 block slots of each wave (lanes cq,
 // cq + 4, ..., cq + 60), then over the waves through LDS, and store y.
 template <int MT, int WV>
-__device__ __forceinline__ void reduce_store(const StreamArgs& a, float (&red)[WV][MT][SC], float (&yacc)[4][MT],
+__device__ __forceinline__ void reduce_store(const StreamArgs& a, uint16_t* y, float (&red)[WV][MT][SC], float (&yacc)[4][MT],
                                              int tid, int lane, int wave, int strip) {
   const int cq = lane % CQ, ks = lane / CQ;
 #pragma unroll
@@ -275,7 +285,7 @@ __device__ __forceinline__ void reduce_store(const StreamArgs& a, float (&red)[W
       float v = 0.0f;
 #pragma unroll
       for (int w = 0; w < WV; ++w) v += red[w][m][c];
-      a.y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+      y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
     }
   }
 }
@@ -283,7 +293,7 @@ __device__ __forceinline__ void reduce_store(const StreamArgs& a, float (&red)[W
 // Kernel body, specialised on B0, the width of this wave's first run, so the
 // first step can be issued into a typed buffer before the activation staging.
 template <int MT, unsigned BS, int WV, int B0>
-__device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, float (&red)[WV][MT][SC],
+__device__ __forceinline__ void stream_body(const StreamArgs& a, const MatPtrs& mp, uint32_t* lds, float (&red)[WV][MT][SC],
                                             int tid, int lane, int wave, int strip, int wb0, int wb1, int row0) {
   const int cq = lane % CQ, ks = lane / CQ;
   const int col_req = strip * SC + cq * 4;
@@ -291,7 +301,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, 
   const int col = colv ? col_req : a.N - 4;   // scale/zero column for lanes past N
   // The lane's 4 word slots in row 0 of this strip's panel (padding slots of
   // the last panel exist and hold zeros).
-  const uint32_t* panel = a.qweight + (size_t)strip * a.runs.packed_rows * kPanel + cq * 4;
+  const uint32_t* panel = mp.qweight + (size_t)strip * a.runs.packed_rows * kPanel + cq * 4;
   const int nblk = a.K / kBlockRows;
   const int per_wave = (nblk + WV - 1) / WV;
   const int nchunks = (per_wave + a.chunk - 1) / a.chunk;
@@ -310,7 +320,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, 
     // A wave without blocks (K < 32 * waves) reads block 0 and discards it.
     const int blk = wb0 + ks;
     const bool any = wb0 < wb1;
-    issue<B0>(a, panel, blk, row0 + ks * B0, any && colv && blk < seg0_end, any ? wb0 : 0, any ? row0 : 0, col, W0,
+    issue<B0>(a, mp, panel, blk, row0 + ks * B0, any && colv && blk < seg0_end, any ? wb0 : 0, any ? row0 : 0, col, W0,
               P0);
   }
 
@@ -358,25 +368,25 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, uint32_t* lds, 
 
     int blk = c0;
     if (ch == 0 && blk < seg0_end) {
-      run_segment<B0, MT, true>(a, blk, seg0_end, row0, ks, panel, col, colv, xs_w, xsum_w, c0, magic, yacc, W0, P0);
+      run_segment<B0, MT, true>(a, mp, blk, seg0_end, row0, ks, panel, col, colv, xs_w, xsum_w, c0, magic, yacc, W0, P0);
       blk = seg0_end;
     }
     while (blk < c1) {
       int bits, row;
       block_info(a.runs, blk, bits, row);
       const int seg_end = min(c1, run_end_block(a.runs, blk));
-      any_segment<MT, BS>(a, bits, blk, seg_end, row, ks, panel, col, colv, xs_w, xsum_w, c0, magic, yacc);
+      any_segment<MT, BS>(a, mp, bits, blk, seg_end, row, ks, panel, col, colv, xs_w, xsum_w, c0, magic, yacc);
       blk = seg_end;
     }
   }
 
-  reduce_store<MT, WV>(a, red, yacc, tid, lane, wave, strip);
+  reduce_store<MT, WV>(a, mp.y, red, yacc, tid, lane, wave, strip);
 }
 
 template <int MT, unsigned BS, int WV, int B0>
-__device__ __forceinline__ void dispatch_body(const StreamArgs& a, uint32_t* lds, float (&red)[WV][MT][SC], int tid,
+__device__ __forceinline__ void dispatch_body(const StreamArgs& a, const MatPtrs& mp, uint32_t* lds, float (&red)[WV][MT][SC], int tid,
                                               int lane, int wave, int strip, int wb0, int wb1, int row0) {
-  stream_body<MT, BS, WV, B0>(a, lds, red, tid, lane, wave, strip, wb0, wb1, row0);
+  stream_body<MT, BS, WV, B0>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0);
 }
 
 // One kernel per (MT, set of code widths that may occur). BS has bit b set
@@ -392,8 +402,11 @@ __global__ __launch_bounds__(WV * 64) void qgemv_stream_kernel(StreamArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
-  const int strip = (bid % kXcds) * a.strips_per_xcd + bid / kXcds;
-  if (strip >= a.nstrips) return;  // the whole workgroup leaves together
+  const int gstrip = (bid % kXcds) * a.strips_per_xcd + bid / kXcds;
+  if (gstrip >= a.mats * a.nstrips) return;  // the whole workgroup leaves together
+  const int mi = gstrip / a.nstrips;         // matrix of the group
+  const int strip = gstrip - mi * a.nstrips;
+  const MatPtrs mp = a.mat[mi];
 
   const int nblk = a.K / kBlockRows;
   const int wb0 = (wave * nblk) / WV, wb1 = ((wave + 1) * nblk) / WV;
@@ -402,7 +415,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_stream_kernel(StreamArgs a) {
 
 #define QLINEAR_BODY(BB)                                                                     \
   case BB:                                                                                   \
-    if constexpr ((BS >> BB) & 1u) dispatch_body<MT, BS, WV, BB>(a, lds, red, tid, lane, wave, strip, wb0, wb1, row0);                                              \
+    if constexpr ((BS >> BB) & 1u) dispatch_body<MT, BS, WV, BB>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0);                                              \
     return;
   switch (bits0) {
     QLINEAR_BODY(2)
@@ -416,7 +429,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_stream_kernel(StreamArgs a) {
 #undef QLINEAR_BODY
   // This wave has no blocks (K too small for every wave): it still joins the
   // barriers of the staging and the final reduction, which the other waves run.
-  dispatch_body<MT, BS, WV, (BS & 16u) ? 4 : (BS & 4u) ? 2 : (BS & 8u) ? 3 : (BS & 32u) ? 5 : (BS & 64u) ? 6 : 8>(a, lds, red, tid, lane, wave, strip, wb0, wb1, row0);
+  dispatch_body<MT, BS, WV, (BS & 16u) ? 4 : (BS & 4u) ? 2 : (BS & 8u) ? 3 : (BS & 32u) ? 5 : (BS & 64u) ? 6 : 8>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0);
 }
 
 template <int MT, unsigned BS, int WV>
@@ -428,7 +441,7 @@ hipError_t launch_set(StreamArgs a, hipStream_t stream) {
   if (a.chunk < 1) a.chunk = 1;
   const size_t lds = (size_t)WV * stage_words<MT>(a.chunk) * 4;
   a.nstrips = (a.N + SC - 1) / SC;
-  a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
+  a.strips_per_xcd = (a.mats * a.nstrips + kXcds - 1) / kXcds;
   hipLaunchKernelGGL((qgemv_stream_kernel<MT, BS, WV>), dim3(kXcds * a.strips_per_xcd), dim3(WV * 64), lds, stream,
                      a);
   return hipGetLastError();

@@ -31,9 +31,12 @@ struct GemvWorkspace {
 };
 size_t qgemv_workspace_bytes(int K);
 GemvWorkspace qgemv_workspace(void* ws, int K);
+// mats (1 .. 8) matrices sharing the layout, x and perm: host arrays of
+// their device pointers (zeros: NULL, or an array whose entries are all
+// NULL or all not NULL).
 hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M, const int32_t* perm,
-                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y, void* ws,
-                        hipStream_t stream);
+                        int mats, const uint32_t* const* qweights, const uint16_t* const* scales,
+                        const uint8_t* const* zeros, uint16_t* const* ys, void* ws, hipStream_t stream);
 
 // Prefill layer. ws holds the gathered activations, float16 [M][K].
 // launch_qgemm_lds: the multiplication for layouts with several code widths,

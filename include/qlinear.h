@@ -54,6 +54,8 @@ extern "C" {
 #define QLINEAR_MAX_RUNS 64
 /* Largest M accepted by qlinear_qgemv (decode). */
 #define QLINEAR_GEMV_MAX_M 16
+/* Most matrices in one qlinear_qgemv_grouped call. */
+#define QLINEAR_MAX_GROUP 8
 
 /*
  * Description of one packed weight matrix: shape, group size and the
@@ -158,6 +160,27 @@ int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M,
                   const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                   const int32_t* perm, uint16_t* y, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * Several decode layers in one launch: count (1 .. QLINEAR_MAX_GROUP) matrices
+ * that share the layout, the activations x and the permutation perm -- the
+ * projections that read the same input, such as q, k and v, or gate and up
+ * (they are quantized against the same input, so act-order gives them the
+ * same permutation). One launch amortizes the fixed cost of a kernel over all
+ * of them, the point of the blog's fused-QKV kernel ("The Solution",
+ * architecture). For each i < count, computes what qlinear_qgemv computes with
+ * qweights_host[i], scales_host[i], zeros_host[i] into y_host[i].
+ *   qweights_host, scales_host, y_host : HOST arrays of count device pointers
+ *   zeros_host : NULL (all symmetric), or a HOST array of count device
+ *                pointers, all non-NULL
+ * Other arguments and errors as for qlinear_qgemv; INVALID_ARGUMENT also for
+ * count < 1 or a zeros array that mixes NULL and non-NULL entries,
+ * UNSUPPORTED for count > QLINEAR_MAX_GROUP.
+ */
+int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32_t M, int32_t count,
+                          const uint32_t* const* qweights_host, const uint16_t* const* scales_host,
+                          const uint8_t* const* zeros_host, const int32_t* perm, uint16_t* const* y_host,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace of qlinear_qgemm for M tokens, in bytes (no initialization needed). */
 int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes);

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = dq.lib()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     assert sorted(names) == sorted(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -124,6 +124,29 @@ def test_qgemv_validation_before_launch():
     assert _gemv(L, wsb=dq.qgemv_workspace_bytes(L) - 1) == _lib.ERR_WORKSPACE
     assert _gemv(L, M=0) == _lib.OK   # quick return, nothing launched
     assert _gemv(L, M=0, x=None, y=None, ws=None, wsb=0) == _lib.OK  # empty tensors may be NULL
+
+
+def test_qgemv_grouped_validation_before_launch():
+    L = _layout()
+    lib = dq.lib()
+    big = 1 << 30
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    ok = dict(q=arr(FAKE, FAKE), s=arr(FAKE, FAKE), z=None, y=arr(FAKE, FAKE))
+
+    def call(count=2, M=1, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.qlinear_qgemv_grouped(L.ref, FAKE, M, count, a["q"], a["s"], a["z"], None, a["y"], FAKE, big,
+                                         None)
+
+    assert call(count=0) == _lib.ERR_INVALID_ARGUMENT
+    assert call(count=9) == _lib.ERR_UNSUPPORTED
+    assert call(q=None) == _lib.ERR_INVALID_ARGUMENT
+    assert call(q=arr(FAKE, None)) == _lib.ERR_INVALID_ARGUMENT
+    assert call(y=arr(FAKE, FAKE + 2)) == _lib.ERR_MISALIGNED
+    assert call(z=arr(FAKE, None)) == _lib.ERR_INVALID_ARGUMENT      # mixed NULL / non-NULL zero points
+    assert call(M=17) == _lib.ERR_UNSUPPORTED
+    assert call(M=0) == _lib.OK
 
 
 def test_qgemm_validation_before_launch():

@@ -50,3 +50,21 @@ def test_recorded_traffic_is_tied_to_the_kernel_sources(tmp_path, monkeypatch):
     assert bench.recorded_traffic() is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
     assert bench.recorded_traffic() is None
+
+
+def test_grouped_launch_bytes_share_x_and_perm():
+    spec = wl.LLAMA7B_DECODE[0]
+    L = dq.Layout(spec.K, spec.N, spec.group_size, wl.bit_map(spec))
+    one = bench.row_kernel_bytes(L, 1)
+    shared = 4096 * 2 + 4096 * 4
+    assert bench.row_kernel_bytes(L, 1, count=3) == 3 * (one - shared) + shared
+
+
+def test_decode_groups_layer_order():
+    mats = [dict(shape=s, i=i) for i, s in enumerate([0, 0, 0, 0, 1, 1, 2] * 2)]
+    g = bench.decode_groups(mats, True)
+    assert [len(x["mats"]) for x in g] == [3, 1, 2, 1] * 2
+    assert [x["shape"] for x in g] == [0, 0, 1, 2] * 2
+    assert [m["i"] for x in g for m in x["mats"]] == list(range(14))
+    u = bench.decode_groups(mats, False)
+    assert [len(x["mats"]) for x in u] == [1] * 14

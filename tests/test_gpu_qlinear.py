@@ -200,3 +200,46 @@ def test_qgemm_prefill_workload():
     rows = np.unique(np.concatenate([np.arange(0, 2048, 16), [2047]]))
     ref = _ref(inp, inp.x[rows])
     assert_close(y[torch.from_numpy(rows).to(y.device)], ref, spec.name)
+
+
+# ------------------------------------------------------------------ grouped launches
+
+@pytest.mark.parametrize("bits,M,zeros", [([4] * 16, 1, True), ([4] * 16, 4, True), ([3] * 16, 1, False),
+                                          (MIXED_BITS, 1, False), (MIXED_BITS, 3, True)],
+                         ids=["4bit-M1", "4bit-M4", "3bit-M1-sym", "mixed-M1", "mixed-M3"])
+def test_grouped_qgemv_matches_separate_calls(bits, M, zeros):
+    """qlinear_qgemv_grouped over 3 matrices (same layout, x and perm, their
+    own codes, scales and zeros) gives each matrix's qlinear_qgemv result,
+    bit for bit, and the oracle's within tolerance."""
+    say(f"grouped qgemv bits={bits[0]}.. M={M} zeros={zeros}")
+    base = _mixed_inputs(bits, 32, 520, M, seed=300 + M, zeros=zeros)
+    lays = []
+    for i in range(3):
+        inp = _mixed_inputs(bits, 32, 520, M, seed=400 + 10 * M + i, zeros=zeros)
+        # share x and perm with the first matrix
+        inp = wl.LayerInputs(inp.spec, inp.bits, inp.q, inp.zeros, inp.scales, base.perm, base.x)
+        lays.append((inp, GpuLayer(inp)))
+    L0 = lays[0][1]
+    x = L0.x(base.x)
+    ys = dq.qgemv_grouped(L0.layout, x, [g.qweight for _, g in lays], [g.scales for _, g in lays],
+                          None if not zeros else [g.zeros for _, g in lays], L0.perm, L0.ws)
+    for (inp, g), y in zip(lays, ys):
+        y1 = dq.qgemv(g.layout, x, g.qweight, g.scales, g.zeros, L0.perm, g.ws)
+        assert torch.equal(y, y1)
+        assert_close(y, _ref(inp), "grouped")
+
+
+def test_grouped_qgemv_max_group_full_size():
+    """Eight 4096 -> 4096 GPTQ matrices in one launch (the largest group)."""
+    say("grouped qgemv 8 x 4096x4096")
+    spec = wl.LLAMA7B_DECODE[0]
+    inps = [wl.generate(spec, M=1, seed=s) for s in range(8)]
+    lays = [GpuLayer(i) for i in inps]
+    perm = lays[0].perm
+    x = lays[0].x(inps[0].x[:1])
+    ys = dq.qgemv_grouped(lays[0].layout, x, [g.qweight for g in lays], [g.scales for g in lays],
+                          [g.zeros for g in lays], perm, lays[0].ws)
+    for i in (0, 7):
+        ref = oracle.qlinear(inps[0].x[:1], inps[i].q, inps[i].scales, inps[i].zeros, inps[i].bits,
+                             spec.group_size, inps[0].perm)
+        assert_close(ys[i], ref, f"matrix {i}")

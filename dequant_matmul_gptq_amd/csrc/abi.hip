@@ -30,7 +30,8 @@ using namespace qlinear;
 
 // Largest K accepted: the block count is a grid dimension (< 65536).
 constexpr int64_t kMaxK = (int64_t)65535 * kBlockRows;
-// Largest M of qlinear_qgemm: row tiles of 128 in one grid dimension.
+// Largest M of qlinear_qgemm: the several-width kernel takes row tiles of 128
+// in one grid dimension.
 constexpr int64_t kMaxGemmM = (int64_t)65535 * 128;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -211,7 +212,7 @@ int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M, co
                   void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_gemm_operands(layout, x, M, qweight, scales, zeros, perm, y, workspace);
   if (st != QLINEAR_OK || M == 0) return st;
-  if (M > kMaxGemmM) return QLINEAR_ERR_UNSUPPORTED;
+  if (M > kMaxGemmM || !qgemm_supported(*layout)) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemm_workspace_bytes(M, layout->K)) return QLINEAR_ERR_WORKSPACE;
   return hip_status(launch_qgemm(*layout, make_runs(*layout), x, M, qweight, scales, zeros, perm, y, workspace,
                                  (hipStream_t)stream));

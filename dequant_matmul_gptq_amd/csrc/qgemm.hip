@@ -7,8 +7,8 @@
 //    order, and the weights below are used in that same order, so the
 //    contraction is unchanged.
 // 2. gemm_kernel (one code width; several widths go to the kernel in
-//    qgemm_lds.hip): a workgroup of 4 waves computes a 256 x 128 tile of y,
-//    each wave a 128 x 64 quarter as 8 x 4 fragments of
+//    qgemm_lds.hip): a workgroup of 8 waves computes a 256 x 256 tile of y,
+//    the waves as 2 x 4 tiles of 128 x 64, each as 8 x 4 fragments of
 //    v_mfma_f32_16x16x32_f16 (one 32-row block is one MFMA K step).
 //      - B (weights): no LDS. The B operand of a 16 x 16 x 32 MFMA gives
 //        lane l column l % 16 of the fragment and rows 8 (l / 16) .. + 7 of
@@ -18,25 +18,33 @@
 //        four. Each wave dequantizes its fragments exactly to float16 in
 //        registers (w = RNE(s * (q - z)), one rounding); each fragment feeds
 //        8 MFMAs. The packed words run two blocks ahead in a register ring.
-//      - A (activations): two LDS stages; block kb + 1's tile is loaded into
-//        registers during block kb and stored after its MFMAs; one barrier
-//        per block.
-//    Buffer loads take their per-block offsets in scalars. Two workgroups
-//    per CU (256 registers per lane): while one wave unpacks, another
-//    wave's MFMAs keep the matrix core busy.
-//    Accumulation is float32; the epilogue rounds to float16.
+//        For widths whose k-group sits in one or two words (2, 4, 8) block
+//        kb + 1 is dequantized while block kb's MFMAs run, so the unpacking
+//        interleaves with the matrix core inside every wave; the other widths
+//        (which read all b words per column) dequantize block kb in its own
+//        step, which keeps them within 256 registers.
+//      - A (activations): two LDS stages of 64-byte rows, 16-byte chunks
+//        XOR-swizzled so that tile stores and fragment reads are free of bank
+//        conflicts; block kb + 2's tile is loaded into registers during block
+//        kb and stored one step later; one barrier per block.
+//    Buffer loads take their per-block offsets in scalars; offsets are 32-bit,
+//    so the host runs M in row chunks whose activations stay below 2 GiB.
+//    Two waves per SIMD (256 registers per lane). Tiles are dealt to the 8
+//    XCDs in contiguous ranges. Accumulation is float32; the epilogue rounds
+//    to float16.
+#include <algorithm>
+
 #include "qlinear_kernels.hpp"
 
 namespace qlinear {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BM = 256, BN = 128;
-constexpr int WM = 128, WN = 64;             // wave tile: 2 x 2 waves
+constexpr int kThreads = 512;
+constexpr int BM = 256, BN = 256;
+constexpr int WM = 128, WN = 64;             // wave tile: 2 x 4 waves
 constexpr int FM = WM / 16, FN = WN / 16;    // 8 x 4 fragments per wave
-constexpr int kPad = 8;                      // halves of padding per LDS row
-constexpr int kLdsRow = kBlockRows + kPad;   // 40 halves = 80 bytes
+constexpr int kLdsRow = kBlockRows;          // 32 halves = 64 bytes, four 16-byte chunks
 constexpr int kAPieces = BM * kBlockRows / 8 / kThreads;  // 16-byte pieces of an A block per thread
 constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, 32-bit data
 
@@ -179,12 +187,18 @@ __device__ __forceinline__ void load_block(const GemmArgs& a, __amdgpu_buffer_rs
   R.z[S] = __builtin_amdgcn_raw_buffer_load_b32(rz, off.col, a.zeros ? grp * a.N : 0, 0);
 }
 
+// A tile rows are 64 bytes without padding; 16-byte chunk c of row r sits at
+// chunk position c ^ ((r >> 1) & 3). Both the 16-lane groups of the tile
+// stores (4 rows x 4 chunks) and of the fragment reads (16 rows, one chunk)
+// then cover all 64 banks once.
+__device__ __forceinline__ int lds_chunk(int r, int c) { return c ^ ((r >> 1) & 3); }
+
 __device__ __forceinline__ void store_a(uint16_t* stage, int tid, const u32x4 (&pieces)[kAPieces]) {
 #pragma unroll
   for (int i = 0; i < kAPieces; ++i) {
     const int lin = tid + i * kThreads;
     const int r = lin / 4, ch = lin % 4;
-    *reinterpret_cast<u32x4*>(&stage[r * kLdsRow + ch * 8]) = pieces[i];
+    *reinterpret_cast<u32x4*>(&stage[r * kLdsRow + lds_chunk(r, ch) * 8]) = pieces[i];
   }
 }
 
@@ -214,41 +228,63 @@ __device__ __forceinline__ void dequant_block(const GemmArgs& a, const Ring<kW, 
 
 __device__ __forceinline__ void read_a(const uint16_t* stage, int lane, int g, int wr, half8_t (&af)[FM]) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
-    af[i] = *reinterpret_cast<const half8_t*>(&stage[(wr * WM + i * 16 + (lane & 15)) * kLdsRow + 8 * g]);
+  for (int i = 0; i < FM; ++i) {
+    const int row = wr * WM + i * 16 + (lane & 15);
+    af[i] = *reinterpret_cast<const half8_t*>(&stage[row * kLdsRow + lds_chunk(row, g) * 8]);
+  }
 }
 
-// Block kb = kb0 + S (its A tile is in LDS stage S, its B words in ring slot
-// S): load block kb + 1's A pieces and block kb + 2's B words (clamped to the
-// last block), dequantize block kb's B fragments, read its A fragments, run
-// its MFMAs, then store block kb + 1's A pieces into stage S + 1.
+// Whether block kb + 1's B fragments are dequantized during block kb's MFMAs
+// (one or two words per k-group: widths 2, 4, 8).
+template <int kW>
+constexpr bool pipelined() {
+  return kW <= 2;
+}
+
+// Block kb = kb0 + S; its A tile is in LDS stage S, block kb + 1's A pieces
+// in an[S ^ 1]. The step loads block kb + 2's A pieces into an[S], runs block
+// kb's MFMAs and stores block kb + 1's A pieces into stage S ^ 1.
+//   pipelined: block kb's fragments are in bf[S] and block kb + 1's words in
+//     slot S ^ 1; the step dequantizes block kb + 1 into bf[S ^ 1] and then
+//     loads block kb + 3's words into slot S ^ 1.
+//   otherwise: block kb's words are in slot S; the step dequantizes them into
+//     bf[0] and then loads block kb + 2's words into slot S.
+// All loads are clamped to the last block.
 template <unsigned BS, int kW, int S>
 __device__ __forceinline__ void block_step(const GemmArgs& a, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
                                            __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz, int tid, int lane,
                                            int g, int wr, uint32_t magic, const LaneOffsets& off, int kb, int nblk,
-                                           uint16_t* As, Ring<kW, kRing>& R, float4_t (&acc)[FM][FN]) {
+                                           uint16_t* As, Ring<kW, kRing>& R, u32x4 (&an)[2][kAPieces],
+                                           half8_t (&bf)[2][FN], float4_t (&acc)[FM][FN]) {
   constexpr int kStage = BM * kLdsRow;
-  u32x4 an[kAPieces];
-  const int nb1 = min(kb + 1, nblk - 1);
+  constexpr int T = S ^ 1;
+  constexpr bool kPipe = pipelined<kW>();
+  constexpr int kUse = kPipe ? S : 0;   // fragments that this step's MFMAs use
+  const int nb2 = min(kb + 2, nblk - 1);
 #pragma unroll
   for (int i = 0; i < kAPieces; ++i)
-    an[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off.a[i], nb1 * kBlockRows * 2, 0));
-  half8_t bf[FN];
-  dequant_block<BS, kW, kRing, S>(a, R, g, magic, bf);
-  load_block<BS, kW, kRing, S>(a, rx, rw, rs, rz, g, off, min(kb + kRing, nblk - 1), R);
+    an[S][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off.a[i], nb2 * kBlockRows * 2, 0));
   half8_t af[FM];
-  read_a(As + S * kStage, lane, g, wr, af);
+  if constexpr (kPipe) {
+    read_a(As + S * kStage, lane, g, wr, af);
+    dequant_block<BS, kW, kRing, T>(a, R, g, magic, bf[T]);
+    load_block<BS, kW, kRing, T>(a, rx, rw, rs, rz, g, off, min(kb + 3, nblk - 1), R);
+  } else {
+    dequant_block<BS, kW, kRing, S>(a, R, g, magic, bf[0]);
+    load_block<BS, kW, kRing, S>(a, rx, rw, rs, rz, g, off, nb2, R);
+    read_a(As + S * kStage, lane, g, wr, af);
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-  store_a(As + ((S + 1) % kRing) * kStage, tid, an);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[kUse][j], acc[i][j], 0, 0, 0);
+  store_a(As + T * kStage, tid, an[T]);
   __syncthreads();
 }
 
 template <unsigned BS>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   constexpr int kW = max_frag_words<BS>();
   constexpr int D = kRing;
   __shared__ __align__(16) uint16_t As[kRing * BM * kLdsRow];
@@ -256,9 +292,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
+  const int wr = wave >> 2, wc = wave & 3;
+  // Tiles are taken XCD by XCD: workgroups are dispatched round-robin over
+  // the 8 XCDs, so workgroup i works on tile (i % 8) * ceil(T / 8) + i / 8 of
+  // the row-major tile order: an XCD's tiles share rows of A in its L2.
+  const int gx = (a.N + BN - 1) / BN;
+  const int ntiles = gx * ((a.M + BM - 1) / BM);
+  const int bid = blockIdx.x;
+  const int tile = (bid % 8) * ((ntiles + 7) / 8) + bid / 8;
+  if (tile >= ntiles) return;   // the whole workgroup leaves together
+  const int n0 = (tile % gx) * BN;
+  const int m0 = (tile / gx) * BM;
   const int nblk = a.K / kBlockRows;
   const int g = lane >> 4;   // k-group of the lane's B fragments
 
@@ -292,19 +336,26 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = {0.f, 0.f, 0.f, 0.f};
 
-  // Prologue: blocks 0 .. 3 in flight, A tiles of blocks 0 and 1 in stages 0
-  // and 1, block 0's fragments in registers.
+  // Prologue: packed words of blocks 0 and 1 in slots 0 and 1, A pieces of
+  // blocks 0 and 1 loaded, block 0's A tile in stage 0. Pipelined: block 0's
+  // fragments in bf[0] and block 2's words in flight in slot 0.
   static_for<0, D>([&](auto SS) {
     constexpr int S = decltype(SS)::value;
     load_block<BS, kW, D, S>(a, rx, rw, rs, rz, g, off, min(S, nblk - 1), R);
   });
-  {
-    u32x4 a0[kAPieces];
+  u32x4 an[2][kAPieces];
 #pragma unroll
-    for (int i = 0; i < kAPieces; ++i)
-      a0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off.a[i], 0, 0));
-    store_a(As, tid, a0);
+  for (int i = 0; i < kAPieces; ++i) {
+    an[0][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off.a[i], 0, 0));
+    an[1][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+        rx, off.a[i], min(1, nblk - 1) * kBlockRows * 2, 0));
   }
+  half8_t bf[2][FN];
+  if constexpr (pipelined<kW>()) {
+    dequant_block<BS, kW, D, 0>(a, R, g, magic, bf[0]);
+    load_block<BS, kW, D, 0>(a, rx, rw, rs, rz, g, off, min(2, nblk - 1), R);
+  }
+  store_a(As, tid, an[0]);
   __syncthreads();
 
   // Whole rounds of D blocks without conditions (static ring slots, exact
@@ -313,12 +364,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs a) {
   for (int kb0 = 0; kb0 < nfull; kb0 += D) {
     static_for<0, D>([&](auto SS) {
       constexpr int S = decltype(SS)::value;
-      block_step<BS, kW, S>(a, rx, rw, rs, rz, tid, lane, g, wr, magic, off, kb0 + S, nblk, As, R, acc);
+      block_step<BS, kW, S>(a, rx, rw, rs, rz, tid, lane, g, wr, magic, off, kb0 + S, nblk, As, R, an, bf, acc);
     });
   }
   static_for<0, D - 1>([&](auto SS) {
     constexpr int S = decltype(SS)::value;
-    if (nfull + S < nblk) block_step<BS, kW, S>(a, rx, rw, rs, rz, tid, lane, g, wr, magic, off, nfull + S, nblk, As, R, acc);
+    if (nfull + S < nblk) block_step<BS, kW, S>(a, rx, rw, rs, rz, tid, lane, g, wr, magic, off, nfull + S, nblk, As, R, an, bf, acc);
   });
 
   // Epilogue: lane holds C[4*(lane/16) + r][lane % 16] of each 16 x 16 tile;
@@ -352,45 +403,61 @@ void launch_set(const GemmArgs& a, dim3 grid, hipStream_t stream) {
 
 size_t qgemm_workspace_bytes(int M, int K) { return ((size_t)M * K * 2 + 255) / 256 * 256; }
 
-bool qgemm_fits(const qlinear_layout& L, int M) {
-  // Buffer offsets and sizes are 32-bit: every operand must stay below 2^31 bytes.
+bool qgemm_supported(const qlinear_layout& L) {
+  // Buffer offsets and sizes are 32-bit: the packed words and the scales must
+  // stay below 2^31 bytes (the activations are run in row chunks that do).
   const size_t lim = (size_t)1 << 31;
-  return (size_t)M * L.K * 2 < lim && (size_t)L.packed_words * 4 < lim && (size_t)L.groups * L.N * 2 < lim;
+  return (size_t)L.packed_words * 4 < lim && (size_t)L.groups * L.N * 2 < lim;
 }
 
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, void* ws, hipStream_t stream) {
-  uint32_t* xq = reinterpret_cast<uint32_t*>(ws);
-  hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, xq, nullptr, false, stream);
-  if (e != hipSuccess) return e;
-  GemmArgs a;
-  a.xq = reinterpret_cast<const uint16_t*>(xq);
-  a.qweight = qweight;
-  a.scales = scales;
-  a.zeros = zeros;
-  a.y = y;
-  a.M = M;
-  a.K = L.K;
-  a.N = L.N;
-  a.xq_bytes = (int)((size_t)M * L.K * 2);
-  a.qweight_bytes = (int)((size_t)L.packed_words * 4);
-  a.scale_bytes = (int)((size_t)L.groups * L.N * 2);
-  a.runs = runs;
   unsigned set = 0;
   for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
-  // Several code widths: the kernel that dequantizes into LDS block by block.
-  if ((set & (set - 1)) != 0) return launch_qgemm_lds(L, runs, a.xq, M, qweight, scales, zeros, y, stream);
-  const dim3 grid((L.N + BN - 1) / BN, (M + BM - 1) / BM, 1);
-  switch (set) {
-    case 1u << 2: launch_set<1u << 2>(a, grid, stream); break;
-    case 1u << 3: launch_set<1u << 3>(a, grid, stream); break;
-    case 1u << 4: launch_set<1u << 4>(a, grid, stream); break;
-    case 1u << 5: launch_set<1u << 5>(a, grid, stream); break;
-    case 1u << 6: launch_set<1u << 6>(a, grid, stream); break;
-    default: launch_set<1u << 8>(a, grid, stream); break;
+  // Row chunks whose gathered activations stay below 2^31 bytes (32-bit
+  // buffer offsets); a chunk is a whole number of 256-row tiles.
+  const int64_t rows_fit = (((int64_t)1 << 31) - 1) / ((int64_t)L.K * 2);
+  const int chunk = (int)std::min<int64_t>(M, std::max<int64_t>(BM, rows_fit / BM * BM));
+  for (int m0 = 0; m0 < M; m0 += chunk) {
+    const int mc = std::min(chunk, M - m0);
+    uint32_t* xq = reinterpret_cast<uint32_t*>(ws);
+    hipError_t e = launch_gather_pairs(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, nullptr, false, stream);
+    if (e != hipSuccess) return e;
+    uint16_t* yc = y + (size_t)m0 * L.N;
+    // Several code widths: the kernel that dequantizes into LDS block by block.
+    if ((set & (set - 1)) != 0) {
+      e = launch_qgemm_lds(L, runs, reinterpret_cast<const uint16_t*>(xq), mc, qweight, scales, zeros, yc, stream);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    GemmArgs a;
+    a.xq = reinterpret_cast<const uint16_t*>(xq);
+    a.qweight = qweight;
+    a.scales = scales;
+    a.zeros = zeros;
+    a.y = yc;
+    a.M = mc;
+    a.K = L.K;
+    a.N = L.N;
+    a.xq_bytes = (int)((size_t)mc * L.K * 2);
+    a.qweight_bytes = (int)((size_t)L.packed_words * 4);
+    a.scale_bytes = (int)((size_t)L.groups * L.N * 2);
+    a.runs = runs;
+    const int ntiles = ((L.N + BN - 1) / BN) * ((mc + BM - 1) / BM);
+    const dim3 grid(8 * ((ntiles + 7) / 8), 1, 1);
+    switch (set) {
+      case 1u << 2: launch_set<1u << 2>(a, grid, stream); break;
+      case 1u << 3: launch_set<1u << 3>(a, grid, stream); break;
+      case 1u << 4: launch_set<1u << 4>(a, grid, stream); break;
+      case 1u << 5: launch_set<1u << 5>(a, grid, stream); break;
+      case 1u << 6: launch_set<1u << 6>(a, grid, stream); break;
+      default: launch_set<1u << 8>(a, grid, stream); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace qlinear

@@ -45,6 +45,8 @@ hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uin
                             const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y,
                             hipStream_t stream);
 size_t qgemm_workspace_bytes(int M, int K);
+// Whether the packed words and scales fit the prefill kernel's 32-bit offsets.
+bool qgemm_supported(const qlinear_layout& L);
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, void* ws, hipStream_t stream);

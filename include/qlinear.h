@@ -189,6 +189,8 @@ int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_
  * Prefill-sized layer, any M >= 0 (M == 0 as for qlinear_qgemv), same
  * operands and result as qlinear_qgemv.
  * The workspace receives the act-order-gathered activations.
+ * Errors as for qlinear_qgemv; UNSUPPORTED also for M > 65535 * 128, or for
+ * packed words or scales of 2^31 bytes or more.
  */
 int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M,
                   const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,

@@ -202,6 +202,23 @@ def test_qgemm_prefill_workload():
     assert_close(y[torch.from_numpy(rows).to(y.device)], ref, spec.name)
 
 
+def test_qgemm_row_chunks():
+    """Activations of more than 2^31 bytes (M * K * 2): the prefill kernel's
+    offsets are 32-bit, so the rows run in chunks (here 32512 + 556 rows).
+    Rows on both sides of the chunk boundary against the oracle."""
+    K, N, gs, M = 32768, 256, 128, 33068
+    say(f"qgemm row chunks K={K} N={N} M={M}")
+    inp = _mixed_inputs([4] * (K // gs), gs, N, 1, seed=11, zeros=True)
+    layer = GpuLayer(inp)
+    gen = torch.Generator(device=layer.dev).manual_seed(11)
+    x = torch.randn((M, K), generator=gen, device=layer.dev, dtype=torch.float16)
+    y = dq.qgemm(layer.layout, x, layer.qweight, layer.scales, layer.zeros, layer.perm)
+    rows = np.array([0, 1, 255, 32511, 32512, 32513, 32767, M - 2, M - 1])
+    ridx = torch.from_numpy(rows).to(layer.dev)
+    ref = _ref(inp, x[ridx].cpu().numpy())
+    assert_close(y[ridx], ref, "row chunks")
+
+
 # ------------------------------------------------------------------ grouped launches
 
 @pytest.mark.parametrize("bits,M,zeros", [([4] * 16, 1, True), ([4] * 16, 4, True), ([3] * 16, 1, False),

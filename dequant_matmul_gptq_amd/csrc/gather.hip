@@ -1,5 +1,5 @@
-// Act-order gather of the activations into unpacking pair order, shared by
-// the decode and prefill paths.
+// Act-order gather of the activations into unpacking pair order, for the
+// decode and prefill paths.
 //
 //   xq[m][blk][p]  = (x[m][perm[32*blk + lo(p)]], x[m][perm[32*blk + hi(p)]])
 //   xsum[m][blk]   = (sum of the block's 32 values, 1024 * sum of the
@@ -12,6 +12,8 @@
 // order in which the weights come out of the packed words, so the weights
 // never need to be reordered. One thread per (block, pair); the 16 pairs of a
 // block are 16 consecutive lanes, which reduce the block sum with shuffles.
+#include <algorithm>
+
 #include "qlinear_kernels.hpp"
 
 namespace qlinear {
@@ -60,7 +62,50 @@ __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __res
   }
 }
 
+// Prefill variant (no scaling, no sums): a workgroup stages R whole rows of
+// x in LDS with 16-byte loads, then each thread takes pairs idx = tid,
+// tid + 256, ...; a pair's rows and perm entries are looked up once and
+// serve all R rows, whose values come from LDS. Rows of xq are written 1 KiB
+// per iteration, contiguous.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ perm,
+                                                          uint32_t* __restrict__ xq, int M, int K, int R,
+                                                          Runs runs) {
+  extern __shared__ __align__(16) uint16_t xs[];   // R rows of K float16
+  const int m0 = blockIdx.x * R;
+  const int rows = min(R, M - m0);
+  const int n16 = K / 8;   // 16-byte pieces per row (K is a multiple of 32)
+  const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)m0 * K);
+  uint4* dst = reinterpret_cast<uint4*>(xs);
+  for (int i = threadIdx.x; i < rows * n16; i += 256) dst[i] = src[i];
+  __syncthreads();
+  const int pairs = (K / kBlockRows) * kPairsPerBlock;
+  for (int idx = threadIdx.x; idx < pairs; idx += 256) {
+    const int blk = idx / kPairsPerBlock, p = idx % kPairsPerBlock;
+    int lo, hi;
+    pair_rows(block_bits_scan(runs, blk), p, lo, hi);
+    const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;
+    // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
+    const int flo = perm ? (int)min((unsigned)perm[jlo], (unsigned)(K - 1)) : jlo;
+    const int fhi = perm ? (int)min((unsigned)perm[jhi], (unsigned)(K - 1)) : jhi;
+    for (int r = 0; r < rows; ++r)
+      xq[(size_t)(m0 + r) * pairs + idx] = (uint32_t)xs[r * K + flo] | ((uint32_t)xs[r * K + fhi] << 16);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_rows(const Runs& runs, const uint16_t* x, const int32_t* perm, int M, int K,
+                              uint32_t* xq, hipStream_t stream) {
+  const size_t row_bytes = (size_t)K * 2;
+  if (row_bytes > kGatherRowsLds) return launch_gather_pairs(runs, x, perm, M, K, xq, nullptr, false, stream);
+  // Up to 4 rows per workgroup within 32 KiB, at least one row.
+  const int R = (int)std::max<size_t>(1, std::min<size_t>(4, (size_t)32768 / row_bytes));
+  const int grid = (M + R - 1) / R;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), (size_t)R * row_bytes, stream, x, perm, xq, M, K,
+                     R, runs);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather_pairs(const Runs& runs, const uint16_t* x, const int32_t* perm, int M, int K,
                                uint32_t* xq, float2* xsum, bool scaled, hipStream_t stream) {

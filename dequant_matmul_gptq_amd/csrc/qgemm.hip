@@ -422,7 +422,7 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
   for (int m0 = 0; m0 < M; m0 += chunk) {
     const int mc = std::min(chunk, M - m0);
     uint32_t* xq = reinterpret_cast<uint32_t*>(ws);
-    hipError_t e = launch_gather_pairs(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, nullptr, false, stream);
+    hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, stream);
     if (e != hipSuccess) return e;
     uint16_t* yc = y + (size_t)m0 * L.N;
     // Several code widths: the kernel that dequantizes into LDS block by block.

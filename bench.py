@@ -141,39 +141,58 @@ def row_kernel_bytes(layout, M, zeros=True, perm=True, count=1):
     return count * per + M * K * 2 + (K * 4 if perm else 0)
 
 
-# Files whose code makes up the single-row qgemv kernel; recorded counter
-# data is valid only for the exact sources it was taken on.
+# Files whose code makes up a measured kernel; recorded counter data is valid
+# only for the exact sources it was taken on.
 ROW_KERNEL_SOURCES = ("qgemv_m1.hpp", "qgemv_row.hip", "qgemv_stream.hpp", "qgemv_stream.hip", "qlinear_device.hpp")
+GEMM_KERNEL_SOURCES = ("qgemm.hip", "qlinear_kernels.hpp", "qlinear_device.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemv_row_llama7b_decode_traffic.txt")
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_llama13b_mlp_prefill_counters.txt")
 
 
-def row_kernel_digest():
+def sources_digest(sources):
     import hashlib
     h = hashlib.sha256()
-    for f in ROW_KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "dequant_matmul_gptq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per single-row launch measured with FETCH_SIZE and WRITE_SIZE
-    (scaled by the copy-kernel calibration), averaged over the step's
-    launches, from the committed counter summary; None when it is missing or
-    was taken on other kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+def row_kernel_digest():
+    return sources_digest(ROW_KERNEL_SOURCES)
+
+
+def gemm_kernel_digest():
+    return sources_digest(GEMM_KERNEL_SOURCES)
+
+
+def _recorded(path, digest):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE plus
+    WRITE_SIZE, each scaled by the copy-kernel calibration); None when the
+    file is missing or was taken on other kernel sources."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_sources_sha256_16") != row_kernel_digest():
+    if kv.get("kernel_sources_sha256_16") != digest:
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def recorded_traffic():
+    """Single-row qgemv: HBM bytes per launch averaged over the step's launches."""
+    return _recorded(TRAFFIC_FILE, row_kernel_digest())
+
+
+def recorded_gemm_traffic():
+    """qgemm gemm_kernel on the 13B MLP prefill shape: HBM-side bytes per launch."""
+    return _recorded(GEMM_TRAFFIC_FILE, gemm_kernel_digest())
 
 
 def setup_decode(torch, dq, wl, dev):
@@ -426,7 +445,8 @@ def bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream):
             "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_gemm_traffic(),
+            "timed": "whole qlinear_qgemm call: act-order gather kernel + gemm_kernel",
         },
     }
 

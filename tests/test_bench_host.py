@@ -52,6 +52,18 @@ def test_recorded_traffic_is_tied_to_the_kernel_sources(tmp_path, monkeypatch):
     assert bench.recorded_traffic() is None
 
 
+def test_gemm_traffic_follows_its_own_sources(tmp_path, monkeypatch):
+    """The prefill kernel's recorded traffic is keyed to qgemm.hip and its
+    headers, not to the decode kernel's sources."""
+    assert bench.gemm_kernel_digest() != bench.row_kernel_digest()
+    f = tmp_path / "g.txt"
+    f.write_text(f"kernel_sources_sha256_16: {bench.gemm_kernel_digest()}\nhbm_bytes_per_launch: 4.5e8\n")
+    monkeypatch.setattr(bench, "GEMM_TRAFFIC_FILE", str(f))
+    assert bench.recorded_gemm_traffic() == 450000000
+    f.write_text(f"kernel_sources_sha256_16: {bench.row_kernel_digest()}\nhbm_bytes_per_launch: 4.5e8\n")
+    assert bench.recorded_gemm_traffic() is None
+
+
 def test_grouped_launch_bytes_share_x_and_perm():
     spec = wl.LLAMA7B_DECODE[0]
     L = dq.Layout(spec.K, spec.N, spec.group_size, wl.bit_map(spec))

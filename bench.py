@@ -144,7 +144,7 @@ def row_kernel_bytes(layout, M, zeros=True, perm=True, count=1):
 # Files whose code makes up a measured kernel; recorded counter data is valid
 # only for the exact sources it was taken on.
 ROW_KERNEL_SOURCES = ("qgemv_m1.hpp", "qgemv_row.hip", "qgemv_stream.hpp", "qgemv_stream.hip", "qlinear_device.hpp")
-GEMM_KERNEL_SOURCES = ("qgemm.hip", "qlinear_kernels.hpp", "qlinear_device.hpp")
+GEMM_KERNEL_SOURCES = ("qgemm.hip", "mfma_frag.hpp", "qlinear_kernels.hpp", "qlinear_device.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemv_row_llama7b_decode_traffic.txt")
 GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_llama13b_mlp_prefill_counters.txt")
 
@@ -342,6 +342,9 @@ def main():
     log(f"qgemv_row_kernel per launch: avg {tot_us / n_step:.2f} us, {achieved:.0f} GB/s; " +
         ", ".join(f"{p['launch']}: {p['avg_us']} us {p['gbs']} GB/s" for p in per_kind))
     traffic = recorded_traffic()
+    refs = reference_points(torch, stream, spin, [p["algorithmic_bytes"] for p in per_kind])
+    log(f"reference points: empty kernel {refs['empty_kernel_us']} us; same-size copy " +
+        ", ".join(f"{c['bytes_read']} B: {c['read_gbs']} GB/s read" for c in refs["copy"]))
 
     gemm = None if args.no_gemm else bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream)
 
@@ -389,10 +392,43 @@ def main():
             "algorithmic_bytes_per_launch": round(tot_bytes / n_step),
             "per_launch_kind": per_kind,
         },
+        "reference_points": refs,
         "cpu_baseline": cpu,
         "qgemm": gemm,
     }
     print(json.dumps(out), flush=True)
+
+
+def reference_points(torch, stream, spin, sizes):
+    """Two floors that frame the per-launch numbers, timed like the launches
+    (>= 256 back to back behind a spin kernel, between two events):
+    the back-to-back period of an empty kernel (torch.cuda._sleep(0)), and for
+    each launch size S a device-to-device copy that reads S bytes (and writes
+    S), over distinct buffers totalling >= 1 GiB. Its read rate is a
+    streaming-read ceiling of the same size that includes a kernel's fixed
+    cost."""
+    def batch(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(spin)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    empty = batch(lambda i: torch.cuda._sleep(0), 256)
+    copies = []
+    for size in sorted(set(sizes)):
+        nbuf = max(2, -(-(1 << 30) // size))
+        src = [torch.empty(size, dtype=torch.uint8, device=stream.device) for _ in range(nbuf)]
+        dst = [torch.empty(size, dtype=torch.uint8, device=stream.device) for _ in range(nbuf)]
+        for a, b in zip(src, dst):
+            b.copy_(a)
+        us = batch(lambda i: dst[i % nbuf].copy_(src[i % nbuf]), max(256, nbuf))
+        copies.append({"bytes_read": size, "avg_us": round(us, 3), "read_gbs": round(size / (us * 1e-6) / 1e9, 1)})
+        del src, dst
+    return {"empty_kernel_us": round(empty, 3), "copy": copies}
 
 
 def bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream):

@@ -1,6 +1,7 @@
 // Host side of the decode path: the single-row kernel for M = 1, otherwise
-// the act-order gather into the workspace and the multi-row kernel
-// instantiated for the smallest set of code widths covering the layout.
+// the act-order gather into the workspace, then for M <= 4 the multi-row
+// VALU kernel instantiated for the smallest set of code widths covering the
+// layout, and for 5 <= M <= 16 the MFMA kernel.
 #include "qgemv_m1.hpp"
 
 namespace qlinear {
@@ -53,6 +54,14 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   if (stream::single_row(M, L.K, set)) return stream::launch_row_set(set, a, stream);
   // The activations are gathered into the workspace by a kernel of their own.
   const GemvWorkspace w = qgemv_workspace(ws, L.K);
+  if (M > 4 && qgemv_mfma_supported(L)) {
+    // 5 to 16 rows: one MFMA row tile, unscaled activations. (Measured on
+    // MI355X: up to 4 rows the factored VALU kernel below is as fast or
+    // faster; from 8 rows on, the MFMA kernel is 3-7x faster.)
+    const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, nullptr, false, stream);
+    if (e != hipSuccess) return e;
+    return launch_qgemv_mfma(L, runs, w.xq, M, mats, qweights, scales, zeros, ys, stream);
+  }
   const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, w.xsum, true, stream);
   if (e != hipSuccess) return e;
   a.xq = w.xq;

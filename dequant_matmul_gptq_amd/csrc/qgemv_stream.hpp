@@ -465,6 +465,8 @@ hipError_t launch_set_small_m(const StreamArgs& a, hipStream_t stream) {
   return launch_set<4, BS, 4>(a, stream);
 }
 
+constexpr unsigned kLowBits = (1u << 2) | (1u << 3);                            // ~2-3 bpw
+constexpr unsigned kMidBits = (1u << 3) | (1u << 4) | (1u << 5) | (1u << 6);   // ~3.5-5 bpw
 constexpr unsigned kAllBits = (1u << 2) | (1u << 3) | (1u << 4) | (1u << 5) | (1u << 6) | (1u << 8);
 
 // Instantiated in the qgemv_stream_*.hip files: M <= 4 per set of widths,

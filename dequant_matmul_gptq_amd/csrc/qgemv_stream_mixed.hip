@@ -4,8 +4,6 @@
 namespace qlinear {
 namespace stream {
 
-constexpr unsigned kLowBits = (1u << 2) | (1u << 3);                            // ~2-3 bpw
-constexpr unsigned kMidBits = (1u << 3) | (1u << 4) | (1u << 5) | (1u << 6);   // ~3.5-5 bpw
 
 hipError_t launch_mixed(unsigned set, const StreamArgs& a, hipStream_t stream) {
   if ((set & ~kLowBits) == 0) return launch_set_small_m<kLowBits>(a, stream);

@@ -49,6 +49,14 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
 hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uint16_t* xq, int M,
                             const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y,
                             hipStream_t stream);
+// Decode layer for 2 <= M <= 16 on the matrix cores, from activations gathered
+// unscaled into xq (float16 [M][K], unpacking order); the packed words,
+// scales and M * K activations must each stay below 2^31 bytes.
+bool qgemv_mfma_supported(const qlinear_layout& L);
+hipError_t launch_qgemv_mfma(const qlinear_layout& L, const Runs& runs, const uint32_t* xq, int M, int mats,
+                             const uint32_t* const* qweights, const uint16_t* const* scales,
+                             const uint8_t* const* zeros, uint16_t* const* ys, hipStream_t stream);
+
 size_t qgemm_workspace_bytes(int M, int K);
 // Whether the packed words and scales fit the prefill kernel's 32-bit offsets.
 bool qgemm_supported(const qlinear_layout& L);

@@ -73,13 +73,14 @@ def test_qgemv_small_mixed(M, zeros):
     assert_close(y, _ref(inp), f"qgemv M={M}")
 
 
+@pytest.mark.parametrize("M", (4, 12))   # factored VALU kernel / MFMA kernel
 @pytest.mark.parametrize("gs", (32, 64, 128))
 @pytest.mark.parametrize("b", (2, 3, 4, 5, 6, 8))
-def test_qgemv_uniform_widths(b, gs):
-    say(f"qgemv uniform b={b} gs={gs}")
-    inp = _mixed_inputs([b] * (1024 // gs), gs, 776, 4, seed=b * 31 + gs, zeros=True)
+def test_qgemv_uniform_widths(b, gs, M):
+    say(f"qgemv uniform b={b} gs={gs} M={M}")
+    inp = _mixed_inputs([b] * (1024 // gs), gs, 776, M, seed=b * 31 + gs + M, zeros=True)
     y = GpuLayer(inp).qgemv(inp.x)
-    assert_close(y, _ref(inp), f"qgemv b={b} gs={gs}")
+    assert_close(y, _ref(inp), f"qgemv b={b} gs={gs} M={M}")
 
 
 @pytest.mark.parametrize("M", (1, 7, 130, 257))
@@ -222,8 +223,10 @@ def test_qgemm_row_chunks():
 # ------------------------------------------------------------------ grouped launches
 
 @pytest.mark.parametrize("bits,M,zeros", [([4] * 16, 1, True), ([4] * 16, 4, True), ([3] * 16, 1, False),
-                                          (MIXED_BITS, 1, False), (MIXED_BITS, 3, True)],
-                         ids=["4bit-M1", "4bit-M4", "3bit-M1-sym", "mixed-M1", "mixed-M3"])
+                                          (MIXED_BITS, 1, False), (MIXED_BITS, 3, True), ([4] * 16, 8, True),
+                                          (MIXED_BITS, 16, False)],
+                         ids=["4bit-M1", "4bit-M4", "3bit-M1-sym", "mixed-M1", "mixed-M3", "4bit-M8-mfma",
+                              "mixed-M16-mfma"])
 def test_grouped_qgemv_matches_separate_calls(bits, M, zeros):
     """qlinear_qgemv_grouped over 3 matrices (same layout, x and perm, their
     own codes, scales and zeros) gives each matrix's qlinear_qgemv result,

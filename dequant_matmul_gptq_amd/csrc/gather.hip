@@ -2,6 +2,8 @@
 // decode and prefill paths.
 //
 //   xq[m][blk][p]  = (x[m][perm[32*blk + lo(p)]], x[m][perm[32*blk + hi(p)]])
+//
+// (for the MFMA kernels, position p holds pair mfma_pair(b, p) instead)
 //   xsum[m][blk]   = (sum of the block's 32 values, 1024 * sum of the
 //                     scaled values) (optional, decode path)
 //
@@ -23,7 +25,7 @@ namespace {
 __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __restrict__ x,
                                                            const int32_t* __restrict__ perm,
                                                            uint32_t* __restrict__ xq, float2* __restrict__ xsum,
-                                                           int M, int K, int scaled, Runs runs) {
+                                                           int M, int K, int scaled, int mfma, Runs runs) {
   const int nblk = K / kBlockRows;
   const int pairs = nblk * kPairsPerBlock;
   const int idx = blockIdx.x * 256 + threadIdx.x;
@@ -31,7 +33,7 @@ __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __res
   const int blk = live ? idx / kPairsPerBlock : 0, p = idx % kPairsPerBlock;
   const int bits = block_bits_scan(runs, blk);
   int lo, hi;
-  pair_rows(bits, p, lo, hi);
+  pair_rows(bits, mfma ? mfma_pair(bits, p) : p, lo, hi);
   const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;
   // perm entries are clamped into [0, K): a malformed perm cannot address outside x.
   const int flo = perm ? (int)min((unsigned)perm[jlo], (unsigned)(K - 1)) : jlo;
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __res
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
                                                           const int32_t* __restrict__ perm,
                                                           uint32_t* __restrict__ xq, int M, int K, int R,
-                                                          Runs runs) {
+                                                          int mfma, Runs runs) {
   extern __shared__ __align__(16) uint16_t xs[];   // R rows of K float16
   const int m0 = blockIdx.x * R;
   const int rows = min(R, M - m0);
@@ -82,8 +84,9 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
   const int pairs = (K / kBlockRows) * kPairsPerBlock;
   for (int idx = threadIdx.x; idx < pairs; idx += 256) {
     const int blk = idx / kPairsPerBlock, p = idx % kPairsPerBlock;
+    const int bits = block_bits_scan(runs, blk);
     int lo, hi;
-    pair_rows(block_bits_scan(runs, blk), p, lo, hi);
+    pair_rows(bits, mfma ? mfma_pair(bits, p) : p, lo, hi);
     const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;
     // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
     const int flo = perm ? (int)min((unsigned)perm[jlo], (unsigned)(K - 1)) : jlo;
@@ -96,23 +99,23 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
 }  // namespace
 
 hipError_t launch_gather_rows(const Runs& runs, const uint16_t* x, const int32_t* perm, int M, int K,
-                              uint32_t* xq, hipStream_t stream) {
+                              uint32_t* xq, bool mfma, hipStream_t stream) {
   const size_t row_bytes = (size_t)K * 2;
-  if (row_bytes > kGatherRowsLds) return launch_gather_pairs(runs, x, perm, M, K, xq, nullptr, false, stream);
+  if (row_bytes > kGatherRowsLds) return launch_gather_pairs(runs, x, perm, M, K, xq, nullptr, false, mfma, stream);
   // Up to 4 rows per workgroup within 32 KiB, at least one row.
   const int R = (int)std::max<size_t>(1, std::min<size_t>(4, (size_t)32768 / row_bytes));
   const int grid = (M + R - 1) / R;
   hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), (size_t)R * row_bytes, stream, x, perm, xq, M, K,
-                     R, runs);
+                     R, mfma ? 1 : 0, runs);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_pairs(const Runs& runs, const uint16_t* x, const int32_t* perm, int M, int K,
-                               uint32_t* xq, float2* xsum, bool scaled, hipStream_t stream) {
+                               uint32_t* xq, float2* xsum, bool scaled, bool mfma, hipStream_t stream) {
   const int pairs = (K / kBlockRows) * kPairsPerBlock;
   const int gy = M < 65535 ? M : 65535;
   hipLaunchKernelGGL(gather_pairs_kernel, dim3((pairs + 255) / 256, gy, 1), dim3(256), 0, stream, x, perm, xq,
-                     xsum, M, K, scaled ? 1 : 0, runs);
+                     xsum, M, K, scaled ? 1 : 0, mfma ? 1 : 0, runs);
   return hipGetLastError();
 }
 

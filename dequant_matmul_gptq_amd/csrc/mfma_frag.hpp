@@ -4,7 +4,8 @@
 // The B operand of a 16 x 16 x 32 MFMA gives lane l column l % 16 and rows
 // 8 (l / 16) .. + 7 of the 32-row block, i.e. pairs 4g .. 4g + 3 of the
 // block's unpacking order (g = l / 16), with the K order inside the block
-// being the unpacking order (row_lo(p), row_hi(p) at k = 2p, 2p + 1). Each
+// being the MFMA pair order (row_lo(p), row_hi(p) of pair p = mfma_pair(b, q)
+// at k = 2q, 2q + 1; the natural unpacking order except for 3 and 5 bits). Each
 // fragment is dequantized exactly: (1024 + q) - (1024 + z) in float16 is
 // exact, then one rounding of s * (q - z).
 #pragma once
@@ -65,11 +66,31 @@ __device__ __forceinline__ void with_width(int bits, F&& f) {
   }
 }
 
-// The B fragment of k-group g from the words read for it: pairs 4g .. 4g + 3
-// as 1024 + q, then (1024 + q) - (1024 + z) exactly and one rounding of s * d.
+// The B fragment of k-group g from the words read for it: the pairs at
+// positions 4g .. 4g + 3 of the MFMA pair order (mfma_pair) as 1024 + q, then
+// (1024 + q) - (1024 + z) exactly and one rounding of s * d.
+// The words as opaque register values: a lane-dependent choice between
+// elements of the array would otherwise be folded into an indexed load, which
+// puts the array in scratch memory.
+template <int kW>
+__device__ __forceinline__ void opaque_words(const uint32_t (&w)[kW], uint32_t (&v)[kW]) {
+#pragma unroll
+  for (int t = 0; t < kW; ++t) {
+    v[t] = w[t];
+    asm("" : "+v"(v[t]));
+  }
+}
+
 template <int B, int kW>
-__device__ __forceinline__ half8_t dequant_frag(const uint32_t (&w)[kW], int g, half2_t neg_bias, half2_t scale,
+__device__ __forceinline__ half8_t dequant_frag(const uint32_t (&w_in)[kW], int g, half2_t neg_bias, half2_t scale,
                                                uint32_t magic) {
+  uint32_t w[kW];
+  if constexpr (B == 3 || B == 5 || B == 6) {
+    opaque_words(w_in, w);
+  } else {
+#pragma unroll
+    for (int t = 0; t < kW; ++t) w[t] = w_in[t];
+  }
   uint32_t pr[4];
   if constexpr (B == 4 || B == 8) {
     pr[0] = extract_pair<B, 0>(w, magic);
@@ -82,14 +103,42 @@ __device__ __forceinline__ half8_t dequant_frag(const uint32_t (&w)[kW], int g, 
     pr[1] = extract_pair<2, 1>(ws, magic);
     pr[2] = extract_pair<2, 2>(ws, magic);
     pr[3] = extract_pair<2, 3>(ws, magic);
+  } else if constexpr (B == 3) {
+    // MFMA pair order: k-group g < 3 takes slots 0..3 of word g; k-group 3
+    // takes slot 4 of words 0, 1, 2 and the spare pair. Word and shift are
+    // per-lane values, so each lane unpacks only its four pairs.
+    constexpr uint32_t kMask = Fmt<3>::kMask;
+    const bool last = g == 3;
+    const uint32_t wg = g == 0 ? w[0] : g == 1 ? w[1] : w[2];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const uint32_t src = last ? w[r] : wg;
+      const uint32_t sh = last ? 12u : 3u * r;
+      pr[r] = ((src >> sh) & kMask) | magic;
+    }
+    const uint32_t reg = ((wg >> 9) & kMask) | magic;
+    pr[3] = last ? extract_pair<3, 15>(w, magic) : reg;
+  } else if constexpr (B == 5) {
+    // MFMA pair order: k-group g takes slots 0..2 of word g, then slot g of
+    // word 4 (g < 3) or the spare pair (g = 3).
+    constexpr uint32_t kMask = Fmt<5>::kMask;
+    const uint32_t wg = g == 0 ? w[0] : g == 1 ? w[1] : g == 2 ? w[2] : w[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) pr[r] = ((wg >> (5u * r)) & kMask) | magic;
+    const uint32_t reg = ((w[4] >> (5u * (uint32_t)g)) & kMask) | magic;
+    pr[3] = g == 3 ? extract_pair<5, 15>(w, magic) : reg;
   } else {
-    uint32_t all[kPairsPerBlock];
-#pragma unroll
-    for (int p = 0; p < kPairsPerBlock; ++p) all[p] = 0;
-    static_for<0, kPairsPerBlock>([&](auto P) { all[decltype(P)::value] = extract_pair<B, decltype(P)::value>(w, magic); });
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      pr[r] = g == 0 ? all[r] : g == 1 ? all[4 + r] : g == 2 ? all[8 + r] : all[12 + r];
+    static_assert(B == 6, "widths 2, 3, 4, 5, 6, 8");
+    // Natural order: k-group g < 3 holds slots 0, 1 of words 2g and 2g + 1;
+    // k-group 3 the four spare pairs.
+    constexpr uint32_t kMask = Fmt<6>::kMask;
+    const uint32_t wa = g == 0 ? w[0] : g == 1 ? w[2] : w[4];
+    const uint32_t wb = g == 0 ? w[1] : g == 1 ? w[3] : w[5];
+    const bool last = g == 3;
+    pr[0] = last ? extract_pair<6, 12>(w, magic) : (wa & kMask) | magic;
+    pr[1] = last ? extract_pair<6, 13>(w, magic) : ((wa >> 6) & kMask) | magic;
+    pr[2] = last ? extract_pair<6, 14>(w, magic) : (wb & kMask) | magic;
+    pr[3] = last ? extract_pair<6, 15>(w, magic) : ((wb >> 6) & kMask) | magic;
   }
   half8_t f;
 #pragma unroll

@@ -344,11 +344,14 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
   for (int m0 = 0; m0 < M; m0 += chunk) {
     const int mc = std::min(chunk, M - m0);
     uint32_t* xq = reinterpret_cast<uint32_t*>(ws);
-    hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, stream);
+    // MFMA pair order for the register-dequant kernel; natural order for the
+    // kernel that dequantizes into LDS.
+    const bool mixed = (set & (set - 1)) != 0;
+    hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, !mixed, stream);
     if (e != hipSuccess) return e;
     uint16_t* yc = y + (size_t)m0 * L.N;
     // Several code widths: the kernel that dequantizes into LDS block by block.
-    if ((set & (set - 1)) != 0) {
+    if (mixed) {
       e = launch_qgemm_lds(L, runs, reinterpret_cast<const uint16_t*>(xq), mc, qweight, scales, zeros, yc, stream);
       if (e != hipSuccess) return e;
       continue;

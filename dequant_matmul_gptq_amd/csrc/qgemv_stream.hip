@@ -1,7 +1,7 @@
 // Host side of the decode path: the single-row kernel for M = 1, otherwise
-// the act-order gather into the workspace, then for M <= 4 the multi-row
-// VALU kernel instantiated for the smallest set of code widths covering the
-// layout, and for 5 <= M <= 16 the MFMA kernel.
+// the act-order gather into the workspace, then the MFMA kernel (M >= 3, see
+// below) or the multi-row VALU kernel instantiated for the smallest set of
+// code widths covering the layout.
 #include "qgemv_m1.hpp"
 
 namespace qlinear {
@@ -54,15 +54,19 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   if (stream::single_row(M, L.K, set)) return stream::launch_row_set(set, a, stream);
   // The activations are gathered into the workspace by a kernel of their own.
   const GemvWorkspace w = qgemv_workspace(ws, L.K);
-  if (M > 4 && qgemv_mfma_supported(L)) {
-    // 5 to 16 rows: one MFMA row tile, unscaled activations. (Measured on
-    // MI355X: up to 4 rows the factored VALU kernel below is as fast or
-    // faster; from 8 rows on, the MFMA kernel is 3-7x faster.)
-    const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, nullptr, false, stream);
+  // 3 to 16 rows: one MFMA row tile, unscaled activations in MFMA pair order.
+  // Measured on MI355X: the factored VALU kernel below is faster at 2 rows,
+  // and at 3-4 rows for single-width 3, 5 and 6-bit layouts (whose k-groups
+  // spread over several words); the MFMA kernel wins at 3-4 rows on every
+  // other shape measured (up to 1.7x) and from 5 rows on everywhere (3-7x at
+  // 8-16 rows).
+  const bool spread = set == (1u << 3) || set == (1u << 5) || set == (1u << 6);
+  if ((M > 4 || (M > 2 && !spread)) && qgemv_mfma_supported(L)) {
+    const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, nullptr, false, true, stream);
     if (e != hipSuccess) return e;
     return launch_qgemv_mfma(L, runs, w.xq, M, mats, qweights, scales, zeros, ys, stream);
   }
-  const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, w.xsum, true, stream);
+  const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, w.xsum, true, false, stream);
   if (e != hipSuccess) return e;
   a.xq = w.xq;
   a.xsum = w.xsum;

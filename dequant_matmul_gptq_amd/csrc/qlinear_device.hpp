@@ -94,6 +94,24 @@ __host__ __device__ __forceinline__ void pair_rows(int b, int p, int& lo, int& h
   }
 }
 
+// Pair order inside a block for the kernels that feed B fragments of a
+// 16 x 16 x 32 MFMA from the packed words: position q = 4g + r (k-group g of
+// the fragment, r < 4) holds pair mfma_pair(b, q). For 3 and 5 bits it keeps
+// each k-group's pairs in as few words as possible, so a lane unpacks only
+// its own four:
+//   b = 3: g < 3 takes slots 0..3 of word g; g = 3 takes slot 4 of words
+//          0, 1, 2 and the spare pair 15;
+//   b = 5: g takes slots 0..2 of word g, then slot g of word 4 (g < 3) or
+//          the spare pair 15 (g = 3).
+// Other widths keep the natural order (for 6 bits, k-groups 0..2 hold two
+// words each and k-group 3 the four spare pairs).
+__host__ __device__ __forceinline__ int mfma_pair(int b, int q) {
+  const int g = q >> 2, r = q & 3;
+  if (b == 3) return g < 3 ? 5 * g + r : r < 3 ? 5 * r + 4 : 15;
+  if (b == 5) return r < 3 ? 3 * g + r : g < 3 ? 12 + g : 15;
+  return q;
+}
+
 template <int B>
 struct Fmt {
   static constexpr int F = 16 / B;            // codes per half-word

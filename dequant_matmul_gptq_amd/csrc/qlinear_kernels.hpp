@@ -18,13 +18,15 @@ hipError_t launch_dequant(const qlinear_layout& L, const Runs& runs, const uint3
 // Act-order gather into unpacking pair order: xq uint32 [M][K/32][16] (float16
 // pairs, optionally pre-scaled by 2^-pair_exponent), optional block sums
 // xsum float2 [M][K/32] = (sum x, 1024 * sum of the scaled x).
+// mfma: positions in MFMA pair order (mfma_pair), for the kernels that feed
+// MFMA B fragments from the packed words.
 hipError_t launch_gather_pairs(const Runs& runs, const uint16_t* x, const int32_t* perm, int M, int K,
-                               uint32_t* xq, float2* xsum, bool scaled, hipStream_t stream);
+                               uint32_t* xq, float2* xsum, bool scaled, bool mfma, hipStream_t stream);
 // Prefill gather (no scaling, no sums): whole rows of x staged in LDS. Rows of
 // more than kGatherRowsLds bytes use launch_gather_pairs.
 constexpr size_t kGatherRowsLds = 64 * 1024;
 hipError_t launch_gather_rows(const Runs& runs, const uint16_t* x, const int32_t* perm, int M, int K,
-                              uint32_t* xq, hipStream_t stream);
+                              uint32_t* xq, bool mfma, hipStream_t stream);
 
 // Decode layer (M <= 16). For M > 1 (and for rows too long for the fused
 // M = 1 kernel) the workspace receives the gathered activations xq uint32

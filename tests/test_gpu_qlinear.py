@@ -73,7 +73,7 @@ def test_qgemv_small_mixed(M, zeros):
     assert_close(y, _ref(inp), f"qgemv M={M}")
 
 
-@pytest.mark.parametrize("M", (4, 12))   # factored VALU kernel / MFMA kernel
+@pytest.mark.parametrize("M", (2, 4, 12))   # VALU kernel; VALU (3, 5, 6 bits) or MFMA; MFMA
 @pytest.mark.parametrize("gs", (32, 64, 128))
 @pytest.mark.parametrize("b", (2, 3, 4, 5, 6, 8))
 def test_qgemv_uniform_widths(b, gs, M):

@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-group", action="store_true", help="one qgemv launch per matrix (no grouped q/k/v, gate/up)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the M = 2048 qgemm measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config decode points (7B at M = 4, 16; EXL2 at M = 1, 8; 70B at M = 1, 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy a MIB-MiB buffer 3 times (a known-size kernel for HBM counter calibration)")
     return ap.parse_args()
@@ -347,6 +349,7 @@ def main():
         ", ".join(f"{c['bytes_read']} B: {c['read_gbs']} GB/s read" for c in refs["copy"]))
 
     gemm = None if args.no_gemm else bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream)
+    configs = None if args.no_configs else bench_configs(torch, dq, wl, lib, dev, stream, spin)
 
     # ---------------------------------------------------------------- oracle on the host
     cpu = None
@@ -393,6 +396,7 @@ def main():
             "per_launch_kind": per_kind,
         },
         "reference_points": refs,
+        "decode_configs": configs,
         "cpu_baseline": cpu,
         "qgemm": gemm,
     }
@@ -429,6 +433,51 @@ def reference_points(torch, stream, spin, sizes):
         copies.append({"bytes_read": size, "avg_us": round(us, 3), "read_gbs": round(size / (us * 1e-6) / 1e9, 1)})
         del src, dst
     return {"empty_kernel_us": round(empty, 3), "copy": copies}
+
+
+def bench_configs(torch, dq, wl, lib, dev, stream, spin):
+    """qgemv on every (layer, M) of the decode configs that the step does not
+    cover: the 7B shapes at M = 4 and 16, EXL2 4.0 bpw at M = 1 and 8, the 70B
+    EXL2 2.5 bpw pair at M = 1 and 16. Per point, >= 256 calls back to back
+    behind a spin kernel, cycling through distinct weight copies totalling
+    >= 1 GiB (so the Infinity Cache cannot serve them), between two events on
+    the launch stream; GB/s counts the weight bytes (codes, scales, zeros)."""
+    sh = stream.cuda_stream
+    points = []
+    plan = [(s, (4, 16)) for s in wl.LLAMA7B_DECODE] + [(wl.EXL2_MIXED, (1, 8))] + \
+        [(s, (1, 16)) for s in wl.LLAMA70B_EXL2]
+    for spec, Ms in plan:
+        inp = wl.generate(spec, M=max(Ms))
+        L = dq.Layout(spec.K, spec.N, spec.group_size, inp.bits)
+        qw = dq.pack_weights(L, torch.from_numpy(inp.q).to(dev))
+        sc = torch.from_numpy(inp.scales).to(dev)
+        zr = None if inp.zeros is None else torch.from_numpy(inp.zeros).to(dev)
+        pm = torch.from_numpy(inp.perm).to(dev)
+        wbytes = wl.weight_bytes(spec)
+        ncopy = max(2, -(-(1 << 30) // wbytes))
+        copies = [(qw.clone(), sc.clone(), None if zr is None else zr.clone()) for _ in range(ncopy)]
+        ws = dq.qgemv_workspace(L, dev)
+        for M in Ms:
+            x = torch.from_numpy(inp.x[:M].copy()).to(dev)
+            y = torch.empty((M, spec.N), dtype=torch.float16, device=dev)
+            calls = [Launch(lib.qlinear_qgemv, L, x, M, q, c, z, pm, y, ws, sh) for q, c, z in copies]
+            for c in calls[:4]:
+                c()
+            n = max(256, ncopy)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(spin)
+            e0.record(stream)
+            for i in range(n):
+                calls[i % ncopy]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / n
+            points.append({"workload": spec.name, "M": M, "us_per_call": round(us, 2),
+                           "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1)})
+            log(f"config point {spec.name} M={M}: {us:.2f} us, {points[-1]['weight_gbs']} GB/s")
+        del copies, qw
+    return points
 
 
 def bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream):

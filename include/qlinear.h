@@ -28,6 +28,13 @@
  *    (codes in range, perm being a permutation) are not checked.
  *  - Pointers to device data must be 16-byte aligned (QLINEAR_ERR_MISALIGNED).
  *  - N must be a multiple of 8; K a multiple of gs.
+ *  - Non-finite activations: a NaN in row m of x makes row m of y NaN. An
+ *    Inf makes every element of its row non-finite: qlinear_qgemm and
+ *    qlinear_qgemv at 3 <= M <= 16 give the IEEE result of the formula
+ *    (+-Inf, NaN where the weight is 0). qlinear_qgemv at M <= 2, and at
+ *    M <= 4 for single-width 3, 5 or 6-bit layouts, gives NaN: it computes
+ *    the sum in a factored form that subtracts the activations' block sums.
+ *    Other rows are unaffected.
  */
 #ifndef QLINEAR_H
 #define QLINEAR_H

@@ -263,3 +263,40 @@ def test_grouped_qgemv_max_group_full_size():
         ref = oracle.qlinear(inps[0].x[:1], inps[i].q, inps[i].scales, inps[i].zeros, inps[i].bits,
                              spec.group_size, inps[0].perm)
         assert_close(ys[i], ref, f"matrix {i}")
+
+
+# ------------------------------------------------------------------ special values
+
+@pytest.mark.parametrize("op,bits,M,exact", [
+    ("qgemv", [4] * 11, 1, False),        # single-row kernel (factored arithmetic)
+    ("qgemv", MIXED_BITS, 1, False),      # gather + multi-row VALU kernel
+    ("qgemv", MIXED_BITS, 2, False),      # multi-row VALU kernel
+    ("qgemv", MIXED_BITS, 8, True),       # MFMA decode kernel (exact dequantization)
+    ("qgemm", MIXED_BITS, 64, True),      # prefill, several widths
+    ("qgemm", [4] * 11, 64, True),        # prefill, one width
+], ids=["row", "gather-valu-M1", "valu-M2", "mfma-M8", "qgemm-mixed", "qgemm-4bit"])
+def test_nonfinite_activations(op, bits, M, exact):
+    """A NaN activation makes its whole output row NaN; an Inf activation makes
+    every column of its row non-finite (exact-dequant kernels: the IEEE result
+    of the float64 oracle, +-Inf or NaN where the weight is 0; the factored
+    decode kernels subtract 1024 X' - z X and give NaN). Other rows are
+    unaffected."""
+    say(f"non-finite activations {op} M={M}")
+    inp = _mixed_inputs(bits, 32, 520, max(M, 2), seed=77 + M, zeros=True)
+    x = inp.x[:M].copy()
+    K = inp.spec.K
+    x[0, 5] = np.float16(np.nan)
+    if M >= 2:
+        x[1, K - 3] = np.float16(np.inf)
+    lay = GpuLayer(inp)
+    y = (lay.qgemv(x) if op == "qgemv" else lay.qgemm(x)).float().cpu().numpy()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = _ref(inp, x)
+    assert np.isnan(y[0]).all()
+    if M >= 2:
+        assert not np.isfinite(y[1]).any()
+        if exact:
+            assert np.array_equal(np.isnan(y[1]), np.isnan(ref[1]))
+            assert np.array_equal(np.sign(y[1][np.isinf(ref[1])]), np.sign(ref[1][np.isinf(ref[1])]))
+    if M > 2:
+        assert_close(torch.from_numpy(y[2:]), ref[2:], "finite rows")

@@ -48,7 +48,8 @@ struct MfmaArgs {
   MatPtrs mat[kMaxMats];
   int mats, has_zeros;
   int M, K, N, nstrips, strips_per_xcd;
-  int xq_bytes, qweight_bytes, scale_bytes;
+  int xq_bytes, scale_bytes;
+  int64_t packed_words;
   Runs runs;
 };
 
@@ -64,7 +65,7 @@ struct BlockLoads {
 struct Lane {
   __amdgpu_buffer_rsrc_t rx, rw, rs, rz;
   uint32_t xoff;   // byte offset of the lane's A piece in block 0
-  uint32_t woff;   // byte offset of packed row 0 of the lane's first column
+  uint32_t woff;   // byte offset of packed row 0 of the lane's first column in the strip's panels
   uint32_t col;    // the lane's first column (beyond every buffer when past N)
   int g;
 };
@@ -180,7 +181,12 @@ __global__ __launch_bounds__(kWaves * 64) void qgemv_mfma_kernel(MfmaArgs a) {
   Lane L;
   L.g = lane >> 4;
   L.rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, 0, a.xq_bytes, kRsrcWord3);
-  L.rw = __builtin_amdgcn_make_buffer_rsrc((void*)mp.qweight, 0, a.qweight_bytes, kRsrcWord3);
+  // The weight buffer starts at the strip's first panel, so 32-bit offsets
+  // cover any matrix: they only span the strip's FN panels.
+  const int64_t strip_words = (int64_t)FN * a.runs.packed_rows * kPanel;
+  const int64_t first_word = (int64_t)strip * strip_words;
+  L.rw = __builtin_amdgcn_make_buffer_rsrc((void*)(mp.qweight + first_word), 0,
+                                           (int)(min(strip_words, a.packed_words - first_word) * 4), kRsrcWord3);
   L.rs = __builtin_amdgcn_make_buffer_rsrc((void*)mp.scales, 0, a.scale_bytes, kRsrcWord3);
   L.rz = __builtin_amdgcn_make_buffer_rsrc(a.has_zeros ? (void*)mp.zeros : (void*)mp.scales, 0,
                                            a.has_zeros ? a.scale_bytes / 2 : a.scale_bytes, kRsrcWord3);
@@ -192,7 +198,8 @@ __global__ __launch_bounds__(kWaves * 64) void qgemv_mfma_kernel(MfmaArgs a) {
   const int col = strip * kPanel * FN + (lane & 15) * FN;
   const bool cok = col < a.N;
   L.col = cok ? (uint32_t)col : 0x40000000u;
-  L.woff = cok ? (uint32_t)(col / kPanel) * (uint32_t)a.runs.packed_rows * kPanel * 4 + (uint32_t)(col % kPanel) * 4
+  L.woff = cok ? (uint32_t)(col / kPanel - strip * FN) * (uint32_t)a.runs.packed_rows * kPanel * 4 +
+                     (uint32_t)(col % kPanel) * 4
                : 0x80000000u;
 
   const int nblk = a.K / kBlockRows;
@@ -259,10 +266,11 @@ hipError_t launch_set(const MfmaArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool qgemv_mfma_supported(const qlinear_layout& L) {
-  // Buffer offsets and sizes are 32-bit.
+  // Buffer offsets and sizes are 32-bit: the scales and the gathered
+  // activations must stay below 2^31 bytes (the weights are addressed per strip).
   const size_t lim = (size_t)1 << 31;
-  return (size_t)L.packed_words * 4 < lim && (size_t)L.groups * L.N * 2 < lim &&
-         (size_t)QLINEAR_GEMV_MAX_M * L.K * 2 < lim;
+  return (size_t)L.groups * L.N * 2 < lim && (size_t)QLINEAR_GEMV_MAX_M * L.K * 2 < lim &&
+         (size_t)4 * L.packed_rows * kPanel * 4 < lim;
 }
 
 hipError_t launch_qgemv_mfma(const qlinear_layout& L, const Runs& runs, const uint32_t* xq, int M, int mats,
@@ -285,7 +293,7 @@ hipError_t launch_qgemv_mfma(const qlinear_layout& L, const Runs& runs, const ui
   a.nstrips = 0;
   a.strips_per_xcd = 0;
   a.xq_bytes = (int)((size_t)M * L.K * 2);
-  a.qweight_bytes = (int)((size_t)L.packed_words * 4);
+  a.packed_words = L.packed_words;
   a.scale_bytes = (int)((size_t)L.groups * L.N * 2);
   a.runs = runs;
   unsigned set = 0;

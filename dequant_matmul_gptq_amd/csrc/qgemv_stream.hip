@@ -61,7 +61,7 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   // other shape measured (up to 1.7x) and from 5 rows on everywhere (3-7x at
   // 8-16 rows).
   const bool spread = set == (1u << 3) || set == (1u << 5) || set == (1u << 6);
-  if ((M > 4 || (M > 2 && !spread)) && qgemv_mfma_supported(L)) {
+  if (M > 4 || (M > 2 && !spread)) {
     const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, nullptr, false, true, stream);
     if (e != hipSuccess) return e;
     return launch_qgemv_mfma(L, runs, w.xq, M, mats, qweights, scales, zeros, ys, stream);
@@ -70,7 +70,6 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   if (e != hipSuccess) return e;
   a.xq = w.xq;
   a.xsum = w.xsum;
-  if (M > 4) return stream::launch_wide(a, stream);
   if ((set & (set - 1)) == 0) return stream::launch_uniform(set, a, stream);
   return stream::launch_mixed(set, a, stream);
 }

@@ -469,11 +469,10 @@ constexpr unsigned kLowBits = (1u << 2) | (1u << 3);                            
 constexpr unsigned kMidBits = (1u << 3) | (1u << 4) | (1u << 5) | (1u << 6);   // ~3.5-5 bpw
 constexpr unsigned kAllBits = (1u << 2) | (1u << 3) | (1u << 4) | (1u << 5) | (1u << 6) | (1u << 8);
 
-// Instantiated in the qgemv_stream_*.hip files: M <= 4 per set of widths,
-// and 4 < M <= 16 for any widths.
+// Instantiated in the qgemv_stream_*.hip files: M <= 4 per set of widths
+// (larger M runs the MFMA decode kernel).
 hipError_t launch_uniform(unsigned set, const StreamArgs& a, hipStream_t stream);
 hipError_t launch_mixed(unsigned set, const StreamArgs& a, hipStream_t stream);
-hipError_t launch_wide(const StreamArgs& a, hipStream_t stream);
 
 }  // namespace stream
 

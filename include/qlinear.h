@@ -162,6 +162,8 @@ int qlinear_qgemv_workspace_bytes(const qlinear_layout* layout, size_t* bytes);
  *             Must be a permutation of 0..K-1 (not checked).
  *   y       : float16 [M][N], written entirely
  *   workspace, workspace_bytes : see qlinear_qgemv_workspace_bytes
+ * Errors: as for the layout and pointers above; UNSUPPORTED for M > 16, or
+ * for M >= 3 when the scales reach 2^31 bytes (32-bit buffer offsets).
  */
 int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M,
                   const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,

@@ -145,7 +145,7 @@ def row_kernel_bytes(layout, M, zeros=True, perm=True, count=1):
 
 # Files whose code makes up a measured kernel; recorded counter data is valid
 # only for the exact sources it was taken on.
-ROW_KERNEL_SOURCES = ("qgemv_m1.hpp", "qgemv_row.hip", "qgemv_stream.hpp", "qgemv_stream.hip", "qlinear_device.hpp")
+ROW_KERNEL_SOURCES = ("qgemv_m1.hpp", "qgemv_row.hip", "qgemv_stream.hpp", "qlinear_device.hpp")
 GEMM_KERNEL_SOURCES = ("qgemm.hip", "mfma_frag.hpp", "qlinear_kernels.hpp", "qlinear_device.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemv_row_llama7b_decode_traffic.txt")
 GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_llama13b_mlp_prefill_counters.txt")

@@ -7,6 +7,8 @@ device memory and streams only.
 """
 
 from ._lib import (  # noqa: F401
+    ACT_NONE,
+    ACT_SILU,
     EXPORTS,
     GEMV_MAX_M,
     LIB_PATH,

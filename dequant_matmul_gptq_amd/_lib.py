@@ -40,7 +40,12 @@ EXPORTS = (
     "qlinear_qgemv_grouped",
     "qlinear_qgemm_workspace_bytes",
     "qlinear_qgemm",
+    "qlinear_qgemv_fused",
+    "qlinear_qgemm_fused",
 )
+
+ACT_NONE = 0
+ACT_SILU = 1
 
 
 class QlinearError(RuntimeError):
@@ -61,6 +66,14 @@ class qlinear_layout(ctypes.Structure):
         ("run_row", ctypes.c_int32 * (MAX_RUNS + 1)),
         ("run_bits", ctypes.c_int32 * MAX_RUNS),
         ("packed_words", ctypes.c_int64),
+    ]
+
+
+class qlinear_epilogue(ctypes.Structure):
+    _fields_ = [
+        ("bias", ctypes.c_void_p),
+        ("residual", ctypes.c_void_p),
+        ("activation", ctypes.c_int32),
     ]
 
 
@@ -89,6 +102,9 @@ def lib() -> ctypes.CDLL:
         L.qlinear_qgemv_grouped.argtypes = [lp, vp, i32, i32, pp, pp, pp, vp, pp, vp, sz, vp]
         L.qlinear_qgemm_workspace_bytes.argtypes = [lp, i32, ctypes.POINTER(sz)]
         L.qlinear_qgemm.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        ep = ctypes.POINTER(qlinear_epilogue)
+        L.qlinear_qgemv_fused.argtypes = [lp, vp, i32, vp, vp, vp, vp, ep, vp, vp, sz, vp]
+        L.qlinear_qgemm_fused.argtypes = [lp, vp, i32, vp, vp, vp, vp, ep, vp, vp, sz, vp]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -208,14 +224,34 @@ def _gemm_operands(layout, x, qweight, scales, zeros, perm, y):
     return M, y
 
 
+def _epilogue(layout, M, y, bias, residual, activation):
+    """The qlinear_epilogue of a fused call, or None for the plain call."""
+    if bias is None and residual is None and activation == ACT_NONE:
+        return None
+    if bias is not None:
+        _dev(bias, "bias", torch.float16, (layout.N,))
+    if residual is not None:
+        _dev(residual, "residual", torch.float16, (M, layout.N))
+    return qlinear_epilogue(_ptr(bias), _ptr(residual), int(activation))
+
+
 def qgemv(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
           zeros: torch.Tensor | None, perm: torch.Tensor | None, workspace: torch.Tensor,
-          y: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode layer, M = x.shape[0] <= 16. Returns y float16 [M][N]."""
+          y: torch.Tensor | None = None, bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+          activation: int = ACT_NONE) -> torch.Tensor:
+    """Decode layer, M = x.shape[0] <= 16. Returns y float16 [M][N]. With bias
+    [N], residual [M][N] (may be y) or activation ACT_SILU the fused call runs:
+    y = RNE(act(x W + bias) + residual)."""
     M, y = _gemm_operands(layout, x, qweight, scales, zeros, perm, y)
     _dev(workspace, "workspace", torch.uint8)
-    _check(lib().qlinear_qgemv(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
-                               _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemv")
+    epi = _epilogue(layout, M, y, bias, residual, activation)
+    if epi is None:
+        _check(lib().qlinear_qgemv(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
+                                   _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemv")
+    else:
+        _check(lib().qlinear_qgemv_fused(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros),
+                                         _ptr(perm), ctypes.byref(epi), _ptr(y), _ptr(workspace), workspace.numel(),
+                                         _stream(x.device)), "qlinear_qgemv_fused")
     return y
 
 
@@ -247,13 +283,20 @@ def qgemv_grouped(layout: Layout, x: torch.Tensor, qweights, scales, zeros, perm
 
 def qgemm(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
           zeros: torch.Tensor | None, perm: torch.Tensor | None, workspace: torch.Tensor | None = None,
-          y: torch.Tensor | None = None) -> torch.Tensor:
-    """Prefill layer, any M. Returns y float16 [M][N]."""
+          y: torch.Tensor | None = None, bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+          activation: int = ACT_NONE) -> torch.Tensor:
+    """Prefill layer, any M. Returns y float16 [M][N]; epilogue as for qgemv."""
     M, y = _gemm_operands(layout, x, qweight, scales, zeros, perm, y)
     need = qgemm_workspace_bytes(layout, M)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _dev(workspace, "workspace", torch.uint8)
-    _check(lib().qlinear_qgemm(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
-                               _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemm")
+    epi = _epilogue(layout, M, y, bias, residual, activation)
+    if epi is None:
+        _check(lib().qlinear_qgemm(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
+                                   _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemm")
+    else:
+        _check(lib().qlinear_qgemm_fused(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros),
+                                         _ptr(perm), ctypes.byref(epi), _ptr(y), _ptr(workspace), workspace.numel(),
+                                         _stream(x.device)), "qlinear_qgemm_fused")
     return y

@@ -78,6 +78,16 @@ int check_gemm_operands(const qlinear_layout* layout, const uint16_t* x, int32_t
   return QLINEAR_OK;
 }
 
+// The epilogue of a fused call (NULL: none).
+int check_epilogue(const qlinear_epilogue* e, Epilogue& out) {
+  out = Epilogue{nullptr, nullptr, QLINEAR_ACT_NONE};
+  if (!e) return QLINEAR_OK;
+  if (e->activation != QLINEAR_ACT_NONE && e->activation != QLINEAR_ACT_SILU) return QLINEAR_ERR_UNSUPPORTED;
+  if ((e->bias && !aligned16(e->bias)) || (e->residual && !aligned16(e->residual))) return QLINEAR_ERR_MISALIGNED;
+  out = Epilogue{e->bias, e->residual, e->activation};
+  return QLINEAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -164,15 +174,26 @@ int qlinear_qgemv_workspace_bytes(const qlinear_layout* layout, size_t* bytes) {
   return QLINEAR_OK;
 }
 
-int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
-                  const uint16_t* scales, const uint8_t* zeros, const int32_t* perm, uint16_t* y,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+int qlinear_qgemv_fused(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                        const uint16_t* scales, const uint8_t* zeros, const int32_t* perm,
+                        const qlinear_epilogue* epilogue, uint16_t* y, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   int st = check_gemm_operands(layout, x, M, qweight, scales, zeros, perm, y, workspace);
+  if (st != QLINEAR_OK) return st;
+  Epilogue epi;
+  st = check_epilogue(epilogue, epi);
   if (st != QLINEAR_OK || M == 0) return st;
   if (M > QLINEAR_GEMV_MAX_M || (M > 2 && !qgemv_mfma_supported(*layout))) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
   return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, 1, &qweight, &scales,
-                                 zeros ? &zeros : nullptr, &y, workspace, (hipStream_t)stream));
+                                 zeros ? &zeros : nullptr, &y, workspace, epi, (hipStream_t)stream));
+}
+
+int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                  const uint16_t* scales, const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return qlinear_qgemv_fused(layout, x, M, qweight, scales, zeros, perm, nullptr, y, workspace, workspace_bytes,
+                             stream);
 }
 
 int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32_t M, int32_t count,
@@ -196,7 +217,8 @@ int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32
   if (M > QLINEAR_GEMV_MAX_M || (M > 2 && !qgemv_mfma_supported(*layout))) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
   return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, count, qweights_host, scales_host,
-                                 zeros ? zeros_host : nullptr, y_host, workspace, (hipStream_t)stream));
+                                 zeros ? zeros_host : nullptr, y_host, workspace, Epilogue{nullptr, nullptr, 0},
+                                 (hipStream_t)stream));
 }
 
 int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes) {
@@ -207,15 +229,26 @@ int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_
   return QLINEAR_OK;
 }
 
-int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
-                  const uint16_t* scales, const uint8_t* zeros, const int32_t* perm, uint16_t* y,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+int qlinear_qgemm_fused(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                        const uint16_t* scales, const uint8_t* zeros, const int32_t* perm,
+                        const qlinear_epilogue* epilogue, uint16_t* y, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   int st = check_gemm_operands(layout, x, M, qweight, scales, zeros, perm, y, workspace);
+  if (st != QLINEAR_OK) return st;
+  Epilogue epi;
+  st = check_epilogue(epilogue, epi);
   if (st != QLINEAR_OK || M == 0) return st;
   if (M > kMaxGemmM || !qgemm_supported(*layout)) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemm_workspace_bytes(M, layout->K)) return QLINEAR_ERR_WORKSPACE;
-  return hip_status(launch_qgemm(*layout, make_runs(*layout), x, M, qweight, scales, zeros, perm, y, workspace,
+  return hip_status(launch_qgemm(*layout, make_runs(*layout), x, M, qweight, scales, zeros, perm, y, workspace, epi,
                                  (hipStream_t)stream));
+}
+
+int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                  const uint16_t* scales, const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return qlinear_qgemm_fused(layout, x, M, qweight, scales, zeros, perm, nullptr, y, workspace, workspace_bytes,
+                             stream);
 }
 
 }  // extern "C"

@@ -58,6 +58,7 @@ struct GemmArgs {
   int M, K, N;
   int xq_bytes, qweight_bytes, scale_bytes;
   Runs runs;
+  Epilogue epi;
 };
 
 
@@ -304,11 +305,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wr * WM + i * 16 + 4 * (lane >> 4) + r;
         if (m < a.M) {
+          uint16_t h[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            h[j] = __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(a.epi, acc[i][j][r], m, nq + j, a.N));
           u32x2 v;
-          v[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[i][0][r]) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[i][1][r]) << 16);
-          v[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[i][2][r]) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[i][3][r]) << 16);
+          v[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+          v[1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
           *reinterpret_cast<u32x2*>(a.y + (size_t)m * a.N + nq) = v;
         }
       }
@@ -334,7 +337,7 @@ bool qgemm_supported(const qlinear_layout& L) {
 
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
-                        const int32_t* perm, uint16_t* y, void* ws, hipStream_t stream) {
+                        const int32_t* perm, uint16_t* y, void* ws, const Epilogue& epi, hipStream_t stream) {
   unsigned set = 0;
   for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
   // Row chunks whose gathered activations stay below 2^31 bytes (32-bit
@@ -350,9 +353,12 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
     hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, !mixed, stream);
     if (e != hipSuccess) return e;
     uint16_t* yc = y + (size_t)m0 * L.N;
+    Epilogue ec = epi;   // the chunk's rows of the residual
+    if (ec.residual) ec.residual += (size_t)m0 * L.N;
     // Several code widths: the kernel that dequantizes into LDS block by block.
     if (mixed) {
-      e = launch_qgemm_lds(L, runs, reinterpret_cast<const uint16_t*>(xq), mc, qweight, scales, zeros, yc, stream);
+      e = launch_qgemm_lds(L, runs, reinterpret_cast<const uint16_t*>(xq), mc, qweight, scales, zeros, yc, ec,
+                           stream);
       if (e != hipSuccess) return e;
       continue;
     }
@@ -369,6 +375,7 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
     a.qweight_bytes = (int)((size_t)L.packed_words * 4);
     a.scale_bytes = (int)((size_t)L.groups * L.N * 2);
     a.runs = runs;
+    a.epi = ec;
     const int ntiles = ((L.N + BN - 1) / BN) * ((mc + BM - 1) / BM);
     const dim3 grid(8 * ((ntiles + 7) / 8), 1, 1);
     switch (set) {

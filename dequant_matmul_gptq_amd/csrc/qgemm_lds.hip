@@ -24,6 +24,7 @@ struct LdsGemmArgs {
   uint16_t* y;
   int M, K, N;
   Runs runs;
+  Epilogue epi;
 };
 
 // Unpack + dequantize one (block, column) into 16 float16 pairs in LDS.
@@ -143,7 +144,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(LdsGemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wr * 64 + i * 16 + 4 * (lane >> 4) + r;
-        if (m < a.M) a.y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
+        if (m < a.M)
+          a.y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(a.epi, acc[i][j][r], m, n, a.N));
       }
     }
   }
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(LdsGemmArgs a) {
 
 hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uint16_t* xq, int M,
                             const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y,
-                            hipStream_t stream) {
+                            const Epilogue& epi, hipStream_t stream) {
   LdsGemmArgs a;
   a.xq = xq;
   a.qweight = qweight;
@@ -164,6 +166,7 @@ hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uin
   a.K = L.K;
   a.N = L.N;
   a.runs = runs;
+  a.epi = epi;
   const int gmy = (M + BM - 1) / BM;
   hipLaunchKernelGGL(gemm_lds_kernel, dim3((L.N + BN - 1) / BN, gmy, 1), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

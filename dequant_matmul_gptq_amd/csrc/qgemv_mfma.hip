@@ -51,6 +51,7 @@ struct MfmaArgs {
   int xq_bytes, scale_bytes;
   int64_t packed_words;
   Runs runs;
+  Epilogue epi;
 };
 
 // One block's loads for one lane.
@@ -235,7 +236,8 @@ __global__ __launch_bounds__(kWaves * 64) void qgemv_mfma_kernel(MfmaArgs a) {
     for (int w = 0; w < kWaves; ++w) v += red[w][j][l][r];
     const int row = 4 * (l >> 4) + r;
     const int c = strip * kPanel * FN + (l & 15) * FN + j;
-    if (row < a.M && c < a.N) mp.y[(size_t)row * a.N + c] = __builtin_bit_cast(uint16_t, (_Float16)v);
+    if (row < a.M && c < a.N)
+      mp.y[(size_t)row * a.N + c] = __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(a.epi, v, row, c, a.N));
   }
 }
 
@@ -275,7 +277,8 @@ bool qgemv_mfma_supported(const qlinear_layout& L) {
 
 hipError_t launch_qgemv_mfma(const qlinear_layout& L, const Runs& runs, const uint32_t* xq, int M, int mats,
                              const uint32_t* const* qweights, const uint16_t* const* scales,
-                             const uint8_t* const* zeros, uint16_t* const* ys, hipStream_t stream) {
+                             const uint8_t* const* zeros, uint16_t* const* ys, const Epilogue& epi,
+                             hipStream_t stream) {
   MfmaArgs a;
   a.xq = reinterpret_cast<const uint16_t*>(xq);
   a.mats = mats;
@@ -296,6 +299,7 @@ hipError_t launch_qgemv_mfma(const qlinear_layout& L, const Runs& runs, const ui
   a.packed_words = L.packed_words;
   a.scale_bytes = (int)((size_t)L.groups * L.N * 2);
   a.runs = runs;
+  a.epi = epi;
   unsigned set = 0;
   for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
   switch (set) {

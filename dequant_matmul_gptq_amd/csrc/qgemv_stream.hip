@@ -25,7 +25,8 @@ GemvWorkspace qgemv_workspace(void* ws, int K) {
 
 hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M, const int32_t* perm,
                         int mats, const uint32_t* const* qweights, const uint16_t* const* scales,
-                        const uint8_t* const* zeros, uint16_t* const* ys, void* ws, hipStream_t stream) {
+                        const uint8_t* const* zeros, uint16_t* const* ys, void* ws, const Epilogue& epi,
+                        hipStream_t stream) {
   stream::StreamArgs a;
   a.x = x;
   a.perm = perm;
@@ -49,6 +50,7 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   a.xrow_words = 0;
   a.bpg_shift = L.group_size == 128 ? 2 : L.group_size == 64 ? 1 : 0;
   a.runs = runs;
+  a.epi = epi;
   unsigned set = 0;
   for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
   if (stream::single_row(M, L.K, set)) return stream::launch_row_set(set, a, stream);
@@ -64,7 +66,7 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   if (M > 4 || (M > 2 && !spread)) {
     const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, nullptr, false, true, stream);
     if (e != hipSuccess) return e;
-    return launch_qgemv_mfma(L, runs, w.xq, M, mats, qweights, scales, zeros, ys, stream);
+    return launch_qgemv_mfma(L, runs, w.xq, M, mats, qweights, scales, zeros, ys, epi, stream);
   }
   const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, w.xsum, true, false, stream);
   if (e != hipSuccess) return e;

@@ -77,6 +77,7 @@ struct StreamArgs {
   int xrow_words;          // single-row kernel: LDS words holding the x row
   int bpg_shift;           // log2(group_size / 32)
   Runs runs;
+  Epilogue epi;
 };
 
 template <int I, int E, class F>
@@ -285,7 +286,7 @@ __device__ __forceinline__ void reduce_store(const StreamArgs& a, uint16_t* y, f
       float v = 0.0f;
 #pragma unroll
       for (int w = 0; w < WV; ++w) v += red[w][m][c];
-      y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+      y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(a.epi, v, m, n, a.N));
     }
   }
 }

@@ -22,6 +22,22 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// Output epilogue, applied in float32 before the float16 rounding:
+//   y[m][n] = RNE_fp16( act(acc + bias[n]) + residual[m][n] )
+// with act the identity or SiLU, v / (1 + e^-v). Absent terms are NULL / 0.
+struct Epilogue {
+  const uint16_t* bias;       // float16 [N] or NULL
+  const uint16_t* residual;   // float16 [M][N] or NULL (may be the output itself)
+  int act;                    // QLINEAR_ACT_NONE or QLINEAR_ACT_SILU
+};
+
+__device__ __forceinline__ float apply_epilogue(const Epilogue& e, float v, int m, int n, int N) {
+  if (e.bias) v += (float)__builtin_bit_cast(_Float16, e.bias[n]);
+  if (e.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
+  if (e.residual) v += (float)__builtin_bit_cast(_Float16, e.residual[(size_t)m * N + n]);
+  return v;
+}
+
 // Run table in units of 32-row blocks, copied into the kernel arguments.
 struct Runs {
   int nruns;

@@ -43,27 +43,29 @@ GemvWorkspace qgemv_workspace(void* ws, int K);
 // NULL or all not NULL).
 hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M, const int32_t* perm,
                         int mats, const uint32_t* const* qweights, const uint16_t* const* scales,
-                        const uint8_t* const* zeros, uint16_t* const* ys, void* ws, hipStream_t stream);
+                        const uint8_t* const* zeros, uint16_t* const* ys, void* ws, const Epilogue& epi,
+                        hipStream_t stream);
 
 // Prefill layer. ws holds the gathered activations, float16 [M][K].
 // launch_qgemm_lds: the multiplication for layouts with several code widths,
 // from activations already gathered (xq, float16 [M][K]).
 hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uint16_t* xq, int M,
                             const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y,
-                            hipStream_t stream);
-// Decode layer for 2 <= M <= 16 on the matrix cores, from activations gathered
+                            const Epilogue& epi, hipStream_t stream);
+// Decode layer for 3 <= M <= 16 on the matrix cores, from activations gathered
 // unscaled into xq (float16 [M][K], unpacking order); the packed words,
 // scales and M * K activations must each stay below 2^31 bytes.
 bool qgemv_mfma_supported(const qlinear_layout& L);
 hipError_t launch_qgemv_mfma(const qlinear_layout& L, const Runs& runs, const uint32_t* xq, int M, int mats,
                              const uint32_t* const* qweights, const uint16_t* const* scales,
-                             const uint8_t* const* zeros, uint16_t* const* ys, hipStream_t stream);
+                             const uint8_t* const* zeros, uint16_t* const* ys, const Epilogue& epi,
+                             hipStream_t stream);
 
 size_t qgemm_workspace_bytes(int M, int K);
 // Whether the packed words and scales fit the prefill kernel's 32-bit offsets.
 bool qgemm_supported(const qlinear_layout& L);
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
-                        const int32_t* perm, uint16_t* y, void* ws, hipStream_t stream);
+                        const int32_t* perm, uint16_t* y, void* ws, const Epilogue& epi, hipStream_t stream);
 
 }  // namespace qlinear

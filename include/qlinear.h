@@ -64,6 +64,10 @@ extern "C" {
 /* Most matrices in one qlinear_qgemv_grouped call. */
 #define QLINEAR_MAX_GROUP 8
 
+/* Activations of the fused epilogue (qlinear_epilogue.activation). */
+#define QLINEAR_ACT_NONE 0
+#define QLINEAR_ACT_SILU 1 /* v / (1 + exp(-v)), the activation of the Llama MLP */
+
 /*
  * Description of one packed weight matrix: shape, group size and the
  * row-group -> bit-width map, run-length encoded. Filled on the host by
@@ -205,6 +209,39 @@ int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M,
                   const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                   const int32_t* perm, uint16_t* y, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * Output epilogue of the fused calls below: the operations that the GPTQ
+ * kernels fuse into the matmul (ExLlamaV2 project page: scaling, addition,
+ * activation), applied in float32 to each output before its float16
+ * rounding:
+ *   y[m][n] = RNE_fp16( act(acc[m][n] + bias[n]) + residual[m][n] )
+ * where acc is the float32 sum of the plain calls.
+ *   bias       : float16 [N], or NULL
+ *   residual   : float16 [M][N], or NULL; it may be y itself (in place)
+ *   activation : QLINEAR_ACT_NONE or QLINEAR_ACT_SILU
+ * HOST struct, read during the call only.
+ */
+typedef struct qlinear_epilogue {
+  const uint16_t* bias;
+  const uint16_t* residual;
+  int32_t activation;
+} qlinear_epilogue;
+
+/*
+ * qlinear_qgemv and qlinear_qgemm with an output epilogue (NULL = none, the
+ * plain call). Same arguments and errors as the plain calls; also
+ * UNSUPPORTED for an unknown activation, MISALIGNED for a bias or residual
+ * that is not 16-byte aligned.
+ */
+int qlinear_qgemv_fused(const qlinear_layout* layout, const uint16_t* x, int32_t M,
+                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                        const int32_t* perm, const qlinear_epilogue* epilogue, uint16_t* y,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int qlinear_qgemm_fused(const qlinear_layout* layout, const uint16_t* x, int32_t M,
+                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                        const int32_t* perm, const qlinear_epilogue* epilogue, uint16_t* y,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -14,6 +14,8 @@ Every function follows the pages' description of the method:
   (ExLlamaV2 blog, "The Investigation", Finding 3; README, "EXL2 quantization").
 * Fused dequantize-and-multiply with float32 accumulation and a float16 output
   (ExLlamaV2 blog, "How the Fused CUDA Kernel Works").
+* The fused output epilogue: bias, activation, residual (ExLlamaV2 artifact
+  page, GPTQ paragraph: kernels fuse scaling, addition and activation).
 """
 
 from .qlinear_oracle import (  # noqa: F401
@@ -33,4 +35,8 @@ from .qlinear_oracle import (  # noqa: F401
     qlinear,
     qlinear_gidx,
     qlinear_bruteforce,
+    ACT_NONE,
+    ACT_SILU,
+    silu,
+    apply_epilogue,
 )

@@ -23,6 +23,8 @@ gs rows per group, G = K / gs groups, b_g the bit width of group g):
    per-group scaling).
 4. ``y[m][n] = sum_j x[m][perm[j]] * w[j][n]``: the fused matmul of the blog's
    sketch, here computed exactly in float64 (no float16 rounding of w or y).
+5. Optionally the fused epilogue ``act(y + bias) + residual`` (see
+   :func:`apply_epilogue`).
 
 Parity unpinned: nothing here. Every function is pinned by tests that do not
 re-use its formula (see ``tests/test_oracle_pins.py``).
@@ -318,3 +320,38 @@ def qlinear_bruteforce(x, q, scales, zeros, bits, gs: int, perm=None) -> np.ndar
                 acc += float(x[m][p[j]]) * (float(s[g][n]) * (float(q[j][n]) - zz))
             y[m][n] = acc
     return np.array(y, dtype=np.float64)
+
+
+# ---------------------------------------------------------------- epilogue
+#
+# The artifact page's GPTQ paragraph says the kernels fuse scaling, addition
+# and activation into one call. Reading (the pages name neither the terms nor
+# the activation): addition is a per-output bias and a residual, the
+# activation is SiLU (the Llama MLP's), and the order is that of a layer
+# followed by its activation and then the residual stream:
+#   y[m][n] = act(acc[m][n] + bias[n]) + residual[m][n]
+
+ACT_NONE = 0
+ACT_SILU = 1
+
+
+def silu(v) -> np.ndarray:
+    """SiLU in float64: v * sigmoid(v) = v / (1 + exp(-v))."""
+    v = np.asarray(v, np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def apply_epilogue(acc, bias=None, residual=None, activation: int = ACT_NONE) -> np.ndarray:
+    """The fused epilogue on float64 layer outputs acc [M][N]; bias [N] and
+    residual [M][N] are float16 or float64 (None: absent)."""
+    y = np.asarray(acc, np.float64).copy()
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    if activation == ACT_SILU:
+        y = silu(y)
+    elif activation != ACT_NONE:
+        raise ValueError(f"unknown activation {activation}")
+    if residual is not None:
+        y = y + np.asarray(residual, np.float64)
+    return y

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = dq.lib()
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     assert sorted(names) == sorted(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -157,6 +157,26 @@ def test_qgemm_validation_before_launch():
     assert _gemm(L, y=FAKE + 1) == _lib.ERR_MISALIGNED
     assert _gemm(L, M=0) == _lib.OK
     assert _gemm(L, M=0, x=None, y=None, ws=None, wsb=0) == _lib.OK
+
+
+def test_fused_epilogue_validation_before_launch():
+    """The fused calls check the epilogue (activation, alignment) before
+    launching; M = 0 returns OK only once the epilogue is valid."""
+    L = _layout()
+    lib = dq.lib()
+    for fn in (lib.qlinear_qgemv_fused, lib.qlinear_qgemm_fused):
+        def call(epi, M=0, y=FAKE):
+            e = None if epi is None else ctypes.byref(epi)
+            return fn(L.ref, FAKE, M, FAKE, FAKE, None, None, e, y, FAKE, 1 << 30, None)
+
+        E = _lib.qlinear_epilogue
+        assert call(None) == _lib.OK                                     # no epilogue: the plain call
+        assert call(E(FAKE, FAKE, _lib.ACT_SILU)) == _lib.OK
+        assert call(E(None, None, 7)) == _lib.ERR_UNSUPPORTED               # unknown activation
+        assert call(E(FAKE + 2, None, 0)) == _lib.ERR_MISALIGNED             # bias
+        assert call(E(None, FAKE + 8, 0)) == _lib.ERR_MISALIGNED             # residual
+        assert call(E(None, None, 0), M=1, y=None) == _lib.ERR_INVALID_ARGUMENT   # operands still checked
+        assert call(E(None, None, 0), M=17 if fn is lib.qlinear_qgemv_fused else -1) != _lib.OK
 
 
 def test_tampered_layout_is_rejected():

@@ -300,3 +300,45 @@ def test_nonfinite_activations(op, bits, M, exact):
             assert np.array_equal(np.sign(y[1][np.isinf(ref[1])]), np.sign(ref[1][np.isinf(ref[1])]))
     if M > 2:
         assert_close(torch.from_numpy(y[2:]), ref[2:], "finite rows")
+
+
+# ------------------------------------------------------------------ fused epilogue
+
+EPILOGUE_PATHS = [
+    ("qgemv", [4] * 11, 1),        # single-row kernel
+    ("qgemv", MIXED_BITS, 1),      # gather + multi-row VALU kernel
+    ("qgemv", MIXED_BITS, 2),      # multi-row VALU kernel
+    ("qgemv", [4] * 11, 5),        # MFMA decode kernel
+    ("qgemv", MIXED_BITS, 16),     # MFMA decode kernel, several widths
+    ("qgemm", [4] * 11, 100),      # prefill, register dequant
+    ("qgemm", MIXED_BITS, 100),    # prefill, LDS dequant
+]
+
+
+@pytest.mark.parametrize("op,bits,M", EPILOGUE_PATHS,
+                         ids=["row", "gather-valu-M1", "valu-M2", "mfma-M5", "mfma-M16", "qgemm", "qgemm-mixed"])
+@pytest.mark.parametrize("terms", ["bias", "residual", "bias-silu-residual", "silu-inplace-residual"])
+def test_fused_epilogue(op, bits, M, terms):
+    """y = RNE(act(x W + bias) + residual) on every kernel path, against the
+    float64 oracle's layer output followed by its epilogue."""
+    say(f"fused epilogue {op} M={M} {terms}")
+    inp = _mixed_inputs(bits, 32, 520, M, seed=300 + M, zeros=True)
+    lay = GpuLayer(inp)
+    rng = np.random.default_rng(41)
+    N = inp.spec.N
+    bias = rng.standard_normal(N).astype(np.float16) if "bias" in terms else None
+    resid = rng.standard_normal((M, N)).astype(np.float16) if "residual" in terms else None
+    act = dq.ACT_SILU if "silu" in terms else dq.ACT_NONE
+    x = lay.x(inp.x)
+    b_t = None if bias is None else torch.from_numpy(bias).to(lay.dev)
+    r_t = None if resid is None else torch.from_numpy(resid).to(lay.dev)
+    y = None
+    if "inplace" in terms:
+        y = r_t.clone()   # the residual is read from and written to the output
+        r_t = y
+    call = dq.qgemv if op == "qgemv" else dq.qgemm
+    extra = (lay.ws,) if op == "qgemv" else (None,)
+    out = call(lay.layout, x, lay.qweight, lay.scales, lay.zeros, lay.perm, *extra, y=y, bias=b_t, residual=r_t,
+               activation=act)
+    ref = oracle.apply_epilogue(_ref(inp), bias, resid, act)
+    assert_close(out, ref, f"{op} M={M} {terms}")

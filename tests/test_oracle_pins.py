@@ -369,3 +369,37 @@ def test_planted_mistakes_are_caught(golden_dir, monkeypatch):
                 except (AssertionError, ValueError):
                     failed += 1
             assert failed > 0, f"no pin caught the planted slip in {name} ({bad.__name__})"
+
+
+# ------------------------------------------------------------------ epilogue
+
+def test_silu_closed_form_values():
+    """SiLU at points where it is known without the formula: 0 at 0; odd part
+    v/2 (silu(v) - silu(-v) = v); sigmoid(1) = e / (1 + e); saturation to v and
+    to 0 far out."""
+    assert oracle.silu(0.0) == 0.0
+    e = np.e
+    assert np.isclose(oracle.silu(1.0), e / (1.0 + e), rtol=1e-15)
+    v = np.linspace(-6, 6, 25)
+    assert np.allclose(oracle.silu(v) - oracle.silu(-v), v, rtol=0, atol=1e-14)
+    assert np.isclose(oracle.silu(40.0), 40.0, rtol=1e-15)
+    assert abs(oracle.silu(-40.0)) < 1e-15
+    assert np.all(np.diff(oracle.silu(np.linspace(0, 10, 101))) > 0)   # increasing for v > 0
+
+
+def test_epilogue_terms_and_order():
+    """Bias and residual add exactly; the activation sits between them:
+    acc = 1, bias = 1, residual = 1 gives silu(2) + 1, not silu(3) or silu(1) + 2."""
+    acc = np.array([[1.0]])
+    got = oracle.apply_epilogue(acc, np.array([1.0]), np.array([[1.0]]), oracle.ACT_SILU)[0, 0]
+    assert np.isclose(got, 2.0 / (1.0 + np.exp(-2.0)) + 1.0, rtol=1e-15)
+    rng = np.random.default_rng(3)
+    a = rng.standard_normal((3, 8))
+    b = rng.standard_normal(8).astype(np.float16)
+    r = rng.standard_normal((3, 8)).astype(np.float16)
+    y = oracle.apply_epilogue(a, b, r, oracle.ACT_NONE)
+    # (a + b) + r - a equals b + r up to float64 rounding of the sums
+    assert np.allclose(y - a, b.astype(np.float64)[None, :] + r.astype(np.float64), rtol=0, atol=1e-14)
+    assert np.array_equal(oracle.apply_epilogue(a), a)
+    with pytest.raises(ValueError):
+        oracle.apply_epilogue(a, activation=9)

@@ -158,105 +158,133 @@ __device__ __forceinline__ void seg_issue(const StreamArgs& a, const RowLane& L,
                 L.col, rlo, rhi, S);
 }
 
-// All steps of one run segment of this wave, two in flight. With kPre the
-// first two steps were issued already into S0 and S1.
-template <int B, bool kPre>
-__device__ __forceinline__ void row_segment(const StreamArgs& a, const RowLane& L, int blk0, int blk1, int row0,
-                                            float (&yacc)[4], StepRegs& S0, StepRegs& S1) {
+// All steps of the wave's blocks [blk0, blk1) (at least one), two in flight;
+// the first two were issued already into S0 and S1.
+template <int B>
+__device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L, int blk0, int blk1, int row0,
+                                          float (&yacc)[4], StepRegs& S0, StepRegs& S1) {
   int rlo[4], rhi[4];
   float sc[4];
   lane_pairs<B>(L.cq, rlo, rhi, sc);
   const int nsteps = (blk1 - blk0 + KS - 1) / KS;
   auto comp = [&](int i, const StepRegs& S) {
-    // Past the segment the whole quad is idle (zero scale); its pairs come
+    // Past the range the whole quad is idle (zero scale); its pairs come
     // from block blk0 (as its perm entries did).
     const int blk = blk0 + i * KS + L.ks < blk1 ? blk0 + i * KS + L.ks : blk0;
     compute_step<B>(a, S, L.xrow, blk, rlo, rhi, sc, L.magic, yacc);
   };
-  if constexpr (!kPre) {
-    seg_issue<B>(a, L, blk0, blk1, row0, 0, rlo, rhi, S0);
-    seg_issue<B>(a, L, blk0, blk1, row0, 1, rlo, rhi, S1);   // past the end: a duplicate read, zero scale
-  }
-  for (int i = 0; i < nsteps; i += 2) {
+  // Steady state: both buffers are refilled on every pass. (A refill under a
+  // condition turns the buffers into loop-carried copies, and a copy waits for
+  // the load it copies: only one step would stay in flight.)
+  int i = 0;
+  for (; i + 3 < nsteps; i += 2) {
     comp(i, S0);
-    if (i + 2 < nsteps) seg_issue<B>(a, L, blk0, blk1, row0, i + 2, rlo, rhi, S0);
-    if (i + 1 >= nsteps) break;
+    seg_issue<B>(a, L, blk0, blk1, row0, i + 2, rlo, rhi, S0);
     comp(i + 1, S1);
-    if (i + 3 < nsteps) seg_issue<B>(a, L, blk0, blk1, row0, i + 3, rlo, rhi, S1);
+    seg_issue<B>(a, L, blk0, blk1, row0, i + 3, rlo, rhi, S1);
   }
-}
-
-// Dispatch on a run's width (only widths in BS are instantiated).
-template <unsigned BS, class F>
-__device__ __forceinline__ void with_width(int bits, F&& f) {
-  switch (bits) {
-    case 2: if constexpr ((BS >> 2) & 1u) f(std::integral_constant<int, 2>{}); break;
-    case 3: if constexpr ((BS >> 3) & 1u) f(std::integral_constant<int, 3>{}); break;
-    case 4: if constexpr ((BS >> 4) & 1u) f(std::integral_constant<int, 4>{}); break;
-    case 5: if constexpr ((BS >> 5) & 1u) f(std::integral_constant<int, 5>{}); break;
-    case 6: if constexpr ((BS >> 6) & 1u) f(std::integral_constant<int, 6>{}); break;
-    case 8: if constexpr ((BS >> 8) & 1u) f(std::integral_constant<int, 8>{}); break;
-    default: break;
+  // The last 1 to 3 steps (nsteps >= 1); steps i and i + 1 are issued.
+  if (nsteps - i == 3) {
+    comp(i, S0);
+    seg_issue<B>(a, L, blk0, blk1, row0, i + 2, rlo, rhi, S0);
+    comp(i + 1, S1);
+    comp(i + 2, S0);
+  } else {
+    comp(i, S0);
+    if (nsteps - i == 2) comp(i + 1, S1);
   }
 }
 
 // Sixteen-byte pieces of the x row per thread issued before the weights.
 constexpr int kRowPieces = 8;
 
-template <unsigned BS, int WV>
+// A pointer in the global address space: loads through it are global (not
+// flat) loads, which the vector-memory counter alone tracks.
+template <class T>
+using global_ptr = const __attribute__((address_space(1))) T*;
+template <class T>
+__device__ __forceinline__ global_ptr<T> as_global(const void* p) {
+  return (global_ptr<T>)p;
+}
+typedef uint32_t piece_t __attribute__((ext_vector_type(4)));   // 16 bytes of the x row
+
+// One code width B for the whole matrix (one run: block b starts at packed
+// row b * B). Grid: x = 16-column strips, XCD-major; y = matrix of the group.
+// Every kernel argument the first loads need is read up front, and none of
+// those reads depends on another, so the weight stream starts after a single
+// scalar-load round trip.
+template <int B, int WV>
 __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ float red[WV][1][SC];
+
+  // Kernel arguments, all read in one batch: the empty asm takes them as
+  // operands (and hands them back, so they are not read again later).
+  MatPtrs mp = a.mat[blockIdx.y];
+  int K = a.K, N = a.N, spx = a.strips_per_xcd;
+  const uint16_t* xsrc = a.x;
+  Epilogue epi = a.epi;
+  {
+    const int R = a.runs.packed_rows, bpg = a.bpg_shift, hz = a.has_zeros;
+    const int32_t* const perm = a.perm;
+    asm volatile("" : "+s"(K), "+s"(N), "+s"(spx), "+s"(xsrc), "+s"(mp.y), "+s"(epi.bias), "+s"(epi.residual),
+                 "+s"(epi.act)
+                 : "s"(R), "s"(bpg), "s"(hz), "s"(perm), "s"(mp.qweight), "s"(mp.scales), "s"(mp.zeros));
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
-  const int gstrip = (bid % kXcds) * a.strips_per_xcd + bid / kXcds;
-  if (gstrip >= a.mats * a.nstrips) return;  // the whole workgroup leaves together
-  const int mi = gstrip / a.nstrips;         // matrix of the group
-  const int strip = gstrip - mi * a.nstrips;
+  const int strip = (bid % kXcds) * spx + bid / kXcds;
+  if (strip * SC >= N) return;  // the whole workgroup leaves together
 
   // 1. The x row: every piece this thread copies, loaded before anything else.
   constexpr int nthr = WV * 64;
-  const int n16 = a.K / 8;
-  const uint4* xg = reinterpret_cast<const uint4*>(a.x);
-#define QLINEAR_PIECE(u) const uint4 xr##u = xg[min((u) * nthr + tid, n16 - 1)];
+  const int n16 = K / 8;
+  const global_ptr<piece_t> xg = as_global<piece_t>(xsrc);
+#define QLINEAR_PIECE(u) const piece_t xr##u = xg[min((u) * nthr + tid, n16 - 1)];
   QLINEAR_PIECE(0) QLINEAR_PIECE(1) QLINEAR_PIECE(2) QLINEAR_PIECE(3)
   QLINEAR_PIECE(4) QLINEAR_PIECE(5) QLINEAR_PIECE(6) QLINEAR_PIECE(7)
 #undef QLINEAR_PIECE
   static_assert(kRowPieces == 8, "the row prefetch is written out for eight pieces");
+  // The epilogue's operands of this strip's outputs, read now rather than
+  // after the final reduction (a residual that is the output itself is read
+  // before the same thread writes it). Every thread loads, from y when a term
+  // is absent: loads without a branch around them keep the wait before each
+  // LDS store below down to that store's own piece.
+  const int n_out = min(strip * SC + (tid % SC), N - 1);
+  const uint16_t bias_raw = as_global<uint16_t>(epi.bias ? epi.bias : mp.y)[n_out];
+  const uint16_t res_raw = as_global<uint16_t>(epi.residual ? epi.residual : mp.y)[n_out];
   asm volatile("" ::: "memory");   // keep the row loads ahead of the weight loads
 
-  // 2. The first two steps of the wave's first run segment.
-  const int nblk = a.K / kBlockRows;
+  // 2. The first two steps of the wave's blocks, issued by every wave (a wave
+  // without blocks reads block wb0 < K / 32 and computes nothing).
+  const int nblk = K / kBlockRows;
   const int wb0 = (wave * nblk) / WV, wb1 = ((wave + 1) * nblk) / WV;
-  int b0 = 0, row0 = 0;
-  if (wb0 < wb1) block_info(a.runs, wb0, b0, row0);
-  const int seg0_end = wb0 < wb1 ? min(wb1, run_end_block(a.runs, wb0)) : wb0;
+  const int row0 = wb0 * B;
   RowLane L;
-  L.mp = a.mat[mi];
+  L.mp = mp;
   L.cq = lane % CQ;
   L.ks = lane / CQ;
   const int col_req = strip * SC + L.cq * 4;
-  L.colv = col_req < a.N;
-  L.col = L.colv ? col_req : a.N - 4;   // scale/zero column for lanes past N
-  L.panel = L.mp.qweight + (size_t)strip * a.runs.packed_rows * kPanel + L.cq * 4;
-  L.psrc = a.perm ? a.perm : reinterpret_cast<const int32_t*>(L.mp.qweight);   // >= K readable words
+  L.colv = col_req < N;
+  L.col = L.colv ? col_req : N - 4;   // scale/zero column for lanes past N
+  L.panel = mp.qweight + (size_t)strip * a.runs.packed_rows * kPanel + L.cq * 4;
+  L.psrc = a.perm ? a.perm : reinterpret_cast<const int32_t*>(mp.qweight);   // >= K readable words
   L.xrow = reinterpret_cast<const _Float16*>(lds);
   L.magic = vgpr_magic();
   StepRegs S0, S1;
-  with_width<BS>(b0, [&](auto BB) {
-    constexpr int B = decltype(BB)::value;
+  {
     int rlo[4], rhi[4];
     float sc[4];
     lane_pairs<B>(L.cq, rlo, rhi, sc);
-    seg_issue<B>(a, L, wb0, seg0_end, row0, 0, rlo, rhi, S0);
-    seg_issue<B>(a, L, wb0, seg0_end, row0, 1, rlo, rhi, S1);
-  });
+    seg_issue<B>(a, L, wb0, wb1, row0, 0, rlo, rhi, S0);
+    seg_issue<B>(a, L, wb0, wb1, row0, 1, rlo, rhi, S1);   // past the end: a duplicate read, zero scale
+  }
 
   // 3. The row into LDS (clamped threads rewrite the last piece with its own value).
-  uint4* xl = reinterpret_cast<uint4*>(lds);
+  piece_t* xl = reinterpret_cast<piece_t*>(lds);
 #define QLINEAR_STORE(u) xl[min((u) * nthr + tid, n16 - 1)] = xr##u;
   QLINEAR_STORE(0) QLINEAR_STORE(1) QLINEAR_STORE(2) QLINEAR_STORE(3)
   QLINEAR_STORE(4) QLINEAR_STORE(5) QLINEAR_STORE(6) QLINEAR_STORE(7)
@@ -264,41 +292,49 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   for (int i = kRowPieces * nthr + tid; i < n16; i += nthr) xl[i] = xg[i];
   __syncthreads();
 
-  // 4. Stream the wave's blocks, run segment by run segment.
+  // 4. Stream the wave's blocks.
   float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  with_width<BS>(b0, [&](auto BB) { row_segment<decltype(BB)::value, true>(a, L, wb0, seg0_end, row0, yacc, S0, S1); });
-  for (int blk = seg0_end; blk < wb1;) {
-    int bits, row;
-    block_info(a.runs, blk, bits, row);
-    const int seg_end = min(wb1, run_end_block(a.runs, blk));
-    with_width<BS>(bits, [&](auto BB) { row_segment<decltype(BB)::value, false>(a, L, blk, seg_end, row, yacc, S0, S1); });
-    blk = seg_end;
-  }
+  if (wb0 < wb1) row_steps<B>(a, L, wb0, wb1, row0, yacc, S0, S1);
 
-  float y4[4][1] = {{yacc[0]}, {yacc[1]}, {yacc[2]}, {yacc[3]}};
-  reduce_store<1, WV>(a, L.mp.y, red, y4, tid, lane, wave, strip);
+  // Reduce over the 16 block slots of the wave (shuffles), then over the
+  // waves (LDS); the epilogue as apply_epilogue: bias, activation, residual.
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int off = CQ; off < 64; off <<= 1) yacc[c] += __shfl_xor(yacc[c], off, 64);
+  if (L.ks == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) red[wave][0][L.cq * 4 + c] = yacc[c];
+  }
+  __syncthreads();
+  if (tid < SC && strip * SC + tid < N) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WV; ++w) v += red[w][0][tid];
+    if (epi.bias) v += (float)__builtin_bit_cast(_Float16, bias_raw);
+    if (epi.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
+    if (epi.residual) v += (float)__builtin_bit_cast(_Float16, res_raw);
+    ((__attribute__((address_space(1))) uint16_t*)mp.y)[strip * SC + tid] = __builtin_bit_cast(uint16_t, (_Float16)v);
+  }
 }
 
-template <unsigned BS, int WV>
+template <int B, int WV>
 hipError_t launch_row(StreamArgs a, hipStream_t stream) {
   a.nstrips = (a.N + SC - 1) / SC;
-  a.strips_per_xcd = (a.mats * a.nstrips + kXcds - 1) / kXcds;
+  a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
   a.xrow_words = row_words(a.K);
   const size_t lds = (size_t)a.xrow_words * 4;
-  hipLaunchKernelGGL((qgemv_row_kernel<BS, WV>), dim3(kXcds * a.strips_per_xcd), dim3(WV * 64), lds, stream, a);
+  hipLaunchKernelGGL((qgemv_row_kernel<B, WV>), dim3(kXcds * a.strips_per_xcd, a.mats), dim3(WV * 64), lds, stream, a);
   return hipGetLastError();
 }
 
-// kMaxWv: the most waves per workgroup instantiated for this width set.
-template <unsigned BS, int kMaxWv>
-hipError_t launch_row_any(const StreamArgs& a, hipStream_t stream) {
-  if constexpr (kMaxWv >= 8) {
-    if (waves_for(a.N, a.K) >= 8) return launch_row<BS, 8>(a, stream);
-  }
-  return launch_row<BS, 4>(a, stream);
+template <int B>
+hipError_t launch_row_width(const StreamArgs& a, hipStream_t stream) {
+  if (waves_for(a.N, a.K) >= 8) return launch_row<B, 8>(a, stream);
+  return launch_row<B, 4>(a, stream);
 }
 
-// Instantiated in qgemv_row.hip.
+// Instantiated in qgemv_row.hip: `set` holds exactly one code width.
 hipError_t launch_row_set(unsigned set, const StreamArgs& a, hipStream_t stream);
 
 }  // namespace stream

@@ -195,8 +195,6 @@ __device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L,
   }
 }
 
-// Sixteen-byte pieces of the x row per thread issued before the weights.
-constexpr int kRowPieces = 8;
 
 // A pointer in the global address space: loads through it are global (not
 // flat) loads, which the vector-memory counter alone tracks.
@@ -213,7 +211,9 @@ typedef uint32_t piece_t __attribute__((ext_vector_type(4)));   // 16 bytes of t
 // Every kernel argument the first loads need is read up front, and none of
 // those reads depends on another, so the weight stream starts after a single
 // scalar-load round trip.
-template <int B, int WV>
+// P: sixteen-byte pieces of the x row per thread, all loaded before the
+// weights; P * WV * 64 * 16 bytes cover the row.
+template <int B, int WV, int P>
 __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ float red[WV][1][SC];
@@ -243,11 +243,9 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   constexpr int nthr = WV * 64;
   const int n16 = K / 8;
   const global_ptr<piece_t> xg = as_global<piece_t>(xsrc);
-#define QLINEAR_PIECE(u) const piece_t xr##u = xg[min((u) * nthr + tid, n16 - 1)];
-  QLINEAR_PIECE(0) QLINEAR_PIECE(1) QLINEAR_PIECE(2) QLINEAR_PIECE(3)
-  QLINEAR_PIECE(4) QLINEAR_PIECE(5) QLINEAR_PIECE(6) QLINEAR_PIECE(7)
-#undef QLINEAR_PIECE
-  static_assert(kRowPieces == 8, "the row prefetch is written out for eight pieces");
+  piece_t xr[P];
+#pragma unroll
+  for (int u = 0; u < P; ++u) xr[u] = xg[min(u * nthr + tid, n16 - 1)];
   // The epilogue's operands of this strip's outputs, read now rather than
   // after the final reduction (a residual that is the output itself is read
   // before the same thread writes it). Every thread loads, from y when a term
@@ -285,11 +283,8 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
 
   // 3. The row into LDS (clamped threads rewrite the last piece with its own value).
   piece_t* xl = reinterpret_cast<piece_t*>(lds);
-#define QLINEAR_STORE(u) xl[min((u) * nthr + tid, n16 - 1)] = xr##u;
-  QLINEAR_STORE(0) QLINEAR_STORE(1) QLINEAR_STORE(2) QLINEAR_STORE(3)
-  QLINEAR_STORE(4) QLINEAR_STORE(5) QLINEAR_STORE(6) QLINEAR_STORE(7)
-#undef QLINEAR_STORE
-  for (int i = kRowPieces * nthr + tid; i < n16; i += nthr) xl[i] = xg[i];
+#pragma unroll
+  for (int u = 0; u < P; ++u) xl[min(u * nthr + tid, n16 - 1)] = xr[u];
   __syncthreads();
 
   // 4. Stream the wave's blocks.
@@ -318,20 +313,31 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   }
 }
 
-template <int B, int WV>
+template <int B, int WV, int P>
 hipError_t launch_row(StreamArgs a, hipStream_t stream) {
   a.nstrips = (a.N + SC - 1) / SC;
   a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
   a.xrow_words = row_words(a.K);
   const size_t lds = (size_t)a.xrow_words * 4;
-  hipLaunchKernelGGL((qgemv_row_kernel<B, WV>), dim3(kXcds * a.strips_per_xcd, a.mats), dim3(WV * 64), lds, stream, a);
+  hipLaunchKernelGGL((qgemv_row_kernel<B, WV, P>), dim3(kXcds * a.strips_per_xcd, a.mats), dim3(WV * 64), lds, stream,
+                     a);
   return hipGetLastError();
 }
 
+// Four waves per workgroup for every shape. Measured on MI355X (7B decode
+// launches): at 8 waves only one workgroup fits per CU (the kernel needs
+// about 140 VGPRs), which costs up to 1.7x on the grouped launches, and the
+// long-K 11008 -> 4096 launch is also faster at 4 waves (8.4 vs 9.1 us).
+constexpr int kRowWaves = 4;
+
+// x-row pieces per thread: 8 cover K <= 16384, 16 the whole LDS budget.
+constexpr int kRowPiecesShort = 8, kRowPiecesLong = 16;
+static_assert(kRowPiecesLong * kRowWaves * 64 * 16 >= kRowLdsBudget, "x-row pieces must cover the LDS budget");
+
 template <int B>
 hipError_t launch_row_width(const StreamArgs& a, hipStream_t stream) {
-  if (waves_for(a.N, a.K) >= 8) return launch_row<B, 8>(a, stream);
-  return launch_row<B, 4>(a, stream);
+  if (a.K <= kRowPiecesShort * kRowWaves * 64 * 8) return launch_row<B, kRowWaves, kRowPiecesShort>(a, stream);
+  return launch_row<B, kRowWaves, kRowPiecesLong>(a, stream);
 }
 
 // Instantiated in qgemv_row.hip: `set` holds exactly one code width.

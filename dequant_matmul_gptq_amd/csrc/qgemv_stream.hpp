@@ -448,8 +448,9 @@ hipError_t launch_set(StreamArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Waves per workgroup for M = 1 (they split K). Measured on MI355X: 8 waves
-// pay off only when there are few 16-column strips and K is long; 4 otherwise.
+// Waves per workgroup of the multi-row kernel at M = 1 (they split K).
+// Measured on MI355X: 8 waves pay off only when there are few 16-column
+// strips and K is long; 4 otherwise.
 inline int waves_for(int N, int K) {
   const int nstrips = (N + SC - 1) / SC;
   return (nstrips <= 512 && K / kBlockRows >= 256) ? 8 : 4;

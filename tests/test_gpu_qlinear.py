@@ -101,6 +101,29 @@ def test_qgemm_uniform_widths(b, gs):
     assert_close(y, _ref(inp), f"qgemm b={b} gs={gs}")
 
 
+@pytest.mark.parametrize("nblk", (1, 3, 64, 100, 128, 192, 256, 320, 448))
+@pytest.mark.parametrize("b", (2, 3, 4, 5, 6, 8))
+def test_qgemv_row_kernel_steps(b, nblk):
+    """M = 1 with one code width (the single-row kernel): 32-row blocks split
+    over 4 waves, 16 per step, two steps in flight. nblk covers waves with no
+    blocks (1, 3), a single step, ragged splits (100), the steady-state loop
+    and its tails of 2 and 3 steps (256, 320, 448)."""
+    say(f"qgemv row kernel b={b} blocks={nblk}")
+    inp = _mixed_inputs([b] * nblk, 32, 48, 1, seed=b * 1000 + nblk, zeros=True)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv row b={b} blocks={nblk}")
+
+
+@pytest.mark.parametrize("K", (16384, 16416, 28672, 31744))
+def test_qgemv_row_kernel_long_rows(K):
+    """The single-row kernel's x row staging at K = 16384 (8 pieces per
+    thread), just past it and up to the LDS limit (16 pieces)."""
+    say(f"qgemv row kernel long row K={K}")
+    inp = _mixed_inputs([4] * (K // 32), 32, 48, 1, seed=K % 89, zeros=True)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv row K={K}")
+
+
 @pytest.mark.parametrize("K", (31744, 33792))
 def test_qgemv_long_rows(K):
     """M = 1 rows near and past the LDS capacity of the single-row kernel (the

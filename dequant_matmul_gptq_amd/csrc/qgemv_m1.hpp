@@ -158,43 +158,42 @@ __device__ __forceinline__ void seg_issue(const StreamArgs& a, const RowLane& L,
                 L.col, rlo, rhi, S);
 }
 
-// All steps of the wave's blocks [blk0, blk1) (at least one), two in flight;
-// the first two were issued already into S0 and S1.
-template <int B>
+// All steps of the wave's blocks [blk0, blk1) (at least one), D in flight;
+// the first D were issued already into S[0 .. D-1].
+template <int B, int D>
 __device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L, int blk0, int blk1, int row0,
-                                          float (&yacc)[4], StepRegs& S0, StepRegs& S1) {
+                                          float (&yacc)[4], StepRegs (&S)[D]) {
   int rlo[4], rhi[4];
   float sc[4];
   lane_pairs<B>(L.cq, rlo, rhi, sc);
   const int nsteps = (blk1 - blk0 + KS - 1) / KS;
-  auto comp = [&](int i, const StepRegs& S) {
+  auto comp = [&](int i, const StepRegs& R) {
     // Past the range the whole quad is idle (zero scale); its pairs come
     // from block blk0 (as its perm entries did).
     const int blk = blk0 + i * KS + L.ks < blk1 ? blk0 + i * KS + L.ks : blk0;
-    compute_step<B>(a, S, L.xrow, blk, rlo, rhi, sc, L.magic, yacc);
+    compute_step<B>(a, R, L.xrow, blk, rlo, rhi, sc, L.magic, yacc);
   };
-  // Steady state: both buffers are refilled on every pass. (A refill under a
+  // Steady state: every buffer is refilled on every pass. (A refill under a
   // condition turns the buffers into loop-carried copies, and a copy waits for
   // the load it copies: only one step would stay in flight.)
   int i = 0;
-  for (; i + 3 < nsteps; i += 2) {
-    comp(i, S0);
-    seg_issue<B>(a, L, blk0, blk1, row0, i + 2, rlo, rhi, S0);
-    comp(i + 1, S1);
-    seg_issue<B>(a, L, blk0, blk1, row0, i + 3, rlo, rhi, S1);
+  for (; i + 2 * D - 1 < nsteps; i += D) {
+    static_for<0, D>([&](auto Dd) {
+      constexpr int d = decltype(Dd)::value;
+      comp(i + d, S[d]);
+      seg_issue<B>(a, L, blk0, blk1, row0, i + d + D, rlo, rhi, S[d]);
+    });
   }
-  // The last 1 to 3 steps (nsteps >= 1); steps i and i + 1 are issued.
-  if (nsteps - i == 3) {
-    comp(i, S0);
-    seg_issue<B>(a, L, blk0, blk1, row0, i + 2, rlo, rhi, S0);
-    comp(i + 1, S1);
-    comp(i + 2, S0);
-  } else {
-    comp(i, S0);
-    if (nsteps - i == 2) comp(i + 1, S1);
-  }
+  // The last 1 to 2D - 1 steps; those among i .. i + D - 1 are issued.
+  const int r = nsteps - i;
+  static_for<0, 2 * D - 1>([&](auto Tt) {
+    constexpr int t = decltype(Tt)::value;
+    if (t < r) {
+      comp(i + t, S[t % D]);
+      if (t + D < r) seg_issue<B>(a, L, blk0, blk1, row0, i + t + D, rlo, rhi, S[t % D]);
+    }
+  });
 }
-
 
 // A pointer in the global address space: loads through it are global (not
 // flat) loads, which the vector-memory counter alone tracks.
@@ -212,8 +211,8 @@ typedef uint32_t piece_t __attribute__((ext_vector_type(4)));   // 16 bytes of t
 // those reads depends on another, so the weight stream starts after a single
 // scalar-load round trip.
 // P: sixteen-byte pieces of the x row per thread, all loaded before the
-// weights; P * WV * 64 * 16 bytes cover the row.
-template <int B, int WV, int P>
+// weights; P * WV * 64 * 16 bytes cover the row. D: steps in flight per wave.
+template <int B, int WV, int P, int D>
 __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ float red[WV][1][SC];
@@ -256,8 +255,9 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   const uint16_t res_raw = as_global<uint16_t>(epi.residual ? epi.residual : mp.y)[n_out];
   asm volatile("" ::: "memory");   // keep the row loads ahead of the weight loads
 
-  // 2. The first two steps of the wave's blocks, issued by every wave (a wave
-  // without blocks reads block wb0 < K / 32 and computes nothing).
+  // 2. The first D steps of the wave's blocks, issued by every wave (a wave
+  // without blocks reads block wb0 < K / 32 and computes nothing; steps past
+  // the end are duplicate reads with zero scale).
   const int nblk = K / kBlockRows;
   const int wb0 = (wave * nblk) / WV, wb1 = ((wave + 1) * nblk) / WV;
   const int row0 = wb0 * B;
@@ -272,13 +272,15 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   L.psrc = a.perm ? a.perm : reinterpret_cast<const int32_t*>(mp.qweight);   // >= K readable words
   L.xrow = reinterpret_cast<const _Float16*>(lds);
   L.magic = vgpr_magic();
-  StepRegs S0, S1;
+  StepRegs S[D];
   {
     int rlo[4], rhi[4];
     float sc[4];
     lane_pairs<B>(L.cq, rlo, rhi, sc);
-    seg_issue<B>(a, L, wb0, wb1, row0, 0, rlo, rhi, S0);
-    seg_issue<B>(a, L, wb0, wb1, row0, 1, rlo, rhi, S1);   // past the end: a duplicate read, zero scale
+    static_for<0, D>([&](auto Dd) {
+      constexpr int d = decltype(Dd)::value;
+      seg_issue<B>(a, L, wb0, wb1, row0, d, rlo, rhi, S[d]);
+    });
   }
 
   // 3. The row into LDS (clamped threads rewrite the last piece with its own value).
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
 
   // 4. Stream the wave's blocks.
   float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (wb0 < wb1) row_steps<B>(a, L, wb0, wb1, row0, yacc, S0, S1);
+  if (wb0 < wb1) row_steps<B, D>(a, L, wb0, wb1, row0, yacc, S);
 
   // Reduce over the 16 block slots of the wave (shuffles), then over the
   // waves (LDS); the epilogue as apply_epilogue: bias, activation, residual.
@@ -313,13 +315,13 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   }
 }
 
-template <int B, int WV, int P>
+template <int B, int WV, int P, int D>
 hipError_t launch_row(StreamArgs a, hipStream_t stream) {
   a.nstrips = (a.N + SC - 1) / SC;
   a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
   a.xrow_words = row_words(a.K);
   const size_t lds = (size_t)a.xrow_words * 4;
-  hipLaunchKernelGGL((qgemv_row_kernel<B, WV, P>), dim3(kXcds * a.strips_per_xcd, a.mats), dim3(WV * 64), lds, stream,
+  hipLaunchKernelGGL((qgemv_row_kernel<B, WV, P, D>), dim3(kXcds * a.strips_per_xcd, a.mats), dim3(WV * 64), lds, stream,
                      a);
   return hipGetLastError();
 }
@@ -330,14 +332,23 @@ hipError_t launch_row(StreamArgs a, hipStream_t stream) {
 // long-K 11008 -> 4096 launch is also faster at 4 waves (8.4 vs 9.1 us).
 constexpr int kRowWaves = 4;
 
-// x-row pieces per thread: 8 cover K <= 16384, 16 the whole LDS budget.
-constexpr int kRowPiecesShort = 8, kRowPiecesLong = 16;
-static_assert(kRowPiecesLong * kRowWaves * 64 * 16 >= kRowLdsBudget, "x-row pieces must cover the LDS budget");
+// x-row pieces per thread: the fewest of 2, 4, 8 and 16 that cover the row
+// (16 cover the whole LDS budget); a piece past the row is a duplicate load.
+constexpr int kRowPiecesMax = 16;
+static_assert(kRowPiecesMax * kRowWaves * 64 * 16 >= kRowLdsBudget, "x-row pieces must cover the LDS budget");
+
+// Steps in flight per wave. Measured on MI355X: 3 instead of 2 is slower
+// even where each CU holds one workgroup and each wave has 6 steps
+// (11008 -> 4096: 9.1 vs 8.3 us), so every shape keeps two.
+constexpr int kRowDepth = 2;
 
 template <int B>
 hipError_t launch_row_width(const StreamArgs& a, hipStream_t stream) {
-  if (a.K <= kRowPiecesShort * kRowWaves * 64 * 8) return launch_row<B, kRowWaves, kRowPiecesShort>(a, stream);
-  return launch_row<B, kRowWaves, kRowPiecesLong>(a, stream);
+  constexpr int per_piece = kRowWaves * 64 * 8;   // x values per piece index
+  if (a.K <= 2 * per_piece) return launch_row<B, kRowWaves, 2, kRowDepth>(a, stream);
+  if (a.K <= 4 * per_piece) return launch_row<B, kRowWaves, 4, kRowDepth>(a, stream);
+  if (a.K <= 8 * per_piece) return launch_row<B, kRowWaves, 8, kRowDepth>(a, stream);
+  return launch_row<B, kRowWaves, kRowPiecesMax, kRowDepth>(a, stream);
 }
 
 // Instantiated in qgemv_row.hip: `set` holds exactly one code width.

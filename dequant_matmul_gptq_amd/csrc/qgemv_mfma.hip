@@ -169,41 +169,52 @@ template <unsigned BS, int FN>
 __global__ __launch_bounds__(kWaves * 64) void qgemv_mfma_kernel(MfmaArgs a) {
   __shared__ float4_t red[kWaves][FN][64];
 
+  // Kernel arguments, all read in one batch (the matrix is blockIdx.y, so no
+  // read waits on another): the empty asm takes them as operands and hands
+  // them back, so they are not read again later.
+  MatPtrs mp = a.mat[blockIdx.y];
+  int spx = a.strips_per_xcd, nstrips = a.nstrips, M = a.M, K = a.K, N = a.N, R = a.runs.packed_rows;
+  int xq_bytes = a.xq_bytes, scale_bytes = a.scale_bytes, has_zeros = a.has_zeros;
+  int64_t packed_words = a.packed_words;
+  const uint16_t* xq = a.xq;
+  Epilogue epi = a.epi;
+  asm volatile("" : "+s"(mp.qweight), "+s"(mp.scales), "+s"(mp.zeros), "+s"(mp.y), "+s"(spx), "+s"(nstrips),
+               "+s"(M), "+s"(K), "+s"(N), "+s"(R), "+s"(xq_bytes), "+s"(scale_bytes), "+s"(has_zeros),
+               "+s"(packed_words), "+s"(xq), "+s"(epi.bias), "+s"(epi.residual), "+s"(epi.act)
+               : "s"(a.runs.blocks_per_group));
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
-  const int gstrip = (bid % kXcds) * a.strips_per_xcd + bid / kXcds;
-  if (gstrip >= a.mats * a.nstrips) return;   // the whole workgroup leaves together
-  const int mi = gstrip / a.nstrips;
-  const int strip = gstrip - mi * a.nstrips;
-  const MatPtrs mp = a.mat[mi];
+  const int strip = (bid % kXcds) * spx + bid / kXcds;
+  if (strip >= nstrips) return;   // the whole workgroup leaves together
 
   Lane L;
   L.g = lane >> 4;
-  L.rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, 0, a.xq_bytes, kRsrcWord3);
+  L.rx = __builtin_amdgcn_make_buffer_rsrc((void*)xq, 0, xq_bytes, kRsrcWord3);
   // The weight buffer starts at the strip's first panel, so 32-bit offsets
   // cover any matrix: they only span the strip's FN panels.
-  const int64_t strip_words = (int64_t)FN * a.runs.packed_rows * kPanel;
+  const int64_t strip_words = (int64_t)FN * R * kPanel;
   const int64_t first_word = (int64_t)strip * strip_words;
   L.rw = __builtin_amdgcn_make_buffer_rsrc((void*)(mp.qweight + first_word), 0,
-                                           (int)(min(strip_words, a.packed_words - first_word) * 4), kRsrcWord3);
-  L.rs = __builtin_amdgcn_make_buffer_rsrc((void*)mp.scales, 0, a.scale_bytes, kRsrcWord3);
-  L.rz = __builtin_amdgcn_make_buffer_rsrc(a.has_zeros ? (void*)mp.zeros : (void*)mp.scales, 0,
-                                           a.has_zeros ? a.scale_bytes / 2 : a.scale_bytes, kRsrcWord3);
+                                           (int)(min(strip_words, packed_words - first_word) * 4), kRsrcWord3);
+  L.rs = __builtin_amdgcn_make_buffer_rsrc((void*)mp.scales, 0, scale_bytes, kRsrcWord3);
+  L.rz = __builtin_amdgcn_make_buffer_rsrc(has_zeros ? (void*)mp.zeros : (void*)mp.scales, 0,
+                                           has_zeros ? scale_bytes / 2 : scale_bytes, kRsrcWord3);
   const int m = lane & 15;
   // Rows past M and columns past N read at offsets beyond every buffer: the
   // loads return zeros (zero activations, zero scales). N is a multiple of 8,
   // so a lane's FN columns are in or out as a whole.
-  L.xoff = m < a.M ? ((uint32_t)m * (uint32_t)a.K + 8u * (uint32_t)L.g) * 2u : 0x80000000u;
+  L.xoff = m < M ? ((uint32_t)m * (uint32_t)K + 8u * (uint32_t)L.g) * 2u : 0x80000000u;
   const int col = strip * kPanel * FN + (lane & 15) * FN;
-  const bool cok = col < a.N;
+  const bool cok = col < N;
   L.col = cok ? (uint32_t)col : 0x40000000u;
-  L.woff = cok ? (uint32_t)(col / kPanel - strip * FN) * (uint32_t)a.runs.packed_rows * kPanel * 4 +
+  L.woff = cok ? (uint32_t)(col / kPanel - strip * FN) * (uint32_t)R * kPanel * 4 +
                      (uint32_t)(col % kPanel) * 4
                : 0x80000000u;
 
-  const int nblk = a.K / kBlockRows;
+  const int nblk = K / kBlockRows;
   const int b0 = (wave * nblk) / kWaves, b1 = ((wave + 1) * nblk) / kWaves;
   const uint32_t magic = vgpr_magic();
   float4_t acc[FN];
@@ -236,16 +247,18 @@ __global__ __launch_bounds__(kWaves * 64) void qgemv_mfma_kernel(MfmaArgs a) {
     for (int w = 0; w < kWaves; ++w) v += red[w][j][l][r];
     const int row = 4 * (l >> 4) + r;
     const int c = strip * kPanel * FN + (l & 15) * FN + j;
-    if (row < a.M && c < a.N)
-      mp.y[(size_t)row * a.N + c] = __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(a.epi, v, row, c, a.N));
+    if (row < M && c < N)
+      ((__attribute__((address_space(1))) uint16_t*)mp.y)[(size_t)row * N + c] =
+          __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(epi, v, row, c, N));
   }
 }
 
 template <unsigned BS, int FN>
 hipError_t launch_fn(MfmaArgs a, hipStream_t stream) {
   a.nstrips = (a.N + kPanel * FN - 1) / (kPanel * FN);
-  a.strips_per_xcd = (a.mats * a.nstrips + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((qgemv_mfma_kernel<BS, FN>), dim3(kXcds * a.strips_per_xcd), dim3(kWaves * 64), 0, stream, a);
+  a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL((qgemv_mfma_kernel<BS, FN>), dim3(kXcds * a.strips_per_xcd, a.mats), dim3(kWaves * 64), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

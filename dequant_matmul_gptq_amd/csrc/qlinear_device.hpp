@@ -31,10 +31,13 @@ struct Epilogue {
   int act;                    // QLINEAR_ACT_NONE or QLINEAR_ACT_SILU
 };
 
+// bias and residual are device (global) memory: read as such, also where the
+// kernel has passed the pointers through registers the compiler cannot see.
 __device__ __forceinline__ float apply_epilogue(const Epilogue& e, float v, int m, int n, int N) {
-  if (e.bias) v += (float)__builtin_bit_cast(_Float16, e.bias[n]);
+  typedef const __attribute__((address_space(1))) uint16_t* gptr;
+  if (e.bias) v += (float)__builtin_bit_cast(_Float16, ((gptr)e.bias)[n]);
   if (e.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
-  if (e.residual) v += (float)__builtin_bit_cast(_Float16, e.residual[(size_t)m * N + n]);
+  if (e.residual) v += (float)__builtin_bit_cast(_Float16, ((gptr)e.residual)[(size_t)m * N + n]);
   return v;
 }
 

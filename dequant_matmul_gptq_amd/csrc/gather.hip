@@ -26,6 +26,13 @@ __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __res
                                                            const int32_t* __restrict__ perm,
                                                            uint32_t* __restrict__ xq, float2* __restrict__ xsum,
                                                            int M, int K, int scaled, int mfma, Runs runs) {
+  // Every argument read in one scalar batch (the asm takes them and hands
+  // them back, so none is read later behind another wait).
+  {
+    int nruns = runs.nruns, bits0 = runs.run_bits[0];
+    asm volatile("" : "+s"(M), "+s"(K), "+s"(scaled), "+s"(mfma) : "s"(x), "s"(perm), "s"(xq), "s"(xsum), "s"(nruns),
+                 "s"(bits0));
+  }
   const int nblk = K / kBlockRows;
   const int pairs = nblk * kPairsPerBlock;
   const int idx = blockIdx.x * 256 + threadIdx.x;

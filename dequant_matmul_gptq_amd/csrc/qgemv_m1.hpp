@@ -32,8 +32,10 @@ __host__ __device__ constexpr int row_words(int K) { return (K / 2 + 3) / 4 * 4;
 
 // Whether a single-row call runs the single-row kernel: the x row must fit
 // in LDS, and the matrix must have a single code width. (Measured on MI355X:
-// with several widths, the short run segments of each wave and the perm
-// loads at 2-3 bits make the gather kernel plus the multi-row kernel faster.)
+// a version of this kernel that streams several widths, run segment by run
+// segment, needs 205-256 VGPRs for the width sets of EXL2 layouts, and the
+// gather kernel plus the multi-row kernel stay faster: EXL2 4.0 bpw
+// 4096 -> 11008: 16.8 vs 20.0 us; 2.5 bpw 8192 -> 28672: 31.5 vs 38.3 us.)
 inline bool single_row(int M, int K, unsigned set) {
   return M == 1 && (size_t)row_words(K) * 4 <= kRowLdsBudget && (set & (set - 1)) == 0;
 }

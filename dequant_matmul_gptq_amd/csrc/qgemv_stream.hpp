@@ -39,6 +39,8 @@
 // across the waves through LDS.
 #pragma once
 
+#include <algorithm>
+
 #include "qlinear_kernels.hpp"
 
 namespace qlinear {
@@ -76,6 +78,10 @@ struct StreamArgs {
   int chunk;               // blocks per wave staged at a time
   int xrow_words;          // single-row kernel: LDS words holding the x row
   int bpg_shift;           // log2(group_size / 32)
+  // multi-row kernel: each wave's first run segment, set by the host (its
+  // width, or 0 for a wave without blocks, its first packed row and its end
+  // block, the latter also bounded by the first chunk)
+  int wave_bits[kMaxWaves], wave_row[kMaxWaves], wave_end[kMaxWaves];
   Runs runs;
   Epilogue epi;
 };
@@ -295,7 +301,8 @@ __device__ __forceinline__ void reduce_store(const StreamArgs& a, uint16_t* y, f
 // first step can be issued into a typed buffer before the activation staging.
 template <int MT, unsigned BS, int WV, int B0>
 __device__ __forceinline__ void stream_body(const StreamArgs& a, const MatPtrs& mp, uint32_t* lds, float (&red)[WV][MT][SC],
-                                            int tid, int lane, int wave, int strip, int wb0, int wb1, int row0) {
+                                            int tid, int lane, int wave, int strip, int wb0, int wb1, int row0,
+                                            int seg0_end) {
   const int cq = lane % CQ, ks = lane / CQ;
   const int col_req = strip * SC + cq * 4;
   const bool colv = col_req < a.N;
@@ -316,7 +323,6 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const MatPtrs& 
 
   uint4 W0[B0];
   Raw P0;
-  const int seg0_end = wb0 < wb1 ? min(min(wb1, run_end_block(a.runs, wb0)), wb0 + a.chunk) : wb0;
   {
     // A wave without blocks (K < 32 * waves) reads block 0 and discards it.
     const int blk = wb0 + ks;
@@ -386,8 +392,8 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const MatPtrs& 
 
 template <int MT, unsigned BS, int WV, int B0>
 __device__ __forceinline__ void dispatch_body(const StreamArgs& a, const MatPtrs& mp, uint32_t* lds, float (&red)[WV][MT][SC], int tid,
-                                              int lane, int wave, int strip, int wb0, int wb1, int row0) {
-  stream_body<MT, BS, WV, B0>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0);
+                                              int lane, int wave, int strip, int wb0, int wb1, int row0, int seg0_end) {
+  stream_body<MT, BS, WV, B0>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0, seg0_end);
 }
 
 // One kernel per (MT, set of code widths that may occur). BS has bit b set
@@ -402,21 +408,24 @@ __global__ __launch_bounds__(WV * 64) void qgemv_stream_kernel(StreamArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The arguments the first loads need, read in one scalar batch (the matrix
+  // is blockIdx.y and the wave's first run segment comes from the host, so no
+  // read waits on another); later reads of the same fields reuse these.
+  const MatPtrs mp = a.mat[blockIdx.y];
+  const int bits0 = a.wave_bits[wave], row0 = a.wave_row[wave], seg0_end = a.wave_end[wave];
+  asm volatile("" ::"s"(mp.qweight), "s"(mp.scales), "s"(mp.zeros), "s"(mp.y), "s"(bits0), "s"(row0), "s"(seg0_end),
+               "s"(a.strips_per_xcd), "s"(a.nstrips), "s"(a.K), "s"(a.N), "s"(a.M), "s"(a.chunk), "s"(a.bpg_shift),
+               "s"(a.has_zeros), "s"(a.runs.packed_rows), "s"(a.xq), "s"(a.xsum));
   const int bid = blockIdx.x;
-  const int gstrip = (bid % kXcds) * a.strips_per_xcd + bid / kXcds;
-  if (gstrip >= a.mats * a.nstrips) return;  // the whole workgroup leaves together
-  const int mi = gstrip / a.nstrips;         // matrix of the group
-  const int strip = gstrip - mi * a.nstrips;
-  const MatPtrs mp = a.mat[mi];
+  const int strip = (bid % kXcds) * a.strips_per_xcd + bid / kXcds;
+  if (strip >= a.nstrips) return;  // the whole workgroup leaves together
 
   const int nblk = a.K / kBlockRows;
   const int wb0 = (wave * nblk) / WV, wb1 = ((wave + 1) * nblk) / WV;
-  int bits0 = 0, row0 = 0;
-  if (wb0 < wb1) block_info(a.runs, wb0, bits0, row0);
 
 #define QLINEAR_BODY(BB)                                                                     \
   case BB:                                                                                   \
-    if constexpr ((BS >> BB) & 1u) dispatch_body<MT, BS, WV, BB>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0);                                              \
+    if constexpr ((BS >> BB) & 1u) dispatch_body<MT, BS, WV, BB>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0, seg0_end); \
     return;
   switch (bits0) {
     QLINEAR_BODY(2)
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_stream_kernel(StreamArgs a) {
 #undef QLINEAR_BODY
   // This wave has no blocks (K too small for every wave): it still joins the
   // barriers of the staging and the final reduction, which the other waves run.
-  dispatch_body<MT, BS, WV, (BS & 16u) ? 4 : (BS & 4u) ? 2 : (BS & 8u) ? 3 : (BS & 32u) ? 5 : (BS & 64u) ? 6 : 8>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0);
+  dispatch_body<MT, BS, WV, (BS & 16u) ? 4 : (BS & 4u) ? 2 : (BS & 8u) ? 3 : (BS & 32u) ? 5 : (BS & 64u) ? 6 : 8>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0, seg0_end);
 }
 
 template <int MT, unsigned BS, int WV>
@@ -442,9 +451,23 @@ hipError_t launch_set(StreamArgs a, hipStream_t stream) {
   if (a.chunk < 1) a.chunk = 1;
   const size_t lds = (size_t)WV * stage_words<MT>(a.chunk) * 4;
   a.nstrips = (a.N + SC - 1) / SC;
-  a.strips_per_xcd = (a.mats * a.nstrips + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((qgemv_stream_kernel<MT, BS, WV>), dim3(kXcds * a.strips_per_xcd), dim3(WV * 64), lds, stream,
-                     a);
+  a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
+  // Each wave's first run segment, bounded by its first chunk.
+  for (int w = 0; w < WV; ++w) {
+    const int wb0 = (w * nblk) / WV, wb1 = ((w + 1) * nblk) / WV;
+    a.wave_bits[w] = 0;
+    a.wave_row[w] = 0;
+    a.wave_end[w] = wb0;
+    if (wb0 < wb1) {
+      int r = 0;
+      while (r + 1 < a.runs.nruns && wb0 >= a.runs.run_block[r + 1]) ++r;
+      a.wave_bits[w] = a.runs.run_bits[r];
+      a.wave_row[w] = a.runs.run_row[r] + (wb0 - a.runs.run_block[r]) * a.runs.run_bits[r];
+      a.wave_end[w] = std::min(std::min(wb1, a.runs.run_block[r + 1]), wb0 + a.chunk);
+    }
+  }
+  hipLaunchKernelGGL((qgemv_stream_kernel<MT, BS, WV>), dim3(kXcds * a.strips_per_xcd, a.mats), dim3(WV * 64), lds,
+                     stream, a);
   return hipGetLastError();
 }
 

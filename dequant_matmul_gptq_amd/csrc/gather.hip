@@ -81,25 +81,46 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
                                                           uint32_t* __restrict__ xq, int M, int K, int R,
                                                           int mfma, Runs runs) {
   extern __shared__ __align__(16) uint16_t xs[];   // R rows of K float16
+  // Both loops below keep kBatch loads per thread in flight: all loads of a
+  // batch are issued before any of them is used.
+  constexpr int kBatch = 8;
   const int m0 = blockIdx.x * R;
   const int rows = min(R, M - m0);
   const int n16 = K / 8;   // 16-byte pieces per row (K is a multiple of 32)
   const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)m0 * K);
   uint4* dst = reinterpret_cast<uint4*>(xs);
-  for (int i = threadIdx.x; i < rows * n16; i += 256) dst[i] = src[i];
+  const int total = rows * n16;
+  for (int base = threadIdx.x; base < total; base += 256 * kBatch) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = src[min(base + u * 256, total - 1)];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (base + u * 256 < total) dst[base + u * 256] = v[u];
+  }
   __syncthreads();
   const int pairs = (K / kBlockRows) * kPairsPerBlock;
-  for (int idx = threadIdx.x; idx < pairs; idx += 256) {
-    const int blk = idx / kPairsPerBlock, p = idx % kPairsPerBlock;
-    const int bits = block_bits_scan(runs, blk);
-    int lo, hi;
-    pair_rows(bits, mfma ? mfma_pair(bits, p) : p, lo, hi);
-    const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;
-    // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
-    const int flo = perm ? (int)min((unsigned)perm[jlo], (unsigned)(K - 1)) : jlo;
-    const int fhi = perm ? (int)min((unsigned)perm[jhi], (unsigned)(K - 1)) : jhi;
-    for (int r = 0; r < rows; ++r)
-      xq[(size_t)(m0 + r) * pairs + idx] = (uint32_t)xs[r * K + flo] | ((uint32_t)xs[r * K + fhi] << 16);
+  for (int base = threadIdx.x; base < pairs; base += 256 * kBatch) {
+    int flo[kBatch], fhi[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int idx = min(base + u * 256, pairs - 1);
+      const int blk = idx / kPairsPerBlock, p = idx % kPairsPerBlock;
+      const int bits = block_bits_scan(runs, blk);
+      int lo, hi;
+      pair_rows(bits, mfma ? mfma_pair(bits, p) : p, lo, hi);
+      const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;
+      // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
+      flo[u] = perm ? (int)min((unsigned)perm[jlo], (unsigned)(K - 1)) : jlo;
+      fhi[u] = perm ? (int)min((unsigned)perm[jhi], (unsigned)(K - 1)) : jhi;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int idx = base + u * 256;
+      if (idx < pairs)
+        for (int r = 0; r < rows; ++r)
+          xq[(size_t)(m0 + r) * pairs + idx] = (uint32_t)xs[r * K + flo[u]] | ((uint32_t)xs[r * K + fhi[u]] << 16);
+    }
   }
 }
 

@@ -225,7 +225,7 @@ int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_
   int st = check_layout(layout);
   if (st != QLINEAR_OK) return st;
   if (!bytes || M < 0) return QLINEAR_ERR_INVALID_ARGUMENT;
-  *bytes = qgemm_workspace_bytes(M, layout->K);
+  *bytes = qgemm_workspace_bytes(*layout, M);
   return QLINEAR_OK;
 }
 
@@ -239,7 +239,7 @@ int qlinear_qgemm_fused(const qlinear_layout* layout, const uint16_t* x, int32_t
   st = check_epilogue(epilogue, epi);
   if (st != QLINEAR_OK || M == 0) return st;
   if (M > kMaxGemmM || !qgemm_supported(*layout)) return QLINEAR_ERR_UNSUPPORTED;
-  if (workspace_bytes < qgemm_workspace_bytes(M, layout->K)) return QLINEAR_ERR_WORKSPACE;
+  if (workspace_bytes < qgemm_workspace_bytes(*layout, M)) return QLINEAR_ERR_WORKSPACE;
   return hip_status(launch_qgemm(*layout, make_runs(*layout), x, M, qweight, scales, zeros, perm, y, workspace, epi,
                                  (hipStream_t)stream));
 }

@@ -49,24 +49,31 @@ constexpr int FM = WM / 16, FN = WN / 16;    // 8 x 4 fragments per wave
 constexpr int kLdsRow = kBlockRows;          // 32 halves = 64 bytes, four 16-byte chunks
 constexpr int kAPieces = BM * kBlockRows / 8 / kThreads;  // 16-byte pieces of an A block per thread
 
+// Partial sums of a layout with several code widths, run by one launch per
+// run into float32 [M][N] in the workspace.
+enum PartMode : int {
+  kWhole = 0,   // the launch covers all of K: float16 output
+  kFirst = 1,   // first run: write the partial sums
+  kMiddle = 2,  // add into the partial sums
+  kLast = 3,    // partial sums + this run: float16 output
+};
+
 struct GemmArgs {
   const uint16_t* xq;
   const uint32_t* qweight;
   const uint16_t* scales;
   const uint8_t* zeros;
   uint16_t* y;
+  float* part;                 // partial sums (part_mode != kWhole)
   int M, K, N;
   int xq_bytes, qweight_bytes, scale_bytes;
+  int kb_first, kb_end, run_row;   // the blocks of this launch: one run of one width
+  int part_mode;
   Runs runs;
   Epilogue epi;
 };
 
-
-
 constexpr int kRing = 2;   // blocks of B loads in flight; also LDS stages of the A tile
-
-
-
 
 // Register ring of the global loads of D blocks. A lane's 4 column
 // fragments take 4 adjacent columns (its column quad), so each packed-word
@@ -86,17 +93,20 @@ struct LaneOffsets {
   uint32_t col;           // the quad's first column
 };
 
+// The launch's blocks [first, end): one run of one width, starting at packed
+// row `row`.
+struct RunRef {
+  int first, end, row;
+};
+
 template <unsigned BS, int kW, int D, int S>
 __device__ __forceinline__ void load_block(const GemmArgs& a, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
                                            __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz, int g,
-                                           const LaneOffsets& off, int blk, Ring<kW, D>& R) {
-  int bits, row;
-  if constexpr ((BS & (BS - 1)) == 0) {
-    bits = __builtin_ctz(BS);   // one width: block blk starts at packed row blk * b
-    row = blk * bits;
-  } else {
-    block_info(a.runs, blk, bits, row);
-  }
+                                           const LaneOffsets& off, const RunRef& run, int blk, Ring<kW, D>& R) {
+  static_assert((BS & (BS - 1)) == 0, "a launch streams one code width");
+  const int bits = __builtin_ctz(BS);
+  blk = min(blk, run.end - 1);   // loads past the run repeat its last block
+  const int row = run.row + (blk - run.first) * bits;
   R.bits[S] = bits;
   with_width<BS>(bits, [&](auto BB) {
     constexpr int B = decltype(BB)::value;
@@ -172,13 +182,13 @@ constexpr bool pipelined() {
 //     loads block kb + 3's words into slot S ^ 1.
 //   otherwise: block kb's words are in slot S; the step dequantizes them into
 //     bf[0] and then loads block kb + 2's words into slot S.
-// All loads are clamped to the last block.
+// A loads are clamped to the last block of K, B loads to the last of the run.
 template <unsigned BS, int kW, int S>
 __device__ __forceinline__ void block_step(const GemmArgs& a, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
                                            __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz, int tid, int lane,
-                                           int g, int wr, uint32_t magic, const LaneOffsets& off, int kb, int nblk,
-                                           uint16_t* As, Ring<kW, kRing>& R, u32x4 (&an)[2][kAPieces],
-                                           half8_t (&bf)[2][FN], float4_t (&acc)[FM][FN]) {
+                                           int g, int wr, uint32_t magic, const LaneOffsets& off, const RunRef& run,
+                                           int kb, int nblk, uint16_t* As, Ring<kW, kRing>& R,
+                                           u32x4 (&an)[2][kAPieces], half8_t (&bf)[2][FN], float4_t (&acc)[FM][FN]) {
   constexpr int kStage = BM * kLdsRow;
   constexpr int T = S ^ 1;
   constexpr bool kPipe = pipelined<kW>();
@@ -191,10 +201,10 @@ __device__ __forceinline__ void block_step(const GemmArgs& a, __amdgpu_buffer_rs
   if constexpr (kPipe) {
     read_a(As + S * kStage, lane, g, wr, af);
     dequant_block<BS, kW, kRing, T>(a, R, g, magic, bf[T]);
-    load_block<BS, kW, kRing, T>(a, rx, rw, rs, rz, g, off, min(kb + 3, nblk - 1), R);
+    load_block<BS, kW, kRing, T>(a, rx, rw, rs, rz, g, off, run, kb + 3, R);
   } else {
     dequant_block<BS, kW, kRing, S>(a, R, g, magic, bf[0]);
-    load_block<BS, kW, kRing, S>(a, rx, rw, rs, rz, g, off, nb2, R);
+    load_block<BS, kW, kRing, S>(a, rx, rw, rs, rz, g, off, run, kb + 2, R);
     read_a(As + S * kStage, lane, g, wr, af);
   }
 #pragma unroll
@@ -206,7 +216,9 @@ __device__ __forceinline__ void block_step(const GemmArgs& a, __amdgpu_buffer_rs
   __syncthreads();
 }
 
-template <unsigned BS>
+// kRange: the launch covers one run [kb_first, kb_end) of a layout computed
+// run by run (partial sums per part_mode); otherwise all of K, one width.
+template <unsigned BS, bool kRange>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   constexpr int kW = max_frag_words<BS>();
   constexpr int D = kRing;
@@ -227,6 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
   const int n0 = (tile % gx) * BN;
   const int m0 = (tile / gx) * BM;
   const int nblk = a.K / kBlockRows;
+  const RunRef run = kRange ? RunRef{a.kb_first, a.kb_end, a.run_row} : RunRef{0, nblk, 0};
   const int g = lane >> 4;   // k-group of the lane's B fragments
 
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, 0, a.xq_bytes, kRsrcWord3);
@@ -259,40 +272,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = {0.f, 0.f, 0.f, 0.f};
 
-  // Prologue: packed words of blocks 0 and 1 in slots 0 and 1, A pieces of
-  // blocks 0 and 1 loaded, block 0's A tile in stage 0. Pipelined: block 0's
-  // fragments in bf[0] and block 2's words in flight in slot 0.
+  // Prologue: packed words of the launch's blocks f and f + 1 in slots 0 and
+  // 1, their A pieces loaded, block f's A tile in stage 0. Pipelined: block
+  // f's fragments in bf[0] and block f + 2's words in flight in slot 0.
+  const int f = run.first;
   static_for<0, D>([&](auto SS) {
     constexpr int S = decltype(SS)::value;
-    load_block<BS, kW, D, S>(a, rx, rw, rs, rz, g, off, min(S, nblk - 1), R);
+    load_block<BS, kW, D, S>(a, rx, rw, rs, rz, g, off, run, f + S, R);
   });
   u32x4 an[2][kAPieces];
 #pragma unroll
   for (int i = 0; i < kAPieces; ++i) {
-    an[0][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off.a[i], 0, 0));
+    an[0][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off.a[i], f * kBlockRows * 2, 0));
     an[1][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-        rx, off.a[i], min(1, nblk - 1) * kBlockRows * 2, 0));
+        rx, off.a[i], min(f + 1, nblk - 1) * kBlockRows * 2, 0));
   }
   half8_t bf[2][FN];
   if constexpr (pipelined<kW>()) {
     dequant_block<BS, kW, D, 0>(a, R, g, magic, bf[0]);
-    load_block<BS, kW, D, 0>(a, rx, rw, rs, rz, g, off, min(2, nblk - 1), R);
+    load_block<BS, kW, D, 0>(a, rx, rw, rs, rz, g, off, run, f + 2, R);
   }
   store_a(As, tid, an[0]);
   __syncthreads();
 
   // Whole rounds of D blocks without conditions (static ring slots, exact
   // load counts), then the remaining blocks.
-  const int nfull = nblk / D * D;
-  for (int kb0 = 0; kb0 < nfull; kb0 += D) {
+  const int nfull = f + (run.end - f) / D * D;
+  for (int kb0 = f; kb0 < nfull; kb0 += D) {
     static_for<0, D>([&](auto SS) {
       constexpr int S = decltype(SS)::value;
-      block_step<BS, kW, S>(a, rx, rw, rs, rz, tid, lane, g, wr, magic, off, kb0 + S, nblk, As, R, an, bf, acc);
+      block_step<BS, kW, S>(a, rx, rw, rs, rz, tid, lane, g, wr, magic, off, run, kb0 + S, nblk, As, R, an, bf, acc);
     });
   }
   static_for<0, D - 1>([&](auto SS) {
     constexpr int S = decltype(SS)::value;
-    if (nfull + S < nblk) block_step<BS, kW, S>(a, rx, rw, rs, rz, tid, lane, g, wr, magic, off, nfull + S, nblk, As, R, an, bf, acc);
+    if (nfull + S < run.end)
+      block_step<BS, kW, S>(a, rx, rw, rs, rz, tid, lane, g, wr, magic, off, run, nfull + S, nblk, As, R, an, bf, acc);
   });
 
   // Epilogue: lane holds C[4*(lane/16) + r][lane % 16] of each 16 x 16 tile;
@@ -305,10 +320,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wr * WM + i * 16 + 4 * (lane >> 4) + r;
         if (m < a.M) {
+          float v4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = acc[i][j][r];
+          if (kRange && a.part_mode != kWhole) {
+            float4_t* pp = reinterpret_cast<float4_t*>(a.part + (size_t)m * a.N + nq);
+            if (a.part_mode != kFirst) {
+              const float4_t p = *pp;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) v4[j] += p[j];
+            }
+            if (a.part_mode != kLast) {
+              *pp = float4_t{v4[0], v4[1], v4[2], v4[3]};
+              continue;
+            }
+          }
           uint16_t h[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            h[j] = __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(a.epi, acc[i][j][r], m, nq + j, a.N));
+            h[j] = __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(a.epi, v4[j], m, nq + j, a.N));
           u32x2 v;
           v[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
           v[1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
@@ -321,12 +351,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs a) {
 
 template <unsigned BS>
 void launch_set(const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_kernel<BS>), grid, dim3(kThreads), 0, stream, a);
+  if (a.part_mode == kWhole)
+    hipLaunchKernelGGL((gemm_kernel<BS, false>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<BS, true>), grid, dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace
 
-size_t qgemm_workspace_bytes(int M, int K) { return ((size_t)M * K * 2 + 255) / 256 * 256; }
+// Layouts with several code widths are computed one launch per run
+// (register dequantization of that run's width), the runs adding up in
+// float32 partial sums in the workspace, when K holds at least 4096 rows per
+// run boundary: each boundary writes and reads the [M][N] partial sums, about
+// 700 / K of the GEMM's own time. Otherwise the kernel that dequantizes into
+// LDS block by block. (Measured on MI355X: 70B 2.5 bpw 8192 -> 28672, two
+// runs, M = 1024: 647 vs 981 us; EXL2 4.0 bpw 4096 -> 11008, four runs,
+// M = 2048: 415 us either way.)
+bool qgemm_split_runs(const qlinear_layout& L) {
+  unsigned set = 0;
+  for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
+  return (set & (set - 1)) != 0 && (int64_t)(L.nruns - 1) * 4096 <= L.K;
+}
+
+size_t qgemm_workspace_bytes(const qlinear_layout& L, int M) {
+  const size_t xq = ((size_t)M * L.K * 2 + 255) / 256 * 256;
+  return xq + (qgemm_split_runs(L) ? (size_t)M * L.N * 4 : 0);
+}
 
 bool qgemm_supported(const qlinear_layout& L) {
   // Buffer offsets and sizes are 32-bit: the packed words and the scales must
@@ -350,13 +400,14 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
     // MFMA pair order for the register-dequant kernel; natural order for the
     // kernel that dequantizes into LDS.
     const bool mixed = (set & (set - 1)) != 0;
-    hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, !mixed, stream);
+    const bool split = qgemm_split_runs(L);
+    hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, !mixed || split, stream);
     if (e != hipSuccess) return e;
     uint16_t* yc = y + (size_t)m0 * L.N;
     Epilogue ec = epi;   // the chunk's rows of the residual
     if (ec.residual) ec.residual += (size_t)m0 * L.N;
-    // Several code widths: the kernel that dequantizes into LDS block by block.
-    if (mixed) {
+    // Many runs of several code widths: the kernel that dequantizes into LDS.
+    if (mixed && !split) {
       e = launch_qgemm_lds(L, runs, reinterpret_cast<const uint16_t*>(xq), mc, qweight, scales, zeros, yc, ec,
                            stream);
       if (e != hipSuccess) return e;
@@ -376,18 +427,27 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
     a.scale_bytes = (int)((size_t)L.groups * L.N * 2);
     a.runs = runs;
     a.epi = ec;
+    // The float32 partial sums of the chunk's rows follow the activations.
+    a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (((size_t)M * L.K * 2 + 255) / 256 * 256));
     const int ntiles = ((L.N + BN - 1) / BN) * ((mc + BM - 1) / BM);
     const dim3 grid(8 * ((ntiles + 7) / 8), 1, 1);
-    switch (set) {
-      case 1u << 2: launch_set<1u << 2>(a, grid, stream); break;
-      case 1u << 3: launch_set<1u << 3>(a, grid, stream); break;
-      case 1u << 4: launch_set<1u << 4>(a, grid, stream); break;
-      case 1u << 5: launch_set<1u << 5>(a, grid, stream); break;
-      case 1u << 6: launch_set<1u << 6>(a, grid, stream); break;
-      default: launch_set<1u << 8>(a, grid, stream); break;
+    // One launch per run (a single one for one code width).
+    for (int r = 0; r < L.nruns; ++r) {
+      a.kb_first = runs.run_block[r];
+      a.kb_end = runs.run_block[r + 1];
+      a.run_row = runs.run_row[r];
+      a.part_mode = L.nruns == 1 ? kWhole : r == 0 ? kFirst : r + 1 == L.nruns ? kLast : kMiddle;
+      switch (runs.run_bits[r]) {
+        case 2: launch_set<1u << 2>(a, grid, stream); break;
+        case 3: launch_set<1u << 3>(a, grid, stream); break;
+        case 4: launch_set<1u << 4>(a, grid, stream); break;
+        case 5: launch_set<1u << 5>(a, grid, stream); break;
+        case 6: launch_set<1u << 6>(a, grid, stream); break;
+        default: launch_set<1u << 8>(a, grid, stream); break;
+      }
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
     }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }

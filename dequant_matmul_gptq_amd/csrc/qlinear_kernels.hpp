@@ -61,7 +61,10 @@ hipError_t launch_qgemv_mfma(const qlinear_layout& L, const Runs& runs, const ui
                              const uint8_t* const* zeros, uint16_t* const* ys, const Epilogue& epi,
                              hipStream_t stream);
 
-size_t qgemm_workspace_bytes(int M, int K);
+// Bytes of qgemm's workspace: the gathered activations [M][K] float16, then
+// for layouts computed run by run the float32 partial sums [M][N].
+size_t qgemm_workspace_bytes(const qlinear_layout& L, int M);
+bool qgemm_split_runs(const qlinear_layout& L);
 // Whether the packed words and scales fit the prefill kernel's 32-bit offsets.
 bool qgemm_supported(const qlinear_layout& L);
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,

@@ -195,13 +195,17 @@ int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32
                           const uint8_t* const* zeros_host, const int32_t* perm, uint16_t* const* y_host,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace of qlinear_qgemm for M tokens, in bytes (no initialization needed). */
+/* Workspace of qlinear_qgemm for M tokens, in bytes (no initialization needed):
+ * the gathered activations, float16 [M][K], and for a layout with several
+ * code widths that has at least 4096 rows of K per run boundary also float32
+ * partial sums [M][N] (such a layout is computed one launch per run). */
 int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes);
 
 /*
  * Prefill-sized layer, any M >= 0 (M == 0 as for qlinear_qgemv), same
  * operands and result as qlinear_qgemv.
- * The workspace receives the act-order-gathered activations.
+ * The workspace receives the act-order-gathered activations (and the partial
+ * sums described at qlinear_qgemm_workspace_bytes).
  * Errors as for qlinear_qgemv; UNSUPPORTED also for M > 65535 * 128, or for
  * packed words or scales of 2^31 bytes or more.
  */

@@ -92,6 +92,25 @@ def test_qgemm_small_mixed(M, zeros):
     assert_close(y, _ref(inp), f"qgemm M={M}")
 
 
+RUN_SPLIT_BITS = {
+    "2runs-3b2b": [3] * 128 + [2] * 128,               # K = 8192, one run boundary (70B 2.5 bpw shape)
+    "3runs-odd": [6] * 13 + [4] * 200 + [3] * 43,      # K = 8192, runs start at blocks 0, 13 and 213
+}
+
+
+@pytest.mark.parametrize("zeros", (True, False))
+@pytest.mark.parametrize("M", (100, 300))
+@pytest.mark.parametrize("name", sorted(RUN_SPLIT_BITS))
+def test_qgemm_run_by_run(name, M, zeros):
+    """Several code widths with K >= 4096 rows per run boundary: one
+    register-dequant launch per run, adding up in float32 partial sums in the
+    workspace (first / middle / last launch), ragged M over 256-row tiles."""
+    say(f"qgemm run by run {name} M={M} zeros={zeros}")
+    inp = _mixed_inputs(RUN_SPLIT_BITS[name], 32, 520, M, seed=len(name) * 7 + M, zeros=zeros)
+    y = GpuLayer(inp).qgemm(inp.x)
+    assert_close(y, _ref(inp), f"qgemm {name} M={M}")
+
+
 @pytest.mark.parametrize("gs", (32, 128))
 @pytest.mark.parametrize("b", (2, 3, 4, 5, 6, 8))
 def test_qgemm_uniform_widths(b, gs):
@@ -335,11 +354,13 @@ EPILOGUE_PATHS = [
     ("qgemv", MIXED_BITS, 16),     # MFMA decode kernel, several widths
     ("qgemm", [4] * 11, 100),      # prefill, register dequant
     ("qgemm", MIXED_BITS, 100),    # prefill, LDS dequant
+    ("qgemm", [3] * 128 + [2] * 128, 100),   # prefill, one launch per run
 ]
 
 
 @pytest.mark.parametrize("op,bits,M", EPILOGUE_PATHS,
-                         ids=["row", "gather-valu-M1", "valu-M2", "mfma-M5", "mfma-M16", "qgemm", "qgemm-mixed"])
+                         ids=["row", "gather-valu-M1", "valu-M2", "mfma-M5", "mfma-M16", "qgemm", "qgemm-mixed",
+                              "qgemm-runs"])
 @pytest.mark.parametrize("terms", ["bias", "residual", "bias-silu-residual", "silu-inplace-residual"])
 def test_fused_epilogue(op, bits, M, terms):
     """y = RNE(act(x W + bias) + residual) on every kernel path, against the

@@ -86,7 +86,7 @@ __device__ __forceinline__ float quad_sum(float v) {
 
 // Gather the lane's 4 pairs of block blk from the LDS row, exchange them over
 // the quad, then unpack and multiply the block for the lane's 4 columns.
-template <int B>
+template <int B, bool kPerm>
 __device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs& S, const _Float16* xrow, int blk,
                                              const int (&rlo)[4], const int (&rhi)[4], const float (&sc)[4],
                                              uint32_t magic, float (&yacc)[4]) {
@@ -95,8 +95,8 @@ __device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
-    const int flo = a.perm ? (int)min((unsigned)S.pl[r], (unsigned)(a.K - 1)) : blk * kBlockRows + rlo[r];
-    const int fhi = a.perm ? (int)min((unsigned)S.ph[r], (unsigned)(a.K - 1)) : blk * kBlockRows + rhi[r];
+    const int flo = kPerm ? (int)min((unsigned)S.pl[r], (unsigned)(a.K - 1)) : blk * kBlockRows + rlo[r];
+    const int fhi = kPerm ? (int)min((unsigned)S.ph[r], (unsigned)(a.K - 1)) : blk * kBlockRows + rhi[r];
     const float vl = (float)xrow[flo], vh = (float)xrow[fhi];
     const _Float16 sl = (_Float16)(vl * sc[r]), sh = (_Float16)(vh * sc[r]);
     own[r] = (uint32_t)__builtin_bit_cast(uint16_t, sl) | ((uint32_t)__builtin_bit_cast(uint16_t, sh) << 16);
@@ -161,8 +161,9 @@ __device__ __forceinline__ void seg_issue(const StreamArgs& a, const RowLane& L,
 }
 
 // All steps of the wave's blocks [blk0, blk1) (at least one), D in flight;
-// the first D were issued already into S[0 .. D-1].
-template <int B, int D>
+// the first D were issued already into S[0 .. D-1]. kPerm: act-order (the
+// choice is made once per launch, not per pair).
+template <int B, int D, bool kPerm>
 __device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L, int blk0, int blk1, int row0,
                                           float (&yacc)[4], StepRegs (&S)[D]) {
   int rlo[4], rhi[4];
@@ -173,7 +174,7 @@ __device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L,
     // Past the range the whole quad is idle (zero scale); its pairs come
     // from block blk0 (as its perm entries did).
     const int blk = blk0 + i * KS + L.ks < blk1 ? blk0 + i * KS + L.ks : blk0;
-    compute_step<B>(a, R, L.xrow, blk, rlo, rhi, sc, L.magic, yacc);
+    compute_step<B, kPerm>(a, R, L.xrow, blk, rlo, rhi, sc, L.magic, yacc);
   };
   // Steady state: every buffer is refilled on every pass. (A refill under a
   // condition turns the buffers into loop-carried copies, and a copy waits for
@@ -214,7 +215,9 @@ typedef uint32_t piece_t __attribute__((ext_vector_type(4)));   // 16 bytes of t
 // scalar-load round trip.
 // P: sixteen-byte pieces of the x row per thread, all loaded before the
 // weights; P * WV * 64 * 16 bytes cover the row. D: steps in flight per wave.
-template <int B, int WV, int P, int D>
+// kPerm: act-order (perm given), a kernel of its own so that the step loop
+// holds no per-pair choice.
+template <int B, int WV, int P, int D, bool kPerm>
 __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ float red[WV][1][SC];
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
 
   // 4. Stream the wave's blocks.
   float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (wb0 < wb1) row_steps<B, D>(a, L, wb0, wb1, row0, yacc, S);
+  if (wb0 < wb1) row_steps<B, D, kPerm>(a, L, wb0, wb1, row0, yacc, S);
 
   // Reduce over the 16 block slots of the wave (shuffles), then over the
   // waves (LDS); the epilogue as apply_epilogue: bias, activation, residual.
@@ -319,12 +322,12 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
 
 template <int B, int WV, int P, int D>
 hipError_t launch_row(StreamArgs a, hipStream_t stream) {
+  const auto kernel = a.perm ? qgemv_row_kernel<B, WV, P, D, true> : qgemv_row_kernel<B, WV, P, D, false>;
   a.nstrips = (a.N + SC - 1) / SC;
   a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
   a.xrow_words = row_words(a.K);
   const size_t lds = (size_t)a.xrow_words * 4;
-  hipLaunchKernelGGL((qgemv_row_kernel<B, WV, P, D>), dim3(kXcds * a.strips_per_xcd, a.mats), dim3(WV * 64), lds, stream,
-                     a);
+  hipLaunchKernelGGL(kernel, dim3(kXcds * a.strips_per_xcd, a.mats), dim3(WV * 64), lds, stream, a);
   return hipGetLastError();
 }
 

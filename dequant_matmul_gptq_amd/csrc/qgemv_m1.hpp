@@ -97,11 +97,17 @@ __device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs
     // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
     const int flo = kPerm ? (int)min((unsigned)S.pl[r], (unsigned)(a.K - 1)) : blk * kBlockRows + rlo[r];
     const int fhi = kPerm ? (int)min((unsigned)S.ph[r], (unsigned)(a.K - 1)) : blk * kBlockRows + rhi[r];
-    const float vl = (float)xrow[flo], vh = (float)xrow[fhi];
-    const _Float16 sl = (_Float16)(vl * sc[r]), sh = (_Float16)(vh * sc[r]);
-    own[r] = (uint32_t)__builtin_bit_cast(uint16_t, sl) | ((uint32_t)__builtin_bit_cast(uint16_t, sh) << 16);
-    xs += vl + vh;
-    xss += (float)sl + (float)sh;
+    // The pair in float16, scaled by 2^-e with one packed multiply (exact, or
+    // the same rounding of a subnormal as float32 then float16), and both
+    // added into the block sums by a dot product with (1, 1).
+    const uint32_t pair = (uint32_t)__builtin_bit_cast(uint16_t, xrow[flo]) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, xrow[fhi]) << 16);
+    const _Float16 s16 = (_Float16)sc[r];
+    const half2_t scaled = as_half2(pair) * half2_t{s16, s16};
+    own[r] = as_u32(scaled);
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    xs = __builtin_amdgcn_fdot2(as_half2(pair), ones, xs, false);
+    xss = __builtin_amdgcn_fdot2(scaled, ones, xss, false);
   }
   const float X = quad_sum(xs), Xs = quad_sum(xss);
 

@@ -1,9 +1,9 @@
 // Single-row decode kernel (M = 1) on gfx950: the act-order gather happens
 // inside the kernel, so a call is one launch.
 //
-// Work split as in the multi-row kernel: a workgroup of 4 or 8 waves owns a
+// Work split as in the multi-row kernel: a workgroup of 4 waves owns a
 // 16-column panel and the whole K range; lane = (block slot ks, column quad
-// cq); a wave step is 16 consecutive blocks of one run, two steps in flight.
+// cq); a wave step is 16 consecutive blocks, two steps in flight.
 //
 // Activations. The workgroup copies the x row (float16, original order) into
 // LDS; its loads are issued first, before any weight load (vector loads
@@ -134,15 +134,17 @@ __device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs
       acc[c] = __builtin_amdgcn_fdot2(as_half2(v), as_half2(xp), acc[c], false);
     }
   });
-  float s[4], z[4];
-  s[0] = S.P.ok ? half_lo(S.P.s.x) : 0.0f;
-  s[1] = S.P.ok ? half_hi(S.P.s.x) : 0.0f;
-  s[2] = S.P.ok ? half_lo(S.P.s.y) : 0.0f;
-  s[3] = S.P.ok ? half_hi(S.P.s.y) : 0.0f;
+  // A lane without a block this step (past the range or past N) adds nothing.
+  if (S.P.ok) {
+    const float s[4] = {half_lo(S.P.s.x), half_hi(S.P.s.x), half_lo(S.P.s.y), half_hi(S.P.s.y)};
+    // The 4 zero points as bytes of one word (symmetric: 2^(B-1) each).
+    const uint32_t zw = a.has_zeros ? S.P.z : (uint32_t)(1u << (B - 1)) * 0x01010101u;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) z[c] = a.has_zeros ? (float)((S.P.z >> (8 * c)) & 0xFFu) : (float)(1 << (B - 1));
-#pragma unroll
-  for (int c = 0; c < 4; ++c) yacc[c] = fmaf(s[c], fmaf(-z[c], X, acc[c] - 1024.0f * Xs), yacc[c]);
+    for (int c = 0; c < 4; ++c) {
+      const float z = (float)((zw >> (8 * c)) & 0xFFu);
+      yacc[c] = fmaf(s[c], fmaf(-z, X, acc[c] - 1024.0f * Xs), yacc[c]);
+    }
+  }
 }
 
 // Lane context shared by the steps of a wave.

@@ -228,7 +228,7 @@ typedef uint32_t piece_t __attribute__((ext_vector_type(4)));   // 16 bytes of t
 template <int B, int WV, int P, int D, bool kPerm>
 __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
-  __shared__ float red[WV][1][SC];
+  __shared__ float red[WV][4][SC];   // per wave and 16-lane row: the sums of the strip's columns
 
   // Kernel arguments, all read in one batch: the empty asm takes them as
   // operands (and hands them back, so they are not read again later).
@@ -306,21 +306,28 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (wb0 < wb1) row_steps<B, D, kPerm>(a, L, wb0, wb1, row0, yacc, S);
 
-  // Reduce over the 16 block slots of the wave (shuffles), then over the
-  // waves (LDS); the epilogue as apply_epilogue: bias, activation, residual.
+  // Reduce over the block slots: the 4 of each 16-lane row with two DPP row
+  // shifts (lanes 12..15 of a row end up with its sums, one per column
+  // quad), then the 4 rows of each wave and the waves through LDS; the
+  // epilogue as apply_epilogue: bias, activation, residual.
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 4; ++c) {
+    yacc[c] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yacc[c]), 0x114, 0xF,
+                                                                     0xF, true));   // row_shr:4
+    yacc[c] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yacc[c]), 0x118, 0xF,
+                                                                     0xF, true));   // row_shr:8
+  }
+  if ((lane & 15) >= 12) {
 #pragma unroll
-    for (int off = CQ; off < 64; off <<= 1) yacc[c] += __shfl_xor(yacc[c], off, 64);
-  if (L.ks == 0) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) red[wave][0][L.cq * 4 + c] = yacc[c];
+    for (int c = 0; c < 4; ++c) red[wave][lane >> 4][L.cq * 4 + c] = yacc[c];
   }
   __syncthreads();
   if (tid < SC && strip * SC + tid < N) {
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WV; ++w) v += red[w][0][tid];
+    for (int w = 0; w < WV; ++w)
+#pragma unroll
+      for (int row = 0; row < 4; ++row) v += red[w][row][tid];
     if (epi.bias) v += (float)__builtin_bit_cast(_Float16, bias_raw);
     if (epi.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
     if (epi.residual) v += (float)__builtin_bit_cast(_Float16, res_raw);

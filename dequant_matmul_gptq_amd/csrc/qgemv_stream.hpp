@@ -266,23 +266,28 @@ __host__ __device__ constexpr int stage_words(int chunk) {
 // Reduce the lane sums over the 16 block slots of each wave (lanes cq,
 // cq + 4, ..., cq + 60), then over the waves through LDS, and store y.
 template <int MT, int WV>
-__device__ __forceinline__ void reduce_store(const StreamArgs& a, uint16_t* y, float (&red)[WV][MT][SC], float (&yacc)[4][MT],
-                                             int tid, int lane, int wave, int strip) {
-  const int cq = lane % CQ, ks = lane / CQ;
+__device__ __forceinline__ void reduce_store(const StreamArgs& a, uint16_t* y, float (&red)[WV][4][MT][SC],
+                                             float (&yacc)[4][MT], int tid, int lane, int wave, int strip) {
+  const int cq = lane % CQ;
+  // The 4 block slots of each 16-lane row with two DPP row shifts (lanes
+  // 12..15 of a row end up with its sums, one per column quad), then the 4
+  // rows of each wave and the waves through LDS.
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       float v = yacc[c][m];
-#pragma unroll
-      for (int off = CQ; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+      v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF,
+                                                                 true));   // row_shr:4
+      v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF,
+                                                                 true));   // row_shr:8
       yacc[c][m] = v;
     }
-  if (ks == 0) {
+  if ((lane & 15) >= 12) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) red[wave][m][cq * 4 + c] = yacc[c][m];
+      for (int c = 0; c < 4; ++c) red[wave][lane >> 4][m][cq * 4 + c] = yacc[c][m];
   }
   __syncthreads();
   if (tid < SC * MT) {
@@ -291,7 +296,9 @@ __device__ __forceinline__ void reduce_store(const StreamArgs& a, uint16_t* y, f
     if (m < a.M && n < a.N) {
       float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < WV; ++w) v += red[w][m][c];
+      for (int w = 0; w < WV; ++w)
+#pragma unroll
+        for (int row = 0; row < 4; ++row) v += red[w][row][m][c];
       y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(a.epi, v, m, n, a.N));
     }
   }
@@ -300,7 +307,7 @@ __device__ __forceinline__ void reduce_store(const StreamArgs& a, uint16_t* y, f
 // Kernel body, specialised on B0, the width of this wave's first run, so the
 // first step can be issued into a typed buffer before the activation staging.
 template <int MT, unsigned BS, int WV, int B0>
-__device__ __forceinline__ void stream_body(const StreamArgs& a, const MatPtrs& mp, uint32_t* lds, float (&red)[WV][MT][SC],
+__device__ __forceinline__ void stream_body(const StreamArgs& a, const MatPtrs& mp, uint32_t* lds, float (&red)[WV][4][MT][SC],
                                             int tid, int lane, int wave, int strip, int wb0, int wb1, int row0,
                                             int seg0_end) {
   const int cq = lane % CQ, ks = lane / CQ;
@@ -391,7 +398,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const MatPtrs& 
 }
 
 template <int MT, unsigned BS, int WV, int B0>
-__device__ __forceinline__ void dispatch_body(const StreamArgs& a, const MatPtrs& mp, uint32_t* lds, float (&red)[WV][MT][SC], int tid,
+__device__ __forceinline__ void dispatch_body(const StreamArgs& a, const MatPtrs& mp, uint32_t* lds, float (&red)[WV][4][MT][SC], int tid,
                                               int lane, int wave, int strip, int wb0, int wb1, int row0, int seg0_end) {
   stream_body<MT, BS, WV, B0>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0, seg0_end);
 }
@@ -403,7 +410,7 @@ __device__ __forceinline__ void dispatch_body(const StreamArgs& a, const MatPtrs
 template <int MT, unsigned BS, int WV>
 __global__ __launch_bounds__(WV * 64) void qgemv_stream_kernel(StreamArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
-  __shared__ float red[WV][MT][SC];
+  __shared__ float red[WV][4][MT][SC];   // per wave and 16-lane row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

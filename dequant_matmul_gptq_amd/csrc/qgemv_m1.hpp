@@ -36,8 +36,11 @@ __host__ __device__ constexpr int row_words(int K) { return (K / 2 + 3) / 4 * 4;
 // segment, needs 205-256 VGPRs for the width sets of EXL2 layouts, and the
 // gather kernel plus the multi-row kernel stay faster: EXL2 4.0 bpw
 // 4096 -> 11008: 16.8 vs 20.0 us; 2.5 bpw 8192 -> 28672: 31.5 vs 38.3 us.)
+// Activation rows of the kernel instance for M rows: 1, 2 or 4.
+constexpr int row_mt(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
+
 inline bool single_row(int M, int K, unsigned set) {
-  return M == 1 && (size_t)row_words(K) * 4 <= kRowLdsBudget && (set & (set - 1)) == 0;
+  return M <= 4 && (size_t)row_mt(M) * row_words(K) * 4 <= kRowLdsBudget && (set & (set - 1)) == 0;
 }
 
 // Loads of one lane for one step: the block's weights, scale and zero point
@@ -84,32 +87,44 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
-// Gather the lane's 4 pairs of block blk from the LDS row, exchange them over
-// the quad, then unpack and multiply the block for the lane's 4 columns.
-template <int B, bool kPerm>
-__device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs& S, const _Float16* xrow, int blk,
-                                             const int (&rlo)[4], const int (&rhi)[4], const float (&sc)[4],
-                                             uint32_t magic, float (&yacc)[4]) {
-  uint32_t own[4];
-  float xs = 0.0f, xss = 0.0f;
+// Gather the lane's 4 pairs of block blk from each of the MT LDS rows (row m
+// at xrow + m * xstride), exchange them over the quad, then unpack the
+// block's pairs for the lane's 4 columns once and multiply them into every
+// row.
+template <int B, bool kPerm, int MT>
+__device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs& S, const _Float16* xrow, int xstride,
+                                             int blk, const int (&rlo)[4], const int (&rhi)[4], const float (&sc)[4],
+                                             uint32_t magic, float (&yacc)[4][MT]) {
+  uint32_t own[4][MT];
+  float xs[MT], xss[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xs[m] = xss[m] = 0.0f;
+  const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
     const int flo = kPerm ? (int)min((unsigned)S.pl[r], (unsigned)(a.K - 1)) : blk * kBlockRows + rlo[r];
     const int fhi = kPerm ? (int)min((unsigned)S.ph[r], (unsigned)(a.K - 1)) : blk * kBlockRows + rhi[r];
-    // The pair in float16, scaled by 2^-e with one packed multiply (exact, or
-    // the same rounding of a subnormal as float32 then float16), and both
-    // added into the block sums by a dot product with (1, 1).
-    const uint32_t pair = (uint32_t)__builtin_bit_cast(uint16_t, xrow[flo]) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, xrow[fhi]) << 16);
     const _Float16 s16 = (_Float16)sc[r];
-    const half2_t scaled = as_half2(pair) * half2_t{s16, s16};
-    own[r] = as_u32(scaled);
-    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-    xs = __builtin_amdgcn_fdot2(as_half2(pair), ones, xs, false);
-    xss = __builtin_amdgcn_fdot2(scaled, ones, xss, false);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      // The pair in float16, scaled by 2^-e with one packed multiply (exact,
+      // or the same rounding of a subnormal as float32 then float16), and
+      // both added into the block sums by a dot product with (1, 1).
+      const uint32_t pair = (uint32_t)__builtin_bit_cast(uint16_t, xrow[m * xstride + flo]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, xrow[m * xstride + fhi]) << 16);
+      const half2_t scaled = as_half2(pair) * half2_t{s16, s16};
+      own[r][m] = as_u32(scaled);
+      xs[m] = __builtin_amdgcn_fdot2(as_half2(pair), ones, xs[m], false);
+      xss[m] = __builtin_amdgcn_fdot2(scaled, ones, xss[m], false);
+    }
   }
-  const float X = quad_sum(xs), Xs = quad_sum(xss);
+  float X[MT], Xs[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    X[m] = quad_sum(xs[m]);
+    Xs[m] = quad_sum(xss[m]);
+  }
 
   const uint4* W = S.W;
   uint32_t wc[4][B], wsh[4][B];
@@ -124,14 +139,32 @@ __device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int t = 0; t < B; ++t) wsh[c][t] = wc[c][t] >> scaled_shift(B);
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[4][MT];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[c][m] = 0.0f;
   static_for<0, kPairsPerBlock>([&](auto Q) {
     constexpr int Pp = decltype(Q)::value;
-    const uint32_t xp = (uint32_t)__builtin_amdgcn_mov_dpp((int)own[Pp % 4], (Pp / 4) * 0x55, 0xF, 0xF, false);
+    if constexpr (MT == 1) {
+      // (one row: each pair unpacked right before its product)
+      const uint32_t xp = (uint32_t)__builtin_amdgcn_mov_dpp((int)own[Pp % 4][0], (Pp / 4) * 0x55, 0xF, 0xF, false);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t v = extract_pair_scaled<B, Pp>(wc[c], wsh[c], magic);
-      acc[c] = __builtin_amdgcn_fdot2(as_half2(v), as_half2(xp), acc[c], false);
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t v = extract_pair_scaled<B, Pp>(wc[c], wsh[c], magic);
+        acc[c][0] = __builtin_amdgcn_fdot2(as_half2(v), as_half2(xp), acc[c][0], false);
+      }
+    } else {
+      uint32_t v[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = extract_pair_scaled<B, Pp>(wc[c], wsh[c], magic);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const uint32_t xp = (uint32_t)__builtin_amdgcn_mov_dpp((int)own[Pp % 4][m], (Pp / 4) * 0x55, 0xF, 0xF, false);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[c][m] = __builtin_amdgcn_fdot2(as_half2(v[c]), as_half2(xp), acc[c][m], false);
+      }
     }
   });
   // A lane without a block this step (past the range or past N) adds nothing.
@@ -142,7 +175,8 @@ __device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float z = (float)((zw >> (8 * c)) & 0xFFu);
-      yacc[c] = fmaf(s[c], fmaf(-z, X, acc[c] - 1024.0f * Xs), yacc[c]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) yacc[c][m] = fmaf(s[c], fmaf(-z, X[m], acc[c][m] - 1024.0f * Xs[m]), yacc[c][m]);
     }
   }
 }
@@ -152,7 +186,8 @@ struct RowLane {
   MatPtrs mp;
   const uint32_t* panel;
   const int32_t* psrc;
-  const _Float16* xrow;
+  const _Float16* xrow;        // x row 0 in LDS; row m at xrow + m * xstride
+  int xstride;
   int ks, cq, col;
   bool colv;
   uint32_t magic;
@@ -171,9 +206,9 @@ __device__ __forceinline__ void seg_issue(const StreamArgs& a, const RowLane& L,
 // All steps of the wave's blocks [blk0, blk1) (at least one), D in flight;
 // the first D were issued already into S[0 .. D-1]. kPerm: act-order (the
 // choice is made once per launch, not per pair).
-template <int B, int D, bool kPerm>
+template <int B, int D, bool kPerm, int MT>
 __device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L, int blk0, int blk1, int row0,
-                                          float (&yacc)[4], StepRegs (&S)[D]) {
+                                          float (&yacc)[4][MT], StepRegs (&S)[D]) {
   int rlo[4], rhi[4];
   float sc[4];
   lane_pairs<B>(L.cq, rlo, rhi, sc);
@@ -182,7 +217,7 @@ __device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L,
     // Past the range the whole quad is idle (zero scale); its pairs come
     // from block blk0 (as its perm entries did).
     const int blk = blk0 + i * KS + L.ks < blk1 ? blk0 + i * KS + L.ks : blk0;
-    compute_step<B, kPerm>(a, R, L.xrow, blk, rlo, rhi, sc, L.magic, yacc);
+    compute_step<B, kPerm, MT>(a, R, L.xrow, L.xstride, blk, rlo, rhi, sc, L.magic, yacc);
   };
   // Steady state: every buffer is refilled on every pass. (A refill under a
   // condition turns the buffers into loop-carried copies, and a copy waits for
@@ -225,22 +260,23 @@ typedef uint32_t piece_t __attribute__((ext_vector_type(4)));   // 16 bytes of t
 // weights; P * WV * 64 * 16 bytes cover the row. D: steps in flight per wave.
 // kPerm: act-order (perm given), a kernel of its own so that the step loop
 // holds no per-pair choice.
-template <int B, int WV, int P, int D, bool kPerm>
+// MT: activation rows, 1, 2 or 4 (rows from M on repeat row M - 1 and are not stored).
+template <int B, int WV, int P, int D, bool kPerm, int MT>
 __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
-  __shared__ float red[WV][4][SC];   // per wave and 16-lane row: the sums of the strip's columns
+  __shared__ float red[WV][4][MT][SC];   // per wave and 16-lane row: the sums of the strip's columns
 
   // Kernel arguments, all read in one batch: the empty asm takes them as
   // operands (and hands them back, so they are not read again later).
   MatPtrs mp = a.mat[blockIdx.y];
-  int K = a.K, N = a.N, spx = a.strips_per_xcd;
+  int K = a.K, N = a.N, M = a.M, spx = a.strips_per_xcd, xw = a.xrow_words;
   const uint16_t* xsrc = a.x;
   Epilogue epi = a.epi;
   {
     const int R = a.runs.packed_rows, bpg = a.bpg_shift, hz = a.has_zeros;
     const int32_t* const perm = a.perm;
-    asm volatile("" : "+s"(K), "+s"(N), "+s"(spx), "+s"(xsrc), "+s"(mp.y), "+s"(epi.bias), "+s"(epi.residual),
-                 "+s"(epi.act)
+    asm volatile("" : "+s"(K), "+s"(N), "+s"(M), "+s"(spx), "+s"(xw), "+s"(xsrc), "+s"(mp.y), "+s"(epi.bias),
+                 "+s"(epi.residual), "+s"(epi.act)
                  : "s"(R), "s"(bpg), "s"(hz), "s"(perm), "s"(mp.qweight), "s"(mp.scales), "s"(mp.zeros));
   }
 
@@ -251,21 +287,26 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   const int strip = (bid % kXcds) * spx + bid / kXcds;
   if (strip * SC >= N) return;  // the whole workgroup leaves together
 
-  // 1. The x row: every piece this thread copies, loaded before anything else.
+  // 1. The x rows: every piece this thread copies, loaded before anything else.
   constexpr int nthr = WV * 64;
   const int n16 = K / 8;
-  const global_ptr<piece_t> xg = as_global<piece_t>(xsrc);
-  piece_t xr[P];
+  piece_t xr[MT][P];
 #pragma unroll
-  for (int u = 0; u < P; ++u) xr[u] = xg[min(u * nthr + tid, n16 - 1)];
+  for (int m = 0; m < MT; ++m) {
+    const global_ptr<piece_t> xg = as_global<piece_t>(xsrc + (size_t)min(m, M - 1) * K);
+#pragma unroll
+    for (int u = 0; u < P; ++u) xr[m][u] = xg[min(u * nthr + tid, n16 - 1)];
+  }
   // The epilogue's operands of this strip's outputs, read now rather than
   // after the final reduction (a residual that is the output itself is read
   // before the same thread writes it). Every thread loads, from y when a term
   // is absent: loads without a branch around them keep the wait before each
   // LDS store below down to that store's own piece.
+  // Thread tid < 16 MT stores output (row tid / 16, column tid % 16).
   const int n_out = min(strip * SC + (tid % SC), N - 1);
+  const int m_out = min(tid / SC, M - 1);
   const uint16_t bias_raw = as_global<uint16_t>(epi.bias ? epi.bias : mp.y)[n_out];
-  const uint16_t res_raw = as_global<uint16_t>(epi.residual ? epi.residual : mp.y)[n_out];
+  const uint16_t res_raw = as_global<uint16_t>(epi.residual ? epi.residual : mp.y)[(size_t)m_out * N + n_out];
   asm volatile("" ::: "memory");   // keep the row loads ahead of the weight loads
 
   // 2. The first D steps of the wave's blocks, issued by every wave (a wave
@@ -284,6 +325,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   L.panel = mp.qweight + (size_t)strip * a.runs.packed_rows * kPanel + L.cq * 4;
   L.psrc = a.perm ? a.perm : reinterpret_cast<const int32_t*>(mp.qweight);   // >= K readable words
   L.xrow = reinterpret_cast<const _Float16*>(lds);
+  L.xstride = xw * 2;
   L.magic = vgpr_magic();
   StepRegs S[D];
   {
@@ -296,52 +338,68 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
     });
   }
 
-  // 3. The row into LDS (clamped threads rewrite the last piece with its own value).
-  piece_t* xl = reinterpret_cast<piece_t*>(lds);
+  // 3. The rows into LDS (clamped threads rewrite the last piece with its own value).
 #pragma unroll
-  for (int u = 0; u < P; ++u) xl[min(u * nthr + tid, n16 - 1)] = xr[u];
+  for (int m = 0; m < MT; ++m) {
+    piece_t* xl = reinterpret_cast<piece_t*>(lds + m * xw);
+#pragma unroll
+    for (int u = 0; u < P; ++u) xl[min(u * nthr + tid, n16 - 1)] = xr[m][u];
+  }
   __syncthreads();
 
   // 4. Stream the wave's blocks.
-  float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (wb0 < wb1) row_steps<B, D, kPerm>(a, L, wb0, wb1, row0, yacc, S);
+  float yacc[4][MT];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) yacc[c][m] = 0.0f;
+  if (wb0 < wb1) row_steps<B, D, kPerm, MT>(a, L, wb0, wb1, row0, yacc, S);
 
   // Reduce over the block slots: the 4 of each 16-lane row with two DPP row
   // shifts (lanes 12..15 of a row end up with its sums, one per column
   // quad), then the 4 rows of each wave and the waves through LDS; the
   // epilogue as apply_epilogue: bias, activation, residual.
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    yacc[c] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yacc[c]), 0x114, 0xF,
-                                                                     0xF, true));   // row_shr:4
-    yacc[c] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yacc[c]), 0x118, 0xF,
-                                                                     0xF, true));   // row_shr:8
-  }
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float v = yacc[c][m];
+      v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF,
+                                                                 true));   // row_shr:4
+      v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF,
+                                                                 true));   // row_shr:8
+      yacc[c][m] = v;
+    }
   if ((lane & 15) >= 12) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) red[wave][lane >> 4][L.cq * 4 + c] = yacc[c];
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) red[wave][lane >> 4][m][L.cq * 4 + c] = yacc[c][m];
   }
   __syncthreads();
-  if (tid < SC && strip * SC + tid < N) {
+  const int c_out = tid % SC;
+  if (tid < SC * MT && tid / SC < M && strip * SC + c_out < N) {
+    const int m = tid / SC;
     float v = 0.0f;
 #pragma unroll
     for (int w = 0; w < WV; ++w)
 #pragma unroll
-      for (int row = 0; row < 4; ++row) v += red[w][row][tid];
+      for (int row = 0; row < 4; ++row) v += red[w][row][m][c_out];
     if (epi.bias) v += (float)__builtin_bit_cast(_Float16, bias_raw);
     if (epi.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
     if (epi.residual) v += (float)__builtin_bit_cast(_Float16, res_raw);
-    ((__attribute__((address_space(1))) uint16_t*)mp.y)[strip * SC + tid] = __builtin_bit_cast(uint16_t, (_Float16)v);
+    ((__attribute__((address_space(1))) uint16_t*)mp.y)[(size_t)m * N + strip * SC + c_out] =
+        __builtin_bit_cast(uint16_t, (_Float16)v);
   }
 }
 
-template <int B, int WV, int P, int D>
+template <int B, int WV, int P, int D, int MT>
 hipError_t launch_row(StreamArgs a, hipStream_t stream) {
-  const auto kernel = a.perm ? qgemv_row_kernel<B, WV, P, D, true> : qgemv_row_kernel<B, WV, P, D, false>;
+  const auto kernel = a.perm ? qgemv_row_kernel<B, WV, P, D, true, MT> : qgemv_row_kernel<B, WV, P, D, false, MT>;
   a.nstrips = (a.N + SC - 1) / SC;
   a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
   a.xrow_words = row_words(a.K);
-  const size_t lds = (size_t)a.xrow_words * 4;
+  const size_t lds = (size_t)MT * a.xrow_words * 4;
   hipLaunchKernelGGL(kernel, dim3(kXcds * a.strips_per_xcd, a.mats), dim3(WV * 64), lds, stream, a);
   return hipGetLastError();
 }
@@ -362,13 +420,26 @@ static_assert(kRowPiecesMax * kRowWaves * 64 * 16 >= kRowLdsBudget, "x-row piece
 // (11008 -> 4096: 9.1 vs 8.3 us), so every shape keeps two.
 constexpr int kRowDepth = 2;
 
+// MT rows: the pieces per thread that cover K (MT x rows must fit the LDS
+// budget, which single_row() checks: 2 rows need at most 8 pieces, 4 rows 4).
+template <int B, int MT>
+hipError_t launch_row_mt(const StreamArgs& a, hipStream_t stream) {
+  constexpr int per_piece = kRowWaves * 64 * 8;   // x values per piece index
+  if (a.K <= 2 * per_piece) return launch_row<B, kRowWaves, 2, kRowDepth, MT>(a, stream);
+  if (a.K <= 4 * per_piece) return launch_row<B, kRowWaves, 4, kRowDepth, MT>(a, stream);
+  if constexpr (MT <= 2) {
+    if (a.K <= 8 * per_piece) return launch_row<B, kRowWaves, 8, kRowDepth, MT>(a, stream);
+  }
+  if constexpr (MT == 1) return launch_row<B, kRowWaves, kRowPiecesMax, kRowDepth, 1>(a, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int B>
 hipError_t launch_row_width(const StreamArgs& a, hipStream_t stream) {
-  constexpr int per_piece = kRowWaves * 64 * 8;   // x values per piece index
-  if (a.K <= 2 * per_piece) return launch_row<B, kRowWaves, 2, kRowDepth>(a, stream);
-  if (a.K <= 4 * per_piece) return launch_row<B, kRowWaves, 4, kRowDepth>(a, stream);
-  if (a.K <= 8 * per_piece) return launch_row<B, kRowWaves, 8, kRowDepth>(a, stream);
-  return launch_row<B, kRowWaves, kRowPiecesMax, kRowDepth>(a, stream);
+  const int mt = row_mt(a.M);
+  if (mt == 1) return launch_row_mt<B, 1>(a, stream);
+  if (mt == 2) return launch_row_mt<B, 2>(a, stream);
+  return launch_row_mt<B, 4>(a, stream);
 }
 
 // Instantiated in qgemv_row.hip: `set` holds exactly one code width.

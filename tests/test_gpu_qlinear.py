@@ -62,6 +62,25 @@ def test_one_hot_rows_are_exact(op, zeros):
     assert np.array_equal(got.astype(np.float32), want.astype(np.float32))
 
 
+@pytest.mark.parametrize("M", (1, 2, 3, 4))
+@pytest.mark.parametrize("zeros", (True, False))
+def test_one_hot_rows_are_exact_single_row_kernel(M, zeros):
+    """The same bit-exact probe through the single-row kernel (one code width,
+    1 to 4 rows): its factored form s * (acc - 1024 X' - z X) recovers q - z
+    exactly for a single non-zero activation, and rounds s * (q - z) once."""
+    say(f"one-hot single-row kernel M={M} zeros={zeros}")
+    inp = _mixed_inputs([4] * 11, 32, 520, M, seed=6 + M, zeros=zeros)
+    K = inp.spec.K
+    lay = GpuLayer(inp)
+    ks = np.random.default_rng(10 + M).choice(K, M, replace=False)
+    x = np.zeros((M, K), np.float16)
+    x[np.arange(M), ks] = 1.0
+    y = lay.qgemv(x)
+    w16 = oracle.dequant_fp16(inp.q, inp.scales, inp.zeros, inp.bits, 32)
+    want = w16[np.argsort(inp.perm)[ks]]
+    assert np.array_equal(y.cpu().numpy().astype(np.float32), want.astype(np.float32))
+
+
 # ------------------------------------------------------------------ small ragged shapes
 
 @pytest.mark.parametrize("M", (1, 2, 3, 5, 8, 13, 16))
@@ -131,6 +150,19 @@ def test_qgemv_row_kernel_steps(b, nblk):
     inp = _mixed_inputs([b] * nblk, 32, 48, 1, seed=b * 1000 + nblk, zeros=True)
     y = GpuLayer(inp).qgemv(inp.x)
     assert_close(y, _ref(inp), f"qgemv row b={b} blocks={nblk}")
+
+
+@pytest.mark.parametrize("M", (2, 3, 4))
+@pytest.mark.parametrize("nblk", (3, 100, 192, 320))
+@pytest.mark.parametrize("b", (2, 3, 4, 5, 6, 8))
+def test_qgemv_row_kernel_rows(b, nblk, M):
+    """2 to 4 rows through the single-row kernel's multi-row instances (2 or
+    4 x rows in LDS, 3 rows on the 4-row instance with the last row unused):
+    waves without blocks, ragged splits, the steady loop and its tails."""
+    say(f"qgemv row kernel b={b} blocks={nblk} M={M}")
+    inp = _mixed_inputs([b] * nblk, 32, 48, M, seed=b * 1000 + nblk * 7 + M, zeros=True)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv row b={b} blocks={nblk} M={M}")
 
 
 @pytest.mark.parametrize("K", (16384, 16416, 28672, 31744))
@@ -311,12 +343,13 @@ def test_grouped_qgemv_max_group_full_size():
 
 @pytest.mark.parametrize("op,bits,M,exact", [
     ("qgemv", [4] * 11, 1, False),        # single-row kernel (factored arithmetic)
+    ("qgemv", [4] * 11, 4, False),        # single-row kernel, 4 rows
     ("qgemv", MIXED_BITS, 1, False),      # gather + multi-row VALU kernel
     ("qgemv", MIXED_BITS, 2, False),      # multi-row VALU kernel
     ("qgemv", MIXED_BITS, 8, True),       # MFMA decode kernel (exact dequantization)
     ("qgemm", MIXED_BITS, 64, True),      # prefill, several widths
     ("qgemm", [4] * 11, 64, True),        # prefill, one width
-], ids=["row", "gather-valu-M1", "valu-M2", "mfma-M8", "qgemm-mixed", "qgemm-4bit"])
+], ids=["row", "row-M4", "gather-valu-M1", "valu-M2", "mfma-M8", "qgemm-mixed", "qgemm-4bit"])
 def test_nonfinite_activations(op, bits, M, exact):
     """A NaN activation makes its whole output row NaN; an Inf activation makes
     every column of its row non-finite (exact-dequant kernels: the IEEE result
@@ -348,6 +381,7 @@ def test_nonfinite_activations(op, bits, M, exact):
 
 EPILOGUE_PATHS = [
     ("qgemv", [4] * 11, 1),        # single-row kernel
+    ("qgemv", [4] * 11, 3),        # single-row kernel, 4-row instance
     ("qgemv", MIXED_BITS, 1),      # gather + multi-row VALU kernel
     ("qgemv", MIXED_BITS, 2),      # multi-row VALU kernel
     ("qgemv", [4] * 11, 5),        # MFMA decode kernel
@@ -359,7 +393,7 @@ EPILOGUE_PATHS = [
 
 
 @pytest.mark.parametrize("op,bits,M", EPILOGUE_PATHS,
-                         ids=["row", "gather-valu-M1", "valu-M2", "mfma-M5", "mfma-M16", "qgemm", "qgemm-mixed",
+                         ids=["row", "row-M3", "gather-valu-M1", "valu-M2", "mfma-M5", "mfma-M16", "qgemm", "qgemm-mixed",
                               "qgemm-runs"])
 @pytest.mark.parametrize("terms", ["bias", "residual", "bias-silu-residual", "silu-inplace-residual"])
 def test_fused_epilogue(op, bits, M, terms):

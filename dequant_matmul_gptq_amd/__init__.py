@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     QlinearError,
     dequant,
     lib,
+    lora_delta,
+    lora_workspace_bytes,
     pack_weights,
     qgemm,
     qgemm_workspace_bytes,

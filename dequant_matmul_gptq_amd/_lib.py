@@ -42,6 +42,8 @@ EXPORTS = (
     "qlinear_qgemm",
     "qlinear_qgemv_fused",
     "qlinear_qgemm_fused",
+    "qlinear_lora_workspace_bytes",
+    "qlinear_lora_delta",
 )
 
 ACT_NONE = 0
@@ -74,6 +76,7 @@ class qlinear_epilogue(ctypes.Structure):
         ("bias", ctypes.c_void_p),
         ("residual", ctypes.c_void_p),
         ("activation", ctypes.c_int32),
+        ("addend", ctypes.c_void_p),
     ]
 
 
@@ -105,6 +108,8 @@ def lib() -> ctypes.CDLL:
         ep = ctypes.POINTER(qlinear_epilogue)
         L.qlinear_qgemv_fused.argtypes = [lp, vp, i32, vp, vp, vp, vp, ep, vp, vp, sz, vp]
         L.qlinear_qgemm_fused.argtypes = [lp, vp, i32, vp, vp, vp, vp, ep, vp, vp, sz, vp]
+        L.qlinear_lora_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.qlinear_lora_delta.argtypes = [vp, i32, i32, vp, i32, vp, i32, ctypes.c_float, i32, vp, vp, sz, vp]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -224,27 +229,30 @@ def _gemm_operands(layout, x, qweight, scales, zeros, perm, y):
     return M, y
 
 
-def _epilogue(layout, M, y, bias, residual, activation):
+def _epilogue(layout, M, y, bias, residual, activation, addend=None):
     """The qlinear_epilogue of a fused call, or None for the plain call."""
-    if bias is None and residual is None and activation == ACT_NONE:
+    if bias is None and residual is None and activation == ACT_NONE and addend is None:
         return None
     if bias is not None:
         _dev(bias, "bias", torch.float16, (layout.N,))
     if residual is not None:
         _dev(residual, "residual", torch.float16, (M, layout.N))
-    return qlinear_epilogue(_ptr(bias), _ptr(residual), int(activation))
+    if addend is not None:
+        _dev(addend, "addend", torch.float32, (M, layout.N))
+    return qlinear_epilogue(_ptr(bias), _ptr(residual), int(activation), _ptr(addend))
 
 
 def qgemv(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
           zeros: torch.Tensor | None, perm: torch.Tensor | None, workspace: torch.Tensor,
           y: torch.Tensor | None = None, bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
-          activation: int = ACT_NONE) -> torch.Tensor:
+          activation: int = ACT_NONE, addend: torch.Tensor | None = None) -> torch.Tensor:
     """Decode layer, M = x.shape[0] <= 16. Returns y float16 [M][N]. With bias
-    [N], residual [M][N] (may be y) or activation ACT_SILU the fused call runs:
-    y = RNE(act(x W + bias) + residual)."""
+    [N], residual [M][N] (may be y), activation ACT_SILU or addend float32
+    [M][N] (e.g. from lora_delta) the fused call runs:
+    y = RNE(act(x W + addend + bias) + residual)."""
     M, y = _gemm_operands(layout, x, qweight, scales, zeros, perm, y)
     _dev(workspace, "workspace", torch.uint8)
-    epi = _epilogue(layout, M, y, bias, residual, activation)
+    epi = _epilogue(layout, M, y, bias, residual, activation, addend)
     if epi is None:
         _check(lib().qlinear_qgemv(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
                                    _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemv")
@@ -284,14 +292,14 @@ def qgemv_grouped(layout: Layout, x: torch.Tensor, qweights, scales, zeros, perm
 def qgemm(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
           zeros: torch.Tensor | None, perm: torch.Tensor | None, workspace: torch.Tensor | None = None,
           y: torch.Tensor | None = None, bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
-          activation: int = ACT_NONE) -> torch.Tensor:
+          activation: int = ACT_NONE, addend: torch.Tensor | None = None) -> torch.Tensor:
     """Prefill layer, any M. Returns y float16 [M][N]; epilogue as for qgemv."""
     M, y = _gemm_operands(layout, x, qweight, scales, zeros, perm, y)
     need = qgemm_workspace_bytes(layout, M)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _dev(workspace, "workspace", torch.uint8)
-    epi = _epilogue(layout, M, y, bias, residual, activation)
+    epi = _epilogue(layout, M, y, bias, residual, activation, addend)
     if epi is None:
         _check(lib().qlinear_qgemm(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(perm),
                                    _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemm")
@@ -300,3 +308,39 @@ def qgemm(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.
                                          _ptr(perm), ctypes.byref(epi), _ptr(y), _ptr(workspace), workspace.numel(),
                                          _stream(x.device)), "qlinear_qgemm_fused")
     return y
+
+
+def lora_workspace_bytes(M: int, K: int, rank: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().qlinear_lora_workspace_bytes(int(M), int(K), int(rank), ctypes.byref(n)),
+           "qlinear_lora_workspace_bytes")
+    return n.value
+
+
+def lora_delta(x: torch.Tensor, lora_a: torch.Tensor, lora_b: torch.Tensor, scale: float = 1.0,
+               delta: torch.Tensor | None = None, accumulate: bool = False,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """On-the-fly LoRA update delta (+)= scale (x A) B, float32 [M][N], from x
+    float16 [M][K] (original feature order), A float16 [K][r], B float16
+    [r][N]. Pass the result as `addend` of qgemv/qgemm; accumulate=True adds
+    a further adapter into delta."""
+    if x.dim() != 2 or lora_a.dim() != 2 or lora_b.dim() != 2:
+        raise ValueError("x, lora_a and lora_b must be 2-D")
+    M, K = (int(v) for v in x.shape)
+    rank = int(lora_a.shape[1])
+    N = int(lora_b.shape[1])
+    _dev(x, "x", torch.float16)
+    _dev(lora_a, "lora_a", torch.float16, (K, rank))
+    _dev(lora_b, "lora_b", torch.float16, (rank, N))
+    if delta is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs the delta to add to")
+        delta = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _dev(delta, "delta", torch.float32, (M, N))
+    if workspace is None:
+        workspace = torch.empty(max(lora_workspace_bytes(M, K, rank), 256), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    _check(lib().qlinear_lora_delta(_ptr(x), M, K, _ptr(lora_a), rank, _ptr(lora_b), N, float(scale),
+                                    1 if accumulate else 0, _ptr(delta), _ptr(workspace), workspace.numel(),
+                                    _stream(x.device)), "qlinear_lora_delta")
+    return delta

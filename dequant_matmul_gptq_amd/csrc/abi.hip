@@ -80,11 +80,13 @@ int check_gemm_operands(const qlinear_layout* layout, const uint16_t* x, int32_t
 
 // The epilogue of a fused call (NULL: none).
 int check_epilogue(const qlinear_epilogue* e, Epilogue& out) {
-  out = Epilogue{nullptr, nullptr, QLINEAR_ACT_NONE};
+  out = Epilogue{nullptr, nullptr, QLINEAR_ACT_NONE, nullptr};
   if (!e) return QLINEAR_OK;
   if (e->activation != QLINEAR_ACT_NONE && e->activation != QLINEAR_ACT_SILU) return QLINEAR_ERR_UNSUPPORTED;
-  if ((e->bias && !aligned16(e->bias)) || (e->residual && !aligned16(e->residual))) return QLINEAR_ERR_MISALIGNED;
-  out = Epilogue{e->bias, e->residual, e->activation};
+  if ((e->bias && !aligned16(e->bias)) || (e->residual && !aligned16(e->residual)) ||
+      (e->addend && !aligned16(e->addend)))
+    return QLINEAR_ERR_MISALIGNED;
+  out = Epilogue{e->bias, e->residual, e->activation, e->addend};
   return QLINEAR_OK;
 }
 
@@ -217,7 +219,7 @@ int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32
   if (M > QLINEAR_GEMV_MAX_M || (M > 2 && !qgemv_mfma_supported(*layout))) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
   return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, count, qweights_host, scales_host,
-                                 zeros ? zeros_host : nullptr, y_host, workspace, Epilogue{nullptr, nullptr, 0},
+                                 zeros ? zeros_host : nullptr, y_host, workspace, Epilogue{nullptr, nullptr, 0, nullptr},
                                  (hipStream_t)stream));
 }
 
@@ -249,6 +251,28 @@ int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M, co
                   void* workspace, size_t workspace_bytes, void* stream) {
   return qlinear_qgemm_fused(layout, x, M, qweight, scales, zeros, perm, nullptr, y, workspace, workspace_bytes,
                              stream);
+}
+
+int qlinear_lora_workspace_bytes(int32_t M, int32_t K, int32_t rank, size_t* bytes) {
+  if (!bytes || M < 0 || K < 1 || rank < 1) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (rank > QLINEAR_LORA_MAX_RANK || K > QLINEAR_LORA_MAX_DIM) return QLINEAR_ERR_UNSUPPORTED;
+  *bytes = lora_workspace_bytes(M, K, rank);
+  return QLINEAR_OK;
+}
+
+int qlinear_lora_delta(const uint16_t* x, int32_t M, int32_t K, const uint16_t* lora_a, int32_t rank,
+                       const uint16_t* lora_b, int32_t N, float scale, int32_t accumulate, float* delta,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || K < 1 || N < 1 || rank < 1) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (rank > QLINEAR_LORA_MAX_RANK || K > QLINEAR_LORA_MAX_DIM || N > QLINEAR_LORA_MAX_DIM)
+    return QLINEAR_ERR_UNSUPPORTED;
+  if (M == 0) return QLINEAR_OK;
+  if (!x || !lora_a || !lora_b || !delta) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < lora_workspace_bytes(M, K, rank)) return QLINEAR_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(lora_a) || !aligned16(lora_b) || !aligned16(delta) || !aligned16(workspace))
+    return QLINEAR_ERR_MISALIGNED;
+  return hip_status(launch_lora_delta(x, M, K, lora_a, rank, lora_b, N, scale, accumulate != 0, delta, workspace,
+                                      (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,5 +1,7 @@
-// Single-row decode kernel (M = 1) on gfx950: the act-order gather happens
-// inside the kernel, so a call is one launch.
+// Single-launch decode kernel (M = 1 to 4) on gfx950: the act-order gather
+// happens inside the kernel, so a call is one launch. For M > 1 the x rows
+// (1, 2 or 4 of them) all sit in LDS and each weight pair, once unpacked, is
+// used for every row.
 //
 // Work split as in the multi-row kernel: a workgroup of 4 waves owns a
 // 16-column panel and the whole K range; lane = (block slot ks, column quad
@@ -30,15 +32,17 @@ constexpr int kRowLdsBudget = 62 * 1024;  // bytes of LDS for the x row
 // LDS words of the x row (K float16, rounded up to 16 bytes).
 __host__ __device__ constexpr int row_words(int K) { return (K / 2 + 3) / 4 * 4; }
 
-// Whether a single-row call runs the single-row kernel: the x row must fit
-// in LDS, and the matrix must have a single code width. (Measured on MI355X:
-// a version of this kernel that streams several widths, run segment by run
-// segment, needs 205-256 VGPRs for the width sets of EXL2 layouts, and the
-// gather kernel plus the multi-row kernel stay faster: EXL2 4.0 bpw
-// 4096 -> 11008: 16.8 vs 20.0 us; 2.5 bpw 8192 -> 28672: 31.5 vs 38.3 us.)
 // Activation rows of the kernel instance for M rows: 1, 2 or 4.
 constexpr int row_mt(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 
+// Whether a call of M <= 4 rows runs this kernel: the x rows must fit in the
+// LDS budget, and the matrix must have a single code width. (Measured on
+// MI355X: a version of this kernel that streams several widths, run segment
+// by run segment, needs 205-256 VGPRs for the width sets of EXL2 layouts, and
+// the gather kernel plus the multi-row kernel stay faster: EXL2 4.0 bpw
+// 4096 -> 11008: 16.8 vs 20.0 us; 2.5 bpw 8192 -> 28672: 31.5 vs 38.3 us.)
+// The budget is below the 160 KB a workgroup may hold because the rows are
+// staged through registers: 4 rows of K = 11008 would need 128 VGPRs.
 inline bool single_row(int M, int K, unsigned set) {
   return M <= 4 && (size_t)row_mt(M) * row_words(K) * 4 <= kRowLdsBudget && (set & (set - 1)) == 0;
 }
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
     const int R = a.runs.packed_rows, bpg = a.bpg_shift, hz = a.has_zeros;
     const int32_t* const perm = a.perm;
     asm volatile("" : "+s"(K), "+s"(N), "+s"(M), "+s"(spx), "+s"(xw), "+s"(xsrc), "+s"(mp.y), "+s"(epi.bias),
-                 "+s"(epi.residual), "+s"(epi.act)
+                 "+s"(epi.residual), "+s"(epi.act), "+s"(epi.addend)
                  : "s"(R), "s"(bpg), "s"(hz), "s"(perm), "s"(mp.qweight), "s"(mp.scales), "s"(mp.zeros));
   }
 
@@ -299,14 +303,17 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   }
   // The epilogue's operands of this strip's outputs, read now rather than
   // after the final reduction (a residual that is the output itself is read
-  // before the same thread writes it). Every thread loads, from y when a term
-  // is absent: loads without a branch around them keep the wait before each
-  // LDS store below down to that store's own piece.
+  // before the same thread writes it). Every thread loads, from y (or the
+  // first packed word) when a term is absent: loads without a branch around
+  // them keep the wait before each LDS store below down to that store's own
+  // piece.
   // Thread tid < 16 MT stores output (row tid / 16, column tid % 16).
   const int n_out = min(strip * SC + (tid % SC), N - 1);
   const int m_out = min(tid / SC, M - 1);
   const uint16_t bias_raw = as_global<uint16_t>(epi.bias ? epi.bias : mp.y)[n_out];
   const uint16_t res_raw = as_global<uint16_t>(epi.residual ? epi.residual : mp.y)[(size_t)m_out * N + n_out];
+  const float add_val = epi.addend ? as_global<float>(epi.addend)[(size_t)m_out * N + n_out]
+                                   : as_global<float>(reinterpret_cast<const float*>(mp.qweight))[0];
   asm volatile("" ::: "memory");   // keep the row loads ahead of the weight loads
 
   // 2. The first D steps of the wave's blocks, issued by every wave (a wave
@@ -358,7 +365,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   // Reduce over the block slots: the 4 of each 16-lane row with two DPP row
   // shifts (lanes 12..15 of a row end up with its sums, one per column
   // quad), then the 4 rows of each wave and the waves through LDS; the
-  // epilogue as apply_epilogue: bias, activation, residual.
+  // epilogue as apply_epilogue: addend, bias, activation, residual.
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -385,6 +392,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
     for (int w = 0; w < WV; ++w)
 #pragma unroll
       for (int row = 0; row < 4; ++row) v += red[w][row][m][c_out];
+    if (epi.addend) v += add_val;
     if (epi.bias) v += (float)__builtin_bit_cast(_Float16, bias_raw);
     if (epi.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
     if (epi.residual) v += (float)__builtin_bit_cast(_Float16, res_raw);

@@ -180,7 +180,8 @@ __global__ __launch_bounds__(kWaves * 64) void qgemv_mfma_kernel(MfmaArgs a) {
   Epilogue epi = a.epi;
   asm volatile("" : "+s"(mp.qweight), "+s"(mp.scales), "+s"(mp.zeros), "+s"(mp.y), "+s"(spx), "+s"(nstrips),
                "+s"(M), "+s"(K), "+s"(N), "+s"(R), "+s"(xq_bytes), "+s"(scale_bytes), "+s"(has_zeros),
-               "+s"(packed_words), "+s"(xq), "+s"(epi.bias), "+s"(epi.residual), "+s"(epi.act)
+               "+s"(packed_words), "+s"(xq), "+s"(epi.bias), "+s"(epi.residual), "+s"(epi.act),
+               "+s"(epi.addend)
                : "s"(a.runs.blocks_per_group));
 
   const int tid = threadIdx.x;

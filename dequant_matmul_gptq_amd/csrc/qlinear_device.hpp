@@ -29,12 +29,15 @@ struct Epilogue {
   const uint16_t* bias;       // float16 [N] or NULL
   const uint16_t* residual;   // float16 [M][N] or NULL (may be the output itself)
   int act;                    // QLINEAR_ACT_NONE or QLINEAR_ACT_SILU
+  const float* addend;        // float32 [M][N] or NULL (e.g. a LoRA update)
 };
 
-// bias and residual are device (global) memory: read as such, also where the
-// kernel has passed the pointers through registers the compiler cannot see.
+// y = act(v + addend + bias) + residual. The operands are device (global)
+// memory: read as such, also where the kernel has passed the pointers through
+// registers the compiler cannot see.
 __device__ __forceinline__ float apply_epilogue(const Epilogue& e, float v, int m, int n, int N) {
   typedef const __attribute__((address_space(1))) uint16_t* gptr;
+  if (e.addend) v += ((const __attribute__((address_space(1))) float*)e.addend)[(size_t)m * N + n];
   if (e.bias) v += (float)__builtin_bit_cast(_Float16, ((gptr)e.bias)[n]);
   if (e.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
   if (e.residual) v += (float)__builtin_bit_cast(_Float16, ((gptr)e.residual)[(size_t)m * N + n]);

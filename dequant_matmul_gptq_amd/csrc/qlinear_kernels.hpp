@@ -71,4 +71,11 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, void* ws, const Epilogue& epi, hipStream_t stream);
 
+// On-the-fly LoRA update delta (+)= scale (x A) B. The workspace holds the
+// partial sums of x A, float32 [lora_chunks(K)][M][rank].
+int lora_chunks(int K);
+size_t lora_workspace_bytes(int M, int K, int rank);
+hipError_t launch_lora_delta(const uint16_t* x, int M, int K, const uint16_t* A, int rank, const uint16_t* B, int N,
+                             float scale, bool accumulate, float* delta, void* ws, hipStream_t stream);
+
 }  // namespace qlinear

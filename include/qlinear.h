@@ -219,24 +219,27 @@ int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M,
  * kernels fuse into the matmul (ExLlamaV2 project page: scaling, addition,
  * activation), applied in float32 to each output before its float16
  * rounding:
- *   y[m][n] = RNE_fp16( act(acc[m][n] + bias[n]) + residual[m][n] )
+ *   y[m][n] = RNE_fp16( act(acc[m][n] + addend[m][n] + bias[n]) + residual[m][n] )
  * where acc is the float32 sum of the plain calls.
  *   bias       : float16 [N], or NULL
  *   residual   : float16 [M][N], or NULL; it may be y itself (in place)
  *   activation : QLINEAR_ACT_NONE or QLINEAR_ACT_SILU
+ *   addend     : float32 [M][N], or NULL: a term of the layer's own output,
+ *                such as the on-the-fly LoRA update of qlinear_lora_delta
  * HOST struct, read during the call only.
  */
 typedef struct qlinear_epilogue {
   const uint16_t* bias;
   const uint16_t* residual;
   int32_t activation;
+  const float* addend;
 } qlinear_epilogue;
 
 /*
  * qlinear_qgemv and qlinear_qgemm with an output epilogue (NULL = none, the
  * plain call). Same arguments and errors as the plain calls; also
- * UNSUPPORTED for an unknown activation, MISALIGNED for a bias or residual
- * that is not 16-byte aligned.
+ * UNSUPPORTED for an unknown activation, MISALIGNED for a bias, residual or
+ * addend that is not 16-byte aligned.
  */
 int qlinear_qgemv_fused(const qlinear_layout* layout, const uint16_t* x, int32_t M,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
@@ -246,6 +249,37 @@ int qlinear_qgemm_fused(const qlinear_layout* layout, const uint16_t* x, int32_t
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, const qlinear_epilogue* epilogue, uint16_t* y,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * On-the-fly LoRA update of a linear layer (ExLlamaV2 project page, LoRA
+ * adapters: the low-rank pair A, B is applied during the forward pass
+ * instead of being merged into the weights, and several adapters combine
+ * with weights):
+ *   delta[m][n] = scale * sum_j (sum_k x[m][k] * A[k][j]) * B[j][n]      (accumulate == 0)
+ *   delta[m][n] += that                                                  (accumulate != 0)
+ * computed with float32 products and sums (x A first, then times B). Pass
+ * delta as qlinear_epilogue.addend so that the update joins the layer's sum
+ * before bias, activation and the one float16 rounding; call again with
+ * accumulate != 0 for each further adapter.
+ *   x      : float16 [M][K], the layer's input in its original feature order
+ *            (the adapter multiplies x itself, not the act-order gather)
+ *   lora_a : float16 [K][rank];  lora_b : float16 [rank][N]
+ *   rank   : 1 .. QLINEAR_LORA_MAX_RANK
+ *   delta  : float32 [M][N], written (or added to)
+ *   workspace : device scratch of qlinear_lora_workspace_bytes(M, K, rank)
+ *            bytes (partial sums of x A); contents not preserved
+ * M == 0 is a no-op. Errors: INVALID_ARGUMENT for M < 0, K < 1, N < 1, rank
+ * < 1 or a NULL pointer (M > 0); UNSUPPORTED for rank above
+ * QLINEAR_LORA_MAX_RANK or K or N above QLINEAR_LORA_MAX_DIM; MISALIGNED as
+ * for the other calls; WORKSPACE for a workspace that is missing or too
+ * small.
+ */
+#define QLINEAR_LORA_MAX_RANK 64
+#define QLINEAR_LORA_MAX_DIM (65535 * 256) /* largest K and N */
+int qlinear_lora_workspace_bytes(int32_t M, int32_t K, int32_t rank, size_t* bytes);
+int qlinear_lora_delta(const uint16_t* x, int32_t M, int32_t K, const uint16_t* lora_a, int32_t rank,
+                       const uint16_t* lora_b, int32_t N, float scale, int32_t accumulate, float* delta,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

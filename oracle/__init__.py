@@ -16,6 +16,8 @@ Every function follows the pages' description of the method:
   (ExLlamaV2 blog, "How the Fused CUDA Kernel Works").
 * The fused output epilogue: bias, activation, residual (ExLlamaV2 artifact
   page, GPTQ paragraph: kernels fuse scaling, addition and activation).
+* The on-the-fly LoRA update, joined to the epilogue as an addend (ExLlamaV2
+  artifact page, LoRA adapters).
 """
 
 from .qlinear_oracle import (  # noqa: F401
@@ -39,4 +41,5 @@ from .qlinear_oracle import (  # noqa: F401
     ACT_SILU,
     silu,
     apply_epilogue,
+    lora_delta,
 )

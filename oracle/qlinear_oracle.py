@@ -23,8 +23,9 @@ gs rows per group, G = K / gs groups, b_g the bit width of group g):
    per-group scaling).
 4. ``y[m][n] = sum_j x[m][perm[j]] * w[j][n]``: the fused matmul of the blog's
    sketch, here computed exactly in float64 (no float16 rounding of w or y).
-5. Optionally the fused epilogue ``act(y + bias) + residual`` (see
-   :func:`apply_epilogue`).
+5. Optionally the fused epilogue ``act(y + addend + bias) + residual`` (see
+   :func:`apply_epilogue`), where the addend may be the on-the-fly LoRA
+   update of :func:`lora_delta`.
 
 Parity unpinned: nothing here. Every function is pinned by tests that do not
 re-use its formula (see ``tests/test_oracle_pins.py``).
@@ -328,8 +329,10 @@ def qlinear_bruteforce(x, q, scales, zeros, bits, gs: int, perm=None) -> np.ndar
 # and activation into one call. Reading (the pages name neither the terms nor
 # the activation): addition is a per-output bias and a residual, the
 # activation is SiLU (the Llama MLP's), and the order is that of a layer
-# followed by its activation and then the residual stream:
-#   y[m][n] = act(acc[m][n] + bias[n]) + residual[m][n]
+# followed by its activation and then the residual stream. A float32 addend
+# (the LoRA update below) is part of the layer's own output, so it joins acc
+# before the bias:
+#   y[m][n] = act(acc[m][n] + addend[m][n] + bias[n]) + residual[m][n]
 
 ACT_NONE = 0
 ACT_SILU = 1
@@ -342,10 +345,13 @@ def silu(v) -> np.ndarray:
         return v / (1.0 + np.exp(-v))
 
 
-def apply_epilogue(acc, bias=None, residual=None, activation: int = ACT_NONE) -> np.ndarray:
-    """The fused epilogue on float64 layer outputs acc [M][N]; bias [N] and
-    residual [M][N] are float16 or float64 (None: absent)."""
+def apply_epilogue(acc, bias=None, residual=None, activation: int = ACT_NONE, addend=None) -> np.ndarray:
+    """The fused epilogue on float64 layer outputs acc [M][N]; bias [N],
+    residual [M][N] and addend [M][N] are float16, float32 or float64 (None:
+    absent)."""
     y = np.asarray(acc, np.float64).copy()
+    if addend is not None:
+        y = y + np.asarray(addend, np.float64)
     if bias is not None:
         y = y + np.asarray(bias, np.float64)[None, :]
     if activation == ACT_SILU:
@@ -355,3 +361,28 @@ def apply_epilogue(acc, bias=None, residual=None, activation: int = ACT_NONE) ->
     if residual is not None:
         y = y + np.asarray(residual, np.float64)
     return y
+
+
+# ---------------------------------------------------------------- LoRA
+#
+# The artifact page lists LoRA adapters among the capabilities: an adapter is
+# a low-rank pair A [K][r], B [r][N] whose product updates the layer's
+# weights, either merged into them before inference or applied on the fly in
+# the forward pass; several adapters combine with weights. Reading: applied
+# on the fly, adapter i with weight s_i adds s_i (x A_i) B_i to the layer's
+# output, x in its original feature order (the adapter belongs to the
+# unquantized layer, which knows nothing of the act-order permutation). Since
+# x (W + s A B) = x W + s (x A) B, this is the merged layer's output.
+
+def lora_delta(x, adapters) -> np.ndarray:
+    """sum_i s_i (x A_i) B_i in float64. x [M][K]; adapters: a sequence of
+    (A [K][r], B [r][N], s)."""
+    x = np.asarray(x, np.float64)
+    out = None
+    for A, B, s in adapters:
+        t = x @ np.asarray(A, np.float64)                 # [M][r], the down-projection
+        d = float(s) * (t @ np.asarray(B, np.float64))    # [M][N], the up-projection
+        out = d if out is None else out + d
+    if out is None:
+        raise ValueError("at least one adapter")
+    return out

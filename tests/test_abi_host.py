@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = dq.lib()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     assert sorted(names) == sorted(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -175,8 +175,46 @@ def test_fused_epilogue_validation_before_launch():
         assert call(E(None, None, 7)) == _lib.ERR_UNSUPPORTED               # unknown activation
         assert call(E(FAKE + 2, None, 0)) == _lib.ERR_MISALIGNED             # bias
         assert call(E(None, FAKE + 8, 0)) == _lib.ERR_MISALIGNED             # residual
+        assert call(E(None, None, 0, FAKE + 4)) == _lib.ERR_MISALIGNED       # addend
+        assert call(E(None, None, 0, FAKE)) == _lib.OK
         assert call(E(None, None, 0), M=1, y=None) == _lib.ERR_INVALID_ARGUMENT   # operands still checked
         assert call(E(None, None, 0), M=17 if fn is lib.qlinear_qgemv_fused else -1) != _lib.OK
+
+
+def test_epilogue_struct_layout():
+    # bias, residual, activation (padded to 8), addend
+    assert ctypes.sizeof(_lib.qlinear_epilogue) == 32
+    assert _lib.qlinear_epilogue.addend.offset == 24
+
+
+def test_lora_validation_before_launch():
+    lib = dq.lib()
+    K, N, r = 4096, 11008, 16
+    need = dq.lora_workspace_bytes(5, K, r)
+    assert need == 16 * 5 * r * 4                       # float32 partial sums [K / 256][M][rank]
+    assert dq.lora_workspace_bytes(0, K, r) == 0
+
+    def call(x=FAKE, M=5, K=K, a=FAKE, rank=r, b=FAKE, N=N, d=FAKE, ws=FAKE, wsb=need):
+        return lib.qlinear_lora_delta(x, M, K, a, rank, b, N, 0.5, 0, d, ws, wsb, None)
+
+    # every call below is rejected before any launch (the pointers are fake)
+    assert call(M=-1) == _lib.ERR_INVALID_ARGUMENT
+    assert call(K=0) == _lib.ERR_INVALID_ARGUMENT
+    assert call(N=0) == _lib.ERR_INVALID_ARGUMENT
+    assert call(rank=0) == _lib.ERR_INVALID_ARGUMENT
+    assert call(rank=65) == _lib.ERR_UNSUPPORTED
+    assert call(K=65535 * 256 + 1) == _lib.ERR_UNSUPPORTED
+    assert call(N=65535 * 256 + 1) == _lib.ERR_UNSUPPORTED
+    assert call(M=0, x=None, a=None, b=None, d=None, ws=None, wsb=0) == _lib.OK
+    assert call(a=None) == _lib.ERR_INVALID_ARGUMENT
+    assert call(d=None) == _lib.ERR_INVALID_ARGUMENT
+    assert call(ws=None) == _lib.ERR_WORKSPACE
+    assert call(wsb=need - 1) == _lib.ERR_WORKSPACE
+    assert call(b=FAKE + 2) == _lib.ERR_MISALIGNED
+    assert call(d=FAKE + 4) == _lib.ERR_MISALIGNED
+    n = ctypes.c_size_t()
+    assert lib.qlinear_lora_workspace_bytes(1, K, 65, ctypes.byref(n)) == _lib.ERR_UNSUPPORTED
+    assert lib.qlinear_lora_workspace_bytes(1, 0, 8, ctypes.byref(n)) == _lib.ERR_INVALID_ARGUMENT
 
 
 def test_tampered_layout_is_rejected():

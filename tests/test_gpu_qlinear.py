@@ -395,21 +395,29 @@ EPILOGUE_PATHS = [
 @pytest.mark.parametrize("op,bits,M", EPILOGUE_PATHS,
                          ids=["row", "row-M3", "gather-valu-M1", "valu-M2", "mfma-M5", "mfma-M16", "qgemm", "qgemm-mixed",
                               "qgemm-runs"])
-@pytest.mark.parametrize("terms", ["bias", "residual", "bias-silu-residual", "silu-inplace-residual"])
+@pytest.mark.parametrize("terms", ["bias", "residual", "bias-silu-residual", "silu-inplace-residual",
+                                   "lora-bias-silu"])
 def test_fused_epilogue(op, bits, M, terms):
-    """y = RNE(act(x W + bias) + residual) on every kernel path, against the
-    float64 oracle's layer output followed by its epilogue."""
+    """y = RNE(act(x W + addend + bias) + residual) on every kernel path,
+    against the float64 oracle's layer output followed by its epilogue. The
+    addend is an on-the-fly LoRA update (rank 8) from qlinear_lora_delta."""
     say(f"fused epilogue {op} M={M} {terms}")
     inp = _mixed_inputs(bits, 32, 520, M, seed=300 + M, zeros=True)
     lay = GpuLayer(inp)
     rng = np.random.default_rng(41)
-    N = inp.spec.N
+    N, K = inp.spec.N, inp.spec.K
     bias = rng.standard_normal(N).astype(np.float16) if "bias" in terms else None
     resid = rng.standard_normal((M, N)).astype(np.float16) if "residual" in terms else None
     act = dq.ACT_SILU if "silu" in terms else dq.ACT_NONE
     x = lay.x(inp.x)
     b_t = None if bias is None else torch.from_numpy(bias).to(lay.dev)
     r_t = None if resid is None else torch.from_numpy(resid).to(lay.dev)
+    add_t = add_ref = None
+    if "lora" in terms:
+        A = (rng.standard_normal((K, 8)) * (2.0 / np.sqrt(K))).astype(np.float16)
+        B = (rng.standard_normal((8, N)) * 0.5).astype(np.float16)
+        add_t = dq.lora_delta(x, lay.x(A), lay.x(B), scale=0.75)
+        add_ref = oracle.lora_delta(inp.x, [(A, B, 0.75)])
     y = None
     if "inplace" in terms:
         y = r_t.clone()   # the residual is read from and written to the output
@@ -417,6 +425,10 @@ def test_fused_epilogue(op, bits, M, terms):
     call = dq.qgemv if op == "qgemv" else dq.qgemm
     extra = (lay.ws,) if op == "qgemv" else (None,)
     out = call(lay.layout, x, lay.qweight, lay.scales, lay.zeros, lay.perm, *extra, y=y, bias=b_t, residual=r_t,
-               activation=act)
-    ref = oracle.apply_epilogue(_ref(inp), bias, resid, act)
+               activation=act, addend=add_t)
+    ref = oracle.apply_epilogue(_ref(inp), bias, resid, act, addend=add_ref)
     assert_close(out, ref, f"{op} M={M} {terms}")
+    if add_ref is not None:
+        # the update is large enough that dropping it would fail the check above
+        plain = oracle.apply_epilogue(_ref(inp), bias, resid, act)
+        assert np.linalg.norm(ref - plain) > 0.05 * np.linalg.norm(ref)

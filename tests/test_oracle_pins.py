@@ -403,3 +403,133 @@ def test_epilogue_terms_and_order():
     assert np.array_equal(oracle.apply_epilogue(a), a)
     with pytest.raises(ValueError):
         oracle.apply_epilogue(a, activation=9)
+
+
+
+# ------------------------------------------------------------------ LoRA
+
+def _lora_case(rng, M=3, K=64, N=16, r=4):
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    A = (rng.standard_normal((K, r)) * 0.2).astype(np.float16)
+    B = (rng.standard_normal((r, N)) * 0.2).astype(np.float16)
+    return x, A, B
+
+
+def test_lora_rank_one_closed_form():
+    """A = e_i (one-hot column), B = one row b: the update is s x[:, i] b,
+    an outer product, for every i."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((4, 40)).astype(np.float16)
+    b = rng.standard_normal((1, 24)).astype(np.float16)
+    for i in (0, 17, 39):
+        A = np.zeros((40, 1), np.float16)
+        A[i, 0] = 1
+        got = oracle.lora_delta(x, [(A, b, -0.75)])
+        want = -0.75 * np.outer(x[:, i].astype(np.float64), b[0].astype(np.float64))
+        assert np.array_equal(got, want)
+
+
+def test_lora_zero_adapter_and_zero_weight():
+    rng = np.random.default_rng(12)
+    x, A, B = _lora_case(rng)
+    assert np.array_equal(oracle.lora_delta(x, [(A, np.zeros_like(B), 2.0)]), np.zeros((3, 16)))
+    assert np.array_equal(oracle.lora_delta(x, [(A, B, 0.0)]), np.zeros((3, 16)))
+    with pytest.raises(ValueError):
+        oracle.lora_delta(x, [])
+
+
+def test_lora_adapters_combine_as_one_of_concatenated_rank():
+    """Weighted adapters (A1, B1, s1), (A2, B2, s2) are the single adapter
+    A = [A1 | A2], B = [s1 B1 ; s2 B2] of rank r1 + r2 (block products), so a
+    weight applied to the wrong adapter, or cross terms, would show."""
+    rng = np.random.default_rng(13)
+    x, A1, B1 = _lora_case(rng, r=3)
+    _, A2, B2 = _lora_case(rng, r=5)
+    s1, s2 = 0.5, -2.0
+    A = np.concatenate([A1, A2], axis=1).astype(np.float64)
+    B = np.concatenate([s1 * B1.astype(np.float64), s2 * B2.astype(np.float64)], axis=0)
+    got = oracle.lora_delta(x, [(A1, B1, s1), (A2, B2, s2)])
+    assert np.allclose(got, oracle.lora_delta(x, [(A, B, 1.0)]), rtol=1e-13, atol=1e-13)
+
+
+def test_lora_bruteforce_tiny():
+    """Explicit sums over k and j, element by element, on a 2 x 5 x 3 rank-2 case."""
+    rng = np.random.default_rng(14)
+    x, A, B = _lora_case(rng, M=2, K=5, N=3, r=2)
+    got = oracle.lora_delta(x, [(A, B, 1.5)])
+    for m in range(2):
+        for n in range(3):
+            v = 0.0
+            for j in range(2):
+                t = 0.0
+                for k in range(5):
+                    t += float(x[m, k]) * float(A[k, j])
+                v += t * float(B[j, n])
+            assert np.isclose(got[m, n], 1.5 * v, rtol=1e-14, atol=1e-14)
+
+
+def test_lora_merge_identity_through_the_quantized_layer():
+    """On the fly equals merged: with act-order, the layer plus the update
+    through the epilogue (addend, bias, SiLU) equals SiLU(x W' + bias) for
+    the dense merged matrix W' = W + s A B, W in original feature order
+    (stored row j of the quantized matrix holds feature perm[j])."""
+    rng = np.random.default_rng(15)
+    K, N, gs = 128, 16, 32
+    bits = [4, 3, 4, 2]
+    q = np.stack([rng.integers(0, 2 ** bits[j // gs], N) for j in range(K)]).astype(np.uint8)
+    scales = (rng.random((K // gs, N)) * 0.1 + 0.01).astype(np.float16)
+    perm = rng.permutation(K)
+    x, A, B = _lora_case(rng, M=3, K=K, N=N, r=6)
+    bias = rng.standard_normal(N).astype(np.float16)
+    s = 0.8
+    acc = oracle.qlinear(x, q, scales, None, bits, gs, perm=perm)
+    got = oracle.apply_epilogue(acc, bias, None, oracle.ACT_SILU, addend=oracle.lora_delta(x, [(A, B, s)]))
+    w = oracle.dequant(q, scales, None, bits, gs)            # stored order
+    W = np.zeros((K, N))
+    W[perm] = w                                              # original order
+    merged = W + s * (A.astype(np.float64) @ B.astype(np.float64))
+    v = x.astype(np.float64) @ merged + bias.astype(np.float64)[None, :]
+    want = v / (1.0 + np.exp(-v))
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_epilogue_addend_joins_before_the_activation():
+    """acc = 1, addend = 1, bias = 1, residual = 1: silu(3) + 1."""
+    got = oracle.apply_epilogue(np.array([[1.0]]), np.array([1.0]), np.array([[1.0]]), oracle.ACT_SILU,
+                                addend=np.array([[1.0]], np.float32))[0, 0]
+    assert np.isclose(got, 3.0 / (1.0 + np.exp(-3.0)) + 1.0, rtol=1e-15)
+
+
+def test_lora_planted_mistakes_are_caught(monkeypatch):
+    """Plausible slips planted into lora_delta; a LoRA pin must fail for each."""
+    good = qo.lora_delta
+
+    def ignores_weight(x, adapters):
+        return good(x, [(A, B, 1.0) for A, B, _ in adapters])
+
+    def first_adapter_only(x, adapters):
+        return good(x, list(adapters)[:1])
+
+    def reversed_features(x, adapters):
+        return good(np.asarray(x)[:, ::-1], adapters)
+
+    def weight_twice(x, adapters):
+        return good(x, [(A, B, s * s) for A, B, s in adapters])
+
+    pins = [
+        test_lora_rank_one_closed_form,
+        test_lora_adapters_combine_as_one_of_concatenated_rank,
+        test_lora_merge_identity_through_the_quantized_layer,
+        test_lora_bruteforce_tiny,
+    ]
+    for bad in (ignores_weight, first_adapter_only, reversed_features, weight_twice):
+        with monkeypatch.context() as mp:
+            mp.setattr(qo, "lora_delta", bad)
+            mp.setattr(oracle, "lora_delta", bad)
+            failed = 0
+            for pin in pins:
+                try:
+                    pin()
+                except AssertionError:
+                    failed += 1
+            assert failed > 0, f"no pin caught {bad.__name__}"

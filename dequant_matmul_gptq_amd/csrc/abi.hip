@@ -80,13 +80,13 @@ int check_gemm_operands(const qlinear_layout* layout, const uint16_t* x, int32_t
 
 // The epilogue of a fused call (NULL: none).
 int check_epilogue(const qlinear_epilogue* e, Epilogue& out) {
-  out = Epilogue{nullptr, nullptr, QLINEAR_ACT_NONE, nullptr};
+  out = Epilogue{nullptr, nullptr, nullptr, QLINEAR_ACT_NONE};
   if (!e) return QLINEAR_OK;
   if (e->activation != QLINEAR_ACT_NONE && e->activation != QLINEAR_ACT_SILU) return QLINEAR_ERR_UNSUPPORTED;
   if ((e->bias && !aligned16(e->bias)) || (e->residual && !aligned16(e->residual)) ||
       (e->addend && !aligned16(e->addend)))
     return QLINEAR_ERR_MISALIGNED;
-  out = Epilogue{e->bias, e->residual, e->activation, e->addend};
+  out = Epilogue{e->bias, e->residual, e->addend, e->activation};
   return QLINEAR_OK;
 }
 
@@ -219,7 +219,7 @@ int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32
   if (M > QLINEAR_GEMV_MAX_M || (M > 2 && !qgemv_mfma_supported(*layout))) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
   return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, count, qweights_host, scales_host,
-                                 zeros ? zeros_host : nullptr, y_host, workspace, Epilogue{nullptr, nullptr, 0, nullptr},
+                                 zeros ? zeros_host : nullptr, y_host, workspace, Epilogue{nullptr, nullptr, nullptr, 0},
                                  (hipStream_t)stream));
 }
 

@@ -4,16 +4,18 @@
 //   delta[m][n] (+)= scale * sum_j t[m][j] * B[j][n],   t = x A.
 //
 // Two launches, both small next to the quantized matmul they feed:
-//  1. shrink: t = x A, split along K. Workgroup (row tile, K chunk) sums
-//     kLoraChunk rows of K for MB rows of x and writes its partial sums
-//     tpart[chunk][m][j] to the workspace. Lanes are (k slot, j): the RP
-//     lanes of a k slot read one row of A (contiguous) and share x[m][k].
+//  1. shrink: t = x A, split along K. Workgroup (row tile, K chunk) stages
+//     the chunk's kLoraChunk rows of A and the x tile (kShrinkRows rows of
+//     that chunk) in LDS with coalesced loads, then lanes (k slot, j) sum
+//     their products from LDS; the k slots are reduced through LDS and the
+//     partial sums tpart[chunk][m][j] go to the workspace. Each row of A is
+//     read once per row tile, and x once.
 //  2. expand: workgroup (row tile, column tile) sums the partials of its
-//     kExpandRows rows into LDS (times scale), then each thread owns one
-//     column n and runs the rank loop over B's rows (coalesced along n) for
-//     all rows of the tile.
+//     kExpandRows rows into LDS (times scale), in a fixed order; each thread
+//     owns one column n and runs the rank loop (B's rows, coalesced along n)
+//     for all rows of the tile.
 // Everything is float32 after the float16 loads. No atomics: the K split is
-// reduced in the expand kernel, in a fixed order.
+// reduced in the expand kernel, so results do not depend on timing.
 #include "qlinear_kernels.hpp"
 
 namespace qlinear {
@@ -21,42 +23,67 @@ namespace qlinear {
 namespace {
 
 constexpr int kLoraThreads = 256;
-constexpr int kLoraChunk = 256;  // rows of K per shrink workgroup
-constexpr int kExpandRows = 8;   // rows of x per expand workgroup
+constexpr int kLoraChunk = 256;   // rows of K per shrink workgroup
+constexpr int kShrinkRows = 16;   // rows of x per shrink workgroup
+constexpr int kExpandRows = 8;    // rows of x per expand workgroup
 
-// RP: rank padded to 8, 16, 32 or 64. MB = 64 / RP rows of x per workgroup,
-// so that each thread holds MB accumulators whatever the rank.
+// RP: the rank padded to 8, 16, 32 or 64.
 template <int RP>
 __global__ __launch_bounds__(kLoraThreads) void lora_shrink_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                    const uint16_t* __restrict__ A, int r,
                                                                    float* __restrict__ tpart) {
-  constexpr int MB = 64 / RP;
   constexpr int NKS = kLoraThreads / RP;  // k slots
-  __shared__ float red[NKS * MB * RP];
+  __shared__ _Float16 As[kLoraChunk * RP];              // rows k0 .. k0 + kn of A, row stride r
+  __shared__ _Float16 Xs[kShrinkRows][kLoraChunk];
+  __shared__ float red[NKS * kShrinkRows * RP];
   const int tid = threadIdx.x;
-  const int j = tid % RP, ks = tid / RP;
-  const int m0 = blockIdx.x * MB;
+  const int m0 = blockIdx.x * kShrinkRows;
   const int chunk = blockIdx.y;
-  const int k0 = chunk * kLoraChunk, k1 = min(k0 + kLoraChunk, K);
-  float acc[MB];
+  const int k0 = chunk * kLoraChunk, kn = min(kLoraChunk, K - k0);
+  // Staging: every load of a thread is issued before its first LDS store
+  // (fixed trip counts, clamped addresses), so they are all in flight at once.
+  const uint16_t* a_src = A + (size_t)k0 * r;           // the chunk's rows are contiguous
+  const int na = kn * r;
+  uint16_t av[RP];
 #pragma unroll
-  for (int mm = 0; mm < MB; ++mm) acc[mm] = 0.0f;
-#pragma unroll 4
-  for (int k = k0 + ks; k < k1; k += NKS) {
-    const float a = j < r ? (float)__builtin_bit_cast(_Float16, A[(size_t)k * r + j]) : 0.0f;
+  for (int u = 0; u < RP; ++u) av[u] = a_src[min(u * kLoraThreads + tid, na - 1)];
+  constexpr int kXPer = kShrinkRows * kLoraChunk / kLoraThreads;
+  uint16_t xv[kXPer];
 #pragma unroll
-    for (int mm = 0; mm < MB; ++mm) {
-      const int m = min(m0 + mm, M - 1);  // rows past M repeat row M - 1 and are not stored
-      acc[mm] += (float)__builtin_bit_cast(_Float16, x[(size_t)m * K + k]) * a;
+  for (int u = 0; u < kXPer; ++u) {
+    const int i = u * kLoraThreads + tid;
+    const int mm = i / kLoraChunk, kk = i % kLoraChunk;
+    const int m = min(m0 + mm, M - 1);                    // rows past M repeat row M - 1 and are not stored
+    xv[u] = x[(size_t)m * K + k0 + min(kk, kn - 1)];
+  }
+#pragma unroll
+  for (int u = 0; u < RP; ++u)
+    if (u * kLoraThreads + tid < na) As[u * kLoraThreads + tid] = __builtin_bit_cast(_Float16, av[u]);
+#pragma unroll
+  for (int u = 0; u < kXPer; ++u) {
+    const int i = u * kLoraThreads + tid;
+    Xs[i / kLoraChunk][i % kLoraChunk] = i % kLoraChunk < kn ? __builtin_bit_cast(_Float16, xv[u]) : (_Float16)0.0f;
+  }
+  __syncthreads();
+  const int j = tid % RP, ks = tid / RP;
+  float acc[kShrinkRows];
+#pragma unroll
+  for (int mm = 0; mm < kShrinkRows; ++mm) acc[mm] = 0.0f;
+  if (j < r) {
+    for (int k = ks; k < kn; k += NKS) {
+      const float a = (float)As[k * r + j];
+#pragma unroll
+      for (int mm = 0; mm < kShrinkRows; ++mm) acc[mm] += (float)Xs[mm][k] * a;
     }
   }
 #pragma unroll
-  for (int mm = 0; mm < MB; ++mm) red[(ks * MB + mm) * RP + j] = acc[mm];
+  for (int mm = 0; mm < kShrinkRows; ++mm) red[(ks * kShrinkRows + mm) * RP + j] = acc[mm];
   __syncthreads();
-  if (tid < MB * RP) {
-    const int mm = tid / RP, jj = tid % RP;
+  for (int t = tid; t < kShrinkRows * RP; t += kLoraThreads) {
+    const int mm = t / RP, jj = t % RP;
     float v = 0.0f;
-    for (int s = 0; s < NKS; ++s) v += red[(s * MB + mm) * RP + jj];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) v += red[(s * kShrinkRows + mm) * RP + jj];
     const int m = m0 + mm;
     if (m < M && jj < r) tpart[((size_t)chunk * M + m) * r + jj] = v;
   }
@@ -66,25 +93,40 @@ __global__ __launch_bounds__(kLoraThreads) void lora_expand_kernel(const float* 
                                                                    int r, const uint16_t* __restrict__ B, int N,
                                                                    float scale, int accumulate,
                                                                    float* __restrict__ delta) {
-  __shared__ float ts[kExpandRows][64];
+  __shared__ float ts[kExpandRows][QLINEAR_LORA_MAX_RANK];
   const int tid = threadIdx.x;
   const int m0 = blockIdx.x * kExpandRows;
-  for (int i = tid; i < kExpandRows * r; i += kLoraThreads) {
-    const int mm = i / r, j = i % r;
+  for (int e = tid; e < kExpandRows * r; e += kLoraThreads) {
+    const int mm = e / r, j = e % r;
     const int m = m0 + mm;
     float v = 0.0f;
-    if (m < M)
-      for (int c = 0; c < chunks; ++c) v += tpart[((size_t)c * M + m) * r + j];
-    ts[mm][j] = scale * v;
+    if (m < M) {
+      // eight partial sums over the chunks, combined in a fixed order
+      float p[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      const float* src = tpart + (size_t)m * r + j;
+      const size_t stride = (size_t)M * r;
+      int c = 0;
+      for (; c + 8 <= chunks; c += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) p[u] += src[(size_t)(c + u) * stride];
+      }
+      for (int u = 0; c < chunks; ++c, ++u) p[u] += src[(size_t)c * stride];
+      v = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    ts[mm][j] = scale * v;   // zero for rows past M
   }
   __syncthreads();
   const int n = blockIdx.y * kLoraThreads + tid;
   if (n >= N) return;
+  const uint16_t* bcol = B + n;
   float acc[kExpandRows];
 #pragma unroll
   for (int mm = 0; mm < kExpandRows; ++mm) acc[mm] = 0.0f;
+  // Unrolled by 8: the 8 loads of B of a pass are in flight together, and
+  // only the accumulators live across passes.
+#pragma unroll 8
   for (int j = 0; j < r; ++j) {
-    const float b = (float)__builtin_bit_cast(_Float16, B[(size_t)j * N + n]);
+    const float b = (float)__builtin_bit_cast(_Float16, bcol[(size_t)j * N]);
 #pragma unroll
     for (int mm = 0; mm < kExpandRows; ++mm) acc[mm] += ts[mm][j] * b;
   }
@@ -99,11 +141,16 @@ __global__ __launch_bounds__(kLoraThreads) void lora_expand_kernel(const float* 
 }
 
 template <int RP>
-hipError_t launch_shrink(const uint16_t* x, int M, int K, const uint16_t* A, int r, float* tpart,
-                         hipStream_t stream) {
-  constexpr int MB = 64 / RP;
-  hipLaunchKernelGGL(lora_shrink_kernel<RP>, dim3((M + MB - 1) / MB, lora_chunks(K)), dim3(kLoraThreads), 0,
-                     stream, x, M, K, A, r, tpart);
+hipError_t launch_rank(const uint16_t* x, int M, int K, const uint16_t* A, int r, const uint16_t* B, int N,
+                       float scale, bool accumulate, float* delta, float* tpart, hipStream_t stream) {
+  hipLaunchKernelGGL(lora_shrink_kernel<RP>, dim3((M + kShrinkRows - 1) / kShrinkRows, lora_chunks(K)),
+                     dim3(kLoraThreads), 0, stream, x, M, K, A, r, tpart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lora_expand_kernel,
+                     dim3((M + kExpandRows - 1) / kExpandRows, (N + kLoraThreads - 1) / kLoraThreads),
+                     dim3(kLoraThreads), 0, stream, tpart, lora_chunks(K), M, r, B, N, scale, accumulate ? 1 : 0,
+                     delta);
   return hipGetLastError();
 }
 
@@ -118,15 +165,10 @@ size_t lora_workspace_bytes(int M, int K, int rank) {
 hipError_t launch_lora_delta(const uint16_t* x, int M, int K, const uint16_t* A, int rank, const uint16_t* B, int N,
                              float scale, bool accumulate, float* delta, void* ws, hipStream_t stream) {
   float* tpart = static_cast<float*>(ws);
-  hipError_t e = rank <= 8    ? launch_shrink<8>(x, M, K, A, rank, tpart, stream)
-                 : rank <= 16 ? launch_shrink<16>(x, M, K, A, rank, tpart, stream)
-                 : rank <= 32 ? launch_shrink<32>(x, M, K, A, rank, tpart, stream)
-                              : launch_shrink<64>(x, M, K, A, rank, tpart, stream);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lora_expand_kernel, dim3((M + kExpandRows - 1) / kExpandRows, (N + kLoraThreads - 1) / kLoraThreads),
-                     dim3(kLoraThreads), 0, stream, tpart, lora_chunks(K), M, rank, B, N, scale, accumulate ? 1 : 0,
-                     delta);
-  return hipGetLastError();
+  if (rank <= 8) return launch_rank<8>(x, M, K, A, rank, B, N, scale, accumulate, delta, tpart, stream);
+  if (rank <= 16) return launch_rank<16>(x, M, K, A, rank, B, N, scale, accumulate, delta, tpart, stream);
+  if (rank <= 32) return launch_rank<32>(x, M, K, A, rank, B, N, scale, accumulate, delta, tpart, stream);
+  return launch_rank<64>(x, M, K, A, rank, B, N, scale, accumulate, delta, tpart, stream);
 }
 
 }  // namespace qlinear

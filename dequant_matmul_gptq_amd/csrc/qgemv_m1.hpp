@@ -280,7 +280,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
     const int R = a.runs.packed_rows, bpg = a.bpg_shift, hz = a.has_zeros;
     const int32_t* const perm = a.perm;
     asm volatile("" : "+s"(K), "+s"(N), "+s"(M), "+s"(spx), "+s"(xw), "+s"(xsrc), "+s"(mp.y), "+s"(epi.bias),
-                 "+s"(epi.residual), "+s"(epi.act), "+s"(epi.addend)
+                 "+s"(epi.residual), "+s"(epi.act)
                  : "s"(R), "s"(bpg), "s"(hz), "s"(perm), "s"(mp.qweight), "s"(mp.scales), "s"(mp.zeros));
   }
 
@@ -303,17 +303,15 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   }
   // The epilogue's operands of this strip's outputs, read now rather than
   // after the final reduction (a residual that is the output itself is read
-  // before the same thread writes it). Every thread loads, from y (or the
-  // first packed word) when a term is absent: loads without a branch around
-  // them keep the wait before each LDS store below down to that store's own
-  // piece.
+  // before the same thread writes it). Every thread loads, from y when a term
+  // is absent: loads without a branch around them keep the wait before each
+  // LDS store below down to that store's own piece. This kernel takes no
+  // float32 addend (single_row() sends such calls to the other kernels).
   // Thread tid < 16 MT stores output (row tid / 16, column tid % 16).
   const int n_out = min(strip * SC + (tid % SC), N - 1);
   const int m_out = min(tid / SC, M - 1);
   const uint16_t bias_raw = as_global<uint16_t>(epi.bias ? epi.bias : mp.y)[n_out];
   const uint16_t res_raw = as_global<uint16_t>(epi.residual ? epi.residual : mp.y)[(size_t)m_out * N + n_out];
-  const float add_val = epi.addend ? as_global<float>(epi.addend)[(size_t)m_out * N + n_out]
-                                   : as_global<float>(reinterpret_cast<const float*>(mp.qweight))[0];
   asm volatile("" ::: "memory");   // keep the row loads ahead of the weight loads
 
   // 2. The first D steps of the wave's blocks, issued by every wave (a wave
@@ -365,7 +363,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   // Reduce over the block slots: the 4 of each 16-lane row with two DPP row
   // shifts (lanes 12..15 of a row end up with its sums, one per column
   // quad), then the 4 rows of each wave and the waves through LDS; the
-  // epilogue as apply_epilogue: addend, bias, activation, residual.
+  // epilogue as apply_epilogue, without the addend: bias, activation, residual.
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -392,7 +390,6 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
     for (int w = 0; w < WV; ++w)
 #pragma unroll
       for (int row = 0; row < 4; ++row) v += red[w][row][m][c_out];
-    if (epi.addend) v += add_val;
     if (epi.bias) v += (float)__builtin_bit_cast(_Float16, bias_raw);
     if (epi.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
     if (epi.residual) v += (float)__builtin_bit_cast(_Float16, res_raw);

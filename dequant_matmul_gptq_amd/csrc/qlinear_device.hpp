@@ -28,8 +28,8 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 struct Epilogue {
   const uint16_t* bias;       // float16 [N] or NULL
   const uint16_t* residual;   // float16 [M][N] or NULL (may be the output itself)
-  int act;                    // QLINEAR_ACT_NONE or QLINEAR_ACT_SILU
   const float* addend;        // float32 [M][N] or NULL (e.g. a LoRA update)
+  int act;                    // QLINEAR_ACT_NONE or QLINEAR_ACT_SILU
 };
 
 // y = act(v + addend + bias) + residual. The operands are device (global)

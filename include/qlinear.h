@@ -32,9 +32,10 @@
  *    Inf makes every element of its row non-finite: qlinear_qgemm and the
  *    other qlinear_qgemv calls give the IEEE result of the formula (+-Inf,
  *    NaN where the weight is 0). qlinear_qgemv gives NaN at M <= 2, and at
- *    M = 3 or 4 for a single-width layout with 4 K <= 31744 or a width of
- *    3, 5 or 6 bits: it computes the sum in a factored form that subtracts
- *    the activations' block sums. Other rows are unaffected.
+ *    M = 3 or 4 for a single-width layout with a width of 3, 5 or 6 bits or
+ *    (with no epilogue addend) 4 K <= 31744: it computes the sum in a
+ *    factored form that subtracts the activations' block sums. Other rows
+ *    are unaffected.
  */
 #ifndef QLINEAR_H
 #define QLINEAR_H

@@ -400,7 +400,9 @@ EPILOGUE_PATHS = [
 def test_fused_epilogue(op, bits, M, terms):
     """y = RNE(act(x W + addend + bias) + residual) on every kernel path,
     against the float64 oracle's layer output followed by its epilogue. The
-    addend is an on-the-fly LoRA update (rank 8) from qlinear_lora_delta."""
+    addend is an on-the-fly LoRA update (rank 8) from qlinear_lora_delta;
+    calls with one do not run the single-launch decode kernel (the "row"
+    cases then run the gather and multi-row or MFMA kernels)."""
     say(f"fused epilogue {op} M={M} {terms}")
     inp = _mixed_inputs(bits, 32, 520, M, seed=300 + M, zeros=True)
     lay = GpuLayer(inp)

@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-group", action="store_true", help="one qgemv launch per matrix (no grouped q/k/v, gate/up)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the M = 2048 qgemm measurement")
+    ap.add_argument("--no-lora", action="store_true", help="skip the on-the-fly LoRA update timings")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-config decode points (7B at M = 4, 16; EXL2 at M = 1, 8; 70B at M = 1, 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -350,6 +351,7 @@ def main():
 
     gemm = None if args.no_gemm else bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream)
     configs = None if args.no_configs else bench_configs(torch, dq, wl, lib, dev, stream, spin)
+    lora = None if args.no_lora else bench_lora(torch, lib, dev, stream, spin)
 
     # ---------------------------------------------------------------- oracle on the host
     cpu = None
@@ -397,6 +399,7 @@ def main():
         },
         "reference_points": refs,
         "decode_configs": configs,
+        "lora": lora,
         "cpu_baseline": cpu,
         "qgemm": gemm,
     }
@@ -477,6 +480,60 @@ def bench_configs(torch, dq, wl, lib, dev, stream, spin):
                            "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1)})
             log(f"config point {spec.name} M={M}: {us:.2f} us, {points[-1]['weight_gbs']} GB/s")
         del copies, qw
+    return points
+
+
+# On-the-fly LoRA update delta = s (x A) B (float32 [M][N]) at rank 16 on the
+# 7B decode shapes and the 13B MLP prefill shape.
+LORA_POINTS = [(1, 4096, 4096, 16), (1, 4096, 11008, 16), (1, 11008, 4096, 16), (2048, 5120, 13824, 16)]
+
+
+def lora_bytes(M, K, N, r):
+    """Algorithmic HBM bytes of one qlinear_lora_delta call: x, A and B read
+    once (float16), delta written once (float32); the partial sums in the
+    workspace are the kernels' own traffic."""
+    return 2 * M * K + 2 * K * r + 2 * r * N + 4 * M * N
+
+
+def bench_lora(torch, lib, dev, stream, spin):
+    """qlinear_lora_delta (shrink + expand launches) per call, >= 256 calls
+    back to back behind a spin kernel (20 at M = 2048) between two events on
+    the launch stream, against the HBM roofline of its algorithmic bytes."""
+    sh = stream.cuda_stream
+    points = []
+    for M, K, N, r in LORA_POINTS:
+        rng = np.random.default_rng(M + K + N + r)
+        x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float16)).to(dev)
+        A = torch.from_numpy((rng.standard_normal((K, r)) / np.sqrt(K)).astype(np.float16)).to(dev)
+        B = torch.from_numpy(rng.standard_normal((r, N)).astype(np.float16)).to(dev)
+        d = torch.empty((M, N), dtype=torch.float32, device=dev)
+        need = ctypes.c_size_t()
+        assert lib.qlinear_lora_workspace_bytes(M, K, r, ctypes.byref(need)) == 0
+        ws = torch.empty(max(need.value, 256), dtype=torch.uint8, device=dev)
+
+        def call():
+            st = lib.qlinear_lora_delta(x.data_ptr(), M, K, A.data_ptr(), r, B.data_ptr(), N, 0.5, 0, d.data_ptr(),
+                                        ws.data_ptr(), ws.numel(), sh)
+            if st != 0:
+                raise RuntimeError(f"qlinear_lora_delta failed with status {st}")
+
+        for _ in range(4):
+            call()
+        n = 20 if M > 16 else 256
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(spin)
+        e0.record(stream)
+        for _ in range(n):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        nb = lora_bytes(M, K, N, r)
+        gbs = nb / (us * 1e-6) / 1e9
+        points.append({"M": M, "K": K, "N": N, "rank": r, "us_per_call": round(us, 2), "algorithmic_bytes": nb,
+                       "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        log(f"lora M={M} {K}->{N} rank {r}: {us:.2f} us, {gbs:.1f} GB/s")
     return points
 
 

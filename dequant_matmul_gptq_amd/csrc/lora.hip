@@ -13,7 +13,8 @@
 //  2. expand: workgroup (row tile, column tile) sums the partials of its
 //     kExpandRows rows into LDS (times scale), in a fixed order; each thread
 //     owns one column n and runs the rank loop (B's rows, coalesced along n)
-//     for all rows of the tile.
+//     for all rows of the tile, the first 16 rows of B loaded before the
+//     partial sums so that the two latencies overlap.
 // Everything is float32 after the float16 loads. No atomics: the K split is
 // reduced in the expand kernel, so results do not depend on timing.
 #include "qlinear_kernels.hpp"
@@ -26,6 +27,7 @@ constexpr int kLoraThreads = 256;
 constexpr int kLoraChunk = 256;   // rows of K per shrink workgroup
 constexpr int kShrinkRows = 16;   // rows of x per shrink workgroup
 constexpr int kExpandRows = 8;    // rows of x per expand workgroup
+constexpr int kExpandPre = 16;    // ranks of B loaded ahead of the partial sums
 
 // RP: the rank padded to 8, 16, 32 or 64.
 template <int RP>
@@ -96,6 +98,13 @@ __global__ __launch_bounds__(kLoraThreads) void lora_expand_kernel(const float* 
   __shared__ float ts[kExpandRows][QLINEAR_LORA_MAX_RANK];
   const int tid = threadIdx.x;
   const int m0 = blockIdx.x * kExpandRows;
+  const int n = blockIdx.y * kLoraThreads + tid;
+  const uint16_t* bcol = B + min(n, N - 1);  // threads past N load column N - 1 and store nothing
+  // B's first kExpandPre rows of this column, loaded before the partial sums
+  // below so that their latency overlaps (rows past the rank repeat row r - 1).
+  float bpre[kExpandPre];
+#pragma unroll
+  for (int j = 0; j < kExpandPre; ++j) bpre[j] = (float)__builtin_bit_cast(_Float16, bcol[(size_t)min(j, r - 1) * N]);
   for (int e = tid; e < kExpandRows * r; e += kLoraThreads) {
     const int mm = e / r, j = e % r;
     const int m = m0 + mm;
@@ -116,16 +125,21 @@ __global__ __launch_bounds__(kLoraThreads) void lora_expand_kernel(const float* 
     ts[mm][j] = scale * v;   // zero for rows past M
   }
   __syncthreads();
-  const int n = blockIdx.y * kLoraThreads + tid;
   if (n >= N) return;
-  const uint16_t* bcol = B + n;
   float acc[kExpandRows];
 #pragma unroll
   for (int mm = 0; mm < kExpandRows; ++mm) acc[mm] = 0.0f;
-  // Unrolled by 8: the 8 loads of B of a pass are in flight together, and
-  // only the accumulators live across passes.
+#pragma unroll
+  for (int j = 0; j < kExpandPre; ++j) {
+    if (j < r) {
+#pragma unroll
+      for (int mm = 0; mm < kExpandRows; ++mm) acc[mm] += ts[mm][j] * bpre[j];
+    }
+  }
+  // Ranks past kExpandPre, unrolled by 8: the 8 loads of B of a pass are in
+  // flight together, and only the accumulators live across passes.
 #pragma unroll 8
-  for (int j = 0; j < r; ++j) {
+  for (int j = kExpandPre; j < r; ++j) {
     const float b = (float)__builtin_bit_cast(_Float16, bcol[(size_t)j * N]);
 #pragma unroll
     for (int mm = 0; mm < kExpandRows; ++mm) acc[mm] += ts[mm][j] * b;

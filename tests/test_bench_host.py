@@ -80,3 +80,9 @@ def test_decode_groups_layer_order():
     assert [m["i"] for x in g for m in x["mats"]] == list(range(14))
     u = bench.decode_groups(mats, False)
     assert [len(x["mats"]) for x in u] == [1] * 14
+
+
+def test_lora_bytes_count_each_operand_once():
+    # 7B decode 4096 -> 4096 at rank 16: x 8 KiB, A 128 KiB, B 128 KiB, delta 16 KiB
+    assert bench.lora_bytes(1, 4096, 4096, 16) == 2 * 4096 + 2 * 4096 * 16 + 2 * 16 * 4096 + 4 * 4096
+    assert bench.lora_bytes(0, 4096, 4096, 16) == 2 * 4096 * 16 * 2

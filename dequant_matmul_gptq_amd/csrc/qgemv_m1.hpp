@@ -306,7 +306,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   // before the same thread writes it). Every thread loads, from y when a term
   // is absent: loads without a branch around them keep the wait before each
   // LDS store below down to that store's own piece. This kernel takes no
-  // float32 addend (single_row() sends such calls to the other kernels).
+  // float32 addend: the dispatcher sends calls with one to the other kernels.
   // Thread tid < 16 MT stores output (row tid / 16, column tid % 16).
   const int n_out = min(strip * SC + (tid % SC), N - 1);
   const int m_out = min(tid / SC, M - 1);

@@ -28,17 +28,30 @@ __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __res
                                                            int M, int K, int scaled, int mfma, Runs runs) {
   // Every argument read in one scalar batch (the asm takes them and hands
   // them back, so none is read later behind another wait).
-  {
-    int nruns = runs.nruns, bits0 = runs.run_bits[0];
-    asm volatile("" : "+s"(M), "+s"(K), "+s"(scaled), "+s"(mfma) : "s"(x), "s"(perm), "s"(xq), "s"(xsum), "s"(nruns),
-                 "s"(bits0));
+  // The first 8 runs' first blocks and widths are part of that batch: read
+  // inside the run scan, each would be a round trip of its own (entries past
+  // nruns lie inside the table and are ignored).
+  int nruns = runs.nruns;
+  int rb[8], rw[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    rb[r] = runs.run_block[r];
+    rw[r] = runs.run_bits[r];
   }
+  asm volatile("" : "+s"(M), "+s"(K), "+s"(scaled), "+s"(mfma), "+s"(nruns), "+s"(rb[1]), "+s"(rb[2]), "+s"(rb[3]),
+               "+s"(rb[4]), "+s"(rb[5]), "+s"(rb[6]), "+s"(rb[7]), "+s"(rw[0]), "+s"(rw[1]), "+s"(rw[2]), "+s"(rw[3]),
+               "+s"(rw[4]), "+s"(rw[5]), "+s"(rw[6]), "+s"(rw[7])
+               : "s"(x), "s"(perm), "s"(xq), "s"(xsum));
   const int nblk = K / kBlockRows;
   const int pairs = nblk * kPairsPerBlock;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const bool live = idx < pairs;
   const int blk = live ? idx / kPairsPerBlock : 0, p = idx % kPairsPerBlock;
-  const int bits = block_bits_scan(runs, blk);
+  // The width of block blk: that of the last run starting at or before it.
+  int bits = rw[0];
+#pragma unroll
+  for (int r = 1; r < 8; ++r) bits = (r < nruns && blk >= rb[r]) ? rw[r] : bits;
+  for (int r = 8; r < nruns; ++r) bits = blk >= runs.run_block[r] ? runs.run_bits[r] : bits;
   int lo, hi;
   pair_rows(bits, mfma ? mfma_pair(bits, p) : p, lo, hi);
   const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;

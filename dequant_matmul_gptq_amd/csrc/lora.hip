@@ -25,21 +25,22 @@ namespace {
 
 constexpr int kLoraThreads = 256;
 constexpr int kLoraChunk = 256;   // rows of K per shrink workgroup
-constexpr int kShrinkRows = 16;   // rows of x per shrink workgroup
+constexpr int kShrinkRows = 16;   // rows of x per shrink workgroup (1 for a single row)
 constexpr int kExpandRows = 8;    // rows of x per expand workgroup
 constexpr int kExpandPre = 16;    // ranks of B loaded ahead of the partial sums
 
-// RP: the rank padded to 8, 16, 32 or 64.
-template <int RP>
+// RP: the rank padded to 8, 16, 32 or 64. MB: rows of x per workgroup,
+// kShrinkRows, or 1 when M is 1.
+template <int RP, int MB>
 __global__ __launch_bounds__(kLoraThreads) void lora_shrink_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                    const uint16_t* __restrict__ A, int r,
                                                                    float* __restrict__ tpart) {
   constexpr int NKS = kLoraThreads / RP;  // k slots
   __shared__ _Float16 As[kLoraChunk * RP];              // rows k0 .. k0 + kn of A, row stride r
-  __shared__ _Float16 Xs[kShrinkRows][kLoraChunk];
-  __shared__ float red[NKS * kShrinkRows * RP];
+  __shared__ _Float16 Xs[MB][kLoraChunk];
+  __shared__ float red[NKS * MB * RP];
   const int tid = threadIdx.x;
-  const int m0 = blockIdx.x * kShrinkRows;
+  const int m0 = blockIdx.x * MB;
   const int chunk = blockIdx.y;
   const int k0 = chunk * kLoraChunk, kn = min(kLoraChunk, K - k0);
   // Staging: every load of a thread is issued before its first LDS store
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(kLoraThreads) void lora_shrink_kernel(const uint16_
   uint16_t av[RP];
 #pragma unroll
   for (int u = 0; u < RP; ++u) av[u] = a_src[min(u * kLoraThreads + tid, na - 1)];
-  constexpr int kXPer = kShrinkRows * kLoraChunk / kLoraThreads;
+  constexpr int kXPer = MB * kLoraChunk / kLoraThreads;
   uint16_t xv[kXPer];
 #pragma unroll
   for (int u = 0; u < kXPer; ++u) {
@@ -68,24 +69,24 @@ __global__ __launch_bounds__(kLoraThreads) void lora_shrink_kernel(const uint16_
   }
   __syncthreads();
   const int j = tid % RP, ks = tid / RP;
-  float acc[kShrinkRows];
+  float acc[MB];
 #pragma unroll
-  for (int mm = 0; mm < kShrinkRows; ++mm) acc[mm] = 0.0f;
+  for (int mm = 0; mm < MB; ++mm) acc[mm] = 0.0f;
   if (j < r) {
     for (int k = ks; k < kn; k += NKS) {
       const float a = (float)As[k * r + j];
 #pragma unroll
-      for (int mm = 0; mm < kShrinkRows; ++mm) acc[mm] += (float)Xs[mm][k] * a;
+      for (int mm = 0; mm < MB; ++mm) acc[mm] += (float)Xs[mm][k] * a;
     }
   }
 #pragma unroll
-  for (int mm = 0; mm < kShrinkRows; ++mm) red[(ks * kShrinkRows + mm) * RP + j] = acc[mm];
+  for (int mm = 0; mm < MB; ++mm) red[(ks * MB + mm) * RP + j] = acc[mm];
   __syncthreads();
-  for (int t = tid; t < kShrinkRows * RP; t += kLoraThreads) {
+  for (int t = tid; t < MB * RP; t += kLoraThreads) {
     const int mm = t / RP, jj = t % RP;
     float v = 0.0f;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) v += red[(s * kShrinkRows + mm) * RP + jj];
+    for (int s = 0; s < NKS; ++s) v += red[(s * MB + mm) * RP + jj];
     const int m = m0 + mm;
     if (m < M && jj < r) tpart[((size_t)chunk * M + m) * r + jj] = v;
   }
@@ -157,8 +158,9 @@ __global__ __launch_bounds__(kLoraThreads) void lora_expand_kernel(const float* 
 template <int RP>
 hipError_t launch_rank(const uint16_t* x, int M, int K, const uint16_t* A, int r, const uint16_t* B, int N,
                        float scale, bool accumulate, float* delta, float* tpart, hipStream_t stream) {
-  hipLaunchKernelGGL(lora_shrink_kernel<RP>, dim3((M + kShrinkRows - 1) / kShrinkRows, lora_chunks(K)),
-                     dim3(kLoraThreads), 0, stream, x, M, K, A, r, tpart);
+  const auto shrink = M == 1 ? lora_shrink_kernel<RP, 1> : lora_shrink_kernel<RP, kShrinkRows>;
+  const int tiles = M == 1 ? 1 : (M + kShrinkRows - 1) / kShrinkRows;
+  hipLaunchKernelGGL(shrink, dim3(tiles, lora_chunks(K)), dim3(kLoraThreads), 0, stream, x, M, K, A, r, tpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lora_expand_kernel,

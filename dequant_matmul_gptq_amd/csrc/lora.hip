@@ -155,6 +155,79 @@ __global__ __launch_bounds__(kLoraThreads) void lora_expand_kernel(const float* 
   }
 }
 
+// Large M with N a multiple of 4: each thread owns 4 adjacent columns, so a
+// workgroup reads its rows' partial sums once per 1024 columns (not 256), and
+// B and delta move as 8- and 16-byte vectors (a wave stores 1 KiB
+// contiguously).
+__global__ __launch_bounds__(kLoraThreads) void lora_expand4_kernel(const float* __restrict__ tpart, int chunks, int M,
+                                                                    int r, const uint16_t* __restrict__ B, int N,
+                                                                    float scale, int accumulate,
+                                                                    float* __restrict__ delta) {
+  __shared__ float ts[kExpandRows][QLINEAR_LORA_MAX_RANK];
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.x * kExpandRows;
+  const int q = blockIdx.y * kLoraThreads + tid;   // column quad: columns 4q .. 4q + 3
+  const int nq = N / 4;
+  const uint2* bq = reinterpret_cast<const uint2*>(B) + min(q, nq - 1);   // quads past N repeat the last, not stored
+  for (int e = tid; e < kExpandRows * r; e += kLoraThreads) {
+    const int mm = e / r, j = e % r;
+    const int m = m0 + mm;
+    float v = 0.0f;
+    if (m < M) {
+      float p[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      const float* src = tpart + (size_t)m * r + j;
+      const size_t stride = (size_t)M * r;
+      int c = 0;
+      for (; c + 8 <= chunks; c += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) p[u] += src[(size_t)(c + u) * stride];
+      }
+      for (int u = 0; c < chunks; ++c, ++u) p[u] += src[(size_t)c * stride];
+      v = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    ts[mm][j] = scale * v;
+  }
+  __syncthreads();
+  if (q >= nq) return;
+  float acc[kExpandRows][4];
+#pragma unroll
+  for (int mm = 0; mm < kExpandRows; ++mm)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[mm][c] = 0.0f;
+#pragma unroll 4
+  for (int j = 0; j < r; ++j) {
+    const uint2 w = bq[(size_t)j * nq];
+    const float b0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x & 0xFFFFu));
+    const float b1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x >> 16));
+    const float b2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y & 0xFFFFu));
+    const float b3 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y >> 16));
+#pragma unroll
+    for (int mm = 0; mm < kExpandRows; ++mm) {
+      const float t = ts[mm][j];
+      acc[mm][0] += t * b0;
+      acc[mm][1] += t * b1;
+      acc[mm][2] += t * b2;
+      acc[mm][3] += t * b3;
+    }
+  }
+#pragma unroll
+  for (int mm = 0; mm < kExpandRows; ++mm) {
+    const int m = m0 + mm;
+    if (m < M) {
+      float4* d = reinterpret_cast<float4*>(delta + (size_t)m * N) + q;
+      float4 v = make_float4(acc[mm][0], acc[mm][1], acc[mm][2], acc[mm][3]);
+      if (accumulate) {
+        const float4 o = *d;
+        v.x += o.x;
+        v.y += o.y;
+        v.z += o.z;
+        v.w += o.w;
+      }
+      *d = v;
+    }
+  }
+}
+
 template <int RP>
 hipError_t launch_rank(const uint16_t* x, int M, int K, const uint16_t* A, int r, const uint16_t* B, int N,
                        float scale, bool accumulate, float* delta, float* tpart, hipStream_t stream) {
@@ -163,10 +236,18 @@ hipError_t launch_rank(const uint16_t* x, int M, int K, const uint16_t* A, int r
   hipLaunchKernelGGL(shrink, dim3(tiles, lora_chunks(K)), dim3(kLoraThreads), 0, stream, x, M, K, A, r, tpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lora_expand_kernel,
-                     dim3((M + kExpandRows - 1) / kExpandRows, (N + kLoraThreads - 1) / kLoraThreads),
-                     dim3(kLoraThreads), 0, stream, tpart, lora_chunks(K), M, r, B, N, scale, accumulate ? 1 : 0,
-                     delta);
+  if (M > 16 && N % 4 == 0) {
+    const int nq = N / 4;
+    hipLaunchKernelGGL(lora_expand4_kernel,
+                       dim3((M + kExpandRows - 1) / kExpandRows, (nq + kLoraThreads - 1) / kLoraThreads),
+                       dim3(kLoraThreads), 0, stream, tpart, lora_chunks(K), M, r, B, N, scale, accumulate ? 1 : 0,
+                       delta);
+  } else {
+    hipLaunchKernelGGL(lora_expand_kernel,
+                       dim3((M + kExpandRows - 1) / kExpandRows, (N + kLoraThreads - 1) / kLoraThreads),
+                       dim3(kLoraThreads), 0, stream, tpart, lora_chunks(K), M, r, B, N, scale, accumulate ? 1 : 0,
+                       delta);
+  }
   return hipGetLastError();
 }
 

@@ -69,11 +69,13 @@ def test_lora_delta_parity(M, K, N, r):
     _close(got, oracle.lora_delta(x, [(A, B, 0.5)]), f"M={M} K={K} N={N} r={r}")
 
 
-def test_lora_delta_adapters_accumulate():
+@pytest.mark.parametrize("M", [5, 40])
+def test_lora_delta_adapters_accumulate(M):
     """Two adapters with weights: the second call adds into the first's
-    result, as the oracle's weighted sum."""
-    say("lora_delta accumulate")
-    M, K, N = 5, 1024, 640
+    result, as the oracle's weighted sum (M = 40 takes the four-column
+    expand kernel of large M)."""
+    say(f"lora_delta accumulate M={M}")
+    K, N = 1024, 640
     x, A1, B1 = _case(M, K, N, 8, seed=1)
     _, A2, B2 = _case(M, K, N, 40, seed=2)
     xd = _dev(x)

@@ -6,8 +6,9 @@
 // Two launches, both small next to the quantized matmul they feed:
 //  1. shrink: t = x A, split along K. Workgroup (row tile, K chunk) stages
 //     the chunk's kLoraChunk rows of A and the x tile (kShrinkRows rows of
-//     that chunk) in LDS with coalesced loads, then lanes (k slot, j) sum
-//     their products from LDS; the k slots are reduced through LDS and the
+//     that chunk, stored k-major so that one k's rows are one vector read)
+//     in LDS with coalesced loads, then lanes (k slot, j) sum their products
+//     from LDS; the k slots are reduced through LDS and the
 //     partial sums tpart[chunk][m][j] go to the workspace. Each row of A is
 //     read once per row tile, and x once.
 //  2. expand: workgroup (row tile, column tile) sums the partials of its
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(kLoraThreads) void lora_shrink_kernel(const uint16_
                                                                    float* __restrict__ tpart) {
   constexpr int NKS = kLoraThreads / RP;  // k slots
   __shared__ _Float16 As[kLoraChunk * RP];              // rows k0 .. k0 + kn of A, row stride r
-  __shared__ _Float16 Xs[MB][kLoraChunk];
+  __shared__ __align__(16) _Float16 Xs[kLoraChunk][MB];   // transposed: the MB rows of one k are contiguous
   __shared__ float red[NKS * MB * RP];
   const int tid = threadIdx.x;
   const int m0 = blockIdx.x * MB;
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kLoraThreads) void lora_shrink_kernel(const uint16_
 #pragma unroll
   for (int u = 0; u < kXPer; ++u) {
     const int i = u * kLoraThreads + tid;
-    Xs[i / kLoraChunk][i % kLoraChunk] = i % kLoraChunk < kn ? __builtin_bit_cast(_Float16, xv[u]) : (_Float16)0.0f;
+    Xs[i % kLoraChunk][i / kLoraChunk] = i % kLoraChunk < kn ? __builtin_bit_cast(_Float16, xv[u]) : (_Float16)0.0f;
   }
   __syncthreads();
   const int j = tid % RP, ks = tid / RP;
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kLoraThreads) void lora_shrink_kernel(const uint16_
     for (int k = ks; k < kn; k += NKS) {
       const float a = (float)As[k * r + j];
 #pragma unroll
-      for (int mm = 0; mm < MB; ++mm) acc[mm] += (float)Xs[mm][k] * a;
+      for (int mm = 0; mm < MB; ++mm) acc[mm] += (float)Xs[k][mm] * a;
     }
   }
 #pragma unroll

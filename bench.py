@@ -224,8 +224,8 @@ def setup_decode(torch, dq, wl, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the layer's sharding across GPUs is described in DESIGN.md, not implemented).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library runs the layer on one GPU; splitting it across GPUs is not implemented).", file=sys.stderr)
         sys.exit(2)
 
     import torch

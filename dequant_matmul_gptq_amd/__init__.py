@@ -25,6 +25,8 @@ from ._lib import (  # noqa: F401
     qgemm_workspace_bytes,
     qgemv,
     qgemv_grouped,
+    qgemv_noalloc,
+    NOALLOC_MAX_K,
     qgemv_workspace,
     qgemv_workspace_bytes,
     status_string,

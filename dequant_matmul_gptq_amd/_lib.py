@@ -37,6 +37,7 @@ EXPORTS = (
     "qlinear_dequant",
     "qlinear_qgemv_workspace_bytes",
     "qlinear_qgemv",
+    "qlinear_qgemv_noalloc",
     "qlinear_qgemv_grouped",
     "qlinear_qgemm_workspace_bytes",
     "qlinear_qgemm",
@@ -101,6 +102,7 @@ def lib() -> ctypes.CDLL:
         L.qlinear_dequant.argtypes = [lp, vp, vp, vp, vp, vp]
         L.qlinear_qgemv_workspace_bytes.argtypes = [lp, ctypes.POINTER(sz)]
         L.qlinear_qgemv.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.qlinear_qgemv_noalloc.argtypes = [lp, vp, i32, vp, vp, vp, vp, vp, vp]
         pp = ctypes.POINTER(vp)
         L.qlinear_qgemv_grouped.argtypes = [lp, vp, i32, i32, pp, pp, pp, vp, pp, vp, sz, vp]
         L.qlinear_qgemm_workspace_bytes.argtypes = [lp, i32, ctypes.POINTER(sz)]
@@ -260,6 +262,21 @@ def qgemv(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.
         _check(lib().qlinear_qgemv_fused(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros),
                                          _ptr(perm), ctypes.byref(epi), _ptr(y), _ptr(workspace), workspace.numel(),
                                          _stream(x.device)), "qlinear_qgemv_fused")
+    return y
+
+
+NOALLOC_MAX_K = 65536
+
+
+def qgemv_noalloc(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
+                  zeros: torch.Tensor | None, perm: torch.Tensor | None,
+                  y: torch.Tensor | None = None) -> torch.Tensor:
+    """qgemv with the library's static device scratch as its workspace (no
+    allocation by the library; y is allocated here unless given). Calls that
+    overlap in time on one GPU race."""
+    M, y = _gemm_operands(layout, x, qweight, scales, zeros, perm, y)
+    _check(lib().qlinear_qgemv_noalloc(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(scales), _ptr(zeros),
+                                       _ptr(perm), _ptr(y), _stream(x.device)), "qlinear_qgemv_noalloc")
     return y
 
 

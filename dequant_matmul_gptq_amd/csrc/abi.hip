@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "qlinear_kernels.hpp"
 
 namespace qlinear {
@@ -87,6 +89,36 @@ int check_epilogue(const qlinear_epilogue* e, Epilogue& out) {
       (e->addend && !aligned16(e->addend)))
     return QLINEAR_ERR_MISALIGNED;
   out = Epilogue{e->bias, e->residual, e->addend, e->activation};
+  return QLINEAR_OK;
+}
+
+// Device scratch of qlinear_qgemv_noalloc: the decode workspace for any K up
+// to QLINEAR_NOALLOC_MAX_K, held by every GPU the library runs on until the
+// process ends. Zero at load; the decode kernels never need it cleared (they
+// overwrite what they read). Host code never passes this name to a kernel:
+// on the host it is only a stand-in for the symbol, and each device's
+// address comes from hipGetSymbolAddress below.
+constexpr size_t kScratchBytes = (size_t)5 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// The scratch address on the calling thread's current device, looked up once
+// per device with that device current.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return QLINEAR_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return QLINEAR_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return QLINEAR_ERR_HIP;
+  *out = g_scratch_ptr[dev];
   return QLINEAR_OK;
 }
 
@@ -196,6 +228,21 @@ int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M, co
                   void* workspace, size_t workspace_bytes, void* stream) {
   return qlinear_qgemv_fused(layout, x, M, qweight, scales, zeros, perm, nullptr, y, workspace, workspace_bytes,
                              stream);
+}
+
+int qlinear_qgemv_noalloc(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                          const uint16_t* scales, const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                          void* stream) {
+  const int st = check_layout(layout);
+  if (st != QLINEAR_OK) return st;
+  if (layout->K > QLINEAR_NOALLOC_MAX_K) return QLINEAR_ERR_UNSUPPORTED;
+  if (M == 0) return QLINEAR_OK;
+  const size_t need = qgemv_workspace_bytes(layout->K);
+  if (need > kScratchBytes) return QLINEAR_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const int sst = scratch_on_current_device(&ws);
+  if (sst != QLINEAR_OK) return sst;
+  return qlinear_qgemv_fused(layout, x, M, qweight, scales, zeros, perm, nullptr, y, ws, need, stream);
 }
 
 int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32_t M, int32_t count,

@@ -19,7 +19,8 @@
  *  - All data pointers are DEVICE pointers unless the argument name ends in
  *    _host. Matrices are row-major. The caller allocates and owns every
  *    buffer and every stream; the library allocates nothing, keeps no global
- *    state and never synchronizes the host.
+ *    state (but for the static device scratch of qlinear_qgemv_noalloc) and
+ *    never synchronizes the host.
  *  - float16 data is passed as uint16_t bit patterns (IEEE binary16).
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *    asynchronously; a QLINEAR_OK return means the launch was accepted.
@@ -174,6 +175,24 @@ int qlinear_qgemv(const qlinear_layout* layout, const uint16_t* x, int32_t M,
                   const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                   const int32_t* perm, uint16_t* y, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * qlinear_qgemv without a caller-provided workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same operands, result and errors as
+ * qlinear_qgemv; the workspace is a static device array of the library (a
+ * few MiB, held by each GPU the library runs on until the process ends),
+ * found on the calling thread's current device, which `stream` must belong
+ * to. Every call on one GPU shares that array: calls that may overlap in
+ * time on one GPU (different streams) race and must not be issued. The
+ * array needs no clearing between calls. Allocates nothing.
+ * Errors: as qlinear_qgemv; UNSUPPORTED also for K > QLINEAR_NOALLOC_MAX_K;
+ * HIP if the array's device address cannot be obtained.
+ */
+#define QLINEAR_NOALLOC_MAX_K 65536
+int qlinear_qgemv_noalloc(const qlinear_layout* layout, const uint16_t* x, int32_t M,
+                          const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                          const int32_t* perm, uint16_t* y, void* stream);
 
 /*
  * Several decode layers in one launch: count (1 .. QLINEAR_MAX_GROUP) matrices

@@ -24,7 +24,6 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = dq.lib()
     names = declared_functions()
-    assert len(names) == 14, names
     assert sorted(names) == sorted(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n

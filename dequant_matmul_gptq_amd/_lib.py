@@ -45,6 +45,7 @@ EXPORTS = (
     "qlinear_qgemm_fused",
     "qlinear_lora_workspace_bytes",
     "qlinear_lora_delta",
+    "qlinear_read_floor",
 )
 
 ACT_NONE = 0
@@ -112,6 +113,7 @@ def lib() -> ctypes.CDLL:
         L.qlinear_qgemm_fused.argtypes = [lp, vp, i32, vp, vp, vp, vp, ep, vp, vp, sz, vp]
         L.qlinear_lora_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.qlinear_lora_delta.argtypes = [vp, i32, i32, vp, i32, vp, i32, ctypes.c_float, i32, vp, vp, sz, vp]
+        L.qlinear_read_floor.argtypes = [vp, sz, i32, i32, ctypes.c_uint32, vp, vp]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L

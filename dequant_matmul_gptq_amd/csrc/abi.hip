@@ -53,6 +53,9 @@ int check_layout(const qlinear_layout* L) {
   const int bpg = L->group_size / kBlockRows;
   for (int r = 0; r < L->nruns; ++r) {
     if (!supported_bits(L->run_bits[r])) return QLINEAR_ERR_UNSUPPORTED;
+    // Runs are maximal (qlinear_layout_init merges equal neighbours): the
+    // launchers size workspaces and pick kernels from the run count.
+    if (r > 0 && L->run_bits[r] == L->run_bits[r - 1]) return QLINEAR_ERR_INVALID_ARGUMENT;
     const int ng = L->run_group[r + 1] - L->run_group[r];
     if (ng <= 0) return QLINEAR_ERR_INVALID_ARGUMENT;
     if (L->run_row[r + 1] - L->run_row[r] != ng * bpg * L->run_bits[r]) return QLINEAR_ERR_INVALID_ARGUMENT;
@@ -298,6 +301,15 @@ int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M, co
                   void* workspace, size_t workspace_bytes, void* stream) {
   return qlinear_qgemm_fused(layout, x, M, qweight, scales, zeros, perm, nullptr, y, workspace, workspace_bytes,
                              stream);
+}
+
+int qlinear_read_floor(const void* buf, size_t bytes, int32_t loads_per_thread, int32_t workgroups, uint32_t key,
+                       uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 != 0) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (loads_per_thread != 4 && loads_per_thread != 8 && loads_per_thread != 16) return QLINEAR_ERR_UNSUPPORTED;
+  if (workgroups < 1 || workgroups > 65535) return QLINEAR_ERR_UNSUPPORTED;
+  if (!aligned16(buf) || !aligned16(sink)) return QLINEAR_ERR_MISALIGNED;
+  return hip_status(launch_read_floor(buf, bytes, loads_per_thread, workgroups, key, sink, (hipStream_t)stream));
 }
 
 int qlinear_lora_workspace_bytes(int32_t M, int32_t K, int32_t rank, size_t* bytes) {

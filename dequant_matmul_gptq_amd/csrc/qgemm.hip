@@ -404,8 +404,9 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
     hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, !mixed || split, stream);
     if (e != hipSuccess) return e;
     uint16_t* yc = y + (size_t)m0 * L.N;
-    Epilogue ec = epi;   // the chunk's rows of the residual
+    Epilogue ec = epi;   // the chunk's rows of the residual and the addend
     if (ec.residual) ec.residual += (size_t)m0 * L.N;
+    if (ec.addend) ec.addend += (size_t)m0 * L.N;
     // Many runs of several code widths: the kernel that dequantizes into LDS.
     if (mixed && !split) {
       e = launch_qgemm_lds(L, runs, reinterpret_cast<const uint16_t*>(xq), mc, qweight, scales, zeros, yc, ec,

@@ -78,4 +78,10 @@ size_t lora_workspace_bytes(int M, int K, int rank);
 hipError_t launch_lora_delta(const uint16_t* x, int M, int K, const uint16_t* A, int rank, const uint16_t* B, int N,
                              float scale, bool accumulate, float* delta, void* ws, hipStream_t stream);
 
+// Streaming-read floor (measurement helper): grid workgroups of 256 threads
+// read `bytes` (a multiple of 16) with `loads` (4, 8 or 16) 16-byte loads in
+// flight per thread.
+hipError_t launch_read_floor(const void* buf, size_t bytes, int loads, int grid, uint32_t key, uint32_t* sink,
+                             hipStream_t stream);
+
 }  // namespace qlinear

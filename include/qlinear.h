@@ -108,12 +108,16 @@ typedef struct qlinear_layout {
   int64_t packed_words;  /* uint32 words of the packed buffer: ceil(N/16) * packed_rows * 16 */
 } qlinear_layout;
 
-/* Static, human-readable name of a status code. Never NULL. */
+/* Static, human-readable name of a status code. Never NULL. Every failure is
+ * a returned status, where the blog's "Production Considerations" describe
+ * the process simply crashing (on out-of-memory). */
 const char* qlinear_status_string(int status);
 
 /*
  * Fill `layout` for a K x N matrix with `group_size` rows per group and the
- * per-group bit widths bits_host[0 .. K/group_size - 1] (HOST memory, read
+ * per-group bit widths bits_host[0 .. K/group_size - 1]: the q_groups tensor
+ * of an EXL2 matrix, a bit width per group (blog, "How the EXL2 Quantization
+ * Pipeline Works Under the Hood", Step 3). HOST memory, read
  * only during the call). Host-only; touches no GPU.
  * Errors: INVALID_ARGUMENT (NULL, K <= 0, N <= 0), UNSUPPORTED (group size
  * not 32/64/128, K % group_size != 0, N % 8 != 0, a width outside
@@ -123,7 +127,10 @@ int qlinear_layout_init(qlinear_layout* layout, int32_t K, int32_t N, int32_t gr
                         const uint8_t* bits_host);
 
 /*
- * Pack codes into the format above.
+ * Pack codes into the format above: the q_weights tensor, packed values of
+ * varying bit width in uint32 words (blog, Step 3 of the EXL2 pipeline), 4-bit
+ * codes least significant first as in the blog's kernel sketch ("How the
+ * Fused CUDA Kernel Works").
  *   q       : uint8 [K][N], stored row order, each code < 2^b of its group
  *             (larger codes are truncated to their low b bits).
  *   qweight : uint32 [packed_words] in panel order, written entirely.
@@ -131,12 +138,17 @@ int qlinear_layout_init(qlinear_layout* layout, int32_t K, int32_t N, int32_t gr
 int qlinear_pack_weights(const qlinear_layout* layout, const uint8_t* q, uint32_t* qweight,
                          void* stream);
 
-/* Inverse of qlinear_pack_weights: qweight -> q uint8 [K][N] (stored order). */
+/* Inverse of qlinear_pack_weights: qweight -> q uint8 [K][N] (stored order),
+ * the unpacking step of the blog's kernel sketch ("How the Fused CUDA Kernel
+ * Works") for every width. */
 int qlinear_unpack(const qlinear_layout* layout, const uint32_t* qweight, uint8_t* q,
                    void* stream);
 
 /*
- * Dequantize to float16 in stored row order:
+ * Dequantize to float16 in stored row order: the group-wise scaling of GPTQ
+ * codes (artifact page, GPTQ paragraph: a scale per group) and the sketch's
+ * (w - 8) * scale with the zero point generalized (blog, "How the Fused CUDA
+ * Kernel Works"):
  *   w[j][n] = RNE_fp16(s[g][n] * (q[j][n] - z[g][n])), g = j / group_size,
  * rounded once (the product is exact before rounding).
  *   scales : float16 [G][N]
@@ -148,7 +160,9 @@ int qlinear_dequant(const qlinear_layout* layout, const uint32_t* qweight, const
                     const uint8_t* zeros, uint16_t* w, void* stream);
 
 /*
- * Workspace of qlinear_qgemv, in bytes, for any M <= QLINEAR_GEMV_MAX_M. For
+ * Workspace of qlinear_qgemv, in bytes, for any M <= QLINEAR_GEMV_MAX_M: room
+ * for the activations gathered into stored row order, the act-order
+ * remapping of the README's "EXL2 quantization". For
  * M > 1 it receives the act-order-gathered activations and their 32-row
  * block sums (M = 1 gathers inside the kernel's LDS unless K is very large).
  * It is scratch: no initialization is needed and its contents are not
@@ -158,7 +172,11 @@ int qlinear_dequant(const qlinear_layout* layout, const uint32_t* qweight, const
 int qlinear_qgemv_workspace_bytes(const qlinear_layout* layout, size_t* bytes);
 
 /*
- * Decode-sized layer, 1 <= M <= QLINEAR_GEMV_MAX_M. M == 0 returns OK after
+ * Decode-sized layer: the fused kernel of the blog's "How the Fused CUDA
+ * Kernel Works" (load the quantized weights, dequantize them on the fly and
+ * multiply, in one pass with no intermediate weights written), at the token
+ * counts of decoding, where the layer is bound by reading its weights (blog,
+ * "The Investigation"). 1 <= M <= QLINEAR_GEMV_MAX_M. M == 0 returns OK after
  * checking the layout only, and launches nothing (operands may then be NULL).
  *   x       : float16 [M][K], original feature order
  *   qweight : uint32 [packed_words] from qlinear_pack_weights
@@ -215,7 +233,9 @@ int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32
                           const uint8_t* const* zeros_host, const int32_t* perm, uint16_t* const* y_host,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace of qlinear_qgemm for M tokens, in bytes (no initialization needed):
+/* Workspace of qlinear_qgemm for M tokens, in bytes (no initialization needed;
+ * the act-order gather of the README's "EXL2 quantization" and the partial
+ * sums of layouts with several widths):
  * the gathered activations, float16 [M][K], and for a layout with several
  * code widths that has at least 4096 rows of K per run boundary also float32
  * partial sums [M][N] (such a layout is computed one launch per run). */
@@ -223,7 +243,9 @@ int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_
 
 /*
  * Prefill-sized layer, any M >= 0 (M == 0 as for qlinear_qgemv), same
- * operands and result as qlinear_qgemv.
+ * operands and result as qlinear_qgemv: the fused kernel on the matrix cores
+ * (blog, "How the Fused CUDA Kernel Works": the real kernel uses tensor
+ * cores), dequantizing each weight once per tile of tokens.
  * The workspace receives the act-order-gathered activations (and the partial
  * sums described at qlinear_qgemm_workspace_bytes).
  * Errors as for qlinear_qgemv; UNSUPPORTED also for M > 65535 * 128, or for
@@ -300,6 +322,22 @@ int qlinear_lora_workspace_bytes(int32_t M, int32_t K, int32_t rank, size_t* byt
 int qlinear_lora_delta(const uint16_t* x, int32_t M, int32_t K, const uint16_t* lora_a, int32_t rank,
                        const uint16_t* lora_b, int32_t N, float scale, int32_t accumulate, float* delta,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement helper (not part of the layer): the streaming-read floor that
+ * frames the decode kernels' bandwidth, since decode is bound by reading the
+ * weights (ExLlamaV2 blog, "The Investigation": the GPU mostly waits on
+ * memory). Reads `bytes` of device memory at `buf` once, with
+ * `loads_per_thread` (4, 8 or 16) 16-byte loads in flight per thread, over
+ * `workgroups` workgroups of 256 threads striding through the buffer, and
+ * folds the words into one value per thread, which is written to sink[0]
+ * only if it equals `key` (pick a key the data does not produce: nothing is
+ * then written). Asynchronous on `stream`.
+ * Errors: INVALID_ARGUMENT (NULL, bytes < 16 or not a multiple of 16),
+ * UNSUPPORTED (loads_per_thread, workgroups outside 1..65535), MISALIGNED.
+ */
+int qlinear_read_floor(const void* buf, size_t bytes, int32_t loads_per_thread, int32_t workgroups, uint32_t key,
+                       uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -72,3 +72,34 @@ def assert_close(y_gpu: torch.Tensor, y_ref: np.ndarray, what: str = ""):
 
 def fp16_bits(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy().view(np.uint16)
+
+
+GUARD_BYTES = 4096
+GUARD_VALUE = 0xA5
+
+
+class Guarded:
+    """A device buffer of `nbytes` between two guard bands of GUARD_BYTES
+    filled with GUARD_VALUE; `view(dtype, shape)` is the usable middle (16-byte
+    aligned). `intact()` says whether both bands still hold their pattern,
+    i.e. nothing wrote past either end."""
+
+    def __init__(self, nbytes: int, dev, fill: int = GUARD_VALUE):
+        self.nbytes = int(nbytes)
+        self.raw = torch.full((GUARD_BYTES + self.nbytes + GUARD_BYTES,), fill, dtype=torch.uint8, device=dev)
+        self.raw[:GUARD_BYTES] = GUARD_VALUE
+        self.raw[GUARD_BYTES + self.nbytes:] = GUARD_VALUE
+
+    def view(self, dtype, shape):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        assert n <= self.nbytes
+        return self.raw[GUARD_BYTES:GUARD_BYTES + n].view(dtype).view(*shape)
+
+    def bytes(self):
+        return self.raw[GUARD_BYTES:GUARD_BYTES + self.nbytes]
+
+    def intact(self) -> bool:
+        torch.cuda.synchronize()
+        head = self.raw[:GUARD_BYTES]
+        tail = self.raw[GUARD_BYTES + self.nbytes:]
+        return bool((head == GUARD_VALUE).all().item()) and bool((tail == GUARD_VALUE).all().item())

@@ -229,6 +229,18 @@ def test_tampered_layout_is_rejected():
     L = _layout()
     L.c.nruns = 0
     assert _gemm(L) == _lib.ERR_UNSUPPORTED
+    # Two adjacent runs of one width (a split run that qlinear_layout_init
+    # never produces): the launchers size workspaces from the run count, so
+    # such a layout is refused before any launch.
+    L = _layout(K=8192, N=64, gs=32, bits=np.array([4] * 256, np.uint8))
+    assert L.nruns == 1
+    c = L.c
+    c.nruns = 2
+    c.run_group[1], c.run_group[2] = 128, 256
+    c.run_row[1], c.run_row[2] = 128 * 4, 256 * 4
+    c.run_bits[1] = 4
+    assert _gemm(L) == _lib.ERR_INVALID_ARGUMENT
+    assert _gemv(L) == _lib.ERR_INVALID_ARGUMENT
 
 
 def test_pack_unpack_dequant_validation():

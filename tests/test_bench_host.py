@@ -20,25 +20,26 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
-def test_row_kernel_bytes_count_each_operand_once():
+def test_launch_bytes_count_each_operand_once():
     spec = wl.LLAMA7B_DECODE[0]                     # 4096 -> 4096, 4-bit, g128
     L = dq.Layout(spec.K, spec.N, spec.group_size, wl.bit_map(spec))
     codes = 4096 * 4096 // 2
     scales = 32 * 4096 * 2
-    zeros = 32 * 4096                               # uint8 zero points
+    zeros = 32 * 4096 // 2                          # zero points at 4 bits, as in the metric's weight bytes
     act = 4096 * 2 + 4096 * 4 + 4096 * 2            # x, perm, y
-    assert bench.row_kernel_bytes(L, 1) == codes + scales + zeros + act
-    assert bench.row_kernel_bytes(L, 1, zeros=False) == codes + scales + act
-    assert bench.row_kernel_bytes(L, 1, perm=False) == codes + scales + zeros + act - 4096 * 4
-    # the nominal weight bytes count zeros at 4 bits
-    assert wl.weight_bytes(spec) == codes + scales + zeros // 2
+    assert bench.launch_bytes(L, 1) == codes + scales + zeros + act
+    assert bench.launch_bytes(L, 1, zeros=False) == codes + scales + act
+    assert bench.launch_bytes(L, 1, perm=False) == codes + scales + zeros + act - 4096 * 4
+    # one byte model: the weight bytes of the metric are the same terms
+    assert wl.weight_bytes(spec) == codes + scales + zeros
+    assert bench.launch_bytes(L, 1) - act == wl.weight_bytes(spec)
 
 
 def test_mixed_width_codes_bytes():
     bits = np.array([6, 5, 4, 3, 2, 8], np.uint8)
     L = dq.Layout(6 * 32, 64, 32, bits)
     codes = int(sum(int(b) * 32 * 64 for b in bits)) // 8
-    assert bench.row_kernel_bytes(L, 1, zeros=False) == codes + 6 * 64 * 2 + 192 * 2 + 192 * 4 + 64 * 2
+    assert bench.launch_bytes(L, 1, zeros=False) == codes + 6 * 64 * 2 + 192 * 2 + 192 * 4 + 64 * 2
 
 
 def test_recorded_traffic_is_tied_to_the_kernel_sources(tmp_path, monkeypatch):
@@ -67,9 +68,9 @@ def test_gemm_traffic_follows_its_own_sources(tmp_path, monkeypatch):
 def test_grouped_launch_bytes_share_x_and_perm():
     spec = wl.LLAMA7B_DECODE[0]
     L = dq.Layout(spec.K, spec.N, spec.group_size, wl.bit_map(spec))
-    one = bench.row_kernel_bytes(L, 1)
+    one = bench.launch_bytes(L, 1)
     shared = 4096 * 2 + 4096 * 4
-    assert bench.row_kernel_bytes(L, 1, count=3) == 3 * (one - shared) + shared
+    assert bench.launch_bytes(L, 1, count=3) == 3 * (one - shared) + shared
 
 
 def test_decode_groups_layer_order():

@@ -292,6 +292,15 @@ def test_qgemm_row_chunks():
     ridx = torch.from_numpy(rows).to(layer.dev)
     ref = _ref(inp, x[ridx].cpu().numpy())
     assert_close(y[ridx], ref, "row chunks")
+    # The epilogue's per-row operands (residual, float32 addend) follow the
+    # chunks: rows past the first chunk take their own rows of both.
+    resid = torch.randn((M, N), generator=gen, device=layer.dev, dtype=torch.float16)
+    addend = torch.randn((M, N), generator=gen, device=layer.dev, dtype=torch.float32) * 4.0
+    y2 = dq.qgemm(layer.layout, x, layer.qweight, layer.scales, layer.zeros, layer.perm, residual=resid,
+                  addend=addend)
+    ref2 = oracle.apply_epilogue(ref, None, resid[ridx].cpu().numpy(), dq.ACT_NONE,
+                                 addend=addend[ridx].cpu().numpy().astype(np.float64))
+    assert_close(y2[ridx], ref2, "row chunks with residual and addend")
 
 
 # ------------------------------------------------------------------ grouped launches

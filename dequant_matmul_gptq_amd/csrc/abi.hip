@@ -220,7 +220,7 @@ int qlinear_qgemv_fused(const qlinear_layout* layout, const uint16_t* x, int32_t
   Epilogue epi;
   st = check_epilogue(epilogue, epi);
   if (st != QLINEAR_OK || M == 0) return st;
-  if (M > QLINEAR_GEMV_MAX_M || (M > 2 && !qgemv_mfma_supported(*layout))) return QLINEAR_ERR_UNSUPPORTED;
+  if (M > QLINEAR_GEMV_MAX_M || (M > 2 && !qgemv_mx_supported(*layout))) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
   return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, 1, &qweight, &scales,
                                  zeros ? &zeros : nullptr, &y, workspace, epi, (hipStream_t)stream));
@@ -266,7 +266,7 @@ int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32
     if (zeros_host && (zeros_host[i] != nullptr) != zeros) return QLINEAR_ERR_INVALID_ARGUMENT;
   }
   if (M == 0) return QLINEAR_OK;
-  if (M > QLINEAR_GEMV_MAX_M || (M > 2 && !qgemv_mfma_supported(*layout))) return QLINEAR_ERR_UNSUPPORTED;
+  if (M > QLINEAR_GEMV_MAX_M || (M > 2 && !qgemv_mx_supported(*layout))) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
   return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, count, qweights_host, scales_host,
                                  zeros ? zeros_host : nullptr, y_host, workspace, Epilogue{nullptr, nullptr, nullptr, 0},

@@ -53,24 +53,22 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   a.epi = epi;
   unsigned set = 0;
   for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
+  // Measured on MI355X (graph-timed, weights from HBM, 4096^2 to 28672x8192
+  // layers): at 1-2 rows the VALU kernels below are 1.1-1.7x faster than the
+  // matrix-core kernel; at 3-4 rows the single-row kernel still wins on
+  // layers of up to 2 * 4096 * 4096 weights and the matrix-core kernel on
+  // larger ones (1.1-1.4x); from 5 rows on the matrix-core kernel wins (up
+  // to 1.4x; within 8% on 8-bit layouts).
+  const bool row = !epi.addend && stream::single_row(M, L.K, set);
+  if (M >= 3 && !(row && (int64_t)L.K * L.N <= (int64_t)2 * 4096 * 4096))
+    return launch_qgemv_mx(L, runs, x, M, perm, mats, qweights, scales, zeros, ys, ws, epi, stream);
   // The single-launch kernel takes no float32 addend: reading one more kernel
   // argument in its prologue cost 3% on the 7B decode step (measured on
   // MI355X), so calls with an addend (a LoRA update) run the kernels below.
-  if (!epi.addend && stream::single_row(M, L.K, set)) return stream::launch_row_set(set, a, stream);
-  // The activations are gathered into the workspace by a kernel of their own.
+  if (row) return stream::launch_row_set(set, a, stream);
+  // 1-2 rows: the activations are gathered into the workspace (with the
+  // per-block sums of the factored form) by a kernel of their own.
   const GemvWorkspace w = qgemv_workspace(ws, L.K);
-  // 3 to 16 rows: one MFMA row tile, unscaled activations in MFMA pair order.
-  // Measured on MI355X: the factored VALU kernel below is faster at 2 rows,
-  // and at 3-4 rows for single-width 3, 5 and 6-bit layouts (whose k-groups
-  // spread over several words); the MFMA kernel wins at 3-4 rows on every
-  // other shape measured (up to 1.7x) and from 5 rows on everywhere (3-7x at
-  // 8-16 rows).
-  const bool spread = set == (1u << 3) || set == (1u << 5) || set == (1u << 6);
-  if (M > 4 || (M > 2 && !spread)) {
-    const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, nullptr, false, true, stream);
-    if (e != hipSuccess) return e;
-    return launch_qgemv_mfma(L, runs, w.xq, M, mats, qweights, scales, zeros, ys, epi, stream);
-  }
   const hipError_t e = launch_gather_pairs(runs, x, perm, M, L.K, w.xq, w.xsum, true, false, stream);
   if (e != hipSuccess) return e;
   a.xq = w.xq;

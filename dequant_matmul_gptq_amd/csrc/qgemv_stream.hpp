@@ -486,23 +486,22 @@ inline int waves_for(int N, int K) {
   return (nstrips <= 512 && K / kBlockRows >= 256) ? 8 : 4;
 }
 
-// Kernels for M <= 4 with the activations gathered by the gather kernel.
+// Kernels for M <= 2 with the activations gathered by the gather kernel.
 template <unsigned BS>
 hipError_t launch_set_small_m(const StreamArgs& a, hipStream_t stream) {
   if (a.M <= 1) {
     if (waves_for(a.N, a.K) >= 8) return launch_set<1, BS, 8>(a, stream);
     return launch_set<1, BS, 4>(a, stream);
   }
-  if (a.M <= 2) return launch_set<2, BS, 4>(a, stream);
-  return launch_set<4, BS, 4>(a, stream);
+  return launch_set<2, BS, 4>(a, stream);
 }
 
 constexpr unsigned kLowBits = (1u << 2) | (1u << 3);                            // ~2-3 bpw
 constexpr unsigned kMidBits = (1u << 3) | (1u << 4) | (1u << 5) | (1u << 6);   // ~3.5-5 bpw
 constexpr unsigned kAllBits = (1u << 2) | (1u << 3) | (1u << 4) | (1u << 5) | (1u << 6) | (1u << 8);
 
-// Instantiated in the qgemv_stream_*.hip files: M <= 4 per set of widths
-// (larger M runs the MFMA decode kernel).
+// Instantiated in the qgemv_stream_*.hip files: M <= 2 per set of widths
+// (larger M runs the single-row or the matrix-core decode kernel).
 hipError_t launch_uniform(unsigned set, const StreamArgs& a, hipStream_t stream);
 hipError_t launch_mixed(unsigned set, const StreamArgs& a, hipStream_t stream);
 

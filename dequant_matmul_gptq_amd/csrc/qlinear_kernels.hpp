@@ -52,14 +52,20 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
 hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uint16_t* xq, int M,
                             const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y,
                             const Epilogue& epi, hipStream_t stream);
-// Decode layer for 3 <= M <= 16 on the matrix cores, from activations gathered
-// unscaled into xq (float16 [M][K], unpacking order); the packed words,
-// scales and M * K activations must each stay below 2^31 bytes.
-bool qgemv_mfma_supported(const qlinear_layout& L);
-hipError_t launch_qgemv_mfma(const qlinear_layout& L, const Runs& runs, const uint32_t* xq, int M, int mats,
-                             const uint32_t* const* qweights, const uint16_t* const* scales,
-                             const uint8_t* const* zeros, uint16_t* const* ys, const Epilogue& epi,
-                             hipStream_t stream);
+// Decode layer on the matrix cores in factored form, 1 <= M <= 16, any set
+// of code widths (qgemv_mx.hip). One launch with the act-order gather inside
+// the kernel when qgemv_mx_one_launch() holds; otherwise a gather kernel
+// writes the first qgemv_mx_workspace_bytes(K) bytes of the decode
+// workspace (at most qgemv_workspace_bytes(K)) first. The packed words of a
+// 64-column strip and the scales must each stay below 2^31 bytes
+// (qgemv_mx_supported).
+bool qgemv_mx_supported(const qlinear_layout& L);
+bool qgemv_mx_one_launch(const qlinear_layout& L, int M, bool perm);
+size_t qgemv_mx_workspace_bytes(int K);
+hipError_t launch_qgemv_mx(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
+                           const int32_t* perm, int mats, const uint32_t* const* qweights,
+                           const uint16_t* const* scales, const uint8_t* const* zeros, uint16_t* const* ys,
+                           void* ws, const Epilogue& epi, hipStream_t stream);
 
 // Bytes of qgemm's workspace: the gathered activations [M][K] float16, then
 // for layouts computed run by run the float32 partial sums [M][N].

@@ -30,13 +30,11 @@
  *  - Pointers to device data must be 16-byte aligned (QLINEAR_ERR_MISALIGNED).
  *  - N must be a multiple of 8; K a multiple of gs.
  *  - Non-finite activations: a NaN in row m of x makes row m of y NaN. An
- *    Inf makes every element of its row non-finite: qlinear_qgemm and the
- *    other qlinear_qgemv calls give the IEEE result of the formula (+-Inf,
- *    NaN where the weight is 0). qlinear_qgemv gives NaN at M <= 2, and at
- *    M = 3 or 4 for a single-width layout with a width of 3, 5 or 6 bits or
- *    (with no epilogue addend) 4 K <= 31744: it computes the sum in a
- *    factored form that subtracts the activations' block sums. Other rows
- *    are unaffected.
+ *    Inf makes every element of its row non-finite: qlinear_qgemm gives the
+ *    IEEE result of the formula (+-Inf, NaN where the weight is 0); every
+ *    qlinear_qgemv call gives NaN, as it computes the sum in a factored
+ *    form that subtracts the activations' block sums (Inf - Inf). Other
+ *    rows are unaffected.
  */
 #ifndef QLINEAR_H
 #define QLINEAR_H

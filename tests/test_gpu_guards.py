@@ -36,7 +36,8 @@ CASES = [
     ("qgemv", [4] * 11, 520, 4),          # single-launch kernel, 4 rows
     ("qgemv", MIXED, 520, 1),             # several widths at M = 1
     ("qgemv", MIXED, 520, 2),
-    ("qgemv", MIXED, 392, 8),             # MFMA decode
+    ("qgemv", MIXED, 392, 8),             # matrix-core decode, gather kernel + workspace
+    ("qgemv", [6, 5, 4, 4, 3, 3], 392, 3),   # matrix-core decode, one launch (gather in LDS)
     ("qgemv", [3] * 40, 776, 16),
     ("qgemm", [4] * 11, 520, 300),        # prefill, one width
     ("qgemm", MIXED, 392, 130),           # prefill, several widths (LDS dequant)

@@ -92,7 +92,7 @@ def test_qgemv_small_mixed(M, zeros):
     assert_close(y, _ref(inp), f"qgemv M={M}")
 
 
-@pytest.mark.parametrize("M", (2, 4, 12))   # VALU kernel; VALU (3, 5, 6 bits) or MFMA; MFMA
+@pytest.mark.parametrize("M", (2, 4, 12))   # VALU kernel; single-row kernel; matrix-core kernel
 @pytest.mark.parametrize("gs", (32, 64, 128))
 @pytest.mark.parametrize("b", (2, 3, 4, 5, 6, 8))
 def test_qgemv_uniform_widths(b, gs, M):
@@ -137,6 +137,36 @@ def test_qgemm_uniform_widths(b, gs):
     inp = _mixed_inputs([b] * (1024 // gs), gs, 392, 100, seed=b * 17 + gs, zeros=True)
     y = GpuLayer(inp).qgemm(inp.x)
     assert_close(y, _ref(inp), f"qgemm b={b} gs={gs}")
+
+
+MX_FEW_ROW_BITS = {
+    "mid": [6, 5, 5, 4, 4, 4, 3, 3],     # widths 3-6: one launch, gather in the kernel
+    "low": [3, 3, 3, 2, 2],              # widths 2-3
+}
+
+
+@pytest.mark.parametrize("zeros", (True, False))
+@pytest.mark.parametrize("M", (3, 4))
+@pytest.mark.parametrize("name", sorted(MX_FEW_ROW_BITS))
+def test_qgemv_matrix_core_few_rows(name, M, zeros):
+    """3-4 rows of a layout with several widths run the matrix-core kernel in
+    one launch (x rows and perm staged in LDS, gathered run by run); 520
+    columns leave a ragged last strip."""
+    say(f"qgemv matrix-core one launch {name} M={M} zeros={zeros}")
+    inp = _mixed_inputs(MX_FEW_ROW_BITS[name], 32, 520, M, seed=300 + M + 7 * len(name), zeros=zeros)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv {name} M={M}")
+
+
+@pytest.mark.parametrize("M", (3, 4))
+def test_qgemv_matrix_core_large_uniform(M):
+    """3-4 rows of a single-width layer above 2 * 4096^2 weights run the
+    matrix-core kernel (4-bit, 128-row groups: scale units of 4 blocks), with
+    2 columns per lane and a ragged last strip (8200 columns)."""
+    say(f"qgemv matrix-core 4096x8200 M={M}")
+    inp = _mixed_inputs([4] * 32, 128, 8200, M, seed=400 + M, zeros=True)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv 4096x8200 M={M}")
 
 
 @pytest.mark.parametrize("nblk", (1, 3, 64, 100, 128, 192, 256, 320, 448))
@@ -355,16 +385,15 @@ def test_grouped_qgemv_max_group_full_size():
     ("qgemv", [4] * 11, 4, False),        # single-row kernel, 4 rows
     ("qgemv", MIXED_BITS, 1, False),      # gather + multi-row VALU kernel
     ("qgemv", MIXED_BITS, 2, False),      # multi-row VALU kernel
-    ("qgemv", MIXED_BITS, 8, True),       # MFMA decode kernel (exact dequantization)
+    ("qgemv", MIXED_BITS, 8, False),      # matrix-core decode kernel (factored arithmetic)
     ("qgemm", MIXED_BITS, 64, True),      # prefill, several widths
     ("qgemm", [4] * 11, 64, True),        # prefill, one width
 ], ids=["row", "row-M4", "gather-valu-M1", "valu-M2", "mfma-M8", "qgemm-mixed", "qgemm-4bit"])
 def test_nonfinite_activations(op, bits, M, exact):
     """A NaN activation makes its whole output row NaN; an Inf activation makes
-    every column of its row non-finite (exact-dequant kernels: the IEEE result
-    of the float64 oracle, +-Inf or NaN where the weight is 0; the factored
-    decode kernels subtract 1024 X' - z X and give NaN). Other rows are
-    unaffected."""
+    every column of its row non-finite (prefill: the IEEE result of the
+    float64 oracle, +-Inf or NaN where the weight is 0; every decode kernel
+    subtracts 1024 X' + z X and gives NaN). Other rows are unaffected."""
     say(f"non-finite activations {op} M={M}")
     inp = _mixed_inputs(bits, 32, 520, max(M, 2), seed=77 + M, zeros=True)
     x = inp.x[:M].copy()

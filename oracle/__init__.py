@@ -18,6 +18,10 @@ Every function follows the pages' description of the method:
   page, GPTQ paragraph: kernels fuse scaling, addition and activation).
 * The on-the-fly LoRA update, joined to the epilogue as an addend (ExLlamaV2
   artifact page, LoRA adapters).
+* EXL2 two-level scales: 4-bit scale codes times a per-output maximum scale
+  (ExLlamaV2 blog, "How the EXL2 Quantization Pipeline Works Under the Hood",
+  Step 3, and "How the Fused CUDA Kernel Works"). The value of a scale code is
+  a reading of this package (parity unpinned).
 """
 
 from .qlinear_oracle import (  # noqa: F401
@@ -42,4 +46,11 @@ from .qlinear_oracle import (  # noqa: F401
     silu,
     apply_epilogue,
     lora_delta,
+    QSCALE_CODES_PER_WORD,
+    qscale_pack,
+    qscale_unpack,
+    two_level_scales,
+    dequant_qscale,
+    dequant_qscale_fp16,
+    qlinear_qscale,
 )

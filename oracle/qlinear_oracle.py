@@ -27,8 +27,12 @@ gs rows per group, G = K / gs groups, b_g the bit width of group g):
    :func:`apply_epilogue`), where the addend may be the on-the-fly LoRA
    update of :func:`lora_delta`.
 
-Parity unpinned: nothing here. Every function is pinned by tests that do not
-re-use its formula (see ``tests/test_oracle_pins.py``).
+6. EXL2 two-level scales (:func:`dequant_qscale`): 4-bit scale codes packed
+   into ``q_scale`` and one float16 ``q_scale_max`` per output column.
+
+Parity unpinned: the value (c + 1) / 16 that a two-level scale code c stands
+for (a reading; the pages give no mapping). Every function is pinned by tests
+that do not re-use its formula (see ``tests/test_oracle_pins.py``).
 """
 
 from __future__ import annotations
@@ -386,3 +390,95 @@ def lora_delta(x, adapters) -> np.ndarray:
     if out is None:
         raise ValueError("at least one adapter")
     return out
+
+
+# ---------------------------------------------------------------- two-level scales
+#
+# The EXL2 tensor set (ExLlamaV2 blog, "How the EXL2 Quantization Pipeline
+# Works Under the Hood", Step 3) keeps the group scales as 4-bit codes packed
+# into uint32 words (q_scale) beside one float16 maximum scale per output
+# feature (q_scale_max), and the blog's kernel sketch ("How the Fused CUDA
+# Kernel Works") dequantizes a 4-bit weight as (w - 8) * scale * scale_max.
+# The pages give neither the value a scale code stands for nor the order of
+# the codes in a word. Reading:
+#   * code c in [0, 15] stands for the relative scale (c + 1) / 16, so the
+#     largest code is the maximum scale itself and no code means zero;
+#   * the codes run along the output features, 8 per word, least significant
+#     nibble first (the sketch's nibble order for q_weights): column n of
+#     group g is nibble n % 8 of word q_scale[g][n // 8];
+#   * the groups are symmetric, z = 2^(b-1) (the sketch subtracts the
+#     midpoint 8 of a 4-bit code);
+#   * w = (q - z) * ((c + 1) / 16) * scale_max[n], in that order (the
+#     sketch's product; every factor is exact, so the order does not change
+#     the value).
+# Parity unpinned: the mapping c -> (c + 1) / 16 itself. No file and no formula
+# of the pages fixes it; the tests pin the packing, the indexing and the
+# product against the one-level definitions above.
+
+QSCALE_CODES_PER_WORD = 8
+
+
+def qscale_pack(codes) -> np.ndarray:
+    """Scale codes uint8 [G][N] (each < 16, N % 8 == 0) -> q_scale uint32 [G][N/8]."""
+    c = np.asarray(codes)
+    if c.ndim != 2 or c.shape[1] % QSCALE_CODES_PER_WORD:
+        raise ValueError("codes must be [G][N] with N a multiple of 8")
+    if c.size and int(c.max()) > 15:
+        raise ValueError("scale codes are 4-bit")
+    G, N = c.shape
+    words = np.zeros((G, N // QSCALE_CODES_PER_WORD), dtype=np.uint32)
+    for n in range(N):
+        words[:, n // 8] |= c[:, n].astype(np.uint32) << np.uint32(4 * (n % 8))
+    return words
+
+
+def qscale_unpack(words, N: int) -> np.ndarray:
+    """Inverse of :func:`qscale_pack`: uint32 [G][N/8] -> uint8 codes [G][N]."""
+    w = np.asarray(words, dtype=np.uint32)
+    if w.ndim != 2 or w.shape[1] * QSCALE_CODES_PER_WORD != N:
+        raise ValueError("q_scale must be [G][N/8]")
+    c = np.zeros((w.shape[0], N), dtype=np.uint8)
+    for n in range(N):
+        c[:, n] = ((w[:, n // 8] >> np.uint32(4 * (n % 8))) & np.uint32(15)).astype(np.uint8)
+    return c
+
+
+def two_level_scales(q_scale, q_scale_max, N: int) -> np.ndarray:
+    """The effective group scales scale[g][n] * scale_max[n] in float64 [G][N]."""
+    c = qscale_unpack(q_scale, N).astype(np.float64)
+    smax = np.asarray(q_scale_max, dtype=np.float16).astype(np.float64).reshape(-1)
+    if smax.shape[0] != N:
+        raise ValueError("q_scale_max must hold one float16 per output feature")
+    return ((c + 1.0) / 16.0) * smax[None, :]
+
+
+def dequant_qscale(q, q_scale, q_scale_max, bits, gs: int) -> np.ndarray:
+    """w[j][n] = (q[j][n] - 2^(b_g - 1)) * scale[g][n] * scale_max[n], g = j // gs, float64.
+
+    Exact: |q - z| <= 128 (8 bits), c + 1 <= 16 and scale_max has 11
+    significant bits, so the product needs at most 24 bits.
+    """
+    q = np.asarray(q)
+    K, N = q.shape
+    bits = _check_bits(bits, K, gs)
+    s = two_level_scales(q_scale, q_scale_max, N)
+    if s.shape[0] != bits.shape[0]:
+        raise ValueError("q_scale must hold one row per group")
+    z = zero_points(None, bits, N)
+    return (q.astype(np.float64) - np.repeat(z, gs, axis=0)) * np.repeat(s, gs, axis=0)
+
+
+def dequant_qscale_fp16(q, q_scale, q_scale_max, bits, gs: int) -> np.ndarray:
+    """The two-level dequantized weights rounded once to float16."""
+    return dequant_qscale(q, q_scale, q_scale_max, bits, gs).astype(np.float16)
+
+
+def qlinear_qscale(x, q, q_scale, q_scale_max, bits, gs: int, perm=None) -> np.ndarray:
+    """y = x[:, perm] @ w in float64 with the two-level weights of :func:`dequant_qscale`."""
+    x = np.asarray(x, dtype=np.float16).astype(np.float64)
+    q = np.asarray(q)
+    K = q.shape[0]
+    if x.ndim != 2 or x.shape[1] != K:
+        raise ValueError("x must be [M][K]")
+    p = _perm_or_identity(perm, K)
+    return x[:, p] @ dequant_qscale(q, q_scale, q_scale_max, bits, gs)

@@ -533,3 +533,123 @@ def test_lora_planted_mistakes_are_caught(monkeypatch):
                 except AssertionError:
                     failed += 1
             assert failed > 0, f"no pin caught {bad.__name__}"
+
+
+# ------------------------------------------------------------------ two-level scales
+
+def test_qscale_nibble_order_hand_words():
+    # Codes 0..7 in columns 0..7 give the word 0x76543210, the nibble order of
+    # the blog's kernel sketch; codes 15..8 in columns 8..15 give 0x89ABCDEF.
+    c = np.concatenate([np.arange(8), 15 - np.arange(8)]).astype(np.uint8)[None, :]
+    w = oracle.qscale_pack(c)
+    assert w.shape == (1, 2) and int(w[0, 0]) == 0x76543210 and int(w[0, 1]) == 0x89ABCDEF
+    assert np.array_equal(oracle.qscale_unpack(w, 16), c)
+
+
+def test_qscale_round_trip_and_rejects():
+    rng = np.random.default_rng(12)
+    c = rng.integers(0, 16, size=(7, 40), dtype=np.uint8)
+    assert np.array_equal(oracle.qscale_unpack(oracle.qscale_pack(c), 40), c)
+    with pytest.raises(ValueError):
+        oracle.qscale_pack(np.full((1, 8), 16, np.uint8))
+    with pytest.raises(ValueError):
+        oracle.qscale_pack(np.zeros((1, 12), np.uint8))
+
+
+def test_qscale_dequant_hand_values(golden_dir):
+    with open(os.path.join(golden_dir, "qscale_examples.json")) as f:
+        ex = json.load(f)["examples"]
+    for e in ex:
+        b = e["b"]
+        q = np.full((32, 8), e["q"], dtype=np.uint8)
+        codes = np.full((1, 8), e["c"], dtype=np.uint8)
+        smax = np.full(8, int(e["smax_bits"], 16), dtype=np.uint16).view(np.float16)
+        w16 = oracle.dequant_qscale_fp16(q, oracle.qscale_pack(codes), smax, [b], 32)
+        assert (w16 == np.float16(float(e["w16"]))).all(), (e, float(w16[0, 0]))
+
+
+def test_qscale_largest_code_is_the_one_level_scale():
+    # Every code 15: the group scale is 1 and the weights are those of the
+    # one-level definition with scale_max as every group's scale.
+    rng = np.random.default_rng(13)
+    bits = [6, 5, 4, 3, 2, 8]
+    K, N = 32 * len(bits), 24
+    q = np.concatenate([rng.integers(0, 1 << b, size=(32, N), dtype=np.uint8) for b in bits])
+    smax = rng.uniform(0.005, 0.02, size=N).astype(np.float16)
+    words = oracle.qscale_pack(np.full((len(bits), N), 15, np.uint8))
+    one = oracle.dequant(q, np.repeat(smax[None, :], len(bits), axis=0), None, bits, 32)
+    assert np.array_equal(oracle.dequant_qscale(q, words, smax, bits, 32), one)
+
+
+def test_qscale_each_group_and_column_its_own_factor():
+    # Group g, column n holds code (g + 3n) % 16; column n has scale_max 2^-n;
+    # code 12 in every 4-bit row: w = (12 - 8) * ((g + 3n) % 16 + 1)/16 * 2^-n.
+    G, N = 4, 16
+    q = np.full((32 * G, N), 12, dtype=np.uint8)
+    codes = np.array([[(g + 3 * n) % 16 for n in range(N)] for g in range(G)], dtype=np.uint8)
+    smax = (2.0 ** -np.arange(N)).astype(np.float16)
+    w = oracle.dequant_qscale(q, oracle.qscale_pack(codes), smax, [4] * G, 32)
+    for g in range(G):
+        for n in range(N):
+            assert (w[32 * g:32 * (g + 1), n] == 4.0 * ((g + 3 * n) % 16 + 1) / 16.0 * 2.0 ** -n).all()
+
+
+def test_qscale_layer_equals_one_level_layer_with_exact_scales():
+    # With scale_max a power of two, every effective scale (c + 1)/16 * smax is
+    # exact in float16: the two-level layer must equal the one-level layer
+    # (independently pinned) fed those scales, act-order included.
+    rng = np.random.default_rng(14)
+    bits = [5, 4, 4, 3]
+    G, N = len(bits), 32
+    K = 32 * G
+    q = np.concatenate([rng.integers(0, 1 << b, size=(32, N), dtype=np.uint8) for b in bits])
+    codes = rng.integers(0, 16, size=(G, N), dtype=np.uint8)
+    smax = (2.0 ** rng.integers(-9, -5, size=N)).astype(np.float16)
+    s1 = ((codes.astype(np.float64) + 1.0) / 16.0 * smax.astype(np.float64)[None, :]).astype(np.float16)
+    assert np.array_equal(s1.astype(np.float64), (codes + 1.0) / 16.0 * smax.astype(np.float64)[None, :])
+    x = rng.standard_normal((3, K)).astype(np.float16)
+    perm = rng.permutation(K)
+    y2 = oracle.qlinear_qscale(x, q, oracle.qscale_pack(codes), smax, bits, 32, perm)
+    y1 = oracle.qlinear(x, q, s1, None, bits, 32, perm)
+    assert np.allclose(y2, y1, rtol=1e-12, atol=0)
+
+
+def test_qscale_planted_mistakes_are_caught(golden_dir, monkeypatch):
+    """Plant plausible slips into the two-level oracle; a pin must fail for each."""
+    good_pack, good_unpack, good_scales = qo.qscale_pack, qo.qscale_unpack, qo.two_level_scales
+
+    def msb_first_pack(codes):
+        c = np.asarray(codes)
+        w = np.zeros((c.shape[0], c.shape[1] // 8), np.uint32)
+        for n in range(c.shape[1]):
+            w[:, n // 8] |= c[:, n].astype(np.uint32) << np.uint32(4 * (7 - n % 8))
+        return w
+
+    def code_over_16(q_scale, q_scale_max, N):
+        c = good_unpack(q_scale, N).astype(np.float64)
+        return c / 16.0 * np.asarray(q_scale_max, np.float16).astype(np.float64)[None, :]
+
+    def smax_by_group(q_scale, q_scale_max, N):
+        s = good_scales(q_scale, q_scale_max, N)
+        smax = np.asarray(q_scale_max, np.float16).astype(np.float64)
+        return s / smax[None, :] * smax[:s.shape[0], None] if s.shape[0] <= N else s
+
+    def codes_of_next_column(q_scale, q_scale_max, N):
+        c = np.roll(good_unpack(q_scale, N).astype(np.float64), 1, axis=1)
+        return (c + 1.0) / 16.0 * np.asarray(q_scale_max, np.float16).astype(np.float64)[None, :]
+
+    planted = [("qscale_pack", msb_first_pack), ("two_level_scales", code_over_16),
+               ("two_level_scales", smax_by_group), ("two_level_scales", codes_of_next_column)]
+    pins = [test_qscale_nibble_order_hand_words, lambda: test_qscale_dequant_hand_values(golden_dir),
+            test_qscale_each_group_and_column_its_own_factor, test_qscale_largest_code_is_the_one_level_scale]
+    for name, bad in planted:
+        with monkeypatch.context() as mp:
+            mp.setattr(qo, name, bad)
+            mp.setattr(oracle, name, bad)
+            failed = 0
+            for pin in pins:
+                try:
+                    pin()
+                except (AssertionError, ValueError):
+                    failed += 1
+            assert failed > 0, f"no pin caught the planted slip in {name} ({bad.__name__})"

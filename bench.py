@@ -479,12 +479,34 @@ def reference_points(torch, lib, stream, sizes):
 def bench_configs(torch, dq, wl, lib, dev, stream, spin):
     """qgemv on every (layer, M) of the decode configs that the step does not
     cover: the 7B shapes at M = 4 and 16, EXL2 4.0 bpw at M = 1 and 8, the 70B
-    EXL2 2.5 bpw pair at M = 1 and 16. Per point, >= 256 calls back to back
-    behind a spin kernel, cycling through distinct weight copies totalling
-    >= 1 GiB (so the Infinity Cache cannot serve them), between two events on
-    the launch stream; GB/s counts the weight bytes (codes, scales, zeros)."""
+    EXL2 2.5 bpw pair at M = 1 and 16; and the EXL2 layers again with
+    two-level scales (4-bit scale codes and a float16 maximum per output,
+    qlinear_qgemv_qscale). Per point, >= 256 calls back to back behind a spin
+    kernel, cycling through distinct weight copies totalling >= 1 GiB (so the
+    Infinity Cache cannot serve them), between two events on the launch
+    stream; GB/s counts the weight bytes (codes, scales, zeros; two-level:
+    codes, scale codes, maximum scales)."""
     sh = stream.cuda_stream
     points = []
+
+    def time_point(name, M, wbytes, calls, scales_kind):
+        for c in calls[:4]:
+            c()
+        ncopy = len(calls)
+        n = max(256, ncopy)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(spin)
+        e0.record(stream)
+        for i in range(n):
+            calls[i % ncopy]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        points.append({"workload": name, "M": M, "scales": scales_kind, "us_per_call": round(us, 2),
+                       "weight_bytes": wbytes, "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1)})
+        log(f"config point {name} M={M} ({scales_kind} scales): {us:.2f} us, {points[-1]['weight_gbs']} GB/s")
+
     plan = [(s, (4, 16)) for s in wl.LLAMA7B_DECODE] + [(wl.EXL2_MIXED, (1, 8))] + \
         [(s, (1, 16)) for s in wl.LLAMA70B_EXL2]
     for spec, Ms in plan:
@@ -494,30 +516,31 @@ def bench_configs(torch, dq, wl, lib, dev, stream, spin):
         sc = torch.from_numpy(inp.scales).to(dev)
         zr = None if inp.zeros is None else torch.from_numpy(inp.zeros).to(dev)
         pm = torch.from_numpy(inp.perm).to(dev)
+        ws = dq.qgemv_workspace(L, dev)
         wbytes = wl.weight_bytes(spec)
         ncopy = max(2, -(-(1 << 30) // wbytes))
         copies = [(qw.clone(), sc.clone(), None if zr is None else zr.clone()) for _ in range(ncopy)]
-        ws = dq.qgemv_workspace(L, dev)
         for M in Ms:
             x = torch.from_numpy(inp.x[:M].copy()).to(dev)
             y = torch.empty((M, spec.N), dtype=torch.float16, device=dev)
-            calls = [Launch(lib.qlinear_qgemv, L, x, M, q, c, z, pm, y, ws, sh) for q, c, z in copies]
-            for c in calls[:4]:
-                c()
-            n = max(256, ncopy)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            torch.cuda._sleep(spin)
-            e0.record(stream)
-            for i in range(n):
-                calls[i % ncopy]()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / n
-            points.append({"workload": spec.name, "M": M, "us_per_call": round(us, 2),
-                           "weight_gbs": round(wbytes / (us * 1e-6) / 1e9, 1)})
-            log(f"config point {spec.name} M={M}: {us:.2f} us, {points[-1]['weight_gbs']} GB/s")
-        del copies, qw
+            time_point(spec.name, M, wbytes,
+                       [Launch(lib.qlinear_qgemv, L, x, M, q, c, z, pm, y, ws, sh) for q, c, z in copies], "fp16")
+        del copies
+        if spec.symmetric:
+            codes, smax = wl.two_level_scales(spec)
+            qs = dq.pack_qscale(torch.from_numpy(codes).to(dev))
+            qsm = torch.from_numpy(smax).to(dev)
+            wbytes = wl.weight_bytes_two_level(spec)
+            ncopy = max(2, -(-(1 << 30) // wbytes))
+            copies = [(qw.clone(), qs.clone(), qsm.clone()) for _ in range(ncopy)]
+            for M in Ms:
+                x = torch.from_numpy(inp.x[:M].copy()).to(dev)
+                y = torch.empty((M, spec.N), dtype=torch.float16, device=dev)
+                time_point(spec.name, M, wbytes,
+                           [Call(lib.qlinear_qgemv_qscale, L, x, M, q, a, b, pm, None, y, ws, sh) for q, a, b in copies],
+                           "two-level")
+            del copies
+        del qw
     return points
 
 

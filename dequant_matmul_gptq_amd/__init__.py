@@ -31,4 +31,8 @@ from ._lib import (  # noqa: F401
     qgemv_workspace_bytes,
     status_string,
     unpack,
+    pack_qscale,
+    dequant_qscale,
+    qgemv_qscale,
+    qgemm_qscale,
 )

@@ -46,6 +46,10 @@ EXPORTS = (
     "qlinear_lora_workspace_bytes",
     "qlinear_lora_delta",
     "qlinear_read_floor",
+    "qlinear_pack_qscale",
+    "qlinear_dequant_qscale",
+    "qlinear_qgemv_qscale",
+    "qlinear_qgemm_qscale",
 )
 
 ACT_NONE = 0
@@ -114,6 +118,10 @@ def lib() -> ctypes.CDLL:
         L.qlinear_lora_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.qlinear_lora_delta.argtypes = [vp, i32, i32, vp, i32, vp, i32, ctypes.c_float, i32, vp, vp, sz, vp]
         L.qlinear_read_floor.argtypes = [vp, sz, i32, i32, ctypes.c_uint32, vp, vp]
+        L.qlinear_pack_qscale.argtypes = [vp, i32, i32, vp, vp]
+        L.qlinear_dequant_qscale.argtypes = [lp, vp, vp, vp, vp, vp]
+        L.qlinear_qgemv_qscale.argtypes = [lp, vp, i32, vp, vp, vp, vp, ep, vp, vp, sz, vp]
+        L.qlinear_qgemm_qscale.argtypes = [lp, vp, i32, vp, vp, vp, vp, ep, vp, vp, sz, vp]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -363,3 +371,83 @@ def lora_delta(x: torch.Tensor, lora_a: torch.Tensor, lora_b: torch.Tensor, scal
                                     1 if accumulate else 0, _ptr(delta), _ptr(workspace), workspace.numel(),
                                     _stream(x.device)), "qlinear_lora_delta")
     return delta
+
+
+# ---------------------------------------------------------------- two-level scales
+
+def pack_qscale(codes: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """4-bit scale codes uint8 [G][N] -> q_scale int32 [G][N/8] (uint32 bit
+    patterns, 8 codes per word, column n at bits 4 (n % 8))."""
+    if codes.dim() != 2:
+        raise ValueError("codes must be [G][N]")
+    G, N = int(codes.shape[0]), int(codes.shape[1])
+    _dev(codes, "codes", torch.uint8)
+    if out is None:
+        out = torch.empty((G, N // 8), dtype=torch.int32, device=codes.device)
+    _dev(out, "q_scale", torch.int32, (G, N // 8))
+    _check(lib().qlinear_pack_qscale(_ptr(codes), G, N, _ptr(out), _stream(codes.device)), "qlinear_pack_qscale")
+    return out
+
+
+def _qscale_operands(layout, q_scale, q_scale_max):
+    _dev(q_scale, "q_scale", torch.int32, (layout.groups, layout.N // 8))
+    _dev(q_scale_max, "q_scale_max", torch.float16, (layout.N,))
+
+
+def dequant_qscale(layout: Layout, qweight: torch.Tensor, q_scale: torch.Tensor,
+                   q_scale_max: torch.Tensor) -> torch.Tensor:
+    """Two-level dequantized weights float16 [K][N] (stored row order)."""
+    _dev(qweight, "qweight", torch.int32, layout.qweight_shape)
+    _qscale_operands(layout, q_scale, q_scale_max)
+    w = torch.empty((layout.K, layout.N), dtype=torch.float16, device=qweight.device)
+    _check(lib().qlinear_dequant_qscale(layout.ref, _ptr(qweight), _ptr(q_scale), _ptr(q_scale_max), _ptr(w),
+                                        _stream(w.device)), "qlinear_dequant_qscale")
+    return w
+
+
+def _qscale_gemm_operands(layout, x, qweight, q_scale, q_scale_max, perm, y):
+    if x.dim() != 2 or x.shape[1] != layout.K:
+        raise ValueError(f"x must be [M][{layout.K}]")
+    M = int(x.shape[0])
+    _dev(x, "x", torch.float16)
+    _dev(qweight, "qweight", torch.int32, layout.qweight_shape)
+    _qscale_operands(layout, q_scale, q_scale_max)
+    if perm is not None:
+        _dev(perm, "perm", torch.int32, (layout.K,))
+    if y is None:
+        y = torch.empty((M, layout.N), dtype=torch.float16, device=x.device)
+    _dev(y, "y", torch.float16, (M, layout.N))
+    return M, y
+
+
+def qgemv_qscale(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, q_scale: torch.Tensor,
+                 q_scale_max: torch.Tensor, perm: torch.Tensor | None, workspace: torch.Tensor,
+                 y: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+                 residual: torch.Tensor | None = None, activation: int = ACT_NONE,
+                 addend: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode layer with two-level scales (M <= 16); epilogue as for qgemv."""
+    M, y = _qscale_gemm_operands(layout, x, qweight, q_scale, q_scale_max, perm, y)
+    _dev(workspace, "workspace", torch.uint8)
+    epi = _epilogue(layout, M, y, bias, residual, activation, addend)
+    _check(lib().qlinear_qgemv_qscale(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(q_scale), _ptr(q_scale_max),
+                                      _ptr(perm), None if epi is None else ctypes.byref(epi), _ptr(y),
+                                      _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemv_qscale")
+    return y
+
+
+def qgemm_qscale(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, q_scale: torch.Tensor,
+                 q_scale_max: torch.Tensor, perm: torch.Tensor | None, workspace: torch.Tensor | None = None,
+                 y: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+                 residual: torch.Tensor | None = None, activation: int = ACT_NONE,
+                 addend: torch.Tensor | None = None) -> torch.Tensor:
+    """Prefill layer with two-level scales, any M; epilogue as for qgemv."""
+    M, y = _qscale_gemm_operands(layout, x, qweight, q_scale, q_scale_max, perm, y)
+    need = qgemm_workspace_bytes(layout, M)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    epi = _epilogue(layout, M, y, bias, residual, activation, addend)
+    _check(lib().qlinear_qgemm_qscale(layout.ref, _ptr(x), M, _ptr(qweight), _ptr(q_scale), _ptr(q_scale_max),
+                                      _ptr(perm), None if epi is None else ctypes.byref(epi), _ptr(y),
+                                      _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemm_qscale")
+    return y

@@ -85,13 +85,22 @@ int check_gemm_operands(const qlinear_layout* layout, const uint16_t* x, int32_t
 
 // The epilogue of a fused call (NULL: none).
 int check_epilogue(const qlinear_epilogue* e, Epilogue& out) {
-  out = Epilogue{nullptr, nullptr, nullptr, QLINEAR_ACT_NONE};
+  out = Epilogue{nullptr, nullptr, nullptr, QLINEAR_ACT_NONE, nullptr};
   if (!e) return QLINEAR_OK;
   if (e->activation != QLINEAR_ACT_NONE && e->activation != QLINEAR_ACT_SILU) return QLINEAR_ERR_UNSUPPORTED;
   if ((e->bias && !aligned16(e->bias)) || (e->residual && !aligned16(e->residual)) ||
       (e->addend && !aligned16(e->addend)))
     return QLINEAR_ERR_MISALIGNED;
-  out = Epilogue{e->bias, e->residual, e->addend, e->activation};
+  out = Epilogue{e->bias, e->residual, e->addend, e->activation, nullptr};
+  return QLINEAR_OK;
+}
+
+// The two-level scale operands: q_scale (uint32 [G][N/8]) and q_scale_max
+// (float16 [N]), both required; the epilogue then carries q_scale_max.
+int check_qscale(const uint32_t* q_scale, const uint16_t* q_scale_max, Epilogue& epi) {
+  if (!q_scale || !q_scale_max) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_scale) || !aligned16(q_scale_max)) return QLINEAR_ERR_MISALIGNED;
+  epi.scale_max = q_scale_max;
   return QLINEAR_OK;
 }
 
@@ -200,7 +209,8 @@ int qlinear_dequant(const qlinear_layout* layout, const uint32_t* qweight, const
   if (!qweight || !scales || !w) return QLINEAR_ERR_INVALID_ARGUMENT;
   if (!aligned16(qweight) || !aligned16(scales) || !aligned16(w) || (zeros && !aligned16(zeros)))
     return QLINEAR_ERR_MISALIGNED;
-  return hip_status(launch_dequant(*layout, make_runs(*layout), qweight, scales, zeros, w, (hipStream_t)stream));
+  return hip_status(
+      launch_dequant(*layout, make_runs(*layout), qweight, scales, zeros, nullptr, w, (hipStream_t)stream));
 }
 
 int qlinear_qgemv_workspace_bytes(const qlinear_layout* layout, size_t* bytes) {
@@ -269,7 +279,8 @@ int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32
   if (M > QLINEAR_GEMV_MAX_M || (M > 2 && !qgemv_mx_supported(*layout))) return QLINEAR_ERR_UNSUPPORTED;
   if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
   return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, count, qweights_host, scales_host,
-                                 zeros ? zeros_host : nullptr, y_host, workspace, Epilogue{nullptr, nullptr, nullptr, 0},
+                                 zeros ? zeros_host : nullptr, y_host, workspace,
+                                 Epilogue{nullptr, nullptr, nullptr, QLINEAR_ACT_NONE, nullptr},
                                  (hipStream_t)stream));
 }
 
@@ -301,6 +312,64 @@ int qlinear_qgemm(const qlinear_layout* layout, const uint16_t* x, int32_t M, co
                   void* workspace, size_t workspace_bytes, void* stream) {
   return qlinear_qgemm_fused(layout, x, M, qweight, scales, zeros, perm, nullptr, y, workspace, workspace_bytes,
                              stream);
+}
+
+int qlinear_pack_qscale(const uint8_t* codes, int32_t groups, int32_t N, uint32_t* q_scale, void* stream) {
+  if (groups < 0 || N < 0) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (N % 8 != 0) return QLINEAR_ERR_UNSUPPORTED;
+  if (groups == 0 || N == 0) return QLINEAR_OK;
+  if (!codes || !q_scale) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(codes) || !aligned16(q_scale)) return QLINEAR_ERR_MISALIGNED;
+  return hip_status(launch_pack_qscale(codes, groups, N, q_scale, (hipStream_t)stream));
+}
+
+int qlinear_dequant_qscale(const qlinear_layout* layout, const uint32_t* qweight, const uint32_t* q_scale,
+                           const uint16_t* q_scale_max, uint16_t* w, void* stream) {
+  int st = check_layout(layout);
+  if (st != QLINEAR_OK) return st;
+  if (!qweight || !w) return QLINEAR_ERR_INVALID_ARGUMENT;
+  Epilogue epi{};
+  st = check_qscale(q_scale, q_scale_max, epi);
+  if (st != QLINEAR_OK) return st;
+  if (!aligned16(qweight) || !aligned16(w)) return QLINEAR_ERR_MISALIGNED;
+  return hip_status(launch_dequant(*layout, make_runs(*layout), qweight, reinterpret_cast<const uint16_t*>(q_scale),
+                                   nullptr, q_scale_max, w, (hipStream_t)stream));
+}
+
+int qlinear_qgemv_qscale(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                         const uint32_t* q_scale, const uint16_t* q_scale_max, const int32_t* perm,
+                         const qlinear_epilogue* epilogue, uint16_t* y, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  const uint16_t* sc = reinterpret_cast<const uint16_t*>(q_scale);
+  int st = check_gemm_operands(layout, x, M, qweight, sc, nullptr, perm, y, workspace);
+  if (st != QLINEAR_OK) return st;
+  Epilogue epi;
+  st = check_epilogue(epilogue, epi);
+  if (st != QLINEAR_OK || M == 0) return st;
+  st = check_qscale(q_scale, q_scale_max, epi);
+  if (st != QLINEAR_OK) return st;
+  if (M > QLINEAR_GEMV_MAX_M || (M > 2 && !qgemv_mx_supported(*layout))) return QLINEAR_ERR_UNSUPPORTED;
+  if (workspace_bytes < qgemv_workspace_bytes(layout->K)) return QLINEAR_ERR_WORKSPACE;
+  return hip_status(launch_qgemv(*layout, make_runs(*layout), x, M, perm, 1, &qweight, &sc, nullptr, &y, workspace,
+                                 epi, (hipStream_t)stream));
+}
+
+int qlinear_qgemm_qscale(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                         const uint32_t* q_scale, const uint16_t* q_scale_max, const int32_t* perm,
+                         const qlinear_epilogue* epilogue, uint16_t* y, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  const uint16_t* sc = reinterpret_cast<const uint16_t*>(q_scale);
+  int st = check_gemm_operands(layout, x, M, qweight, sc, nullptr, perm, y, workspace);
+  if (st != QLINEAR_OK) return st;
+  Epilogue epi;
+  st = check_epilogue(epilogue, epi);
+  if (st != QLINEAR_OK || M == 0) return st;
+  st = check_qscale(q_scale, q_scale_max, epi);
+  if (st != QLINEAR_OK) return st;
+  if (M > kMaxGemmM || !qgemm_supported(*layout)) return QLINEAR_ERR_UNSUPPORTED;
+  if (workspace_bytes < qgemm_workspace_bytes(*layout, M)) return QLINEAR_ERR_WORKSPACE;
+  return hip_status(launch_qgemm(*layout, make_runs(*layout), x, M, qweight, sc, nullptr, perm, y, workspace, epi,
+                                 (hipStream_t)stream));
 }
 
 int qlinear_read_floor(const void* buf, size_t bytes, int32_t loads_per_thread, int32_t workgroups, uint32_t key,

@@ -397,18 +397,18 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
   for (int m0 = 0; m0 < M; m0 += chunk) {
     const int mc = std::min(chunk, M - m0);
     uint32_t* xq = reinterpret_cast<uint32_t*>(ws);
-    // MFMA pair order for the register-dequant kernel; natural order for the
-    // kernel that dequantizes into LDS.
+    // Many runs of several code widths, or two-level scales (whose codes only
+    // that kernel reads): the kernel that dequantizes into LDS. MFMA pair
+    // order for the register-dequant kernel; natural order for the other.
     const bool mixed = (set & (set - 1)) != 0;
-    const bool split = qgemm_split_runs(L);
-    hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, !mixed || split, stream);
+    const bool lds = (mixed && !qgemm_split_runs(L)) || epi.scale_max != nullptr;
+    hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, !lds, stream);
     if (e != hipSuccess) return e;
     uint16_t* yc = y + (size_t)m0 * L.N;
     Epilogue ec = epi;   // the chunk's rows of the residual and the addend
     if (ec.residual) ec.residual += (size_t)m0 * L.N;
     if (ec.addend) ec.addend += (size_t)m0 * L.N;
-    // Many runs of several code widths: the kernel that dequantizes into LDS.
-    if (mixed && !split) {
+    if (lds) {
       e = launch_qgemm_lds(L, runs, reinterpret_cast<const uint16_t*>(xq), mc, qweight, scales, zeros, yc, ec,
                            stream);
       if (e != hipSuccess) return e;

@@ -37,7 +37,12 @@ __device__ __forceinline__ void dequant_to_lds(const LdsGemmArgs& a, int row, in
   _Float16 s = (_Float16)0.0f;
   int z = 1 << (B - 1);
   if (valid) {
-    s = __builtin_bit_cast(_Float16, a.scales[(size_t)g * a.N + n]);
+    // Two-level scales: the group factor c + 1, exact in float16, so that
+    // s * (q - z) stays an exact integer; scale_max / 16 comes in the epilogue.
+    if (a.epi.scale_max)
+      s = (_Float16)qscale_factor(reinterpret_cast<const uint32_t*>(a.scales)[(size_t)g * (a.N / 8) + n / 8], n);
+    else
+      s = __builtin_bit_cast(_Float16, a.scales[(size_t)g * a.N + n]);
     if (a.zeros) z = a.zeros[(size_t)g * a.N + n];
   }
   const _Float16 nb = (_Float16)(-(1024 + z));

@@ -80,7 +80,9 @@ struct MxArgs {
   int nstrips, strips_per_xcd;
   int packed_rows;
   int64_t packed_words;
-  int scale_bytes;
+  int scale_bytes;       // bytes of the scales operand (float16 [G][N], or two-level codes [G][N/8] uint32)
+  int scale_row_bytes;   // bytes per group row of the scales operand
+  int two_level;         // 1: the scales operand holds two-level scale codes
   int lds_perm, lds_xg;   // byte offsets of the LDS regions (one-launch modes)
   // Each wave's blocks [b0, b1) (whole groups) and its first segment (the
   // part of the run holding b0): its end block, first packed row and width.
@@ -150,8 +152,10 @@ struct Lane {
   uint32_t sbase;     // byte offset of the lane's first scale in a scale row
   uint32_t zbase;
   uint32_t xoff;      // A fragment offset inside a block's fragments (bytes)
-  uint32_t sshift;    // bit position of the lane's first scale in its loaded dword
+  uint32_t sshift;    // bit position of the lane's first scale (or scale code) in its loaded dword
   uint32_t zshift;    // bit position of the lane's first zero point in its loaded dword
+  uint32_t srow;      // bytes per group row of the scales operand
+  bool tl;            // two-level scale codes in place of float16 scales
   uint32_t magic;
   int g;              // k-group
   int n;              // column of the lane inside a 16-column fragment
@@ -212,7 +216,7 @@ __device__ __forceinline__ void issue_words(const Lane& L, const WidthConsts<B>&
 template <int B, int FN, int UB, int kMode>
 __device__ __forceinline__ void issue_params(const Lane& L, int blk, int grp, int N, Slot<B, FN, UB>& S) {
   const uint32_t go = (uint32_t)grp * (uint32_t)N;
-  S.s0 = load_scales<FN>(L.rs, L.sbase, go * 2u, S.s1);
+  S.s0 = load_scales<FN>(L.rs, L.sbase, (uint32_t)grp * L.srow, S.s1);
   S.z = load_zeros(L.rz, L.zbase, go);
   if constexpr (kMode == kGathered) {
 #pragma unroll
@@ -248,7 +252,7 @@ __device__ __forceinline__ float row_bcast(float v, int lane_in_row) {
 // broadcast from columns 0 and 1 of the sums.
 template <int FN, int kMode>
 __device__ __forceinline__ void epilogue(uint32_t s0, uint32_t s1, uint32_t zw, uint32_t sshift, uint32_t zshift,
-                                         int zsym, int hz,
+                                         bool tl, int zsym, int hz,
                                          const float4_t (&c0)[FN], const float4_t (&c1)[FN], const float4_t& sa0,
                                          const float4_t& sa1, bool two_chains, float4_t (&y)[FN]) {
   float Xs[4], X[4];
@@ -258,12 +262,15 @@ __device__ __forceinline__ void epilogue(uint32_t s0, uint32_t s1, uint32_t zw, 
     Xs[r] = 1024.0f * row_bcast(v, 0);
     X[r] = row_bcast(v, 1);
   }
-  const uint32_t sl = FN == 1 ? s0 >> sshift : s0;
+  const uint32_t sl = (FN == 1 || tl) ? s0 >> sshift : s0;
   const uint32_t zl = zw >> zshift;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const uint32_t sw = j < 2 ? sl : s1;
-    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw >> (16 * (j & 1))));
+    // Two-level scales: the code's factor c + 1 (scale_max / 16 is applied
+    // in the final epilogue).
+    const float s = tl ? (float)(((sl >> (4 * j)) & 15u) + 1u)
+                       : (float)__builtin_bit_cast(_Float16, (uint16_t)(sw >> (16 * (j & 1))));
     const float z = hz ? (float)((zl >> (8 * j)) & 0xFFu) : (float)zsym;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -337,13 +344,13 @@ __device__ __forceinline__ Acc<FN> segment(const MxArgs& a, const Lane& L, const
     if (i > 0) {
       // The previous unit: its epilogue, then its slot takes unit i - 1 + D.
       const Slot<B, FN, UB>& sp = S[dp];
-      epilogue<FN, kMode>(sp.s0, sp.s1, sp.z, L.sshift, L.zshift, zsym, hz, A.acc[p ^ 1][0], A.acc[p ^ 1][1], A.sacc[p ^ 1][0],
+      epilogue<FN, kMode>(sp.s0, sp.s1, sp.z, L.sshift, L.zshift, L.tl, zsym, hz, A.acc[p ^ 1][0], A.acc[p ^ 1][1], A.sacc[p ^ 1][0],
                           A.sacc[p ^ 1][1], kTwo, A.y);
       if (steady) fill(i - 1 + D, S[dp]);
       else if (i - 1 + D < n) fill(i - 1 + D, S[dp]);
     }
     if (i == n - 1)
-      epilogue<FN, kMode>(s.s0, s.s1, s.z, L.sshift, L.zshift, zsym, hz, A.acc[p][0], A.acc[p][1], A.sacc[p][0], A.sacc[p][1], kTwo,
+      epilogue<FN, kMode>(s.s0, s.s1, s.z, L.sshift, L.zshift, L.tl, zsym, hz, A.acc[p][0], A.acc[p][1], A.sacc[p][0], A.sacc[p][1], kTwo,
                           A.y);
   };
 
@@ -440,14 +447,15 @@ __global__ __launch_bounds__(kThreads) void qgemv_mx_kernel(MxArgs a) {
   // takes them and hands them back, so none is read later behind another wait).
   MatPtrs mp = a.mat[blockIdx.y];
   int M = a.M, K = a.K, N = a.N, spx = a.strips_per_xcd, nstrips = a.nstrips, R = a.packed_rows;
-  int bpg_shift = a.bpg_shift, scale_bytes = a.scale_bytes, hz = a.has_zeros;
+  int bpg_shift = a.bpg_shift, scale_bytes = a.scale_bytes, hz = a.has_zeros, srow = a.scale_row_bytes,
+      tl = a.two_level;
   int64_t packed_words = a.packed_words;
   int b0 = a.wave_b0[wave], b1 = a.wave_b1[wave], s_end = a.wave_send[wave], row0 = a.wave_row0[wave];
   int bits0 = a.wave_bits0[wave], lds_perm = a.lds_perm, lds_xg = a.lds_xg;
   const uint16_t* xsrc16 = a.x;
   const int32_t* perm = a.perm;
   asm volatile("" : "+s"(mp.qweight), "+s"(mp.scales), "+s"(mp.zeros), "+s"(mp.y), "+s"(M), "+s"(K), "+s"(N),
-               "+s"(spx), "+s"(nstrips), "+s"(R), "+s"(bpg_shift), "+s"(scale_bytes), "+s"(hz),
+               "+s"(spx), "+s"(nstrips), "+s"(R), "+s"(bpg_shift), "+s"(scale_bytes), "+s"(hz), "+s"(srow), "+s"(tl),
                "+s"(packed_words), "+s"(b0), "+s"(b1), "+s"(s_end), "+s"(row0), "+s"(bits0), "+s"(lds_perm),
                "+s"(lds_xg), "+s"(xsrc16), "+s"(perm));
 
@@ -473,8 +481,15 @@ __global__ __launch_bounds__(kThreads) void qgemv_mx_kernel(MxArgs a) {
   // Lanes past N read the last columns (valid addresses) and are never stored.
   const int col = col_req < N ? col_req : N - FN;
   L.wbase = (uint32_t)(col / kPanel - strip * FN) * (uint32_t)R * kPanel * 4 + (uint32_t)(col % kPanel) * 4;
-  L.sbase = (uint32_t)(col & ~1) * 2;                       // FN >= 2: col is even
-  L.sshift = (uint32_t)(col & 1) * 16;
+  L.srow = (uint32_t)srow;
+  L.tl = tl != 0;
+  if (tl) {   // the word of 8 scale codes holding the lane's columns
+    L.sbase = (uint32_t)(col / 8) * 4;
+    L.sshift = 4u * (uint32_t)(col & 7);
+  } else {
+    L.sbase = (uint32_t)(col & ~1) * 2;                     // FN >= 2: col is even
+    L.sshift = (uint32_t)(col & 1) * 16;
+  }
   L.zbase = hz ? (uint32_t)(col & ~3) : (uint32_t)(col & ~1) * 2;   // FN == 4: col is a multiple of 4
   L.zshift = (uint32_t)(col & 3) * 8;
   const int mrow = min(lane & 15, M - 1);   // the A row of this lane (rows past M repeat row M - 1)
@@ -723,7 +738,9 @@ hipError_t launch_qgemv_mx(const qlinear_layout& L, const Runs& runs, const uint
   a.bpg_shift = bpg == 4 ? 2 : bpg == 2 ? 1 : 0;
   a.packed_rows = L.packed_rows;
   a.packed_words = L.packed_words;
-  a.scale_bytes = (int)((size_t)L.groups * L.N * 2);
+  a.two_level = epi.scale_max != nullptr;
+  a.scale_row_bytes = a.two_level ? L.N / 2 : L.N * 2;
+  a.scale_bytes = (int)((size_t)L.groups * a.scale_row_bytes);
   a.runs = runs;
   a.epi = epi;
   unsigned set = 0;

@@ -59,7 +59,10 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   // layers of up to 2 * 4096 * 4096 weights and the matrix-core kernel on
   // larger ones (1.1-1.4x); from 5 rows on the matrix-core kernel wins (up
   // to 1.4x; within 8% on 8-bit layouts).
-  const bool row = !epi.addend && stream::single_row(M, L.K, set);
+  // Two-level scales run the kernels that read scale codes: the matrix-core
+  // kernel, and the multi-row kernel's several-width instances.
+  const bool tl = epi.scale_max != nullptr;
+  const bool row = !epi.addend && !tl && stream::single_row(M, L.K, set);
   if (M >= 3 && !(row && (int64_t)L.K * L.N <= (int64_t)2 * 4096 * 4096))
     return launch_qgemv_mx(L, runs, x, M, perm, mats, qweights, scales, zeros, ys, ws, epi, stream);
   // The single-launch kernel takes no float32 addend: reading one more kernel
@@ -73,7 +76,7 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   if (e != hipSuccess) return e;
   a.xq = w.xq;
   a.xsum = w.xsum;
-  if ((set & (set - 1)) == 0) return stream::launch_uniform(set, a, stream);
+  if (!tl && (set & (set - 1)) == 0) return stream::launch_uniform(set, a, stream);
   return stream::launch_mixed(set, a, stream);
 }
 

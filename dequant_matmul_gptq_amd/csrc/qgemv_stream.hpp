@@ -101,8 +101,14 @@ __device__ __forceinline__ float half_hi(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
+// Bit of a kernel's width set that marks two-level scales (4-bit codes in
+// place of the float16 scales; scale_max comes in the epilogue).
+constexpr unsigned kTwoLevelBit = 1u << 16;
+template <unsigned BS>
+constexpr bool two_level() { return (BS & kTwoLevelBit) != 0; }
+
 struct Raw {
-  uint2 s;      // 4 float16 scales
+  uint2 s;      // 4 float16 scales (two-level: the code word, and the shift of the lane's first code)
   uint32_t z;   // 4 uint8 zero points
   bool ok;      // false: the lane has no block this step (contributes nothing)
 };
@@ -116,12 +122,22 @@ struct Raw {
 // loads in flight exactly (a branch around a load makes it wait for all of
 // them). A lane without work (ok == false) reads the valid block `blk_safe`
 // at `row_safe` instead and gets a zero scale, which zeroes its contribution.
-template <int B>
+template <int B, bool kTL = false>
 __device__ __forceinline__ void issue(const StreamArgs& a, const MatPtrs& mp, const uint32_t* panel, int blk,
                                       int row, bool ok, int blk_safe, int row_safe, int scol, uint4 (&W)[B], Raw& P) {
   const uint32_t* p = panel + (size_t)(ok ? row : row_safe) * kPanel;
 #pragma unroll
   for (int t = 0; t < B; ++t) W[t] = *reinterpret_cast<const uint4*>(p + t * kPanel);
+  if constexpr (kTL) {
+    // The word of 8 scale codes holding the lane's 4 columns (symmetric
+    // groups: no zero points). The shift is applied where the code is used.
+    const size_t gw = (size_t)((ok ? blk : blk_safe) >> a.bpg_shift) * (a.N / 8) + scol / 8;
+    P.s.x = reinterpret_cast<const uint32_t*>(mp.scales)[gw];
+    P.s.y = 4u * (uint32_t)(scol & 7);
+    P.z = 0u;
+    P.ok = ok;
+    return;
+  }
   const size_t g = (size_t)((ok ? blk : blk_safe) >> a.bpg_shift) * a.N + scol;
   const uint2 sv = *reinterpret_cast<const uint2*>(mp.scales + g);
   // Without zero points, read the scales again (any valid address): the value
@@ -136,7 +152,7 @@ __device__ __forceinline__ void issue(const StreamArgs& a, const MatPtrs& mp, co
 // Unpack and multiply one block (this lane's 4 columns), then fold in the
 // block's scale, zero point and bias. xs_blk points at pair 0 of the block for
 // activation row 0; rows are `row_stride` words apart. xs_sum likewise.
-template <int B, int MT>
+template <int B, int MT, bool kTL>
 __device__ __forceinline__ void compute(const StreamArgs& a, const uint4 (&W)[B], const Raw& P,
                                         const uint32_t* __restrict__ xs_blk, int row_stride,
                                         const float2* __restrict__ xsum_blk, int sum_stride, uint32_t magic,
@@ -181,10 +197,15 @@ __device__ __forceinline__ void compute(const StreamArgs& a, const uint4 (&W)[B]
   });
 
   float s[4], z[4];
-  s[0] = P.ok ? half_lo(P.s.x) : 0.0f;
-  s[1] = P.ok ? half_hi(P.s.x) : 0.0f;
-  s[2] = P.ok ? half_lo(P.s.y) : 0.0f;
-  s[3] = P.ok ? half_hi(P.s.y) : 0.0f;
+  if constexpr (kTL) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[c] = P.ok ? (float)(((P.s.x >> (P.s.y + 4 * c)) & 15u) + 1u) : 0.0f;
+  } else {
+    s[0] = P.ok ? half_lo(P.s.x) : 0.0f;
+    s[1] = P.ok ? half_hi(P.s.x) : 0.0f;
+    s[2] = P.ok ? half_lo(P.s.y) : 0.0f;
+    s[3] = P.ok ? half_hi(P.s.y) : 0.0f;
+  }
 #pragma unroll
   for (int c = 0; c < 4; ++c) z[c] = a.has_zeros ? (float)((P.z >> (8 * c)) & 0xFFu) : (float)(1 << (B - 1));
 #pragma unroll
@@ -200,18 +221,18 @@ __device__ __forceinline__ void compute(const StreamArgs& a, const uint4 (&W)[B]
 // packed row is row0. The staged activations of block blk sit at LDS slot
 // blk - lds_blk0 of this wave's area. With kPre, the first step's words and
 // parameters are already in Wa / Pa.
-template <int B, int MT, bool kPre>
+template <int B, int MT, bool kPre, bool kTL>
 __device__ __forceinline__ void run_segment(const StreamArgs& a, const MatPtrs& mp, int blk0, int blk1, int row0, int ks,
                                             const uint32_t* panel, int col, bool colv, const uint32_t* xs_w, const float2* xsum_w, int lds_blk0,
                                             uint32_t magic, float (&yacc)[4][MT], uint4 (&Wa)[B], Raw& Pa) {
   const int nsteps = (blk1 - blk0 + KS - 1) / KS;
   auto lane_issue = [&](int i, uint4 (&W)[B], Raw& P) {
     const int blk = blk0 + i * KS + ks;
-    issue<B>(a, mp, panel, blk, row0 + (i * KS + ks) * B, colv && blk < blk1, blk0, row0, col, W, P);
+    issue<B, kTL>(a, mp, panel, blk, row0 + (i * KS + ks) * B, colv && blk < blk1, blk0, row0, col, W, P);
   };
   auto lane_compute = [&](int i, const uint4 (&W)[B], const Raw& P) {
     const int bl = min(blk0 + i * KS + ks, blk1 - 1) - lds_blk0;   // clamped: idle lanes hold zeros
-    compute<B, MT>(a, W, P, xs_w + bl * kPairsPerBlock, a.chunk * kPairsPerBlock, xsum_w + bl, a.chunk, magic,
+    compute<B, MT, kTL>(a, W, P, xs_w + bl * kPairsPerBlock, a.chunk * kPairsPerBlock, xsum_w + bl, a.chunk, magic,
                    yacc);
   };
   if constexpr (!kPre) lane_issue(0, Wa, Pa);
@@ -242,7 +263,7 @@ __device__ __forceinline__ void any_segment(const StreamArgs& a, const MatPtrs& 
     if constexpr ((BS >> BB) & 1u) {                                                                       \
       uint4 W[BB];                                                                                         \
       Raw P;                                                                                               \
-      run_segment<BB, MT, false>(a, mp, blk0, blk1, row0, ks, panel, col, colv, xs_w, xsum_w, lds_blk0, magic, yacc, W, P); \
+      run_segment<BB, MT, false, two_level<BS>()>(a, mp, blk0, blk1, row0, ks, panel, col, colv, xs_w, xsum_w, lds_blk0, magic, yacc, W, P); \
     }                                                                                                      \
     break;
   switch (bits) {
@@ -334,7 +355,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const MatPtrs& 
     // A wave without blocks (K < 32 * waves) reads block 0 and discards it.
     const int blk = wb0 + ks;
     const bool any = wb0 < wb1;
-    issue<B0>(a, mp, panel, blk, row0 + ks * B0, any && colv && blk < seg0_end, any ? wb0 : 0, any ? row0 : 0, col, W0,
+    issue<B0, two_level<BS>()>(a, mp, panel, blk, row0 + ks * B0, any && colv && blk < seg0_end, any ? wb0 : 0, any ? row0 : 0, col, W0,
               P0);
   }
 
@@ -382,7 +403,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const MatPtrs& 
 
     int blk = c0;
     if (ch == 0 && blk < seg0_end) {
-      run_segment<B0, MT, true>(a, mp, blk, seg0_end, row0, ks, panel, col, colv, xs_w, xsum_w, c0, magic, yacc, W0, P0);
+      run_segment<B0, MT, true, two_level<BS>()>(a, mp, blk, seg0_end, row0, ks, panel, col, colv, xs_w, xsum_w, c0, magic, yacc, W0, P0);
       blk = seg0_end;
     }
     while (blk < c1) {

@@ -30,13 +30,24 @@ struct Epilogue {
   const uint16_t* residual;   // float16 [M][N] or NULL (may be the output itself)
   const float* addend;        // float32 [M][N] or NULL (e.g. a LoRA update)
   int act;                    // QLINEAR_ACT_NONE or QLINEAR_ACT_SILU
+  // Two-level scales: float16 q_scale_max [N], or NULL. When set, the
+  // kernels read the scales operand as 4-bit codes c (uint32 [G][N/8], 8 per
+  // word, column n at bits 4 (n % 8)) and weigh group g by (c + 1); the
+  // remaining factor scale_max[n] / 16 is applied here, once per output.
+  const uint16_t* scale_max;
 };
 
-// y = act(v + addend + bias) + residual. The operands are device (global)
-// memory: read as such, also where the kernel has passed the pointers through
-// registers the compiler cannot see.
+// The float32 factor of a two-level scale code: c + 1 (exact).
+__device__ __forceinline__ float qscale_factor(uint32_t word, int n) {
+  return (float)(((word >> (4 * (n & 7))) & 15u) + 1u);
+}
+
+// y = act(v * scale_max / 16 + addend + bias) + residual. The operands are
+// device (global) memory: read as such, also where the kernel has passed the
+// pointers through registers the compiler cannot see.
 __device__ __forceinline__ float apply_epilogue(const Epilogue& e, float v, int m, int n, int N) {
   typedef const __attribute__((address_space(1))) uint16_t* gptr;
+  if (e.scale_max) v *= (float)__builtin_bit_cast(_Float16, ((gptr)e.scale_max)[n]) * 0.0625f;
   if (e.addend) v += ((const __attribute__((address_space(1))) float*)e.addend)[(size_t)m * N + n];
   if (e.bias) v += (float)__builtin_bit_cast(_Float16, ((gptr)e.bias)[n]);
   if (e.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));

@@ -12,8 +12,13 @@ hipError_t launch_pack(const qlinear_layout& L, const Runs& runs, const uint8_t*
                        hipStream_t stream);
 hipError_t launch_unpack(const qlinear_layout& L, const Runs& runs, const uint32_t* qweight, uint8_t* q,
                          hipStream_t stream);
+// scale_max non-NULL: scales holds two-level scale codes (uint32 [G][N/8]).
 hipError_t launch_dequant(const qlinear_layout& L, const Runs& runs, const uint32_t* qweight,
-                          const uint16_t* scales, const uint8_t* zeros, uint16_t* w, hipStream_t stream);
+                          const uint16_t* scales, const uint8_t* zeros, const uint16_t* scale_max, uint16_t* w,
+                          hipStream_t stream);
+// q_scale words [groups][N/8] from 4-bit codes [groups][N] (N % 8 == 0).
+hipError_t launch_pack_qscale(const uint8_t* codes, int64_t groups, int64_t N, uint32_t* words,
+                              hipStream_t stream);
 
 // Act-order gather into unpacking pair order: xq uint32 [M][K/32][16] (float16
 // pairs, optionally pre-scaled by 2^-pair_exponent), optional block sums

@@ -291,6 +291,45 @@ int qlinear_qgemm_fused(const qlinear_layout* layout, const uint16_t* x, int32_t
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * EXL2 two-level scales (ExLlamaV2 blog, "How the EXL2 Quantization Pipeline
+ * Works Under the Hood", Step 3: q_scale holds 4-bit group scales packed into
+ * uint32 words, q_scale_max one float16 maximum scale per output feature;
+ * "How the Fused CUDA Kernel Works": a weight dequantizes as
+ * (w - midpoint) * scale * scale_max). The pages fix neither the value of a
+ * scale code nor the code order; this library reads them as:
+ *   scale[g][n] = (c[g][n] + 1) / 16 with c = (q_scale[g][n / 8] >> 4 (n % 8)) & 15
+ *   w[j][n]     = (q[j][n] - 2^(b_g - 1)) * scale[g][n] * q_scale_max[n]
+ * Groups are symmetric (no zero points).
+ *   q_scale     : uint32 [G][N / 8], device
+ *   q_scale_max : float16 [N], device
+ *
+ * qlinear_pack_qscale writes q_scale from 4-bit codes: codes uint8 [groups][N]
+ * (device, each taken modulo 16), N a multiple of 8. groups == 0 or N == 0 is
+ * a no-op. Errors: INVALID_ARGUMENT for negative sizes or a NULL pointer,
+ * UNSUPPORTED for N % 8 != 0, MISALIGNED for pointers not 16-byte aligned.
+ *
+ * qlinear_dequant_qscale, qlinear_qgemv_qscale and qlinear_qgemm_qscale are
+ * qlinear_dequant, qlinear_qgemv_fused and qlinear_qgemm_fused with
+ * (q_scale, q_scale_max) in place of (scales, zeros): same layout, operands,
+ * workspace, epilogue (NULL = none) and errors, and also INVALID_ARGUMENT
+ * for a NULL q_scale or q_scale_max, MISALIGNED for either not 16-byte
+ * aligned. The dequantized float16 weight is the single rounding of the
+ * exact product. The matmuls weigh each group by c + 1 and multiply the
+ * float32 sum by q_scale_max[n] / 16 before the epilogue.
+ */
+int qlinear_pack_qscale(const uint8_t* codes, int32_t groups, int32_t N, uint32_t* q_scale, void* stream);
+int qlinear_dequant_qscale(const qlinear_layout* layout, const uint32_t* qweight, const uint32_t* q_scale,
+                           const uint16_t* q_scale_max, uint16_t* w, void* stream);
+int qlinear_qgemv_qscale(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                         const uint32_t* q_scale, const uint16_t* q_scale_max, const int32_t* perm,
+                         const qlinear_epilogue* epilogue, uint16_t* y, void* workspace, size_t workspace_bytes,
+                         void* stream);
+int qlinear_qgemm_qscale(const qlinear_layout* layout, const uint16_t* x, int32_t M, const uint32_t* qweight,
+                         const uint32_t* q_scale, const uint16_t* q_scale_max, const int32_t* perm,
+                         const qlinear_epilogue* epilogue, uint16_t* y, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * On-the-fly LoRA update of a linear layer (ExLlamaV2 project page, LoRA
  * adapters: the low-rank pair A, B is applied during the forward pass
  * instead of being merged into the weights, and several adapters combine

@@ -268,3 +268,32 @@ def test_workspace_sizes():
     many = _layout(K=4096, N=512, gs=32, bits=np.array([4, 3] * 10 + [4] * 108, np.uint8))
     assert many.nruns == 21
     assert dq.qgemm_workspace_bytes(many, 100) == (100 * 4096 * 2 + 255) // 256 * 256
+
+
+def test_two_level_scale_validation_before_launch():
+    L = _layout()
+    lib = dq.lib()
+    E = _lib
+
+    def gemv(qs=FAKE, qsm=FAKE, M=1, wsb=1 << 30, **kw):
+        return lib.qlinear_qgemv_qscale(L.ref, FAKE, M, FAKE, qs, qsm, None, None, FAKE, FAKE, wsb, None)
+
+    def gemm(qs=FAKE, qsm=FAKE, M=1, wsb=1 << 30):
+        return lib.qlinear_qgemm_qscale(L.ref, FAKE, M, FAKE, qs, qsm, None, None, FAKE, FAKE, wsb, None)
+
+    for f in (gemv, gemm):
+        assert f(qsm=None) == E.ERR_INVALID_ARGUMENT
+        assert f(qs=None) == E.ERR_INVALID_ARGUMENT
+        assert f(qsm=FAKE + 2) == E.ERR_MISALIGNED
+        assert f(qs=FAKE + 4) == E.ERR_MISALIGNED
+        assert f(M=-1) == E.ERR_INVALID_ARGUMENT
+        assert f(M=0, qsm=None) == E.OK          # quick return before the operands are checked
+        assert f(wsb=0) == E.ERR_WORKSPACE
+    assert gemv(M=17) == E.ERR_UNSUPPORTED
+    assert lib.qlinear_dequant_qscale(L.ref, FAKE, FAKE, None, FAKE, None) == E.ERR_INVALID_ARGUMENT
+    assert lib.qlinear_dequant_qscale(L.ref, FAKE, FAKE + 4, FAKE, FAKE, None) == E.ERR_MISALIGNED
+    assert lib.qlinear_pack_qscale(FAKE, 4, 12, FAKE, None) == E.ERR_UNSUPPORTED
+    assert lib.qlinear_pack_qscale(FAKE, -1, 8, FAKE, None) == E.ERR_INVALID_ARGUMENT
+    assert lib.qlinear_pack_qscale(None, 4, 8, FAKE, None) == E.ERR_INVALID_ARGUMENT
+    assert lib.qlinear_pack_qscale(FAKE + 1, 4, 8, FAKE, None) == E.ERR_MISALIGNED
+    assert lib.qlinear_pack_qscale(None, 0, 8, None, None) == E.OK

@@ -127,3 +127,24 @@ def weight_bytes(spec: LayerSpec) -> int:
     sb = G * spec.N * 2
     zb = 0 if spec.symmetric else G * spec.N // 2
     return qb + sb + zb
+
+
+def two_level_scales(spec: LayerSpec, seed: int | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """EXL2 two-level scale inputs of a symmetric layer: 4-bit scale codes
+    uint8 [G][N], uniform over 0..15, and q_scale_max float16 [N], uniform in
+    [0.005, 0.02) like the one-level scales. Drawn from a generator of their
+    own (seed + 1), so the layer's other inputs are those of generate()."""
+    rng = np.random.default_rng((spec.seed if seed is None else seed) + 1)
+    G = spec.K // spec.group_size
+    codes = rng.integers(0, 16, size=(G, spec.N), dtype=np.uint8)
+    smax = rng.uniform(0.005, 0.02, size=spec.N).astype(np.float16)
+    return codes, smax
+
+
+def weight_bytes_two_level(spec: LayerSpec) -> int:
+    """Algorithmic weight bytes with two-level scales: codes at b bits, 4-bit
+    scale codes and one float16 maximum scale per output (no zero points)."""
+    G = spec.K // spec.group_size
+    bits = bit_map(spec).astype(np.int64)
+    qb = int((bits * spec.group_size).sum()) * spec.N // 8
+    return qb + G * spec.N // 2 + 2 * spec.N

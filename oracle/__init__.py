@@ -22,6 +22,9 @@ Every function follows the pages' description of the method:
   (ExLlamaV2 blog, "How the EXL2 Quantization Pipeline Works Under the Hood",
   Step 3, and "How the Fused CUDA Kernel Works"). The value of a scale code is
   a reading of this package (parity unpinned).
+* The Q4/Q6/Q8 KV-cache codec (ExLlamaV2 blog, comparison table and "How to
+  Use Effectively", Step 2): a block format of this package's own
+  (``kv_oracle``), since the pages give only the modes and their savings.
 """
 
 from .qlinear_oracle import (  # noqa: F401
@@ -53,4 +56,15 @@ from .qlinear_oracle import (  # noqa: F401
     dequant_qscale,
     dequant_qscale_fp16,
     qlinear_qscale,
+)
+from .kv_oracle import (  # noqa: F401
+    KV_BITS,
+    KV_GROUPS,
+    kv_scales,
+    kv_codes,
+    kv_pack,
+    kv_unpack,
+    kv_quantize,
+    kv_dequantize,
+    kv_bytes_per_element,
 )

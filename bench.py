@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-group", action="store_true", help="one qgemv launch per matrix (no grouped q/k/v, gate/up)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the M = 2048 qgemm measurement")
     ap.add_argument("--no-lora", action="store_true", help="skip the on-the-fly LoRA update timings")
+    ap.add_argument("--no-kv", action="store_true", help="skip the KV-cache codec timings")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-config decode points (7B at M = 4, 16; EXL2 at M = 1, 8; 70B at M = 1, 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -381,6 +382,7 @@ def main():
     gemm = None if args.no_gemm else bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream)
     configs = None if args.no_configs else bench_configs(torch, dq, wl, lib, dev, stream, spin)
     lora = None if args.no_lora else bench_lora(torch, lib, dev, stream, spin)
+    kv = None if args.no_kv else bench_kv(torch, lib, dev, stream, spin)
 
     # ---------------------------------------------------------------- oracle on the host
     cpu = None
@@ -431,6 +433,7 @@ def main():
         "reference_points": refs,
         "decode_configs": configs,
         "lora": lora,
+        "kv_codec": kv,
         "cpu_baseline": cpu,
         "qgemm": gemm,
     }
@@ -595,6 +598,71 @@ def bench_lora(torch, lib, dev, stream, spin):
         points.append({"M": M, "K": K, "N": N, "rank": r, "us_per_call": round(us, 2), "algorithmic_bytes": nb,
                        "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
         log(f"lora M={M} {K}->{N} rank {r}: {us:.2f} us, {gbs:.1f} GB/s")
+    return points
+
+
+# KV-cache codec points: one layer's key (or value) cache of a 70B-class
+# model at 32K tokens (8 key/value heads x 32768 tokens, head dimension 128),
+# per (bits, block size).
+KV_ROWS, KV_D = 8 * 32768, 128
+KV_POINTS = [(4, 128), (6, 128), (8, 128), (4, 32)]
+
+
+def kv_bytes(elements, bits, group):
+    """Algorithmic HBM bytes of one codec call over `elements` values: the
+    float16 values on one side, the codes and block scales on the other."""
+    return elements * 2 + elements * bits // 8 + elements // group * 2
+
+
+def bench_kv(torch, lib, dev, stream, spin):
+    """qlinear_kv_quant and qlinear_kv_dequant on KV_ROWS x KV_D values,
+    >= 64 calls back to back behind a spin kernel, cycling through distinct
+    buffers of >= 1 GiB in all (so the Infinity Cache cannot serve them),
+    between two events on the launch stream, against the HBM roofline."""
+    sh = stream.cuda_stream
+    E = KV_ROWS * KV_D
+    rng = np.random.default_rng(21)
+    x0 = torch.from_numpy((rng.standard_normal((KV_ROWS, KV_D)) *
+                           rng.uniform(0.05, 4.0, size=(KV_ROWS, 1))).astype(np.float16)).to(dev)
+    points = []
+    for bits, group in KV_POINTS:
+        nb = kv_bytes(E, bits, group)
+        ncopy = max(2, -(-(1 << 30) // nb))
+        xs = [x0.clone() for _ in range(ncopy)]
+        cs = [torch.empty(E * bits // 32, dtype=torch.int32, device=dev) for _ in range(ncopy)]
+        ss = [torch.empty(E // group, dtype=torch.float16, device=dev) for _ in range(ncopy)]
+        for quant in (True, False):
+            def call(i):
+                j = i % ncopy
+                if quant:
+                    st = lib.qlinear_kv_quant(xs[j].data_ptr(), KV_ROWS, KV_D, bits, group, cs[j].data_ptr(),
+                                              ss[j].data_ptr(), sh)
+                else:
+                    st = lib.qlinear_kv_dequant(cs[j].data_ptr(), ss[j].data_ptr(), KV_ROWS, KV_D, bits, group,
+                                                xs[j].data_ptr(), sh)
+                if st != 0:
+                    raise RuntimeError(f"kv codec failed with status {st}")
+
+            for i in range(ncopy):
+                call(i)
+            n = max(64, ncopy)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(spin)
+            e0.record(stream)
+            for i in range(n):
+                call(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / n
+            gbs = nb / (us * 1e-6) / 1e9
+            points.append({"op": "quant" if quant else "dequant", "bits": bits, "group": group, "rows": KV_ROWS,
+                           "D": KV_D, "us_per_call": round(us, 2), "algorithmic_bytes": nb, "gbs": round(gbs, 1),
+                           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                           "bytes_per_element": bits / 8 + 2 / group})
+            log(f"kv {'quant' if quant else 'dequant'} Q{bits} G={group} {KV_ROWS}x{KV_D}: {us:.2f} us, "
+                f"{gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+        del xs, cs, ss
     return points
 
 

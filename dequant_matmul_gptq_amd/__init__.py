@@ -35,4 +35,6 @@ from ._lib import (  # noqa: F401
     dequant_qscale,
     qgemv_qscale,
     qgemm_qscale,
+    kv_quant,
+    kv_dequant,
 )

@@ -50,6 +50,8 @@ EXPORTS = (
     "qlinear_dequant_qscale",
     "qlinear_qgemv_qscale",
     "qlinear_qgemm_qscale",
+    "qlinear_kv_quant",
+    "qlinear_kv_dequant",
 )
 
 ACT_NONE = 0
@@ -122,6 +124,9 @@ def lib() -> ctypes.CDLL:
         L.qlinear_dequant_qscale.argtypes = [lp, vp, vp, vp, vp, vp]
         L.qlinear_qgemv_qscale.argtypes = [lp, vp, i32, vp, vp, vp, vp, ep, vp, vp, sz, vp]
         L.qlinear_qgemm_qscale.argtypes = [lp, vp, i32, vp, vp, vp, vp, ep, vp, vp, sz, vp]
+        i64 = ctypes.c_int64
+        L.qlinear_kv_quant.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
+        L.qlinear_kv_dequant.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -451,3 +456,42 @@ def qgemm_qscale(layout: Layout, x: torch.Tensor, qweight: torch.Tensor, q_scale
                                       _ptr(perm), None if epi is None else ctypes.byref(epi), _ptr(y),
                                       _ptr(workspace), workspace.numel(), _stream(x.device)), "qlinear_qgemm_qscale")
     return y
+
+
+# ---------------------------------------------------------------- KV-cache codec
+
+def kv_quant(x: torch.Tensor, bits: int, group: int, codes: torch.Tensor | None = None,
+             scales: torch.Tensor | None = None):
+    """x float16 [..., D] -> (codes int32 [..., D * bits / 32] (uint32 bit
+    patterns), scales float16 [..., D / group]); leading dimensions are rows."""
+    _dev(x, "x", torch.float16)
+    D = int(x.shape[-1])
+    rows = x.numel() // D if D else 0
+    lead = tuple(x.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (D * bits // 32,), dtype=torch.int32, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead + (D // group if group else 0,), dtype=torch.float16, device=x.device)
+    _dev(codes, "codes", torch.int32, lead + (D * bits // 32,))
+    _dev(scales, "scales", torch.float16, lead + (D // group,))
+    _check(lib().qlinear_kv_quant(_ptr(x), rows, D, int(bits), int(group), _ptr(codes), _ptr(scales),
+                                  _stream(x.device)), "qlinear_kv_quant")
+    return codes, scales
+
+
+def kv_dequant(codes: torch.Tensor, scales: torch.Tensor, D: int, bits: int, group: int,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """(codes, scales) of kv_quant -> float16 [..., D]."""
+    _dev(codes, "codes", torch.int32)
+    _dev(scales, "scales", torch.float16)
+    lead = tuple(codes.shape[:-1])
+    if tuple(codes.shape) != lead + (D * bits // 32,):
+        raise ValueError("codes must be [..., D * bits / 32]")
+    _dev(scales, "scales", torch.float16, lead + (D // group,))
+    rows = int(np.prod(lead)) if lead else 1
+    if out is None:
+        out = torch.empty(lead + (D,), dtype=torch.float16, device=codes.device)
+    _dev(out, "out", torch.float16, lead + (D,))
+    _check(lib().qlinear_kv_dequant(_ptr(codes), _ptr(scales), rows, int(D), int(bits), int(group), _ptr(out),
+                                    _stream(codes.device)), "qlinear_kv_dequant")
+    return out

@@ -372,6 +372,33 @@ int qlinear_qgemm_qscale(const qlinear_layout* layout, const uint16_t* x, int32_
                                  (hipStream_t)stream));
 }
 
+// The codec's shape and operand checks (shared by both directions).
+static int check_kv(const void* x, int64_t rows, int32_t D, int32_t bits, int32_t group, const void* codes,
+                    const void* scales) {
+  if (rows < 0 || D <= 0) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (bits != 4 && bits != 6 && bits != 8) return QLINEAR_ERR_UNSUPPORTED;
+  if ((group != 32 && group != 64 && group != 128) || D % group != 0) return QLINEAR_ERR_UNSUPPORTED;
+  if (rows > ((int64_t)1 << 42) / D) return QLINEAR_ERR_UNSUPPORTED;
+  if (rows == 0) return QLINEAR_OK;
+  if (!x || !codes || !scales) return QLINEAR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || ((uintptr_t)codes & 3u) || ((uintptr_t)scales & 1u)) return QLINEAR_ERR_MISALIGNED;
+  return QLINEAR_OK;
+}
+
+int qlinear_kv_quant(const uint16_t* x, int64_t rows, int32_t D, int32_t bits, int32_t group, uint32_t* codes,
+                     uint16_t* scales, void* stream) {
+  const int st = check_kv(x, rows, D, bits, group, codes, scales);
+  if (st != QLINEAR_OK || rows == 0) return st;
+  return hip_status(launch_kv_quant(x, rows * D, bits, group, codes, scales, (hipStream_t)stream));
+}
+
+int qlinear_kv_dequant(const uint32_t* codes, const uint16_t* scales, int64_t rows, int32_t D, int32_t bits,
+                       int32_t group, uint16_t* x, void* stream) {
+  const int st = check_kv(x, rows, D, bits, group, codes, scales);
+  if (st != QLINEAR_OK || rows == 0) return st;
+  return hip_status(launch_kv_dequant(codes, scales, rows * D, bits, group, x, (hipStream_t)stream));
+}
+
 int qlinear_read_floor(const void* buf, size_t bytes, int32_t loads_per_thread, int32_t workgroups, uint32_t key,
                        uint32_t* sink, void* stream) {
   if (!buf || !sink || bytes < 16 || bytes % 16 != 0) return QLINEAR_ERR_INVALID_ARGUMENT;

@@ -16,6 +16,13 @@ hipError_t launch_unpack(const qlinear_layout& L, const Runs& runs, const uint32
 hipError_t launch_dequant(const qlinear_layout& L, const Runs& runs, const uint32_t* qweight,
                           const uint16_t* scales, const uint8_t* zeros, const uint16_t* scale_max, uint16_t* w,
                           hipStream_t stream);
+// KV-cache codec over `elements` float16 values (rows of D, blocks of
+// group in {32, 64, 128} elements, bits in {4, 6, 8}; elements % group == 0):
+// codes uint32 [elements * bits / 32], scales float16 [elements / group].
+hipError_t launch_kv_quant(const uint16_t* x, int64_t elements, int bits, int group, uint32_t* codes,
+                           uint16_t* scales, hipStream_t stream);
+hipError_t launch_kv_dequant(const uint32_t* codes, const uint16_t* scales, int64_t elements, int bits, int group,
+                             uint16_t* x, hipStream_t stream);
 // q_scale words [groups][N/8] from 4-bit codes [groups][N] (N % 8 == 0).
 hipError_t launch_pack_qscale(const uint8_t* codes, int64_t groups, int64_t N, uint32_t* words,
                               hipStream_t stream);

@@ -330,6 +330,36 @@ int qlinear_qgemm_qscale(const qlinear_layout* layout, const uint16_t* x, int32_
                          void* stream);
 
 /*
+ * Q4 / Q6 / Q8 KV-cache codec (ExLlamaV2 blog: Q4, Q6 and Q8 cache modes next
+ * to FP16, "How to Use Effectively", Step 2, where Q8 saves 50% of the cache
+ * memory and Q4 75%). The pages give no format; this library's is:
+ *   x      : float16 [rows][D], rows of D values (e.g. one head's key or
+ *            value vector per token), cut into blocks of `group` elements
+ *   scales : float16 [rows][D / group], s = RNE_fp16(max|x| / (2^(bits-1) - 1))
+ *            of each block, computed in float32
+ *   codes  : uint32 [rows][D * bits / 32]: per block a little-endian bit
+ *            stream, element i at bits bits*i .. bits*i + bits - 1, holding
+ *            clamp(rint(x / s), -2^(bits-1), 2^(bits-1) - 1) + 2^(bits-1)
+ *            (float32 division, ties to even; a block with s = 0 holds the
+ *            midpoint code)
+ *   dequantized value: RNE_fp16(s * (code - 2^(bits-1)))
+ * bits in {4, 6, 8}; group in {32, 64, 128}; D a multiple of group. Stored
+ * bytes per element: bits / 8 + 2 / group (Q4 at group 128: 25.8% of FP16).
+ * Inputs must be finite. A cache of several heads, layers or tokens is one
+ * call with rows = their product; appending one token is a call on that
+ * token's rows (pointers offset by the caller).
+ * Pointers are device pointers: x 16-byte aligned, codes 4-byte aligned,
+ * scales 2-byte aligned (else MISALIGNED). rows == 0 is a no-op.
+ * Errors: INVALID_ARGUMENT for rows < 0, D < 1 or a NULL pointer (rows > 0);
+ * UNSUPPORTED for other bits or group, D % group != 0, or rows * D above 2^42.
+ * Asynchronous on `stream`.
+ */
+int qlinear_kv_quant(const uint16_t* x, int64_t rows, int32_t D, int32_t bits, int32_t group, uint32_t* codes,
+                     uint16_t* scales, void* stream);
+int qlinear_kv_dequant(const uint32_t* codes, const uint16_t* scales, int64_t rows, int32_t D, int32_t bits,
+                       int32_t group, uint16_t* x, void* stream);
+
+/*
  * On-the-fly LoRA update of a linear layer (ExLlamaV2 project page, LoRA
  * adapters: the low-rank pair A, B is applied during the forward pass
  * instead of being merged into the weights, and several adapters combine

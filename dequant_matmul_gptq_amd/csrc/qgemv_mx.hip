@@ -61,13 +61,18 @@ constexpr int kThreads = kWaves * 64;
 
 enum Mode : int {
   kFewRows = 1,   // one launch, M <= 4
+  kExact = 4,     // flag: B dequantized exactly (no sums MFMA, no per-unit epilogue)
   kGathered = 2,  // activations gathered by the gather kernel into the workspace
 };
 
 // Rows of the activations' fragments and sums per block / unit.
+// The activation mode (kFewRows or kGathered) and the B form of a mode value.
+constexpr int base_mode(int m) { return m & 3; }
+constexpr bool exact_mode(int m) { return (m & kExact) != 0; }
+
 template <int kMode>
 constexpr int rows_stored() {
-  return kMode == kFewRows ? 4 : 16;
+  return base_mode(kMode) == kFewRows ? 4 : 16;
 }
 
 struct MxArgs {
@@ -140,7 +145,7 @@ struct Slot {
 template <int B, int FN, int UB, int kMode>
 constexpr int depth() {
   const int words = UB * mx::loads(B) * FN;
-  int d = kMode == kGathered ? 40 / (words + 4 * UB) : 32 / words;
+  int d = base_mode(kMode) == kGathered ? 40 / (words + 4 * UB) : 32 / words;
   d = d < 2 ? 2 : d > 8 ? 8 : d;
   return d & ~1;
 }
@@ -218,7 +223,7 @@ __device__ __forceinline__ void issue_params(const Lane& L, int blk, int grp, in
   const uint32_t go = (uint32_t)grp * (uint32_t)N;
   S.s0 = load_scales<FN>(L.rs, L.sbase, (uint32_t)grp * L.srow, S.s1);
   S.z = load_zeros(L.rz, L.zbase, go);
-  if constexpr (kMode == kGathered) {
+  if constexpr (base_mode(kMode) == kGathered) {
 #pragma unroll
     for (int b = 0; b < UB; ++b)
       S.x[b] = __builtin_bit_cast(u32x4,
@@ -309,8 +314,76 @@ __device__ __forceinline__ Acc<FN> segment(const MxArgs& a, const Lane& L, const
     static_for<0, D>([&](auto Dd) { fill(decltype(Dd)::value, S[decltype(Dd)::value]); });
   }
   half8_t af[2][UB];
-  if constexpr (kMode != kGathered) lds_frags<UB, kMode>(a, L, lds, blk0, af[0]);
+  if constexpr (base_mode(kMode) != kGathered) lds_frags<UB, kMode>(a, L, lds, blk0, af[0]);
   const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (exact_mode(kMode)) {
+    // Exact B: each pair (1024 + q 2^e) - (1024 + z 2^e) = (q - z) 2^e exactly
+    // (1024 + z 2^e is a multiple of 2^e below 2^15, so exact in float16 for
+    // any uint8 z), times s with one rounding; the A side carries 2^-e, so
+    // A B = x RNE(s (q - z)) exactly. The accumulators (two per unit parity)
+    // run over all of K; there is no per-unit epilogue and no sums MFMA.
+    auto unit_ex = [&](int i, auto Dd, bool steady) {
+      constexpr int d = decltype(Dd)::value;
+      constexpr int p = d & 1;
+      Slot<B, FN, UB>& s = S[d];
+      if constexpr (base_mode(kMode) != kGathered) {
+        const int in = i + 1 < n ? i + 1 : i;
+        lds_frags<UB, kMode>(a, L, lds, blk0 + in * UB, af[p ^ 1]);
+      }
+      half2_t sc2[FN], bias2[FN][4];
+      {
+        const uint32_t sl = (FN == 1 || L.tl) ? s.s0 >> L.sshift : s.s0;
+        const uint32_t zl = s.z >> L.zshift;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const uint32_t sw = j < 2 ? sl : s.s1;
+          const _Float16 sh = L.tl ? (_Float16)(float)(((sl >> (4 * j)) & 15u) + 1u)
+                                   : __builtin_bit_cast(_Float16, (uint16_t)(sw >> (16 * (j & 1))));
+          sc2[j] = half2_t{sh, sh};
+          const float zf = hz ? (float)((zl >> (8 * j)) & 0xFFu) : (float)zsym;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const _Float16 bh = (_Float16)(1024.0f + zf * (float)(1 << mx::exponent(B, r)));
+            bias2[j][r] = half2_t{bh, bh};
+          }
+        }
+      }
+      static_for<0, UB>([&](auto Bb) {
+        constexpr int b = decltype(Bb)::value;
+        constexpr int ch = b & 1;
+        half8_t ab;
+        if constexpr (base_mode(kMode) == kGathered) ab = __builtin_bit_cast(half8_t, s.x[b]);
+        else ab = af[p][b];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          uint32_t w[mx::loads(B)];
+#pragma unroll
+          for (int k = 0; k < mx::loads(B); ++k) w[k] = elem<FN>(s.w[b][k], j);
+          uint32_t q[4];
+          mx::extract<B>(w, L.magic, c.sh2, c.c3, c.c5, c.c6, q);
+          half2_t h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = (__builtin_bit_cast(half2_t, q[r]) - bias2[j][r]) * sc2[j];
+          const half8_t bf = half8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+          A.acc[p][ch][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ab, bf, A.acc[p][ch][j], 0, 0, 0);
+        }
+      });
+      // The slot's words and parameters are read: it takes unit i + D.
+      if (steady) fill(i + D, s);
+      else if (i + D < n) fill(i + D, s);
+    };
+    int i = 0;
+    for (; i + 2 * D <= n; i += D) static_for<0, D>([&](auto Dd) { unit_ex(i + decltype(Dd)::value, Dd, true); });
+    static_for<0, D>([&](auto Dd) {
+      if (i + (int)decltype(Dd)::value < n) unit_ex(i + decltype(Dd)::value, Dd, false);
+    });
+    i += D;
+    static_for<0, D>([&](auto Dd) {
+      if (i + (int)decltype(Dd)::value < n) unit_ex(i + decltype(Dd)::value, Dd, false);
+    });
+    return A;
+  }
 
   // Unit i from slot d (its parity d & 1: D is even and rounds start at multiples of D).
   auto unit = [&](int i, auto Dd, bool steady) {
@@ -318,7 +391,7 @@ __device__ __forceinline__ Acc<FN> segment(const MxArgs& a, const Lane& L, const
     constexpr int p = d & 1;
     constexpr int dp = (d + D - 1) % D;   // the previous unit's slot
     Slot<B, FN, UB>& s = S[d];
-    if constexpr (kMode != kGathered) {
+    if constexpr (base_mode(kMode) != kGathered) {
       const int in = i + 1 < n ? i + 1 : i;
       lds_frags<UB, kMode>(a, L, lds, blk0 + in * UB, af[p ^ 1]);
     }
@@ -327,7 +400,7 @@ __device__ __forceinline__ Acc<FN> segment(const MxArgs& a, const Lane& L, const
       constexpr int ch = kTwo ? (b & 1) : 0;     // two accumulation chains per unit of 4 blocks
       constexpr bool fresh = b < (kTwo ? 2 : 1);
       half8_t ab;
-      if constexpr (kMode == kGathered) ab = __builtin_bit_cast(half8_t, s.x[b]);
+      if constexpr (base_mode(kMode) == kGathered) ab = __builtin_bit_cast(half8_t, s.x[b]);
       else ab = af[p][b];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -494,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_mx_kernel(MxArgs a) {
   L.zshift = (uint32_t)(col & 3) * 8;
   const int mrow = min(lane & 15, M - 1);   // the A row of this lane (rows past M repeat row M - 1)
   L.xoff = (uint32_t)(mrow * 32 + 8 * L.g) * 2;
-  if constexpr (kMode == kGathered) {
+  if constexpr (base_mode(kMode) == kGathered) {
     const int nblk = K / kBlockRows;
     L.rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.xg, 0, (int)((size_t)nblk * MS * 64), kRsrcWord3);
   } else {
@@ -521,7 +594,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_mx_kernel(MxArgs a) {
     constexpr int B0 = decltype(B0c)::value;
     Slot<B0, FN, UB> S0[depth<B0, FN, UB, kMode>()];
 
-    if constexpr (kMode != kGathered) {
+    if constexpr (base_mode(kMode) != kGathered) {
       // 1. x rows and perm into LDS, no registers: wave-wide 16-byte
       // global-to-LDS loads (lane l of a load fills bytes 16 l .. 16 l + 15
       // of a 1 KiB piece). Pieces past the end re-read the last 16 bytes and
@@ -551,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_mx_kernel(MxArgs a) {
     if (n0 > 0) pre_issue<B0, FN, UB, kMode>(L, row0, S0);
     asm volatile("" ::: "memory");
 
-    if constexpr (kMode != kGathered) {
+    if constexpr (base_mode(kMode) != kGathered) {
       // 3. Wait for the staging loads only (they precede the weight loads,
       // and loads complete in order), then gather. A wave without blocks
       // issued no weight loads and waits for all.
@@ -610,6 +683,10 @@ __global__ __launch_bounds__(kThreads) void qgemv_mx_kernel(MxArgs a) {
   // 5. The waves' partial tiles summed through LDS, then the epilogue and
   // the float16 store. Lane l holds rows 4 (l / 16) + r of column l % 16 of
   // each fragment.
+  if constexpr (exact_mode(kMode)) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) A.y[j] = (A.acc[0][0][j] + A.acc[0][1][j]) + (A.acc[1][0][j] + A.acc[1][1][j]);
+  }
   __syncthreads();   // every wave is done with the staged activations
   Red<FN>* red = reinterpret_cast<Red<FN>*>(lds);
 #pragma unroll
@@ -674,8 +751,12 @@ hipError_t launch_mode(const MxArgs& a, int fn, size_t lds, hipStream_t stream) 
 
 template <unsigned BS, int UB>
 hipError_t launch_set(const MxArgs& a, int fn, int mode, size_t lds, hipStream_t stream) {
-  if (mode == kFewRows) return launch_mode<BS, UB, kFewRows>(a, fn, lds, stream);
-  return launch_mode<BS, UB, kGathered>(a, fn, lds, stream);
+  switch (mode) {
+    case kFewRows: return launch_mode<BS, UB, kFewRows>(a, fn, lds, stream);
+    case kFewRows | kExact: return launch_mode<BS, UB, kFewRows | kExact>(a, fn, lds, stream);
+    case kGathered | kExact: return launch_mode<BS, UB, kGathered | kExact>(a, fn, lds, stream);
+    default: return launch_mode<BS, UB, kGathered>(a, fn, lds, stream);
+  }
 }
 
 }  // namespace mxk
@@ -786,12 +867,17 @@ hipError_t launch_qgemv_mx(const qlinear_layout& L, const Runs& runs, const uint
     if (e != hipSuccess) return e;
     lds = sizeof(mxk::Red<4>) / 4 * fn;
   }
+  // B dequantized exactly when every block has a scale of its own (the
+  // factored form's per-unit epilogue would run per block).
+  const bool exact = ub == 1;
+  if (exact) mode |= mxk::kExact;
   if (set == mxk::kSet4) {
     if (ub == 4) return mxk::launch_set<mxk::kSet4, 4>(a, fn, mode, lds, stream);
     return mxk::launch_set<mxk::kSet4, 1>(a, fn, mode, lds, stream);
   }
   if ((set & ~stream::kLowBits) == 0) return mxk::launch_set<stream::kLowBits, 1>(a, fn, mode, lds, stream);
   if ((set & ~stream::kMidBits) == 0) return mxk::launch_set<stream::kMidBits, 1>(a, fn, mode, lds, stream);
+  if (exact) return mxk::launch_mode<stream::kAllBits, 1, mxk::kGathered | mxk::kExact>(a, fn, lds, stream);
   return mxk::launch_mode<stream::kAllBits, 1, mxk::kGathered>(a, fn, lds, stream);
 }
 

@@ -30,10 +30,14 @@
  *  - Pointers to device data must be 16-byte aligned (QLINEAR_ERR_MISALIGNED).
  *  - N must be a multiple of 8; K a multiple of gs.
  *  - Non-finite activations: a NaN in row m of x makes row m of y NaN. An
- *    Inf makes every element of its row non-finite: qlinear_qgemm gives the
- *    IEEE result of the formula (+-Inf, NaN where the weight is 0); every
- *    qlinear_qgemv call gives NaN, as it computes the sum in a factored
- *    form that subtracts the activations' block sums (Inf - Inf). Other
+ *    Inf makes every element of its row non-finite. Where the weights are
+ *    dequantized exactly the result is the IEEE one of the formula (+-Inf,
+ *    NaN where the weight is 0): qlinear_qgemm, and qlinear_qgemv at M >= 3
+ *    on layouts where every 32-row block has a scale of its own (groups of
+ *    32 or 64 rows, or any width but 4 bits) unless the single-row kernel
+ *    takes the call (one width, M = 3 or 4, K N <= 2 * 4096^2, no addend).
+ *    The other qlinear_qgemv calls compute the sum in a factored form that
+ *    subtracts the activations' block sums (Inf - Inf) and give NaN. Other
  *    rows are unaffected.
  */
 #ifndef QLINEAR_H

@@ -380,22 +380,25 @@ def test_grouped_qgemv_max_group_full_size():
 
 # ------------------------------------------------------------------ special values
 
-@pytest.mark.parametrize("op,bits,M,exact", [
-    ("qgemv", [4] * 11, 1, False),        # single-row kernel (factored arithmetic)
-    ("qgemv", [4] * 11, 4, False),        # single-row kernel, 4 rows
-    ("qgemv", MIXED_BITS, 1, False),      # gather + multi-row VALU kernel
-    ("qgemv", MIXED_BITS, 2, False),      # multi-row VALU kernel
-    ("qgemv", MIXED_BITS, 8, False),      # matrix-core decode kernel (factored arithmetic)
-    ("qgemm", MIXED_BITS, 64, True),      # prefill, several widths
-    ("qgemm", [4] * 11, 64, True),        # prefill, one width
-], ids=["row", "row-M4", "gather-valu-M1", "valu-M2", "mfma-M8", "qgemm-mixed", "qgemm-4bit"])
-def test_nonfinite_activations(op, bits, M, exact):
+@pytest.mark.parametrize("op,bits,gs,M,exact", [
+    ("qgemv", [4] * 11, 32, 1, False),     # single-row kernel (factored arithmetic)
+    ("qgemv", [4] * 11, 32, 4, False),     # single-row kernel, 4 rows
+    ("qgemv", MIXED_BITS, 32, 1, False),   # gather + multi-row VALU kernel
+    ("qgemv", MIXED_BITS, 32, 2, False),   # multi-row VALU kernel
+    ("qgemv", MIXED_BITS, 32, 8, True),    # matrix-core kernel, exact dequantization (a scale per block)
+    ("qgemv", [4] * 6, 128, 8, False),     # matrix-core kernel, factored (4-bit, 128-row groups)
+    ("qgemm", MIXED_BITS, 32, 64, True),   # prefill, several widths
+    ("qgemm", [4] * 11, 32, 64, True),     # prefill, one width
+], ids=["row", "row-M4", "gather-valu-M1", "valu-M2", "mfma-exact-M8", "mfma-factored-M8", "qgemm-mixed",
+        "qgemm-4bit"])
+def test_nonfinite_activations(op, bits, gs, M, exact):
     """A NaN activation makes its whole output row NaN; an Inf activation makes
-    every column of its row non-finite (prefill: the IEEE result of the
-    float64 oracle, +-Inf or NaN where the weight is 0; every decode kernel
-    subtracts 1024 X' + z X and gives NaN). Other rows are unaffected."""
-    say(f"non-finite activations {op} M={M}")
-    inp = _mixed_inputs(bits, 32, 520, max(M, 2), seed=77 + M, zeros=True)
+    every column of its row non-finite (kernels that dequantize exactly: the
+    IEEE result of the float64 oracle, +-Inf or NaN where the weight is 0; the
+    factored decode kernels subtract 1024 X' + z X and give NaN). Other rows
+    are unaffected."""
+    say(f"non-finite activations {op} M={M} gs={gs}")
+    inp = _mixed_inputs(bits, gs, 520, max(M, 2), seed=77 + M, zeros=True)
     x = inp.x[:M].copy()
     K = inp.spec.K
     x[0, 5] = np.float16(np.nan)

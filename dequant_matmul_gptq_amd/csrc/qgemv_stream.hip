@@ -1,7 +1,8 @@
-// Host side of the decode path: the single-row kernel for M = 1, otherwise
-// the act-order gather into the workspace, then the MFMA kernel (M >= 3, see
-// below) or the multi-row VALU kernel instantiated for the smallest set of
-// code widths covering the layout.
+// Host side of the decode path: one launch for one row (the single-row
+// kernel, or its several-width form) and for 2-4 rows of one width, the
+// matrix-core kernel from 3 rows on (see below), otherwise the act-order
+// gather into the workspace, then the multi-row VALU kernel instantiated for
+// the smallest set of code widths covering the layout.
 #include "qgemv_m1.hpp"
 
 namespace qlinear {
@@ -69,6 +70,13 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   // argument in its prologue cost 3% on the 7B decode step (measured on
   // MI355X), so calls with an addend (a LoRA update) run the kernels below.
   if (row) return stream::launch_row_set(set, a, stream);
+  // One row, several widths: the one-launch kernel that runs the single-row
+  // scheme run segment by segment.
+  if (!epi.addend && !tl && stream::mixed_row(M, L.K, L.N, mats, set)) {
+    if ((set & ~stream::kLowBits) == 0) return stream::launch_rowmix_low(a, stream);
+    if ((set & ~stream::kMidBits) == 0) return stream::launch_rowmix_mid(a, stream);
+    return stream::launch_rowmix_all(a, stream);
+  }
   // 1-2 rows: the activations are gathered into the workspace (with the
   // per-block sums of the factored form) by a kernel of their own.
   const GemvWorkspace w = qgemv_workspace(ws, L.K);

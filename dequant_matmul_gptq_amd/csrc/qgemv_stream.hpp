@@ -82,6 +82,8 @@ struct StreamArgs {
   // width, or 0 for a wave without blocks, its first packed row and its end
   // block, the latter also bounded by the first chunk)
   int wave_bits[kMaxWaves], wave_row[kMaxWaves], wave_end[kMaxWaves];
+  // one-launch several-width kernel: wave w's blocks are [wave_begin[w], wave_begin[w + 1])
+  int wave_begin[kMaxWaves + 1];
   Runs runs;
   Epilogue epi;
 };
@@ -470,6 +472,31 @@ __global__ __launch_bounds__(WV * 64) void qgemv_stream_kernel(StreamArgs a) {
   dispatch_body<MT, BS, WV, (BS & 16u) ? 4 : (BS & 4u) ? 2 : (BS & 8u) ? 3 : (BS & 32u) ? 5 : (BS & 64u) ? 6 : 8>(a, mp, lds, red, tid, lane, wave, strip, wb0, wb1, row0, seg0_end);
 }
 
+// Equal split of the K blocks over WV waves (wave w: [w nblk / WV, (w + 1) nblk / WV)).
+inline void equal_waves(StreamArgs& a, int WV) {
+  const int nblk = a.K / kBlockRows;
+  for (int w = 0; w <= WV; ++w) a.wave_begin[w] = (w * nblk) / WV;
+}
+
+// Each wave's first run segment: its width (0 for a wave without blocks),
+// first packed row and end block, the latter bounded by `limit` blocks; the
+// waves' ranges come from wave_begin.
+inline void first_segments(StreamArgs& a, int WV, int limit) {
+  for (int w = 0; w < WV; ++w) {
+    const int wb0 = a.wave_begin[w], wb1 = a.wave_begin[w + 1];
+    a.wave_bits[w] = 0;
+    a.wave_row[w] = 0;
+    a.wave_end[w] = wb0;
+    if (wb0 < wb1) {
+      int r = 0;
+      while (r + 1 < a.runs.nruns && wb0 >= a.runs.run_block[r + 1]) ++r;
+      a.wave_bits[w] = a.runs.run_bits[r];
+      a.wave_row[w] = a.runs.run_row[r] + (wb0 - a.runs.run_block[r]) * a.runs.run_bits[r];
+      a.wave_end[w] = std::min(std::min(wb1, a.runs.run_block[r + 1]), wb0 + limit);
+    }
+  }
+}
+
 template <int MT, unsigned BS, int WV>
 hipError_t launch_set(StreamArgs a, hipStream_t stream) {
   const int nblk = a.K / kBlockRows;
@@ -480,20 +507,8 @@ hipError_t launch_set(StreamArgs a, hipStream_t stream) {
   const size_t lds = (size_t)WV * stage_words<MT>(a.chunk) * 4;
   a.nstrips = (a.N + SC - 1) / SC;
   a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
-  // Each wave's first run segment, bounded by its first chunk.
-  for (int w = 0; w < WV; ++w) {
-    const int wb0 = (w * nblk) / WV, wb1 = ((w + 1) * nblk) / WV;
-    a.wave_bits[w] = 0;
-    a.wave_row[w] = 0;
-    a.wave_end[w] = wb0;
-    if (wb0 < wb1) {
-      int r = 0;
-      while (r + 1 < a.runs.nruns && wb0 >= a.runs.run_block[r + 1]) ++r;
-      a.wave_bits[w] = a.runs.run_bits[r];
-      a.wave_row[w] = a.runs.run_row[r] + (wb0 - a.runs.run_block[r]) * a.runs.run_bits[r];
-      a.wave_end[w] = std::min(std::min(wb1, a.runs.run_block[r + 1]), wb0 + a.chunk);
-    }
-  }
+  equal_waves(a, WV);   // as the kernel splits K
+  first_segments(a, WV, a.chunk);   // each bounded by the wave's first chunk
   hipLaunchKernelGGL((qgemv_stream_kernel<MT, BS, WV>), dim3(kXcds * a.strips_per_xcd, a.mats), dim3(WV * 64), lds,
                      stream, a);
   return hipGetLastError();

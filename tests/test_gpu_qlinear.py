@@ -35,6 +35,7 @@ def _ref(inp, x=None):
 
 
 MIXED_BITS = [6, 6, 5, 5, 4, 4, 4, 3, 3, 2, 8]   # 11 blocks of 32 rows, 6 runs
+LONG_MIXED = [3] * 528 + [2] * 528              # K = 33792 at 32-row groups: past the one-launch kernel's LDS limit
 
 
 # ------------------------------------------------------------------ one-hot probes
@@ -216,6 +217,57 @@ def test_qgemv_long_rows(K):
     assert_close(y, _ref(inp), f"qgemv K={K}")
 
 
+# One row, several widths: the one-launch kernel that runs the single-row
+# scheme segment by segment (waves split at run boundaries near the equal
+# split points).
+ROWMIX_BITS = {
+    "exl2-4.0bpw": [6] * 13 + [5] * 13 + [4] * 64 + [3] * 38,   # 4 runs, splits moved to 26 / 64 / 90
+    "boundary-in-wave": [4] * 48 + [3] * 80,                    # a wave of two segments of 16 blocks
+    "all-widths": [8, 6, 5, 4, 3, 2] * 3,                       # every width, 18 runs
+    "low": [3] * 40 + [2] * 24,
+    "max-runs": [4, 3] * 32,                                     # 64 runs: one block per segment
+    "two-blocks": [4, 3],                                        # waves without blocks
+    "three-blocks": [5, 3, 5],
+}
+
+
+@pytest.mark.parametrize("act_order", (True, False))
+@pytest.mark.parametrize("zeros", (True, False))
+@pytest.mark.parametrize("name", sorted(ROWMIX_BITS))
+def test_qgemv_one_launch_mixed(name, zeros, act_order):
+    say(f"qgemv one-launch mixed {name} zeros={zeros} act_order={act_order}")
+    inp = _mixed_inputs(ROWMIX_BITS[name], 32, 520, 1, seed=len(name) * 31 + 2 * zeros + act_order, zeros=zeros,
+                        act_order=act_order)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"one-launch mixed {name}")
+
+
+@pytest.mark.parametrize("K", (4128, 8224, 16416, 31744))
+def test_qgemv_one_launch_mixed_row_pieces(K):
+    """x-row pieces per thread: 4, 8 and 16 (K just past 4096, 8192 and
+    16384), and the LDS limit."""
+    say(f"qgemv one-launch mixed K={K}")
+    nb = K // 32
+    inp = _mixed_inputs([5] * (nb // 3) + [4] * (nb - nb // 3), 32, 48, 1, seed=K % 101, zeros=True)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"one-launch mixed K={K}")
+
+
+def test_qgemv_one_launch_mixed_one_hot():
+    """One-hot rows through the one-launch several-width kernel: exact."""
+    say("qgemv one-launch mixed one-hot")
+    inp = _mixed_inputs(ROWMIX_BITS["exl2-4.0bpw"], 32, 520, 1, seed=13, zeros=True)
+    K = inp.spec.K
+    lay = GpuLayer(inp)
+    w16 = oracle.dequant_fp16(inp.q, inp.scales, inp.zeros, inp.bits, 32)
+    inv = np.argsort(inp.perm)
+    for k in np.random.default_rng(3).choice(K, 6, replace=False):
+        x = np.zeros((1, K), np.float16)
+        x[0, k] = 1.0
+        got = lay.qgemv(x).cpu().numpy()[0]
+        assert np.array_equal(got.astype(np.float32), w16[inv[k]].astype(np.float32)), k
+
+
 def test_no_act_order_and_single_group():
     say("no act-order, one group")
     inp = _mixed_inputs([4], 32, 8, 3, seed=1, zeros=True, act_order=False)
@@ -383,14 +435,15 @@ def test_grouped_qgemv_max_group_full_size():
 @pytest.mark.parametrize("op,bits,gs,M,exact", [
     ("qgemv", [4] * 11, 32, 1, False),     # single-row kernel (factored arithmetic)
     ("qgemv", [4] * 11, 32, 4, False),     # single-row kernel, 4 rows
-    ("qgemv", MIXED_BITS, 32, 1, False),   # gather + multi-row VALU kernel
+    ("qgemv", MIXED_BITS, 32, 1, False),   # one-launch several-width kernel
+    ("qgemv", LONG_MIXED, 32, 1, False),   # gather + multi-row VALU kernel (K past the one-launch LDS limit)
     ("qgemv", MIXED_BITS, 32, 2, False),   # multi-row VALU kernel
     ("qgemv", MIXED_BITS, 32, 8, True),    # matrix-core kernel, exact dequantization (a scale per block)
     ("qgemv", [4] * 6, 128, 8, False),     # matrix-core kernel, factored (4-bit, 128-row groups)
     ("qgemm", MIXED_BITS, 32, 64, True),   # prefill, several widths
     ("qgemm", [4] * 11, 32, 64, True),     # prefill, one width
-], ids=["row", "row-M4", "gather-valu-M1", "valu-M2", "mfma-exact-M8", "mfma-factored-M8", "qgemm-mixed",
-        "qgemm-4bit"])
+], ids=["row", "row-M4", "rowmix-M1", "gather-valu-M1", "valu-M2", "mfma-exact-M8", "mfma-factored-M8",
+        "qgemm-mixed", "qgemm-4bit"])
 def test_nonfinite_activations(op, bits, gs, M, exact):
     """A NaN activation makes its whole output row NaN; an Inf activation makes
     every column of its row non-finite (kernels that dequantize exactly: the
@@ -423,7 +476,8 @@ def test_nonfinite_activations(op, bits, gs, M, exact):
 EPILOGUE_PATHS = [
     ("qgemv", [4] * 11, 1),        # single-row kernel
     ("qgemv", [4] * 11, 3),        # single-row kernel, 4-row instance
-    ("qgemv", MIXED_BITS, 1),      # gather + multi-row VALU kernel
+    ("qgemv", MIXED_BITS, 1),      # one-launch several-width kernel (with an addend: gather + multi-row VALU kernel)
+    ("qgemv", LONG_MIXED, 1),      # gather + multi-row VALU kernel (K past the one-launch LDS limit)
     ("qgemv", MIXED_BITS, 2),      # multi-row VALU kernel
     ("qgemv", [4] * 11, 5),        # MFMA decode kernel
     ("qgemv", MIXED_BITS, 16),     # MFMA decode kernel, several widths
@@ -434,8 +488,8 @@ EPILOGUE_PATHS = [
 
 
 @pytest.mark.parametrize("op,bits,M", EPILOGUE_PATHS,
-                         ids=["row", "row-M3", "gather-valu-M1", "valu-M2", "mfma-M5", "mfma-M16", "qgemm", "qgemm-mixed",
-                              "qgemm-runs"])
+                         ids=["row", "row-M3", "rowmix-M1", "gather-valu-M1", "valu-M2", "mfma-M5", "mfma-M16", "qgemm",
+                              "qgemm-mixed", "qgemm-runs"])
 @pytest.mark.parametrize("terms", ["bias", "residual", "bias-silu-residual", "silu-inplace-residual",
                                    "lora-bias-silu"])
 def test_fused_epilogue(op, bits, M, terms):

@@ -67,12 +67,12 @@ __device__ __forceinline__ void lane_pairs(int cq, int (&rlo)[4], int (&rhi)[4],
 // The perm entries follow the block alone (blk_ok), not the lane's columns:
 // the four lanes of a quad exchange the pairs of one block, so a lane whose
 // columns lie past N must still gather its quad's block.
-template <int B>
+template <int B, bool kTL = false>
 __device__ __forceinline__ void issue_step(const StreamArgs& a, const MatPtrs& mp, const uint32_t* panel,
                                            const int32_t* psrc, int blk,
                                            int row, bool blk_ok, bool ok, int blk_safe, int row_safe, int col,
                                            const int (&rlo)[4], const int (&rhi)[4], StepRegs& S) {
-  issue<B>(a, mp, panel, blk, row, ok, blk_safe, row_safe, col, reinterpret_cast<uint4(&)[B]>(S.W), S.P);
+  issue<B, kTL>(a, mp, panel, blk, row, ok, blk_safe, row_safe, col, reinterpret_cast<uint4(&)[B]>(S.W), S.P);
   const int32_t* pb = psrc + (size_t)(blk_ok ? blk : blk_safe) * kBlockRows;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -91,8 +91,9 @@ __device__ __forceinline__ float quad_sum(float v) {
 // Gather the lane's 4 pairs of block blk from each of the MT LDS rows (row m
 // at xrow + m * xstride), exchange them over the quad, then unpack the
 // block's pairs for the lane's 4 columns once and multiply them into every
-// row.
-template <int B, bool kPerm, int MT>
+// row. kTL: two-level scales (the block's weight is its 4-bit scale code + 1;
+// the factor scale_max / 16 comes in the epilogue).
+template <int B, bool kPerm, int MT, bool kTL = false>
 __device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs& S, const _Float16* xrow, int xstride,
                                              int blk, const int (&rlo)[4], const int (&rhi)[4], const float (&sc)[4],
                                              uint32_t magic, float (&yacc)[4][MT]) {
@@ -170,9 +171,19 @@ __device__ __forceinline__ void compute_step(const StreamArgs& a, const StepRegs
   });
   // A lane without a block this step (past the range or past N) adds nothing.
   if (S.P.ok) {
-    const float s[4] = {half_lo(S.P.s.x), half_hi(S.P.s.x), half_lo(S.P.s.y), half_hi(S.P.s.y)};
-    // The 4 zero points as bytes of one word (symmetric: 2^(B-1) each).
-    const uint32_t zw = a.has_zeros ? S.P.z : (uint32_t)(1u << (B - 1)) * 0x01010101u;
+    float s[4];
+    if constexpr (kTL) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[c] = (float)(((S.P.s.x >> (S.P.s.y + 4 * c)) & 15u) + 1u);
+    } else {
+      s[0] = half_lo(S.P.s.x);
+      s[1] = half_hi(S.P.s.x);
+      s[2] = half_lo(S.P.s.y);
+      s[3] = half_hi(S.P.s.y);
+    }
+    // The 4 zero points as bytes of one word (symmetric: 2^(B-1) each; two-level
+    // scales are symmetric).
+    const uint32_t zw = (!kTL && a.has_zeros) ? S.P.z : (uint32_t)(1u << (B - 1)) * 0x01010101u;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float z = (float)((zw >> (8 * c)) & 0xFFu);
@@ -195,19 +206,19 @@ struct RowLane {
 };
 
 // Step i of the segment [blk0, blk1) starting at packed row row0.
-template <int B>
+template <int B, bool kTL = false>
 __device__ __forceinline__ void seg_issue(const StreamArgs& a, const RowLane& L, int blk0, int blk1, int row0, int i,
                                           const int (&rlo)[4], const int (&rhi)[4], StepRegs& S) {
   const int blk = blk0 + i * KS + L.ks;
   const bool blk_ok = blk < blk1;
-  issue_step<B>(a, L.mp, L.panel, L.psrc, blk, row0 + (i * KS + L.ks) * B, blk_ok, L.colv && blk_ok, blk0, row0,
+  issue_step<B, kTL>(a, L.mp, L.panel, L.psrc, blk, row0 + (i * KS + L.ks) * B, blk_ok, L.colv && blk_ok, blk0, row0,
                 L.col, rlo, rhi, S);
 }
 
 // All steps of the wave's blocks [blk0, blk1) (at least one), D in flight;
 // the first D were issued already into S[0 .. D-1]. kPerm: act-order (the
 // choice is made once per launch, not per pair).
-template <int B, int D, bool kPerm, int MT>
+template <int B, int D, bool kPerm, int MT, bool kTL = false>
 __device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L, int blk0, int blk1, int row0,
                                           float (&yacc)[4][MT], StepRegs (&S)[D]) {
   int rlo[4], rhi[4];
@@ -218,7 +229,7 @@ __device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L,
     // Past the range the whole quad is idle (zero scale); its pairs come
     // from block blk0 (as its perm entries did).
     const int blk = blk0 + i * KS + L.ks < blk1 ? blk0 + i * KS + L.ks : blk0;
-    compute_step<B, kPerm, MT>(a, R, L.xrow, L.xstride, blk, rlo, rhi, sc, L.magic, yacc);
+    compute_step<B, kPerm, MT, kTL>(a, R, L.xrow, L.xstride, blk, rlo, rhi, sc, L.magic, yacc);
   };
   // Steady state: every buffer is refilled on every pass. (A refill under a
   // condition turns the buffers into loop-carried copies, and a copy waits for
@@ -228,7 +239,7 @@ __device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L,
     static_for<0, D>([&](auto Dd) {
       constexpr int d = decltype(Dd)::value;
       comp(i + d, S[d]);
-      seg_issue<B>(a, L, blk0, blk1, row0, i + d + D, rlo, rhi, S[d]);
+      seg_issue<B, kTL>(a, L, blk0, blk1, row0, i + d + D, rlo, rhi, S[d]);
     });
   }
   // The last 1 to 2D - 1 steps; those among i .. i + D - 1 are issued.
@@ -237,7 +248,7 @@ __device__ __forceinline__ void row_steps(const StreamArgs& a, const RowLane& L,
     constexpr int t = decltype(Tt)::value;
     if (t < r) {
       comp(i + t, S[t % D]);
-      if (t + D < r) seg_issue<B>(a, L, blk0, blk1, row0, i + t + D, rlo, rhi, S[t % D]);
+      if (t + D < r) seg_issue<B, kTL>(a, L, blk0, blk1, row0, i + t + D, rlo, rhi, S[t % D]);
     }
   });
 }
@@ -474,8 +485,9 @@ __device__ __forceinline__ void for_width(int bits, F&& f) {
   }
 }
 
-// Whether an M = 1 call with several widths runs the one-launch kernel
-// below: the x row must fit the LDS budget, and the call must have at most
+// Whether an M = 1 call with several widths (or two-level scales, any
+// widths) runs the one-launch kernel below: the x row must fit the LDS
+// budget, and the call must have at most
 // 1024 strips of 16 columns (4 workgroups per CU). Past that the gather
 // kernel plus the multi-row kernel win: the latter holds more waves per SIMD
 // (fewer registers), which pays once the grid takes several rounds.
@@ -483,13 +495,15 @@ __device__ __forceinline__ void for_width(int bits, F&& f) {
 // multi-row): 4.0 bpw 4096 -> 11008 (688 strips) 11.9 vs 14.8 us; 2.5 bpw
 // 28672 -> 8192 (512 strips) 30.8 vs 31.0 us; 2.5 bpw 8192 -> 28672 (1792
 // strips) 31.4 vs 29.4 us.
-inline bool mixed_row(int M, int K, int N, int mats, unsigned set) {
+inline bool mixed_row(int M, int K, int N, int mats, unsigned set, bool two_level) {
   const int64_t strips = (int64_t)((N + SC - 1) / SC) * mats;
-  return M == 1 && (size_t)row_words(K) * 4 <= kRowLdsBudget && (set & (set - 1)) != 0 && strips <= 1024;
+  return M == 1 && (size_t)row_words(K) * 4 <= kRowLdsBudget && ((set & (set - 1)) != 0 || two_level) &&
+         strips <= 1024;
 }
 
 template <unsigned BS, int WV, int P, int D, bool kPerm>
 __global__ __launch_bounds__(WV * 64) void qgemv_rowmix_kernel(StreamArgs a) {
+  constexpr bool kTL = two_level<BS>();   // two-level scales: scale codes, scale_max in the epilogue
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ float red[WV][4][1][SC];
 
@@ -528,6 +542,8 @@ __global__ __launch_bounds__(WV * 64) void qgemv_rowmix_kernel(StreamArgs a) {
   const int n_out = min(strip * SC + (tid % SC), N - 1);
   const uint16_t bias_raw = as_global<uint16_t>(epi.bias ? epi.bias : mp.y)[n_out];
   const uint16_t res_raw = as_global<uint16_t>(epi.residual ? epi.residual : mp.y)[n_out];
+  uint16_t smax_raw = 0;
+  if constexpr (kTL) smax_raw = as_global<uint16_t>(epi.scale_max)[n_out];
   asm volatile("" ::: "memory");   // keep the row loads ahead of the weight loads
 
   RowLane L;
@@ -567,11 +583,11 @@ __global__ __launch_bounds__(WV * 64) void qgemv_rowmix_kernel(StreamArgs a) {
     lane_pairs<B>(L.cq, rlo, rhi, sc);
     static_for<0, D>([&](auto Dd) {
       constexpr int d = decltype(Dd)::value;
-      seg_issue<B>(a, L, wb0, seg0_end, row0, d, rlo, rhi, S[d]);
+      seg_issue<B, kTL>(a, L, wb0, seg0_end, row0, d, rlo, rhi, S[d]);
     });
     store_row();
     __syncthreads();
-    row_steps<B, D, kPerm, 1>(a, L, wb0, seg0_end, row0, yacc, S);
+    row_steps<B, D, kPerm, 1, kTL>(a, L, wb0, seg0_end, row0, yacc, S);
   });
   if (wb0 < wb1) {
     for (int blk = seg0_end; blk < wb1;) {
@@ -588,11 +604,11 @@ __global__ __launch_bounds__(WV * 64) void qgemv_rowmix_kernel(StreamArgs a) {
         lane_pairs<B>(cq, rlo, rhi, sc);
         static_for<0, D>([&](auto Dd) {
           constexpr int d = decltype(Dd)::value;
-          seg_issue<B>(a, L, blk, seg_end, row, d, rlo, rhi, T[d]);
+          seg_issue<B, kTL>(a, L, blk, seg_end, row, d, rlo, rhi, T[d]);
         });
         RowLane Lc = L;
         Lc.cq = cq;
-        row_steps<B, D, kPerm, 1>(a, Lc, blk, seg_end, row, yacc, T);
+        row_steps<B, D, kPerm, 1, kTL>(a, Lc, blk, seg_end, row, yacc, T);
       });
       blk = seg_end;
     }
@@ -621,6 +637,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_rowmix_kernel(StreamArgs a) {
     for (int w = 0; w < WV; ++w)
 #pragma unroll
       for (int row = 0; row < 4; ++row) v += red[w][row][0][c_out];
+    if constexpr (kTL) v *= (float)__builtin_bit_cast(_Float16, smax_raw) * 0.0625f;
     if (epi.bias) v += (float)__builtin_bit_cast(_Float16, bias_raw);
     if (epi.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
     if (epi.residual) v += (float)__builtin_bit_cast(_Float16, res_raw);
@@ -686,6 +703,10 @@ hipError_t launch_rowmix_set(const StreamArgs& a, hipStream_t stream) {
 hipError_t launch_rowmix_low(const StreamArgs& a, hipStream_t stream);
 hipError_t launch_rowmix_mid(const StreamArgs& a, hipStream_t stream);
 hipError_t launch_rowmix_all(const StreamArgs& a, hipStream_t stream);
+// The same with two-level scales (in the qgemv_rowmix_tl_*.hip files).
+hipError_t launch_rowmix_low_tl(const StreamArgs& a, hipStream_t stream);
+hipError_t launch_rowmix_mid_tl(const StreamArgs& a, hipStream_t stream);
+hipError_t launch_rowmix_all_tl(const StreamArgs& a, hipStream_t stream);
 
 }  // namespace stream
 

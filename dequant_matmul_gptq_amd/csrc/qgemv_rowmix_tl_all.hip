@@ -1,0 +1,13 @@
+// One-launch M = 1 decode kernels with two-level scales (4-bit scale codes
+// and a float16 maximum per output), widths any of 2, 3, 4, 5, 6 and 8 bits.
+#include "qgemv_m1.hpp"
+
+namespace qlinear {
+namespace stream {
+
+hipError_t launch_rowmix_all_tl(const StreamArgs& a, hipStream_t stream) {
+  return launch_rowmix_set<kAllBits | kTwoLevelBit>(a, stream);
+}
+
+}  // namespace stream
+}  // namespace qlinear

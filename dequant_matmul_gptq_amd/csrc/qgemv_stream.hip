@@ -70,12 +70,14 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   // argument in its prologue cost 3% on the 7B decode step (measured on
   // MI355X), so calls with an addend (a LoRA update) run the kernels below.
   if (row) return stream::launch_row_set(set, a, stream);
-  // One row, several widths: the one-launch kernel that runs the single-row
-  // scheme run segment by segment.
-  if (!epi.addend && !tl && stream::mixed_row(M, L.K, L.N, mats, set)) {
-    if ((set & ~stream::kLowBits) == 0) return stream::launch_rowmix_low(a, stream);
-    if ((set & ~stream::kMidBits) == 0) return stream::launch_rowmix_mid(a, stream);
-    return stream::launch_rowmix_all(a, stream);
+  // One row, several widths (or two-level scales): the one-launch kernel
+  // that runs the single-row scheme run segment by segment.
+  if (!epi.addend && stream::mixed_row(M, L.K, L.N, mats, set, tl)) {
+    if ((set & ~stream::kLowBits) == 0)
+      return tl ? stream::launch_rowmix_low_tl(a, stream) : stream::launch_rowmix_low(a, stream);
+    if ((set & ~stream::kMidBits) == 0)
+      return tl ? stream::launch_rowmix_mid_tl(a, stream) : stream::launch_rowmix_mid(a, stream);
+    return tl ? stream::launch_rowmix_all_tl(a, stream) : stream::launch_rowmix_all(a, stream);
   }
   // 1-2 rows: the activations are gathered into the workspace (with the
   // per-block sums of the factored form) by a kernel of their own.

@@ -98,9 +98,10 @@ def test_one_hot_rows_are_exact(op, M):
 @pytest.mark.parametrize("M", (1, 2, 3, 4, 5, 8, 16))
 @pytest.mark.parametrize("name", ("mixed", "mid", "4bit-g128", "3bit"))
 def test_qgemv_qscale_small(name, M):
-    """Multi-row kernel (1-2 rows), matrix-core kernel in one launch (3-4
-    rows, widths 3-6) or with the gather kernel (8-bit runs, 5+ rows); single
-    widths run the several-width instances."""
+    """One-launch several-width kernel (1 row), multi-row kernel (2 rows),
+    matrix-core kernel in one launch (3-4 rows, widths 3-6) or with the
+    gather kernel (8-bit runs, 5+ rows); single widths run the several-width
+    instances."""
     say(f"qgemv_qscale {name} M={M}")
     bits, gs = {"mixed": (MIXED, 32), "mid": (MID, 32), "4bit-g128": ([4] * 6, 128), "3bit": ([3] * 9, 32)}[name]
     inp, codes, smax = _inputs(bits, gs, 520, M, seed=60 + M + len(name))
@@ -127,10 +128,19 @@ def test_qscale_epilogue():
     resid = rng.standard_normal((5, 520)).astype(np.float16)
     ref = oracle.apply_epilogue(lay.ref(inp.x), bias=bias, residual=resid, activation=oracle.ACT_SILU)
     for op in ("qgemv", "qgemm"):
-        for M in (2, 5):
+        for M in (1, 2, 5):
             f = lay.qgemv if op == "qgemv" else lay.qgemm
             y = f(inp.x[:M], bias=lay.x(bias), residual=lay.x(resid[:M]), activation=dq.ACT_SILU)
             assert_close(y, ref[:M], f"qscale epilogue {op} M={M}")
+
+
+def test_qgemv_qscale_long_row():
+    """One row past the one-launch kernel's LDS limit (K = 33792): gather
+    kernel plus multi-row kernel."""
+    say("qgemv_qscale long row")
+    inp, codes, smax = _inputs([3] * 528 + [2] * 528, 32, 48, 1, seed=95)
+    lay = QscaleLayer(inp, codes, smax)
+    assert_close(lay.qgemv(inp.x), lay.ref(inp.x), "qgemv_qscale K=33792")
 
 
 DECODE_CASES = [(wl.EXL2_MIXED, 1), (wl.EXL2_MIXED, 8)] + [(s, M) for s in wl.LLAMA70B_EXL2 for M in (1, 16)]

@@ -37,8 +37,8 @@ constexpr int row_mt(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 
 // Whether a call of M <= 4 rows runs this kernel: the x rows must fit in the
 // LDS budget, and the matrix must have a single code width (one row of
-// several widths runs qgemv_rowmix_kernel below). The budget is below the
-// 160 KB a workgroup may hold because the rows are staged through
+// several widths runs qgemv_rowmix_kernel, qgemv_rowmix.hpp). The budget is
+// below the 160 KB a workgroup may hold because the rows are staged through
 // registers: 4 rows of K = 11008 would need 128 VGPRs.
 inline bool single_row(int M, int K, unsigned set) {
   return M <= 4 && (size_t)row_mt(M) * row_words(K) * 4 <= kRowLdsBudget && (set & (set - 1)) == 0;
@@ -457,256 +457,6 @@ hipError_t launch_row_width(const StreamArgs& a, hipStream_t stream) {
 
 // Instantiated in qgemv_row.hip: `set` holds exactly one code width.
 hipError_t launch_row_set(unsigned set, const StreamArgs& a, hipStream_t stream);
-
-// ---------------------------------------------------------------------------
-// Several code widths at M = 1 (EXL2 layouts), in one launch: the scheme of
-// qgemv_row_kernel, run segment by segment. A wave's K range is cut at the
-// run boundaries; each segment has its width fixed at compile time (a switch
-// over the widths of the set BS) and refills its own D steps, so the
-// pipeline restarts at a boundary. The host gives each wave its K range and
-// first segment (width, first packed row, end block), so the first D steps
-// are issued right after the x row loads, as in the single-width kernel.
-// Register use: the first segment's issue, row staging and steps sit in one
-// width branch (two branches joined by the in-flight step registers cost
-// 20-40 VGPRs more), and the per-width lane constants are recomputed inside
-// the segment loop rather than hoisted out of it for every width.
-
-// Calls f(integral_constant<int, b>) for the width b = bits if BS holds it.
-template <unsigned BS, class F>
-__device__ __forceinline__ void for_width(int bits, F&& f) {
-  switch (bits) {
-    case 2: if constexpr ((BS >> 2) & 1u) f(std::integral_constant<int, 2>{}); break;
-    case 3: if constexpr ((BS >> 3) & 1u) f(std::integral_constant<int, 3>{}); break;
-    case 4: if constexpr ((BS >> 4) & 1u) f(std::integral_constant<int, 4>{}); break;
-    case 5: if constexpr ((BS >> 5) & 1u) f(std::integral_constant<int, 5>{}); break;
-    case 6: if constexpr ((BS >> 6) & 1u) f(std::integral_constant<int, 6>{}); break;
-    case 8: if constexpr ((BS >> 8) & 1u) f(std::integral_constant<int, 8>{}); break;
-    default: break;
-  }
-}
-
-// Whether an M = 1 call with several widths (or two-level scales, any
-// widths) runs the one-launch kernel below: the x row must fit the LDS
-// budget, and the call must have at most
-// 1024 strips of 16 columns (4 workgroups per CU). Past that the gather
-// kernel plus the multi-row kernel win: the latter holds more waves per SIMD
-// (fewer registers), which pays once the grid takes several rounds.
-// Measured on MI355X (graph-timed, EXL2 layers, one-launch vs gather +
-// multi-row): 4.0 bpw 4096 -> 11008 (688 strips) 11.9 vs 14.8 us; 2.5 bpw
-// 28672 -> 8192 (512 strips) 30.8 vs 31.0 us; 2.5 bpw 8192 -> 28672 (1792
-// strips) 31.4 vs 29.4 us.
-inline bool mixed_row(int M, int K, int N, int mats, unsigned set, bool two_level) {
-  const int64_t strips = (int64_t)((N + SC - 1) / SC) * mats;
-  return M == 1 && (size_t)row_words(K) * 4 <= kRowLdsBudget && ((set & (set - 1)) != 0 || two_level) &&
-         strips <= 1024;
-}
-
-template <unsigned BS, int WV, int P, int D, bool kPerm>
-__global__ __launch_bounds__(WV * 64) void qgemv_rowmix_kernel(StreamArgs a) {
-  constexpr bool kTL = two_level<BS>();   // two-level scales: scale codes, scale_max in the epilogue
-  extern __shared__ __align__(16) uint32_t lds[];
-  __shared__ float red[WV][4][1][SC];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Kernel arguments, all read in one batch (the wave's first segment too).
-  MatPtrs mp = a.mat[blockIdx.y];
-  int K = a.K, N = a.N, spx = a.strips_per_xcd, xw = a.xrow_words;
-  const uint16_t* xsrc = a.x;
-  Epilogue epi = a.epi;
-  int bits0 = a.wave_bits[wave], row0 = a.wave_row[wave], seg0_end = a.wave_end[wave];
-  int wb0 = a.wave_begin[wave], wb1 = a.wave_begin[wave + 1];
-  {
-    const int R = a.runs.packed_rows, bpg = a.bpg_shift, hz = a.has_zeros, nruns = a.runs.nruns;
-    const int32_t* const perm = a.perm;
-    asm volatile("" : "+s"(K), "+s"(N), "+s"(spx), "+s"(xw), "+s"(xsrc), "+s"(mp.y), "+s"(epi.bias),
-                 "+s"(epi.residual), "+s"(epi.act), "+s"(bits0), "+s"(row0), "+s"(seg0_end), "+s"(wb0), "+s"(wb1)
-                 : "s"(R), "s"(bpg), "s"(hz), "s"(nruns), "s"(perm), "s"(mp.qweight), "s"(mp.scales),
-                   "s"(mp.zeros));
-  }
-  const int bid = blockIdx.x;
-  const int strip = (bid % kXcds) * spx + bid / kXcds;
-  if (strip * SC >= N) return;  // the whole workgroup leaves together
-
-  // 1. The x row: every piece this thread copies, loaded before anything else.
-  constexpr int nthr = WV * 64;
-  const int n16 = K / 8;
-  piece_t xr[P];
-  {
-    const global_ptr<piece_t> xg = as_global<piece_t>(xsrc);
-#pragma unroll
-    for (int u = 0; u < P; ++u) xr[u] = xg[min(u * nthr + tid, n16 - 1)];
-  }
-  // The epilogue's operands of this strip's outputs (as in qgemv_row_kernel).
-  const int n_out = min(strip * SC + (tid % SC), N - 1);
-  const uint16_t bias_raw = as_global<uint16_t>(epi.bias ? epi.bias : mp.y)[n_out];
-  const uint16_t res_raw = as_global<uint16_t>(epi.residual ? epi.residual : mp.y)[n_out];
-  uint16_t smax_raw = 0;
-  if constexpr (kTL) smax_raw = as_global<uint16_t>(epi.scale_max)[n_out];
-  asm volatile("" ::: "memory");   // keep the row loads ahead of the weight loads
-
-  RowLane L;
-  L.mp = mp;
-  L.cq = lane % CQ;
-  L.ks = lane / CQ;
-  const int col_req = strip * SC + L.cq * 4;
-  L.colv = col_req < N;
-  L.col = L.colv ? col_req : N - 4;   // scale/zero column for lanes past N
-  L.panel = mp.qweight + (size_t)strip * a.runs.packed_rows * kPanel + L.cq * 4;
-  L.psrc = a.perm ? a.perm : reinterpret_cast<const int32_t*>(mp.qweight);   // >= K readable words
-  L.xrow = reinterpret_cast<const _Float16*>(lds);
-  L.xstride = xw * 2;
-  L.magic = vgpr_magic();
-
-  // 2. The first D steps of the first segment, then 3. the row into LDS.
-  // Both sit in the width's branch, so the wait before each LDS store covers
-  // that store's own piece and none of the weight loads issued after it.
-  // (A wave without blocks has width 0: it only stores its pieces.)
-  auto store_row = [&]() {
-    piece_t* xl = reinterpret_cast<piece_t*>(lds);
-#pragma unroll
-    for (int u = 0; u < P; ++u) xl[min(u * nthr + tid, n16 - 1)] = xr[u];
-  };
-  float yacc[4][1];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) yacc[c][0] = 0.0f;
-  if (bits0 == 0) {
-    store_row();
-    __syncthreads();
-  }
-  for_width<BS>(bits0, [&](auto Bc) {
-    constexpr int B = decltype(Bc)::value;
-    StepRegs S[D];
-    int rlo[4], rhi[4];
-    float sc[4];
-    lane_pairs<B>(L.cq, rlo, rhi, sc);
-    static_for<0, D>([&](auto Dd) {
-      constexpr int d = decltype(Dd)::value;
-      seg_issue<B, kTL>(a, L, wb0, seg0_end, row0, d, rlo, rhi, S[d]);
-    });
-    store_row();
-    __syncthreads();
-    row_steps<B, D, kPerm, 1, kTL>(a, L, wb0, seg0_end, row0, yacc, S);
-  });
-  if (wb0 < wb1) {
-    for (int blk = seg0_end; blk < wb1;) {
-      int bits, row;
-      block_info(a.runs, blk, bits, row);
-      const int seg_end = min(wb1, run_end_block(a.runs, blk));
-      for_width<BS>(bits, [&](auto Bc) {
-        constexpr int B = decltype(Bc)::value;
-        StepRegs T[D];
-        int rlo[4], rhi[4];
-        float sc[4];
-        int cq = L.cq;
-        asm volatile("" : "+v"(cq));   // keeps the lane's pair rows inside the loop (not hoisted per width)
-        lane_pairs<B>(cq, rlo, rhi, sc);
-        static_for<0, D>([&](auto Dd) {
-          constexpr int d = decltype(Dd)::value;
-          seg_issue<B, kTL>(a, L, blk, seg_end, row, d, rlo, rhi, T[d]);
-        });
-        RowLane Lc = L;
-        Lc.cq = cq;
-        row_steps<B, D, kPerm, 1, kTL>(a, Lc, blk, seg_end, row, yacc, T);
-      });
-      blk = seg_end;
-    }
-  }
-
-  // 5. Reduce over the block slots, the wave's rows and the waves; epilogue
-  // and store, as in qgemv_row_kernel.
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float v = yacc[c][0];
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF,
-                                                               true));   // row_shr:4
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF,
-                                                               true));   // row_shr:8
-    yacc[c][0] = v;
-  }
-  if ((lane & 15) >= 12) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) red[wave][lane >> 4][0][L.cq * 4 + c] = yacc[c][0];
-  }
-  __syncthreads();
-  const int c_out = tid % SC;
-  if (tid < SC && strip * SC + c_out < N) {
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WV; ++w)
-#pragma unroll
-      for (int row = 0; row < 4; ++row) v += red[w][row][0][c_out];
-    if constexpr (kTL) v *= (float)__builtin_bit_cast(_Float16, smax_raw) * 0.0625f;
-    if (epi.bias) v += (float)__builtin_bit_cast(_Float16, bias_raw);
-    if (epi.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
-    if (epi.residual) v += (float)__builtin_bit_cast(_Float16, res_raw);
-    ((__attribute__((address_space(1))) uint16_t*)mp.y)[strip * SC + c_out] =
-        __builtin_bit_cast(uint16_t, (_Float16)v);
-  }
-}
-
-// The waves' K ranges: each point of the equal split moves to the nearest
-// run boundary less than half a wave's share away (and past the previous
-// point, so that no wave is left empty). A boundary
-// inside a wave's range restarts its pipeline, and the wave of the most
-// segments sets the workgroup's time; on EXL2 layouts (a few runs, widest
-// first) the moved points also balance the weight bytes per wave better
-// (EXL2 4.0 bpw 4096 -> 11008, runs of 13, 13, 64 and 38 blocks: splits
-// 26 / 64 / 90 in place of 32 / 64 / 96).
-inline void snapped_waves(StreamArgs& a, int WV) {
-  const int nblk = a.K / kBlockRows;
-  const int half = nblk / (2 * WV);
-  a.wave_begin[0] = 0;
-  for (int w = 1; w < WV; ++w) {
-    const int eq = (w * nblk) / WV;
-    int best = eq, dist = half;
-    for (int r = 1; r < a.runs.nruns; ++r) {
-      const int b = a.runs.run_block[r];
-      const int d = b > eq ? b - eq : eq - b;
-      if (d < dist && b > a.wave_begin[w - 1]) {
-        dist = d;
-        best = b;
-      }
-    }
-    a.wave_begin[w] = std::max(best, a.wave_begin[w - 1]);
-  }
-  a.wave_begin[WV] = nblk;
-}
-
-template <unsigned BS, int P>
-hipError_t launch_rowmix(StreamArgs a, hipStream_t stream) {
-  const auto kernel = a.perm ? qgemv_rowmix_kernel<BS, kRowWaves, P, kRowDepth, true>
-                             : qgemv_rowmix_kernel<BS, kRowWaves, P, kRowDepth, false>;
-  a.nstrips = (a.N + SC - 1) / SC;
-  a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
-  a.xrow_words = row_words(a.K);
-  snapped_waves(a, kRowWaves);
-  first_segments(a, kRowWaves, a.K / kBlockRows);
-  const size_t lds = (size_t)a.xrow_words * 4;
-  hipLaunchKernelGGL(kernel, dim3(kXcds * a.strips_per_xcd, a.mats), dim3(kRowWaves * 64), lds, stream, a);
-  return hipGetLastError();
-}
-
-// The pieces per thread that cover K (mixed_row() bounds K by the LDS budget).
-template <unsigned BS>
-hipError_t launch_rowmix_set(const StreamArgs& a, hipStream_t stream) {
-  constexpr int per_piece = kRowWaves * 64 * 8;
-  if (a.K <= 2 * per_piece) return launch_rowmix<BS, 2>(a, stream);
-  if (a.K <= 4 * per_piece) return launch_rowmix<BS, 4>(a, stream);
-  if (a.K <= 8 * per_piece) return launch_rowmix<BS, 8>(a, stream);
-  return launch_rowmix<BS, kRowPiecesMax>(a, stream);
-}
-
-// Instantiated in the qgemv_rowmix_*.hip files, one per set of widths:
-// the smallest instantiated set that covers `set`.
-hipError_t launch_rowmix_low(const StreamArgs& a, hipStream_t stream);
-hipError_t launch_rowmix_mid(const StreamArgs& a, hipStream_t stream);
-hipError_t launch_rowmix_all(const StreamArgs& a, hipStream_t stream);
-// The same with two-level scales (in the qgemv_rowmix_tl_*.hip files).
-hipError_t launch_rowmix_low_tl(const StreamArgs& a, hipStream_t stream);
-hipError_t launch_rowmix_mid_tl(const StreamArgs& a, hipStream_t stream);
-hipError_t launch_rowmix_all_tl(const StreamArgs& a, hipStream_t stream);
 
 }  // namespace stream
 

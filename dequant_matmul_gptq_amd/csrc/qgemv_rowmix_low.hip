@@ -1,6 +1,6 @@
 // One-launch M = 1 decode kernels for layouts of several code widths,
 // widths 2-3 bits (EXL2 at about 2-3 bpw).
-#include "qgemv_m1.hpp"
+#include "qgemv_rowmix.hpp"
 
 namespace qlinear {
 namespace stream {

@@ -3,7 +3,7 @@
 // matrix-core kernel from 3 rows on (see below), otherwise the act-order
 // gather into the workspace, then the multi-row VALU kernel instantiated for
 // the smallest set of code widths covering the layout.
-#include "qgemv_m1.hpp"
+#include "qgemv_rowmix.hpp"
 
 namespace qlinear {
 

@@ -3,8 +3,9 @@
 Each case draws a bit map (runs of random widths in random order, up to 12
 runs), a group size, a ragged N, M, act-order or not, zero points or not,
 and one of: plain qgemv, qgemv with two-level scales, a grouped qgemv, qgemm
-(plain or two-level), or a fused epilogue. Tolerances as everywhere:
-relative Frobenius error <= 1e-3 and max error <= 1e-2 * max|y_ref|."""
+(plain or two-level), or a fused epilogue. A second set holds M = 1 (decode
+kinds only). Tolerances as everywhere: relative Frobenius error <= 1e-3 and
+max error <= 1e-2 * max|y_ref|."""
 
 import numpy as np
 import pytest
@@ -19,12 +20,15 @@ pytestmark = pytest.mark.gpu
 
 WIDTHS = (2, 3, 4, 5, 6, 8)
 KINDS = ("qgemv", "qgemv-qscale", "grouped", "qgemm", "qgemm-qscale", "fused")
+KINDS_M1 = ("qgemv", "qgemv-qscale", "grouped", "fused")
 N_CASES = 72
+N_CASES_M1 = 32   # one row: the one-launch several-width kernel (run segments, moved wave splits)
 
 
 def _case(i):
     rng = np.random.default_rng(1000 + i)
-    kind = KINDS[i % len(KINDS)]
+    m1 = i >= N_CASES
+    kind = KINDS_M1[i % len(KINDS_M1)] if m1 else KINDS[i % len(KINDS)]
     gs = int(rng.choice((32, 64, 128)))
     nruns = int(rng.integers(1, 13))
     widths = [int(w) for w in rng.choice(WIDTHS, size=nruns)]
@@ -35,7 +39,10 @@ def _case(i):
     G = len(groups)
     K = G * gs
     N = int(rng.integers(1, 80)) * 8
-    M = int(rng.integers(1, 17)) if kind not in ("qgemm", "qgemm-qscale") else int(rng.integers(1, 300))
+    if m1:
+        M = 1
+    else:
+        M = int(rng.integers(1, 17)) if kind not in ("qgemm", "qgemm-qscale") else int(rng.integers(1, 300))
     act_order = bool(rng.integers(0, 2))
     two = "qscale" in kind
     zeros = (not two) and bool(rng.integers(0, 2))
@@ -43,7 +50,7 @@ def _case(i):
                 zeros=zeros, seed=2000 + i)
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
+@pytest.mark.parametrize("i", range(N_CASES + N_CASES_M1))
 def test_random_layout(i):
     c = _case(i)
     say(f"random layout {i}: {c['kind']} K={c['K']} N={c['N']} gs={c['gs']} M={c['M']} "

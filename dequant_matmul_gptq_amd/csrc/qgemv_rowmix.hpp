@@ -37,18 +37,21 @@ __device__ __forceinline__ void for_width(int bits, F&& f) {
 
 // Whether an M = 1 call with several widths (or two-level scales, any
 // widths) runs the one-launch kernel below: the x row must fit the LDS
-// budget, and the call must have at most
-// 1024 strips of 16 columns (4 workgroups per CU). Past that the gather
-// kernel plus the multi-row kernel win: the latter holds more waves per SIMD
-// (fewer registers), which pays once the grid takes several rounds.
-// Measured on MI355X (graph-timed, EXL2 layers, one-launch vs gather +
-// multi-row): 4.0 bpw 4096 -> 11008 (688 strips) 11.9 vs 14.8 us; 2.5 bpw
-// 28672 -> 8192 (512 strips) 30.8 vs 31.0 us; 2.5 bpw 8192 -> 28672 (1792
-// strips) 31.4 vs 29.4 us.
+// budget, and the call must have at most 1024 strips of 16 columns (4
+// workgroups per CU), or 256 for rows of more than 16384 values (16 x-row
+// pieces per thread, about 200 VGPRs). Past that the gather kernel plus the
+// multi-row kernel win: the latter holds more waves per SIMD (fewer
+// registers), which pays once the grid takes several rounds. Measured on
+// MI355X (graph-timed, M = 1, one launch vs gather + multi-row):
+//   EXL2 4.0 bpw 4096 -> 11008 (688 strips)          11.9 vs 14.8 us
+//   2.5 bpw 8192 -> 28672 (1792 strips)              31.4 vs 29.4 us
+//   3/2-bit 16384 -> 8192 (512) / -> 2048 (128)       18.1 / 10.1 vs 18.8 / 12.1 us
+//   3/2-bit 28672 -> 8192 (512) / -> 4096 (256)       30.9 / 17.4 vs 29.8 / 20.1 us
 inline bool mixed_row(int M, int K, int N, int mats, unsigned set, bool two_level) {
   const int64_t strips = (int64_t)((N + SC - 1) / SC) * mats;
+  const int64_t max_strips = K > 16384 ? 256 : 1024;
   return M == 1 && (size_t)row_words(K) * 4 <= kRowLdsBudget && ((set & (set - 1)) != 0 || two_level) &&
-         strips <= 1024;
+         strips <= max_strips;
 }
 
 template <unsigned BS, int WV, int P, int D, bool kPerm>

@@ -1,4 +1,4 @@
-// One-launch M = 1 decode kernels for layouts of several code widths,
+// One-launch M = 1-2 decode kernels for layouts of several code widths,
 // widths any of 2, 3, 4, 5, 6 and 8 bits.
 #include "qgemv_rowmix.hpp"
 

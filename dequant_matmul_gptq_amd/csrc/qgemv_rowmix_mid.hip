@@ -1,4 +1,4 @@
-// One-launch M = 1 decode kernels for layouts of several code widths,
+// One-launch M = 1-2 decode kernels for layouts of several code widths,
 // widths 3-6 bits (EXL2 at about 3.5-5 bpw).
 #include "qgemv_rowmix.hpp"
 

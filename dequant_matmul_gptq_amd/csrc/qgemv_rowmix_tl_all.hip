@@ -1,4 +1,4 @@
-// One-launch M = 1 decode kernels with two-level scales (4-bit scale codes
+// One-launch M = 1-2 decode kernels with two-level scales (4-bit scale codes
 // and a float16 maximum per output), widths any of 2, 3, 4, 5, 6 and 8 bits.
 #include "qgemv_rowmix.hpp"
 

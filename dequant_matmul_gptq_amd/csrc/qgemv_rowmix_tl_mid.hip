@@ -1,4 +1,4 @@
-// One-launch M = 1 decode kernels with two-level scales (4-bit scale codes
+// One-launch M = 1-2 decode kernels with two-level scales (4-bit scale codes
 // and a float16 maximum per output), widths 3-6 bits (EXL2 at about 3.5-5 bpw).
 #include "qgemv_rowmix.hpp"
 

@@ -1,8 +1,8 @@
-// Host side of the decode path: one launch for one row (the single-row
-// kernel, or its several-width form) and for 2-4 rows of one width, the
-// matrix-core kernel from 3 rows on (see below), otherwise the act-order
-// gather into the workspace, then the multi-row VALU kernel instantiated for
-// the smallest set of code widths covering the layout.
+// Host side of the decode path: one launch for 1-4 rows of one width (the
+// single-row kernel) and for 1-2 rows of several widths (its several-width
+// form), the matrix-core kernel from 3 rows on (see below), otherwise the
+// act-order gather into the workspace, then the multi-row VALU kernel
+// instantiated for the smallest set of code widths covering the layout.
 #include "qgemv_rowmix.hpp"
 
 namespace qlinear {
@@ -70,8 +70,8 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   // argument in its prologue cost 3% on the 7B decode step (measured on
   // MI355X), so calls with an addend (a LoRA update) run the kernels below.
   if (row) return stream::launch_row_set(set, a, stream);
-  // One row, several widths (or two-level scales): the one-launch kernel
-  // that runs the single-row scheme run segment by segment.
+  // One or two rows, several widths (or two-level scales): the one-launch
+  // kernel that runs the single-row scheme run segment by segment.
   if (!epi.addend && stream::mixed_row(M, L.K, L.N, mats, set, tl)) {
     if ((set & ~stream::kLowBits) == 0)
       return tl ? stream::launch_rowmix_low_tl(a, stream) : stream::launch_rowmix_low(a, stream);

@@ -206,13 +206,13 @@ def test_qgemv_row_kernel_long_rows(K):
     assert_close(y, _ref(inp), f"qgemv row K={K}")
 
 
-@pytest.mark.parametrize("K", (31744, 33792))
-def test_qgemv_long_rows(K):
-    """M = 1 rows near and past the LDS capacity of the single-row kernel (the
-    longer one runs the multi-row path)."""
-    say(f"qgemv long row K={K}")
+@pytest.mark.parametrize("K,M", [(31744, 1), (33792, 1), (16416, 2), (33792, 2)])
+def test_qgemv_long_rows(K, M):
+    """Rows near and past the LDS capacity of the one-launch kernels (past
+    it: the gather kernel plus the multi-row kernel, at 1 and 2 rows)."""
+    say(f"qgemv long row K={K} M={M}")
     bits = [3] * (K // 64) + [2] * (K // 64)
-    inp = _mixed_inputs(bits, 32, 48, 1, seed=K % 97, zeros=False)
+    inp = _mixed_inputs(bits, 32, 48, M, seed=K % 97 + M, zeros=False)
     y = GpuLayer(inp).qgemv(inp.x)
     assert_close(y, _ref(inp), f"qgemv K={K}")
 
@@ -231,26 +231,27 @@ ROWMIX_BITS = {
 }
 
 
+@pytest.mark.parametrize("M", (1, 2))
 @pytest.mark.parametrize("act_order", (True, False))
 @pytest.mark.parametrize("zeros", (True, False))
 @pytest.mark.parametrize("name", sorted(ROWMIX_BITS))
-def test_qgemv_one_launch_mixed(name, zeros, act_order):
-    say(f"qgemv one-launch mixed {name} zeros={zeros} act_order={act_order}")
-    inp = _mixed_inputs(ROWMIX_BITS[name], 32, 520, 1, seed=len(name) * 31 + 2 * zeros + act_order, zeros=zeros,
-                        act_order=act_order)
+def test_qgemv_one_launch_mixed(name, zeros, act_order, M):
+    say(f"qgemv one-launch mixed {name} zeros={zeros} act_order={act_order} M={M}")
+    inp = _mixed_inputs(ROWMIX_BITS[name], 32, 520, M, seed=len(name) * 31 + 2 * zeros + act_order + 5 * M,
+                        zeros=zeros, act_order=act_order)
     y = GpuLayer(inp).qgemv(inp.x)
-    assert_close(y, _ref(inp), f"one-launch mixed {name}")
+    assert_close(y, _ref(inp), f"one-launch mixed {name} M={M}")
 
 
-@pytest.mark.parametrize("K", (4128, 8224, 16416, 31744))
-def test_qgemv_one_launch_mixed_row_pieces(K):
-    """x-row pieces per thread: 4, 8 and 16 (K just past 4096, 8192 and
-    16384), and the LDS limit."""
-    say(f"qgemv one-launch mixed K={K}")
+@pytest.mark.parametrize("K,M", [(4128, 1), (8224, 1), (16416, 1), (31744, 1), (4128, 2), (8224, 2), (15872, 2)])
+def test_qgemv_one_launch_mixed_row_pieces(K, M):
+    """x-row pieces per thread: 4, 8 and 16 at one row (K just past 4096,
+    8192 and 16384), 4 and 8 at two rows, and the LDS limit of each."""
+    say(f"qgemv one-launch mixed K={K} M={M}")
     nb = K // 32
-    inp = _mixed_inputs([5] * (nb // 3) + [4] * (nb - nb // 3), 32, 48, 1, seed=K % 101, zeros=True)
+    inp = _mixed_inputs([5] * (nb // 3) + [4] * (nb - nb // 3), 32, 48, M, seed=K % 101 + M, zeros=True)
     y = GpuLayer(inp).qgemv(inp.x)
-    assert_close(y, _ref(inp), f"one-launch mixed K={K}")
+    assert_close(y, _ref(inp), f"one-launch mixed K={K} M={M}")
 
 
 def test_qgemv_one_launch_mixed_one_hot():
@@ -437,12 +438,12 @@ def test_grouped_qgemv_max_group_full_size():
     ("qgemv", [4] * 11, 32, 4, False),     # single-row kernel, 4 rows
     ("qgemv", MIXED_BITS, 32, 1, False),   # one-launch several-width kernel
     ("qgemv", LONG_MIXED, 32, 1, False),   # gather + multi-row VALU kernel (K past the one-launch LDS limit)
-    ("qgemv", MIXED_BITS, 32, 2, False),   # multi-row VALU kernel
+    ("qgemv", MIXED_BITS, 32, 2, False),   # one-launch several-width kernel, 2 rows
     ("qgemv", MIXED_BITS, 32, 8, True),    # matrix-core kernel, exact dequantization (a scale per block)
     ("qgemv", [4] * 6, 128, 8, False),     # matrix-core kernel, factored (4-bit, 128-row groups)
     ("qgemm", MIXED_BITS, 32, 64, True),   # prefill, several widths
     ("qgemm", [4] * 11, 32, 64, True),     # prefill, one width
-], ids=["row", "row-M4", "rowmix-M1", "gather-valu-M1", "valu-M2", "mfma-exact-M8", "mfma-factored-M8",
+], ids=["row", "row-M4", "rowmix-M1", "gather-valu-M1", "rowmix-M2", "mfma-exact-M8", "mfma-factored-M8",
         "qgemm-mixed", "qgemm-4bit"])
 def test_nonfinite_activations(op, bits, gs, M, exact):
     """A NaN activation makes its whole output row NaN; an Inf activation makes
@@ -478,7 +479,7 @@ EPILOGUE_PATHS = [
     ("qgemv", [4] * 11, 3),        # single-row kernel, 4-row instance
     ("qgemv", MIXED_BITS, 1),      # one-launch several-width kernel (with an addend: gather + multi-row VALU kernel)
     ("qgemv", LONG_MIXED, 1),      # gather + multi-row VALU kernel (K past the one-launch LDS limit)
-    ("qgemv", MIXED_BITS, 2),      # multi-row VALU kernel
+    ("qgemv", MIXED_BITS, 2),      # one-launch several-width kernel, 2 rows
     ("qgemv", [4] * 11, 5),        # MFMA decode kernel
     ("qgemv", MIXED_BITS, 16),     # MFMA decode kernel, several widths
     ("qgemm", [4] * 11, 100),      # prefill, register dequant
@@ -488,7 +489,7 @@ EPILOGUE_PATHS = [
 
 
 @pytest.mark.parametrize("op,bits,M", EPILOGUE_PATHS,
-                         ids=["row", "row-M3", "rowmix-M1", "gather-valu-M1", "valu-M2", "mfma-M5", "mfma-M16", "qgemm",
+                         ids=["row", "row-M3", "rowmix-M1", "gather-valu-M1", "rowmix-M2", "mfma-M5", "mfma-M16", "qgemm",
                               "qgemm-mixed", "qgemm-runs"])
 @pytest.mark.parametrize("terms", ["bias", "residual", "bias-silu-residual", "silu-inplace-residual",
                                    "lora-bias-silu"])

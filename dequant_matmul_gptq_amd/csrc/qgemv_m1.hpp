@@ -273,7 +273,9 @@ typedef uint32_t piece_t __attribute__((ext_vector_type(4)));   // 16 bytes of t
 // kPerm: act-order (perm given), a kernel of its own so that the step loop
 // holds no per-pair choice.
 // MT: activation rows, 1, 2 or 4 (rows from M on repeat row M - 1 and are not stored).
-template <int B, int WV, int P, int D, bool kPerm, int MT>
+// kAddend: the epilogue adds a float32 addend (an instance of its own: the
+// pointer is read only where it is used).
+template <int B, int WV, int P, int D, bool kPerm, int MT, bool kAddend = false>
 __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ float red[WV][4][MT][SC];   // per wave and 16-lane row: the sums of the strip's columns
@@ -290,6 +292,11 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
     asm volatile("" : "+s"(K), "+s"(N), "+s"(M), "+s"(spx), "+s"(xw), "+s"(xsrc), "+s"(mp.y), "+s"(epi.bias),
                  "+s"(epi.residual), "+s"(epi.act)
                  : "s"(R), "s"(bpg), "s"(hz), "s"(perm), "s"(mp.qweight), "s"(mp.scales), "s"(mp.zeros));
+  }
+  const float* addp = nullptr;
+  if constexpr (kAddend) {
+    addp = epi.addend;
+    asm volatile("" : "+s"(addp));
   }
 
   const int tid = threadIdx.x;
@@ -320,6 +327,8 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   const int m_out = min(tid / SC, M - 1);
   const uint16_t bias_raw = as_global<uint16_t>(epi.bias ? epi.bias : mp.y)[n_out];
   const uint16_t res_raw = as_global<uint16_t>(epi.residual ? epi.residual : mp.y)[(size_t)m_out * N + n_out];
+  float add_v = 0.0f;
+  if constexpr (kAddend) add_v = as_global<float>(addp)[(size_t)m_out * N + n_out];
   asm volatile("" ::: "memory");   // keep the row loads ahead of the weight loads
 
   // 2. The first D steps of the wave's blocks, issued by every wave (a wave
@@ -398,6 +407,7 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
     for (int w = 0; w < WV; ++w)
 #pragma unroll
       for (int row = 0; row < 4; ++row) v += red[w][row][m][c_out];
+    if constexpr (kAddend) v += add_v;
     if (epi.bias) v += (float)__builtin_bit_cast(_Float16, bias_raw);
     if (epi.act == QLINEAR_ACT_SILU) v = v / (1.0f + __expf(-v));
     if (epi.residual) v += (float)__builtin_bit_cast(_Float16, res_raw);
@@ -406,9 +416,10 @@ __global__ __launch_bounds__(WV * 64) void qgemv_row_kernel(StreamArgs a) {
   }
 }
 
-template <int B, int WV, int P, int D, int MT>
+template <int B, int WV, int P, int D, int MT, bool kAddend>
 hipError_t launch_row(StreamArgs a, hipStream_t stream) {
-  const auto kernel = a.perm ? qgemv_row_kernel<B, WV, P, D, true, MT> : qgemv_row_kernel<B, WV, P, D, false, MT>;
+  const auto kernel = a.perm ? qgemv_row_kernel<B, WV, P, D, true, MT, kAddend>
+                             : qgemv_row_kernel<B, WV, P, D, false, MT, kAddend>;
   a.nstrips = (a.N + SC - 1) / SC;
   a.strips_per_xcd = (a.nstrips + kXcds - 1) / kXcds;
   a.xrow_words = row_words(a.K);
@@ -418,9 +429,10 @@ hipError_t launch_row(StreamArgs a, hipStream_t stream) {
 }
 
 // Four waves per workgroup for every shape. Measured on MI355X (7B decode
-// launches): at 8 waves only one workgroup fits per CU (the kernel needs
-// about 140 VGPRs), which costs up to 1.7x on the grouped launches, and the
-// long-K 11008 -> 4096 launch is also faster at 4 waves (8.4 vs 9.1 us).
+// launches, graph-timed): 8 waves take 9.29 / 5.02 / 14.99 / 8.53 us against
+// 7.61 / 4.48 / 11.67 / 7.82 us on 3 x 4096^2, 4096^2, 2 x 4096 -> 11008 and
+// 11008 -> 4096, although two 8-wave workgroups fit per CU (112 VGPRs for the
+// 4-bit instance): a wave then holds a single step of 16 blocks.
 constexpr int kRowWaves = 4;
 
 // x-row pieces per thread: the fewest of 2, 4, 8 and 16 that cover the row
@@ -435,28 +447,30 @@ constexpr int kRowDepth = 2;
 
 // MT rows: the pieces per thread that cover K (MT x rows must fit the LDS
 // budget, which single_row() checks: 2 rows need at most 8 pieces, 4 rows 4).
-template <int B, int MT>
+template <int B, int MT, bool kAddend>
 hipError_t launch_row_mt(const StreamArgs& a, hipStream_t stream) {
   constexpr int per_piece = kRowWaves * 64 * 8;   // x values per piece index
-  if (a.K <= 2 * per_piece) return launch_row<B, kRowWaves, 2, kRowDepth, MT>(a, stream);
-  if (a.K <= 4 * per_piece) return launch_row<B, kRowWaves, 4, kRowDepth, MT>(a, stream);
+  if (a.K <= 2 * per_piece) return launch_row<B, kRowWaves, 2, kRowDepth, MT, kAddend>(a, stream);
+  if (a.K <= 4 * per_piece) return launch_row<B, kRowWaves, 4, kRowDepth, MT, kAddend>(a, stream);
   if constexpr (MT <= 2) {
-    if (a.K <= 8 * per_piece) return launch_row<B, kRowWaves, 8, kRowDepth, MT>(a, stream);
+    if (a.K <= 8 * per_piece) return launch_row<B, kRowWaves, 8, kRowDepth, MT, kAddend>(a, stream);
   }
-  if constexpr (MT == 1) return launch_row<B, kRowWaves, kRowPiecesMax, kRowDepth, 1>(a, stream);
+  if constexpr (MT == 1) return launch_row<B, kRowWaves, kRowPiecesMax, kRowDepth, 1, kAddend>(a, stream);
   return hipErrorInvalidValue;
 }
 
-template <int B>
+template <int B, bool kAddend>
 hipError_t launch_row_width(const StreamArgs& a, hipStream_t stream) {
   const int mt = row_mt(a.M);
-  if (mt == 1) return launch_row_mt<B, 1>(a, stream);
-  if (mt == 2) return launch_row_mt<B, 2>(a, stream);
-  return launch_row_mt<B, 4>(a, stream);
+  if (mt == 1) return launch_row_mt<B, 1, kAddend>(a, stream);
+  if (mt == 2) return launch_row_mt<B, 2, kAddend>(a, stream);
+  return launch_row_mt<B, 4, kAddend>(a, stream);
 }
 
-// Instantiated in qgemv_row.hip: `set` holds exactly one code width.
+// Instantiated in qgemv_row.hip (no addend) and qgemv_row_addend.hip (with a
+// float32 addend): `set` holds exactly one code width.
 hipError_t launch_row_set(unsigned set, const StreamArgs& a, hipStream_t stream);
+hipError_t launch_row_set_addend(unsigned set, const StreamArgs& a, hipStream_t stream);
 
 }  // namespace stream
 

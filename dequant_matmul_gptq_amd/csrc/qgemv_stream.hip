@@ -63,13 +63,13 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   // Two-level scales run the kernels that read scale codes: the matrix-core
   // kernel, and the multi-row kernel's several-width instances.
   const bool tl = epi.scale_max != nullptr;
-  const bool row = !epi.addend && !tl && stream::single_row(M, L.K, set);
+  const bool row = !tl && stream::single_row(M, L.K, set);
   if (M >= 3 && !(row && (int64_t)L.K * L.N <= (int64_t)2 * 4096 * 4096))
     return launch_qgemv_mx(L, runs, x, M, perm, mats, qweights, scales, zeros, ys, ws, epi, stream);
-  // The single-launch kernel takes no float32 addend: reading one more kernel
-  // argument in its prologue cost 3% on the 7B decode step (measured on
-  // MI355X), so calls with an addend (a LoRA update) run the kernels below.
-  if (row) return stream::launch_row_set(set, a, stream);
+  // A float32 addend (a LoRA update) runs instances of their own: reading one
+  // more kernel argument in the prologue cost 3% on the 7B decode step
+  // (measured on MI355X), so the plain instances do not.
+  if (row) return epi.addend ? stream::launch_row_set_addend(set, a, stream) : stream::launch_row_set(set, a, stream);
   // One or two rows, several widths (or two-level scales): the one-launch
   // kernel that runs the single-row scheme run segment by segment.
   if (!epi.addend && stream::mixed_row(M, L.K, L.N, mats, set, tl)) {

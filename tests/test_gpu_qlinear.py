@@ -476,6 +476,7 @@ def test_nonfinite_activations(op, bits, gs, M, exact):
 
 EPILOGUE_PATHS = [
     ("qgemv", [4] * 11, 1),        # single-row kernel
+    ("qgemv", [4] * 11, 2),        # single-row kernel, 2-row instance
     ("qgemv", [4] * 11, 3),        # single-row kernel, 4-row instance
     ("qgemv", MIXED_BITS, 1),      # one-launch several-width kernel (with an addend: gather + multi-row VALU kernel)
     ("qgemv", LONG_MIXED, 1),      # gather + multi-row VALU kernel (K past the one-launch LDS limit)
@@ -489,7 +490,7 @@ EPILOGUE_PATHS = [
 
 
 @pytest.mark.parametrize("op,bits,M", EPILOGUE_PATHS,
-                         ids=["row", "row-M3", "rowmix-M1", "gather-valu-M1", "rowmix-M2", "mfma-M5", "mfma-M16", "qgemm",
+                         ids=["row", "row-M2", "row-M3", "rowmix-M1", "gather-valu-M1", "rowmix-M2", "mfma-M5", "mfma-M16", "qgemm",
                               "qgemm-mixed", "qgemm-runs"])
 @pytest.mark.parametrize("terms", ["bias", "residual", "bias-silu-residual", "silu-inplace-residual",
                                    "lora-bias-silu"])

@@ -5,62 +5,195 @@
 // width; w = RNE(s * (q - z)), one rounding), then v_mfma_f32_16x16x32_f16
 // accumulates in float32. The activations were gathered by act-order into
 // unpacking pair order beforehand, as for the single-width kernel.
-#include "qlinear_kernels.hpp"
+//
+// Every global load of a step (A pieces, packed words, scale, zero point) is
+// a buffer load with a per-lane offset fixed for the whole kernel and a
+// scalar per-step offset, issued unconditionally and before the first wait:
+// rows past M repeat row M - 1 and columns past N repeat column N - 1 (their
+// outputs are not stored), so no load sits behind a branch. The scale and
+// zero-point modes are template parameters for the same reason. A block's
+// width and first packed row come from a scalar run cursor that moves along K
+// with the blocks.
+#include "mfma_frag.hpp"
 
 namespace qlinear {
 
 namespace {
 
+using frag::kRsrcWord3;
+using frag::u32x4;
+
 constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kPad = 8;                 // halves of padding per LDS row
 constexpr int kLdsRow = BK + kPad;      // 72 halves = 144 bytes
+constexpr int kAPieces = BM * BK / 8 / kThreads;   // 16-byte A pieces per thread per step
 
 struct LdsGemmArgs {
   const uint16_t* xq;
   const uint32_t* qweight;
-  const uint16_t* scales;
+  const uint16_t* scales;   // float16 [groups][N], or packed 4-bit codes [groups][N / 8] (two-level)
   const uint8_t* zeros;
   uint16_t* y;
   int M, K, N;
+  int xq_bytes, qweight_bytes, scale_bytes, zero_bytes;
   Runs runs;
   Epilogue epi;
 };
 
-// Unpack + dequantize one (block, column) into 16 float16 pairs in LDS.
-template <int B>
-__device__ __forceinline__ void dequant_to_lds(const LdsGemmArgs& a, int row, int g, int n, bool valid,
-                                               uint32_t* dst /* 16 words */) {
-  uint32_t w[B];
-#pragma unroll
-  for (int t = 0; t < B; ++t) w[t] = valid ? a.qweight[word_index(a.runs.packed_rows, row + t, n)] : 0u;
-  _Float16 s = (_Float16)0.0f;
-  int z = 1 << (B - 1);
-  if (valid) {
-    // Two-level scales: the group factor c + 1, exact in float16, so that
-    // s * (q - z) stays an exact integer; scale_max / 16 comes in the epilogue.
-    if (a.epi.scale_max)
-      s = (_Float16)qscale_factor(reinterpret_cast<const uint32_t*>(a.scales)[(size_t)g * (a.N / 8) + n / 8], n);
-    else
-      s = __builtin_bit_cast(_Float16, a.scales[(size_t)g * a.N + n]);
-    if (a.zeros) z = a.zeros[(size_t)g * a.N + n];
+// The run of the blocks a wave is at: blocks advance along K, so the run
+// index only moves forward and its table entries are read when a block
+// crosses into the next run (wave-uniform, scalar registers).
+struct RunCursor {
+  int r;      // run index
+  int b0;     // its first block
+  int row0;   // its first packed row
+  int bits;   // its code width
+  int next;   // first block of run r + 1 (K / 32 after the last run)
+};
+
+// Width and first packed row of block blk (wave-uniform, not below the
+// cursor's first block).
+__device__ __forceinline__ void run_of(const LdsGemmArgs& a, RunCursor& c, int blk, int& bits, int& row) {
+  while (blk >= c.next) {
+    ++c.r;
+    c.b0 = c.next;
+    c.row0 = a.runs.run_row[c.r];
+    c.bits = a.runs.run_bits[c.r];
+    c.next = a.runs.run_block[c.r + 1];
   }
+  bits = c.bits;
+  row = c.row0 + (blk - c.b0) * c.bits;
+}
+
+// Per-lane buffer offsets (bytes) that do not change along K.
+struct LaneOffsets {
+  uint32_t a[kAPieces];   // A piece (row, 16-byte chunk) at K = 0
+  uint32_t w;             // packed row 0 of the lane's column
+  uint32_t s;             // the column's scale (or its scale code's word) in group 0
+  uint32_t z;             // the column's zero point in group 0
+};
+
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t x, w, s, z;
+};
+
+// The packed words, scale and zero point of (block at packed row `row`, group
+// g) for the lane's column: loads only.
+template <int B, bool kTL, bool kZeros>
+struct BLoads {
+  uint32_t w[B];
+  uint32_t s;
+  uint32_t z;
+};
+
+template <int B, bool kTL, bool kZeros>
+__device__ __forceinline__ BLoads<B, kTL, kZeros> load_b(const LdsGemmArgs& a, const Rsrc& rs, const LaneOffsets& off,
+                                                         int row, int g) {
+  BLoads<B, kTL, kZeros> v;
+  const int wrow = row * kPanel * 4;   // rows of a panel are 16 words apart
+#pragma unroll
+  for (int t = 0; t < B; ++t) v.w[t] = __builtin_amdgcn_raw_buffer_load_b32(rs.w, off.w, wrow + t * kPanel * 4, 0);
+  if constexpr (kTL)
+    v.s = __builtin_amdgcn_raw_buffer_load_b32(rs.s, off.s, g * (a.N / 8) * 4, 0);
+  else
+    v.s = __builtin_amdgcn_raw_buffer_load_b16(rs.s, off.s, g * a.N * 2, 0);
+  if constexpr (kZeros) v.z = __builtin_amdgcn_raw_buffer_load_b8(rs.z, off.z, g * a.N, 0);
+  return v;
+}
+
+// Unpack + dequantize the loaded (block, column) into 16 float16 pairs in LDS.
+// Two-level scales: the group factor c + 1, exact in float16, so that
+// s * (q - z) stays an exact integer; scale_max / 16 comes in the epilogue.
+template <int B, bool kTL, bool kZeros>
+__device__ __forceinline__ void dequant_to_lds(const BLoads<B, kTL, kZeros>& v, int ncol, uint32_t* dst) {
+  const _Float16 s = kTL ? (_Float16)qscale_factor(v.s, ncol) : __builtin_bit_cast(_Float16, (uint16_t)v.s);
+  const int z = kZeros ? (int)v.z : 1 << (B - 1);
   const _Float16 nb = (_Float16)(-(1024 + z));
   const half2_t scale = {s, s}, neg_bias = {nb, nb};
   uint32_t pr[kPairsPerBlock];
-  extract_all_pairs<B>(w, pr);
+  extract_all_pairs<B>(v.w, pr);
 #pragma unroll
   for (int q4 = 0; q4 < kPairsPerBlock / 4; ++q4) {
-    uint4 v;
-    v.x = as_u32(dequant_pair(pr[4 * q4 + 0], neg_bias, scale));
-    v.y = as_u32(dequant_pair(pr[4 * q4 + 1], neg_bias, scale));
-    v.z = as_u32(dequant_pair(pr[4 * q4 + 2], neg_bias, scale));
-    v.w = as_u32(dequant_pair(pr[4 * q4 + 3], neg_bias, scale));
-    *reinterpret_cast<uint4*>(dst + 4 * q4) = v;
+    u32x4 o;
+    o[0] = as_u32(dequant_pair(pr[4 * q4 + 0], neg_bias, scale));
+    o[1] = as_u32(dequant_pair(pr[4 * q4 + 1], neg_bias, scale));
+    o[2] = as_u32(dequant_pair(pr[4 * q4 + 2], neg_bias, scale));
+    o[3] = as_u32(dequant_pair(pr[4 * q4 + 3], neg_bias, scale));
+    *reinterpret_cast<u32x4*>(dst + 4 * q4) = o;
   }
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_lds_kernel(LdsGemmArgs a) {
+// Fill the LDS tiles of the step at block kb: the A tile (128 rows x 64
+// halves) and this wave's block kb + bsub of the B tile, dequantized at
+// width B. kTail: K ends after block kb (odd block count), so the second
+// half of the A tile is zero and the waves of the second block store zeros.
+template <int B, bool kTL, bool kZeros, bool kTail>
+__device__ __forceinline__ void fill_step(const LdsGemmArgs& a, const Rsrc& rs, const LaneOffsets& off, int tid, int kb,
+                                          int blk, int row, int ncol, bool bzero, uint16_t* As, uint32_t* bdst) {
+  u32x4 av[kAPieces];
+#pragma unroll
+  for (int i = 0; i < kAPieces; ++i)
+    av[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.x, off.a[i], kb * kBlockRows * 2, 0));
+  BLoads<B, kTL, kZeros> bl;
+  if (!kTail || !bzero) bl = load_b<B, kTL, kZeros>(a, rs, off, row, blk / a.runs.blocks_per_group);
+  // A stores wait only for the A loads (the B loads were issued after them).
+#pragma unroll
+  for (int i = 0; i < kAPieces; ++i) {
+    const int lin = tid + i * kThreads;
+    const int r = lin / (BK / 8), ch = lin % (BK / 8);
+    u32x4 v = av[i];
+    if constexpr (kTail)
+      if (ch >= BK / 16) v = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(As + r * kLdsRow + ch * 8) = v;
+  }
+  if (kTail && bzero) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<u32x4*>(bdst + 4 * q4) = u32x4{0u, 0u, 0u, 0u};
+  } else {
+    dequant_to_lds<B, kTL, kZeros>(bl, ncol, bdst);
+  }
+}
+
+// One K-step: both LDS tiles filled (the width's branch is uniform per wave),
+// then 2 x 16 MFMAs per wave.
+template <bool kTL, bool kZeros, bool kTail>
+__device__ __forceinline__ void k_step(const LdsGemmArgs& a, const Rsrc& rs, RunCursor& cur, const LaneOffsets& off,
+                                       int tid, int lane, int wr, int wc, int bsub, int kb, int nblk, int ncol,
+                                       uint16_t* As, uint16_t* Bs, float4_t (&acc)[4][4]) {
+  const int blk = __builtin_amdgcn_readfirstlane(kb + bsub);
+  const bool bzero = kTail && blk >= nblk;   // wave-uniform
+  int bits = 4, row = 0;
+  if (!bzero) run_of(a, cur, blk, bits, row);
+  uint32_t* bdst = reinterpret_cast<uint32_t*>(Bs + (tid % BN) * kLdsRow + bsub * kBlockRows);
+  switch (bits) {
+    case 2: fill_step<2, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
+    case 3: fill_step<3, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
+    case 4: fill_step<4, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
+    case 5: fill_step<5, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
+    case 6: fill_step<6, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
+    default: fill_step<8, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int kk = 0; kk < BK; kk += 32) {
+    half8_t af[4], bf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[i] = *reinterpret_cast<const half8_t*>(As + (wr * 64 + i * 16 + (lane & 15)) * kLdsRow + kk + 8 * (lane >> 4));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bf[j] = *reinterpret_cast<const half8_t*>(Bs + (wc * 64 + j * 16 + (lane & 15)) * kLdsRow + kk + 8 * (lane >> 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  }
+  __syncthreads();
+}
+
+template <bool kTL, bool kZeros>
+__global__ __launch_bounds__(kThreads, 3) void gemm_lds_kernel(LdsGemmArgs a) {
   __shared__ __align__(16) uint16_t As[BM * kLdsRow];
   __shared__ __align__(16) uint16_t Bs[BN * kLdsRow];
 
@@ -72,72 +205,40 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(LdsGemmArgs a) {
   const int m0 = blockIdx.y * BM;
   const int nblk = a.K / kBlockRows;
 
+  Rsrc rs;
+  rs.x = __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, 0, a.xq_bytes, kRsrcWord3);
+  rs.w = __builtin_amdgcn_make_buffer_rsrc((void*)a.qweight, 0, a.qweight_bytes, kRsrcWord3);
+  rs.s = __builtin_amdgcn_make_buffer_rsrc((void*)a.scales, 0, a.scale_bytes, kRsrcWord3);
+  rs.z = __builtin_amdgcn_make_buffer_rsrc(kZeros ? (void*)a.zeros : (void*)a.scales, 0,
+                                           kZeros ? a.zero_bytes : a.scale_bytes, kRsrcWord3);
+
+  // B work item of this thread: block bsub of each step (the same for a
+  // whole wave), column tid % 128 of the tile.
+  const int bsub = tid / BN;
+  const int ncol = n0 + tid % BN;
+  const int nc = min(ncol, a.N - 1);
+  LaneOffsets off;
+#pragma unroll
+  for (int i = 0; i < kAPieces; ++i) {
+    const int lin = tid + i * kThreads;
+    const int m = min(m0 + lin / (BK / 8), a.M - 1);
+    off.a[i] = ((uint32_t)m * (uint32_t)a.K + (uint32_t)(lin % (BK / 8)) * 8) * 2;
+  }
+  off.w = (uint32_t)word_index(a.runs.packed_rows, 0, nc) * 4;
+  off.s = kTL ? (uint32_t)(nc / 8) * 4 : (uint32_t)nc * 2;
+  off.z = (uint32_t)nc;
+
   float4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = {0.f, 0.f, 0.f, 0.f};
 
-  // B-tile work item of this thread: block (tid / 128) of the step, column tid % 128.
-  const int bsub = tid / BN;
-  const int bn = tid % BN;
-  const int ncol = n0 + bn;
-  const bool nvalid = ncol < a.N;
-
-  for (int kb = 0; kb < nblk; kb += BK / kBlockRows) {
-    // A tile: 128 rows x 64 halves, 16 bytes per thread per pass.
-#pragma unroll
-    for (int i = 0; i < (BM * BK / 8) / kThreads; ++i) {
-      const int lin = tid + i * kThreads;
-      const int r = lin / (BK / 8), ch = lin % (BK / 8);
-      const int m = m0 + r;
-      const int k = kb * kBlockRows + ch * 8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (m < a.M && k < a.K) v = *reinterpret_cast<const uint4*>(a.xq + (size_t)m * a.K + k);
-      *reinterpret_cast<uint4*>(As + r * kLdsRow + ch * 8) = v;
-    }
-    // B tile: dequantize block kb + bsub for column ncol.
-    {
-      const int blk = kb + bsub;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(Bs + bn * kLdsRow + bsub * kBlockRows);
-      if (blk < nblk) {
-        int bits, row;
-        block_info(a.runs, blk, bits, row);
-        const int g = blk / a.runs.blocks_per_group;
-        switch (bits) {
-          case 2: dequant_to_lds<2>(a, row, g, ncol, nvalid, dst); break;
-          case 3: dequant_to_lds<3>(a, row, g, ncol, nvalid, dst); break;
-          case 4: dequant_to_lds<4>(a, row, g, ncol, nvalid, dst); break;
-          case 5: dequant_to_lds<5>(a, row, g, ncol, nvalid, dst); break;
-          case 6: dequant_to_lds<6>(a, row, g, ncol, nvalid, dst); break;
-          case 8: dequant_to_lds<8>(a, row, g, ncol, nvalid, dst); break;
-          default: break;
-        }
-      } else {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<uint4*>(dst + 4 * q4) = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      half8_t af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(As + (wr * 64 + i * 16 + (lane & 15)) * kLdsRow + kk +
-                                                  8 * (lane >> 4));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(Bs + (wc * 64 + j * 16 + (lane & 15)) * kLdsRow + kk +
-                                                  8 * (lane >> 4));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
-  }
+  RunCursor cur{0, 0, a.runs.run_row[0], a.runs.run_bits[0], a.runs.run_block[1]};
+  const int nfull = nblk & ~1;   // steps whose two blocks are both inside K
+  for (int kb = 0; kb < nfull; kb += BK / kBlockRows)
+    k_step<kTL, kZeros, false>(a, rs, cur, off, tid, lane, wr, wc, bsub, kb, nblk, ncol, As, Bs, acc);
+  if (nfull < nblk) k_step<kTL, kZeros, true>(a, rs, cur, off, tid, lane, wr, wc, bsub, nfull, nblk, ncol, As, Bs, acc);
 
   // Epilogue: lane holds C[4*(lane/16) + r][lane % 16] of each 16 x 16 tile.
 #pragma unroll
@@ -170,10 +271,27 @@ hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uin
   a.M = M;
   a.K = L.K;
   a.N = L.N;
+  // Byte sizes for the buffer resources: the caller keeps the activations of
+  // a call below 2^31 bytes, and qgemm_supported the weights and scales.
+  const bool tl = epi.scale_max != nullptr;
+  a.xq_bytes = (int)((size_t)M * L.K * 2);
+  a.qweight_bytes = (int)((size_t)L.packed_words * 4);
+  a.scale_bytes = (int)(tl ? (size_t)L.groups * (L.N / 8) * 4 : (size_t)L.groups * L.N * 2);
+  a.zero_bytes = (int)((size_t)L.groups * L.N);
   a.runs = runs;
   a.epi = epi;
-  const int gmy = (M + BM - 1) / BM;
-  hipLaunchKernelGGL(gemm_lds_kernel, dim3((L.N + BN - 1) / BN, gmy, 1), dim3(kThreads), 0, stream, a);
+  const dim3 grid((L.N + BN - 1) / BN, (M + BM - 1) / BM, 1);
+  if (tl) {
+    if (zeros)
+      hipLaunchKernelGGL((gemm_lds_kernel<true, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_lds_kernel<true, false>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (zeros)
+      hipLaunchKernelGGL((gemm_lds_kernel<false, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_lds_kernel<false, false>), grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

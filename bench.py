@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-group", action="store_true", help="one qgemv launch per matrix (no grouped q/k/v, gate/up)")
-    ap.add_argument("--no-gemm", action="store_true", help="skip the M = 2048 qgemm measurement")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the M = 2048 qgemm measurements")
     ap.add_argument("--no-lora", action="store_true", help="skip the on-the-fly LoRA update timings")
     ap.add_argument("--no-kv", action="store_true", help="skip the KV-cache codec timings")
     ap.add_argument("--no-configs", action="store_true",
@@ -380,6 +380,7 @@ def main():
         ", ".join(f"{f['bytes']} B: {f['best_us']} us ({f['read_gbs']} GB/s)" for f in refs["read_floor"]))
 
     gemm = None if args.no_gemm else bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream)
+    gemm_mixed = None if args.no_gemm else bench_gemm_mixed(args, torch, dq, wl, oracle, lib, dev, stream)
     configs = None if args.no_configs else bench_configs(torch, dq, wl, lib, dev, stream, spin)
     lora = None if args.no_lora else bench_lora(torch, lib, dev, stream, spin)
     kv = None if args.no_kv else bench_kv(torch, lib, dev, stream, spin)
@@ -436,6 +437,7 @@ def main():
         "kv_codec": kv,
         "cpu_baseline": cpu,
         "qgemm": gemm,
+        "qgemm_mixed": gemm_mixed,
     }
     print(json.dumps(out), flush=True)
 
@@ -720,6 +722,63 @@ def bench_gemm(args, torch, dq, wl, oracle, lib, dev, stream):
             "timed": "whole qlinear_qgemm call: act-order gather kernel + gemm_kernel",
         },
     }
+
+
+def bench_gemm_mixed(args, torch, dq, wl, oracle, lib, dev, stream):
+    """qgemm on the EXL2 4.0 bpw 4096->11008 layer (four runs of widths 6, 5,
+    4 and 3: the kernel that dequantizes into LDS) at M = 2048, with float16
+    scales and with two-level scales; each checked against the oracle on
+    sampled rows, then timed over --gemm-iters calls."""
+    sh = stream.cuda_stream
+    spec = wl.EXL2_MIXED
+    M = 2048
+    inp = wl.generate(spec, M=M)
+    L = dq.Layout(spec.K, spec.N, spec.group_size, inp.bits)
+    qw = dq.pack_weights(L, torch.from_numpy(inp.q).to(dev))
+    pm = torch.from_numpy(inp.perm).to(dev)
+    x = torch.from_numpy(inp.x).to(dev)
+    y = torch.empty((M, spec.N), dtype=torch.float16, device=dev)
+    gws = torch.empty(dq.qgemm_workspace_bytes(L, M), dtype=torch.uint8, device=dev)
+    rows = np.arange(0, M, 128)
+    codes, smax = wl.two_level_scales(spec)
+    sc = torch.from_numpy(inp.scales).to(dev)
+    qs = dq.pack_qscale(torch.from_numpy(codes).to(dev))
+    qsm = torch.from_numpy(smax).to(dev)
+    cases = [
+        ("fp16", Launch(lib.qlinear_qgemm, L, x, M, qw, sc, None, pm, y, gws, sh),
+         lambda: oracle.qlinear(inp.x[rows], inp.q, inp.scales, None, inp.bits, spec.group_size, inp.perm)),
+        ("two-level", Call(lib.qlinear_qgemm_qscale, L, x, M, qw, qs, qsm, pm, None, y, gws, sh),
+         lambda: oracle.qlinear_qscale(inp.x[rows], inp.q, oracle.qscale_pack(codes), smax, inp.bits, spec.group_size,
+                                       inp.perm)),
+    ]
+    flops = 2.0 * M * spec.K * spec.N
+    out = []
+    for kind, gl, ref_fn in cases:
+        gl()
+        torch.cuda.synchronize()
+        ref = ref_fn()
+        d = y[torch.from_numpy(rows).to(dev)].float().cpu().numpy() - ref
+        rel = float(np.linalg.norm(d) / np.linalg.norm(ref))
+        if rel > 1e-3 or float(np.abs(d).max()) > 1e-2 * float(np.abs(ref).max()):
+            raise RuntimeError(f"mixed-width qgemm ({kind} scales) disagrees with the oracle: rel_fro={rel:.2e}")
+        for _ in range(3):
+            gl()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(args.gemm_iters):
+            gl()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        ms = g0.elapsed_time(g1) / args.gemm_iters
+        tflops = flops / (ms * 1e-3) / 1e12
+        log(f"qgemm EXL2 4.0 bpw M={M} ({kind} scales): {ms * 1e3:.1f} us per call -> {tflops:.1f} TFLOP/s "
+            f"({tflops / MFMA_F16_PEAK_TFLOPS:.1%} of fp16 MFMA peak), rel_fro={rel:.1e}")
+        out.append({"workload": f"{spec.name}, M={M}", "scales": kind, "value": round(tflops, 2),
+                    "unit": "TFLOP/s", "ms_per_call": round(ms, 5),
+                    "frac_of_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)})
+    return out
 
 
 def cpu_baseline(inp, wbytes):

@@ -25,9 +25,15 @@ using frag::u32x4;
 
 constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kPad = 8;                 // halves of padding per LDS row
-constexpr int kLdsRow = BK + kPad;      // 72 halves = 144 bytes
+constexpr int kLdsRow = BK;            // 64 halves = 128 bytes, eight 16-byte chunks
 constexpr int kAPieces = BM * BK / 8 / kThreads;   // 16-byte A pieces per thread per step
+
+// LDS tiles are rows of 64 halves without padding; 16-byte chunk c of row r
+// sits at chunk position c ^ ((r >> 1) & 7). A 16-lane group of a 16-byte
+// access then touches each of the 64 banks once, both for 16 consecutive rows
+// at one chunk (fragment reads, B-tile stores) and for 2 rows x 8 chunks
+// (A-tile stores).
+__device__ __forceinline__ int lds_at(int r, int c) { return r * kLdsRow + ((c ^ ((r >> 1) & 7)) << 3); }
 
 struct LdsGemmArgs {
   const uint16_t* xq;
@@ -106,7 +112,8 @@ __device__ __forceinline__ BLoads<B, kTL, kZeros> load_b(const LdsGemmArgs& a, c
 // Two-level scales: the group factor c + 1, exact in float16, so that
 // s * (q - z) stays an exact integer; scale_max / 16 comes in the epilogue.
 template <int B, bool kTL, bool kZeros>
-__device__ __forceinline__ void dequant_to_lds(const BLoads<B, kTL, kZeros>& v, int ncol, uint32_t* dst) {
+__device__ __forceinline__ void dequant_to_lds(const BLoads<B, kTL, kZeros>& v, int ncol, uint16_t* Bs, int brow,
+                                               int bchunk) {
   const _Float16 s = kTL ? (_Float16)qscale_factor(v.s, ncol) : __builtin_bit_cast(_Float16, (uint16_t)v.s);
   const int z = kZeros ? (int)v.z : 1 << (B - 1);
   const _Float16 nb = (_Float16)(-(1024 + z));
@@ -120,17 +127,18 @@ __device__ __forceinline__ void dequant_to_lds(const BLoads<B, kTL, kZeros>& v, 
     o[1] = as_u32(dequant_pair(pr[4 * q4 + 1], neg_bias, scale));
     o[2] = as_u32(dequant_pair(pr[4 * q4 + 2], neg_bias, scale));
     o[3] = as_u32(dequant_pair(pr[4 * q4 + 3], neg_bias, scale));
-    *reinterpret_cast<u32x4*>(dst + 4 * q4) = o;
+    *reinterpret_cast<u32x4*>(Bs + lds_at(brow, bchunk + q4)) = o;
   }
 }
 
 // Fill the LDS tiles of the step at block kb: the A tile (128 rows x 64
-// halves) and this wave's block kb + bsub of the B tile, dequantized at
-// width B. kTail: K ends after block kb (odd block count), so the second
+// halves) and this wave's block kb + bsub of the B tile (row brow: the
+// thread's column; chunks bchunk .. bchunk + 3), dequantized at width B. kTail: K ends after block kb (odd block count), so the second
 // half of the A tile is zero and the waves of the second block store zeros.
 template <int B, bool kTL, bool kZeros, bool kTail>
 __device__ __forceinline__ void fill_step(const LdsGemmArgs& a, const Rsrc& rs, const LaneOffsets& off, int tid, int kb,
-                                          int blk, int row, int ncol, bool bzero, uint16_t* As, uint32_t* bdst) {
+                                          int blk, int row, int ncol, bool bzero, uint16_t* As, uint16_t* Bs, int brow,
+                                          int bchunk) {
   u32x4 av[kAPieces];
 #pragma unroll
   for (int i = 0; i < kAPieces; ++i)
@@ -145,13 +153,13 @@ __device__ __forceinline__ void fill_step(const LdsGemmArgs& a, const Rsrc& rs, 
     u32x4 v = av[i];
     if constexpr (kTail)
       if (ch >= BK / 16) v = u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(As + r * kLdsRow + ch * 8) = v;
+    *reinterpret_cast<u32x4*>(As + lds_at(r, ch)) = v;
   }
   if (kTail && bzero) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<u32x4*>(bdst + 4 * q4) = u32x4{0u, 0u, 0u, 0u};
+    for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<u32x4*>(Bs + lds_at(brow, bchunk + q4)) = u32x4{0u, 0u, 0u, 0u};
   } else {
-    dequant_to_lds<B, kTL, kZeros>(bl, ncol, bdst);
+    dequant_to_lds<B, kTL, kZeros>(bl, ncol, Bs, brow, bchunk);
   }
 }
 
@@ -165,14 +173,14 @@ __device__ __forceinline__ void k_step(const LdsGemmArgs& a, const Rsrc& rs, Run
   const bool bzero = kTail && blk >= nblk;   // wave-uniform
   int bits = 4, row = 0;
   if (!bzero) run_of(a, cur, blk, bits, row);
-  uint32_t* bdst = reinterpret_cast<uint32_t*>(Bs + (tid % BN) * kLdsRow + bsub * kBlockRows);
+  const int brow = tid % BN, bchunk = bsub * (kBlockRows / 8);
   switch (bits) {
-    case 2: fill_step<2, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
-    case 3: fill_step<3, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
-    case 4: fill_step<4, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
-    case 5: fill_step<5, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
-    case 6: fill_step<6, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
-    default: fill_step<8, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, bdst); break;
+    case 2: fill_step<2, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
+    case 3: fill_step<3, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
+    case 4: fill_step<4, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
+    case 5: fill_step<5, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
+    case 6: fill_step<6, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
+    default: fill_step<8, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
   }
   __syncthreads();
 #pragma unroll
@@ -180,10 +188,10 @@ __device__ __forceinline__ void k_step(const LdsGemmArgs& a, const Rsrc& rs, Run
     half8_t af[4], bf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const half8_t*>(As + (wr * 64 + i * 16 + (lane & 15)) * kLdsRow + kk + 8 * (lane >> 4));
+      af[i] = *reinterpret_cast<const half8_t*>(As + lds_at(wr * 64 + i * 16 + (lane & 15), kk / 8 + (lane >> 4)));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      bf[j] = *reinterpret_cast<const half8_t*>(Bs + (wc * 64 + j * 16 + (lane & 15)) * kLdsRow + kk + 8 * (lane >> 4));
+      bf[j] = *reinterpret_cast<const half8_t*>(Bs + lds_at(wc * 64 + j * 16 + (lane & 15), kk / 8 + (lane >> 4)));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -201,7 +201,7 @@ __device__ __forceinline__ void k_step(const LdsGemmArgs& a, const Rsrc& rs, Run
 }
 
 template <bool kTL, bool kZeros>
-__global__ __launch_bounds__(kThreads, 3) void gemm_lds_kernel(LdsGemmArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void gemm_lds_kernel(LdsGemmArgs a) {
   __shared__ __align__(16) uint16_t As[BM * kLdsRow];
   __shared__ __align__(16) uint16_t Bs[BN * kLdsRow];
 

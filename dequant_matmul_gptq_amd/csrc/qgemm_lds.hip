@@ -29,11 +29,24 @@ constexpr int kLdsRow = BK;            // 64 halves = 128 bytes, eight 16-byte c
 constexpr int kAPieces = BM * BK / 8 / kThreads;   // 16-byte A pieces per thread per step
 
 // LDS tiles are rows of 64 halves without padding; 16-byte chunk c of row r
-// sits at chunk position c ^ ((r >> 1) & 7). A 16-lane group of a 16-byte
-// access then touches each of the 64 banks once, both for 16 consecutive rows
-// at one chunk (fragment reads, B-tile stores) and for 2 rows x 8 chunks
-// (A-tile stores).
-__device__ __forceinline__ int lds_at(int r, int c) { return r * kLdsRow + ((c ^ ((r >> 1) & 7)) << 3); }
+// sits at chunk position c ^ (r & 7). Measured with SQ_LDS_BANK_CONFLICT on
+// gfx950: a 16-byte store is conflict-free when each 8 consecutive lanes
+// write 8 distinct 16-byte slots of a 128-byte window, which holds for the
+// A-tile stores (8 lanes: one row's 8 chunks) and, with this swizzle, for the
+// B-tile stores (8 lanes: 8 consecutive rows at one chunk; the swizzle
+// c ^ ((r >> 1) & 7) cost 8 conflict cycles per store). The fragment reads
+// (16 consecutive rows at one chunk) are conflict-free with either.
+__device__ __forceinline__ int lds_at(int r, int c) { return r * kLdsRow + ((c ^ (r & 7)) << 3); }
+
+// Per-lane LDS offsets (halves) of the tile accesses, set once: the low three
+// bits of the row are the same in every access a lane makes, so each access
+// is one of these plus a multiple of 8 rows.
+struct LdsOffsets {
+  int a_st;      // A-tile store of piece 0 (piece i: + 32 i rows)
+  int b_st[4];   // B-tile stores: chunks bchunk .. bchunk + 3 of the thread's row
+  int a_rd[2];   // A fragment 0 at K offsets 0 and 32 (fragment i: + 16 i rows)
+  int b_rd[2];   // B fragment 0, likewise
+};
 
 struct LdsGemmArgs {
   const uint16_t* xq;
@@ -112,8 +125,8 @@ __device__ __forceinline__ BLoads<B, kTL, kZeros> load_b(const LdsGemmArgs& a, c
 // Two-level scales: the group factor c + 1, exact in float16, so that
 // s * (q - z) stays an exact integer; scale_max / 16 comes in the epilogue.
 template <int B, bool kTL, bool kZeros>
-__device__ __forceinline__ void dequant_to_lds(const BLoads<B, kTL, kZeros>& v, int ncol, uint16_t* Bs, int brow,
-                                               int bchunk) {
+__device__ __forceinline__ void dequant_to_lds(const BLoads<B, kTL, kZeros>& v, int ncol, uint16_t* Bs,
+                                               const LdsOffsets& lo) {
   const _Float16 s = kTL ? (_Float16)qscale_factor(v.s, ncol) : __builtin_bit_cast(_Float16, (uint16_t)v.s);
   const int z = kZeros ? (int)v.z : 1 << (B - 1);
   const _Float16 nb = (_Float16)(-(1024 + z));
@@ -127,18 +140,18 @@ __device__ __forceinline__ void dequant_to_lds(const BLoads<B, kTL, kZeros>& v, 
     o[1] = as_u32(dequant_pair(pr[4 * q4 + 1], neg_bias, scale));
     o[2] = as_u32(dequant_pair(pr[4 * q4 + 2], neg_bias, scale));
     o[3] = as_u32(dequant_pair(pr[4 * q4 + 3], neg_bias, scale));
-    *reinterpret_cast<u32x4*>(Bs + lds_at(brow, bchunk + q4)) = o;
+    *reinterpret_cast<u32x4*>(Bs + lo.b_st[q4]) = o;
   }
 }
 
 // Fill the LDS tiles of the step at block kb: the A tile (128 rows x 64
-// halves) and this wave's block kb + bsub of the B tile (row brow: the
-// thread's column; chunks bchunk .. bchunk + 3), dequantized at width B. kTail: K ends after block kb (odd block count), so the second
+// halves) and this wave's block kb + bsub of the B tile (the thread's
+// column: four chunks of its row), dequantized at width B. kTail: K ends after block kb (odd block count), so the second
 // half of the A tile is zero and the waves of the second block store zeros.
 template <int B, bool kTL, bool kZeros, bool kTail>
 __device__ __forceinline__ void fill_step(const LdsGemmArgs& a, const Rsrc& rs, const LaneOffsets& off, int tid, int kb,
-                                          int blk, int row, int ncol, bool bzero, uint16_t* As, uint16_t* Bs, int brow,
-                                          int bchunk) {
+                                          int blk, int row, int ncol, bool bzero, uint16_t* As, uint16_t* Bs,
+                                          const LdsOffsets& lo) {
   u32x4 av[kAPieces];
 #pragma unroll
   for (int i = 0; i < kAPieces; ++i)
@@ -148,18 +161,16 @@ __device__ __forceinline__ void fill_step(const LdsGemmArgs& a, const Rsrc& rs, 
   // A stores wait only for the A loads (the B loads were issued after them).
 #pragma unroll
   for (int i = 0; i < kAPieces; ++i) {
-    const int lin = tid + i * kThreads;
-    const int r = lin / (BK / 8), ch = lin % (BK / 8);
     u32x4 v = av[i];
     if constexpr (kTail)
-      if (ch >= BK / 16) v = u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(As + lds_at(r, ch)) = v;
+      if (tid % (BK / 8) >= BK / 16) v = u32x4{0u, 0u, 0u, 0u};   // chunks of the block past K
+    *reinterpret_cast<u32x4*>(As + lo.a_st + i * (kThreads / (BK / 8)) * kLdsRow) = v;
   }
   if (kTail && bzero) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<u32x4*>(Bs + lds_at(brow, bchunk + q4)) = u32x4{0u, 0u, 0u, 0u};
+    for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<u32x4*>(Bs + lo.b_st[q4]) = u32x4{0u, 0u, 0u, 0u};
   } else {
-    dequant_to_lds<B, kTL, kZeros>(bl, ncol, Bs, brow, bchunk);
+    dequant_to_lds<B, kTL, kZeros>(bl, ncol, Bs, lo);
   }
 }
 
@@ -167,20 +178,19 @@ __device__ __forceinline__ void fill_step(const LdsGemmArgs& a, const Rsrc& rs, 
 // then 2 x 16 MFMAs per wave.
 template <bool kTL, bool kZeros, bool kTail>
 __device__ __forceinline__ void k_step(const LdsGemmArgs& a, const Rsrc& rs, RunCursor& cur, const LaneOffsets& off,
-                                       int tid, int lane, int wr, int wc, int bsub, int kb, int nblk, int ncol,
-                                       uint16_t* As, uint16_t* Bs, float4_t (&acc)[4][4]) {
+                                       const LdsOffsets& lo, int tid, int bsub, int kb, int nblk, int ncol, uint16_t* As,
+                                       uint16_t* Bs, float4_t (&acc)[4][4]) {
   const int blk = __builtin_amdgcn_readfirstlane(kb + bsub);
   const bool bzero = kTail && blk >= nblk;   // wave-uniform
   int bits = 4, row = 0;
   if (!bzero) run_of(a, cur, blk, bits, row);
-  const int brow = tid % BN, bchunk = bsub * (kBlockRows / 8);
   switch (bits) {
-    case 2: fill_step<2, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
-    case 3: fill_step<3, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
-    case 4: fill_step<4, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
-    case 5: fill_step<5, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
-    case 6: fill_step<6, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
-    default: fill_step<8, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, brow, bchunk); break;
+    case 2: fill_step<2, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, lo); break;
+    case 3: fill_step<3, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, lo); break;
+    case 4: fill_step<4, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, lo); break;
+    case 5: fill_step<5, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, lo); break;
+    case 6: fill_step<6, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, lo); break;
+    default: fill_step<8, kTL, kZeros, kTail>(a, rs, off, tid, kb, blk, row, ncol, bzero, As, Bs, lo); break;
   }
   __syncthreads();
 #pragma unroll
@@ -188,10 +198,10 @@ __device__ __forceinline__ void k_step(const LdsGemmArgs& a, const Rsrc& rs, Run
     half8_t af[4], bf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const half8_t*>(As + lds_at(wr * 64 + i * 16 + (lane & 15), kk / 8 + (lane >> 4)));
+      af[i] = *reinterpret_cast<const half8_t*>(As + lo.a_rd[kk / 32] + i * 16 * kLdsRow);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      bf[j] = *reinterpret_cast<const half8_t*>(Bs + lds_at(wc * 64 + j * 16 + (lane & 15), kk / 8 + (lane >> 4)));
+      bf[j] = *reinterpret_cast<const half8_t*>(Bs + lo.b_rd[kk / 32] + j * 16 * kLdsRow);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -235,6 +245,15 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_lds_kernel(LdsGemmArgs a) {
   off.w = (uint32_t)word_index(a.runs.packed_rows, 0, nc) * 4;
   off.s = kTL ? (uint32_t)(nc / 8) * 4 : (uint32_t)nc * 2;
   off.z = (uint32_t)nc;
+  LdsOffsets lo;
+  lo.a_st = lds_at(tid / (BK / 8), tid % (BK / 8));
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) lo.b_st[q4] = lds_at(tid % BN, bsub * (kBlockRows / 8) + q4);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    lo.a_rd[h] = lds_at(wr * 64 + (lane & 15), h * 4 + (lane >> 4));
+    lo.b_rd[h] = lds_at(wc * 64 + (lane & 15), h * 4 + (lane >> 4));
+  }
 
   float4_t acc[4][4];
 #pragma unroll
@@ -245,8 +264,8 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_lds_kernel(LdsGemmArgs a) {
   RunCursor cur{0, 0, a.runs.run_row[0], a.runs.run_bits[0], a.runs.run_block[1]};
   const int nfull = nblk & ~1;   // steps whose two blocks are both inside K
   for (int kb = 0; kb < nfull; kb += BK / kBlockRows)
-    k_step<kTL, kZeros, false>(a, rs, cur, off, tid, lane, wr, wc, bsub, kb, nblk, ncol, As, Bs, acc);
-  if (nfull < nblk) k_step<kTL, kZeros, true>(a, rs, cur, off, tid, lane, wr, wc, bsub, nfull, nblk, ncol, As, Bs, acc);
+    k_step<kTL, kZeros, false>(a, rs, cur, off, lo, tid, bsub, kb, nblk, ncol, As, Bs, acc);
+  if (nfull < nblk) k_step<kTL, kZeros, true>(a, rs, cur, off, lo, tid, bsub, nfull, nblk, ncol, As, Bs, acc);
 
   // Epilogue: lane holds C[4*(lane/16) + r][lane % 16] of each 16 x 16 tile.
 #pragma unroll

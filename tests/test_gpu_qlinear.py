@@ -112,6 +112,44 @@ def test_qgemm_small_mixed(M, zeros):
     assert_close(y, _ref(inp), f"qgemm M={M}")
 
 
+# Layouts for the kernel that dequantizes each 32-row block into LDS: runs of
+# one block each (every K-step of two blocks crosses a run boundary, and the
+# run cursor passes several runs at once), an odd block count (the K tail
+# step with its zeroed half) and an even one, and more than 8 runs.
+LDS_KERNEL_BITS = {
+    "1-block-runs-odd": [2, 3, 4, 5, 6, 8, 6, 5, 4, 3, 2, 8, 3],     # 13 blocks, 13 runs
+    "1-block-runs-even": [8, 2, 6, 3, 5, 4, 8, 2, 6, 3, 5, 4, 8, 2],  # 14 blocks, 14 runs
+    "long-odd": [6] * 7 + [4] * 30 + [3] * 18 + [5] * 3 + [2] * 9,  # 67 blocks, 5 runs
+}
+
+
+# (zero points, two-level scales): two-level scales are defined for symmetric layers only
+@pytest.mark.parametrize("zeros,two_level", ((True, False), (False, False), (False, True)))
+@pytest.mark.parametrize("name", sorted(LDS_KERNEL_BITS))
+def test_qgemm_lds_kernel_edges(name, zeros, two_level):
+    """The several-width prefill kernel at its edges: M = 130 and N = 136
+    (ragged over its 128 x 128 tiles: rows and columns past the matrix read
+    the last valid one and are not stored), odd and even block counts, runs of
+    one block, with float16 or two-level scales and with or without zero
+    points, against the oracle."""
+    say(f"qgemm LDS kernel {name} zeros={zeros} two_level={two_level}")
+    M, N = 130, 136
+    inp = _mixed_inputs(LDS_KERNEL_BITS[name], 32, N, M, seed=len(name) * 13 + zeros, zeros=zeros)
+    lay = GpuLayer(inp)
+    if not two_level:
+        assert_close(lay.qgemm(inp.x), _ref(inp), f"qgemm {name}")
+        return
+    rng = np.random.default_rng(77)
+    G = len(inp.bits)
+    codes = rng.integers(0, 16, size=(G, N), dtype=np.uint8)
+    smax = rng.uniform(0.005, 0.02, size=N).astype(np.float16)
+    dev = device()
+    y = dq.qgemm_qscale(lay.layout, lay.x(inp.x), lay.qweight, dq.pack_qscale(torch.from_numpy(codes).to(dev)),
+                        torch.from_numpy(smax).to(dev), lay.perm)
+    ref = oracle.qlinear_qscale(inp.x, inp.q, oracle.qscale_pack(codes), smax, inp.bits, 32, inp.perm)
+    assert_close(y, ref, f"qgemm_qscale {name}")
+
+
 RUN_SPLIT_BITS = {
     "2runs-3b2b": [3] * 128 + [2] * 128,               # K = 8192, one run boundary (70B 2.5 bpw shape)
     "3runs-odd": [6] * 13 + [4] * 200 + [3] * 43,      # K = 8192, runs start at blocks 0, 13 and 213

@@ -398,6 +398,31 @@ def test_qgemm_prefill_workload():
     assert_close(y[torch.from_numpy(rows).to(y.device)], ref, spec.name)
 
 
+@pytest.mark.parametrize("two_level", (False, True))
+def test_qgemm_exl2_prefill_full_size(two_level):
+    """EXL2 4.0 bpw 4096 -> 11008 (widths 6, 5, 4, 3: the kernel that
+    dequantizes into LDS) at M = 2048, as the bench times it, with float16 or
+    two-level scales: the oracle checks every 16th row and the last, in full
+    float64."""
+    spec = wl.EXL2_MIXED
+    M = 2048
+    say(f"qgemm EXL2 prefill {spec.name} M={M} two_level={two_level}")
+    inp = wl.generate(spec, M=M)
+    lay = GpuLayer(inp)
+    rows = np.unique(np.concatenate([np.arange(0, M, 16), [M - 1]]))
+    if two_level:
+        dev = device()
+        codes, smax = wl.two_level_scales(spec)
+        y = dq.qgemm_qscale(lay.layout, lay.x(inp.x), lay.qweight, dq.pack_qscale(torch.from_numpy(codes).to(dev)),
+                            torch.from_numpy(smax).to(dev), lay.perm)
+        ref = oracle.qlinear_qscale(inp.x[rows], inp.q, oracle.qscale_pack(codes), smax, inp.bits, spec.group_size,
+                                    inp.perm)
+    else:
+        y = lay.qgemm(inp.x)
+        ref = _ref(inp, inp.x[rows])
+    assert_close(y[torch.from_numpy(rows).to(y.device)], ref, f"{spec.name} two_level={two_level}")
+
+
 def test_qgemm_row_chunks():
     """Activations of more than 2^31 bytes (M * K * 2): the prefill kernel's
     offsets are 32-bit, so the rows run in chunks (here 32512 + 556 rows).

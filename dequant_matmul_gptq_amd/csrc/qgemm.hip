@@ -361,21 +361,25 @@ void launch_set(const GemmArgs& a, dim3 grid, hipStream_t stream) {
 
 // Layouts with several code widths are computed one launch per run
 // (register dequantization of that run's width), the runs adding up in
-// float32 partial sums in the workspace, when K holds at least 4096 rows per
-// run boundary: each boundary writes and reads the [M][N] partial sums, about
-// 700 / K of the GEMM's own time. Otherwise the kernel that dequantizes into
-// LDS block by block. (Measured on MI355X: 70B 2.5 bpw 8192 -> 28672, two
-// runs, M = 1024: 647 vs 981 us; EXL2 4.0 bpw 4096 -> 11008, four runs,
-// M = 2048: 415 us either way.)
-bool qgemm_split_runs(const qlinear_layout& L) {
+// float32 partial sums in the workspace, when K holds at least 16384 rows per
+// run boundary (each boundary writes and reads the [M][N] partial sums, about
+// 700 / K of the GEMM's own time) and the launch fills at least one round of
+// 256 x 256 tiles on the 256 CUs. Otherwise the kernel that dequantizes into
+// LDS block by block, whose 128 x 128 tiles fill the chip at smaller grids.
+// Measured on MI355X (us, run by run vs LDS kernel, M = 512 / 1024 / 2048):
+//   70B 2.5 bpw 28672 -> 8192, two runs:  888 / 970 / 1277 vs 632 / 786 / 1327
+//   70B 2.5 bpw 8192 -> 28672, two runs:  358 / 693 / 1333 vs 349 / 641 / 1192
+//   EXL2 4.0 bpw 4096 -> 11008, four runs: the LDS kernel at every M.
+bool qgemm_split_runs(const qlinear_layout& L, int M) {
   unsigned set = 0;
   for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
-  return (set & (set - 1)) != 0 && (int64_t)(L.nruns - 1) * 4096 <= L.K;
+  const int64_t tiles = (int64_t)((L.N + BN - 1) / BN) * ((M + BM - 1) / BM);
+  return (set & (set - 1)) != 0 && (int64_t)(L.nruns - 1) * 16384 <= L.K && tiles >= 256;
 }
 
 size_t qgemm_workspace_bytes(const qlinear_layout& L, int M) {
   const size_t xq = ((size_t)M * L.K * 2 + 255) / 256 * 256;
-  return xq + (qgemm_split_runs(L) ? (size_t)M * L.N * 4 : 0);
+  return xq + (qgemm_split_runs(L, M) ? (size_t)M * L.N * 4 : 0);
 }
 
 bool qgemm_supported(const qlinear_layout& L) {
@@ -401,7 +405,7 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
     // that kernel reads): the kernel that dequantizes into LDS. MFMA pair
     // order for the register-dequant kernel; natural order for the other.
     const bool mixed = (set & (set - 1)) != 0;
-    const bool lds = (mixed && !qgemm_split_runs(L)) || epi.scale_max != nullptr;
+    const bool lds = (mixed && !qgemm_split_runs(L, M)) || epi.scale_max != nullptr;
     hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, !lds, stream);
     if (e != hipSuccess) return e;
     uint16_t* yc = y + (size_t)m0 * L.N;

@@ -82,7 +82,8 @@ hipError_t launch_qgemv_mx(const qlinear_layout& L, const Runs& runs, const uint
 // Bytes of qgemm's workspace: the gathered activations [M][K] float16, then
 // for layouts computed run by run the float32 partial sums [M][N].
 size_t qgemm_workspace_bytes(const qlinear_layout& L, int M);
-bool qgemm_split_runs(const qlinear_layout& L);
+// Whether a call of M rows on a layout of several widths runs one launch per run.
+bool qgemm_split_runs(const qlinear_layout& L, int M);
 // Whether the packed words and scales fit the prefill kernel's 32-bit offsets.
 bool qgemm_supported(const qlinear_layout& L);
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,

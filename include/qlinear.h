@@ -239,8 +239,9 @@ int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32
  * the act-order gather of the README's "EXL2 quantization" and the partial
  * sums of layouts with several widths):
  * the gathered activations, float16 [M][K], and for a layout with several
- * code widths that has at least 4096 rows of K per run boundary also float32
- * partial sums [M][N] (such a layout is computed one launch per run). */
+ * code widths that has at least 16384 rows of K per run boundary, when
+ * ceil(N / 256) * ceil(M / 256) >= 256, also float32 partial sums [M][N]
+ * (such a call is computed one launch per run). */
 int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes);
 
 /*

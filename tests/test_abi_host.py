@@ -258,13 +258,17 @@ def test_workspace_sizes():
     # gathered activations float16 [16][K] + block sums float2 [16][K/32], 256-byte rounded
     assert dq.qgemv_workspace_bytes(L) == 16 * 4096 * 2 + 16 * 128 * 8
     assert dq.qgemm_workspace_bytes(L, 2048) == 2048 * 4096 * 2
-    # Several code widths with >= 4096 rows of K per run boundary: one launch
-    # per run, whose float32 partial sums [M][N] follow the 256-byte rounded
-    # activations.
-    few = _layout(K=8192, N=512, gs=32, bits=np.array([6] * 16 + [4] * 176 + [3] * 64, np.uint8))
+    # Several code widths with >= 16384 rows of K per run boundary and at
+    # least 256 tiles of 256 x 256: one launch per run, whose float32 partial
+    # sums [M][N] follow the 256-byte rounded activations.
+    few = _layout(K=32768, N=4096, gs=32, bits=np.array([6] * 64 + [4] * 448 + [3] * 512, np.uint8))
     assert few.nruns == 3
-    assert dq.qgemm_workspace_bytes(few, 100) == (100 * 8192 * 2 + 255) // 256 * 256 + 100 * 512 * 4
-    # More run boundaries for K: the kernel that dequantizes into LDS, no partial sums.
+    assert dq.qgemm_workspace_bytes(few, 4096) == (4096 * 32768 * 2 + 255) // 256 * 256 + 4096 * 4096 * 4
+    # Fewer tiles (16 x 8 at M = 2048), or fewer rows per boundary: the kernel
+    # that dequantizes into LDS, no partial sums.
+    assert dq.qgemm_workspace_bytes(few, 2048) == 2048 * 32768 * 2
+    short = _layout(K=8192, N=4096, gs=32, bits=np.array([6] * 16 + [4] * 176 + [3] * 64, np.uint8))
+    assert dq.qgemm_workspace_bytes(short, 4096) == 4096 * 8192 * 2
     many = _layout(K=4096, N=512, gs=32, bits=np.array([4, 3] * 10 + [4] * 108, np.uint8))
     assert many.nruns == 21
     assert dq.qgemm_workspace_bytes(many, 100) == (100 * 4096 * 2 + 255) // 256 * 256

@@ -41,7 +41,7 @@ CASES = [
     ("qgemv", [3] * 40, 776, 16),
     ("qgemm", [4] * 11, 520, 300),        # prefill, one width
     ("qgemm", MIXED, 392, 130),           # prefill, several widths (LDS dequant)
-    ("qgemm", [3] * 128 + [2] * 128, 264, 70),   # prefill run by run (float32 partial sums in the workspace)
+    ("qgemm", [3] * 128 + [2] * 128, 264, 70),   # prefill, two long runs on a small grid (LDS dequant)
 ]
 
 
@@ -64,6 +64,29 @@ def test_writes_stay_inside_y_and_workspace(op, bits, N, M):
     assert wb.intact(), "a write landed outside the workspace"
     ref = oracle.qlinear(inp.x, inp.q, inp.scales, inp.zeros, inp.bits, 32, inp.perm)
     assert_close(y, ref, f"{op} M={M}")
+
+
+def test_run_by_run_writes_stay_inside_y_and_workspace():
+    """Prefill run by run (two runs of 8192 rows, 16 x 16 tiles of 256 x 256,
+    M ragged): the float32 partial sums sit in the workspace after the
+    gathered activations. y starts as NaN bytes, so every element must come
+    out finite; the oracle checks every 64th row and the last."""
+    bits, N, M = [3] * 256 + [2] * 256, 4096, 4000
+    say(f"guard bands qgemm run by run blocks={len(bits)} N={N} M={M}")
+    inp = _inputs(bits, 32, N, M, seed=91, zeros=False)
+    lay = GpuLayer(inp)
+    nws = dq.qgemm_workspace_bytes(lay.layout, M)
+    assert nws == (M * inp.spec.K * 2 + 255) // 256 * 256 + M * N * 4, "expected the run-by-run path"
+    yb = Guarded(M * N * 2, lay.dev, fill=0xFF)
+    y = yb.view(torch.float16, (M, N))
+    wb = Guarded(nws, lay.dev, fill=0xFF)
+    dq.qgemm(lay.layout, lay.x(inp.x), lay.qweight, lay.scales, lay.zeros, lay.perm, wb.bytes(), y=y)
+    assert yb.intact(), "a write landed outside y"
+    assert wb.intact(), "a write landed outside the workspace"
+    assert bool(torch.isfinite(y).all().item()), "an element of y was not written"
+    rows = np.unique(np.concatenate([np.arange(0, M, 64), [M - 1]]))
+    ref = oracle.qlinear(inp.x[rows], inp.q, inp.scales, inp.zeros, inp.bits, 32, inp.perm)
+    assert_close(y[torch.from_numpy(rows).to(y.device)], ref, f"qgemm run by run M={M}")
 
 
 def test_grouped_full_size_gate_up():

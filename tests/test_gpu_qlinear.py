@@ -151,22 +151,27 @@ def test_qgemm_lds_kernel_edges(name, zeros, two_level):
 
 
 RUN_SPLIT_BITS = {
-    "2runs-3b2b": [3] * 128 + [2] * 128,               # K = 8192, one run boundary (70B 2.5 bpw shape)
-    "3runs-odd": [6] * 13 + [4] * 200 + [3] * 43,      # K = 8192, runs start at blocks 0, 13 and 213
+    "2runs-3b2b": [3] * 512 + [2] * 512,               # K = 32768, one run boundary (70B 2.5 bpw widths)
+    "3runs-odd": [6] * 13 + [4] * 700 + [3] * 311,     # K = 32768, runs start at blocks 0, 13 and 713
 }
 
 
-@pytest.mark.parametrize("zeros", (True, False))
-@pytest.mark.parametrize("M", (100, 300))
-@pytest.mark.parametrize("name", sorted(RUN_SPLIT_BITS))
+@pytest.mark.parametrize("name,M,zeros", (("2runs-3b2b", 4096, True), ("2runs-3b2b", 4000, False),
+                                          ("3runs-odd", 4000, True), ("3runs-odd", 4096, False)))
 def test_qgemm_run_by_run(name, M, zeros):
-    """Several code widths with K >= 4096 rows per run boundary: one
-    register-dequant launch per run, adding up in float32 partial sums in the
-    workspace (first / middle / last launch), ragged M over 256-row tiles."""
+    """Several code widths with K >= 16384 rows per run boundary and a grid
+    of 16 x 16 tiles of 256 x 256 (N = 4096): one register-dequant launch
+    per run, adding up in float32 partial sums in the workspace (first /
+    middle / last launch), M even or ragged over the tiles. The oracle checks
+    every 64th row and the last, in full float64."""
     say(f"qgemm run by run {name} M={M} zeros={zeros}")
-    inp = _mixed_inputs(RUN_SPLIT_BITS[name], 32, 520, M, seed=len(name) * 7 + M, zeros=zeros)
-    y = GpuLayer(inp).qgemm(inp.x)
-    assert_close(y, _ref(inp), f"qgemm {name} M={M}")
+    N = 4096
+    inp = _mixed_inputs(RUN_SPLIT_BITS[name], 32, N, M, seed=len(name) * 7 + M, zeros=zeros)
+    lay = GpuLayer(inp)
+    assert dq.qgemm_workspace_bytes(lay.layout, M) > M * inp.spec.K * 2, "expected the run-by-run path"
+    y = lay.qgemm(inp.x)
+    rows = np.unique(np.concatenate([np.arange(0, M, 64), [M - 1]]))
+    assert_close(y[torch.from_numpy(rows).to(y.device)], _ref(inp, inp.x[rows]), f"qgemm {name} M={M}")
 
 
 @pytest.mark.parametrize("gs", (32, 128))

@@ -377,9 +377,45 @@ bool qgemm_split_runs(const qlinear_layout& L, int M) {
   return (set & (set - 1)) != 0 && (int64_t)(L.nruns - 1) * 16384 <= L.K && tiles >= 256;
 }
 
+// Slices of K for a call on the LDS-dequant kernel: a grid of few 128 x 128
+// tiles leaves most of the about 1024 workgroup slots (four per CU) empty
+// while each tile walks all of K, so K is cut into up to 16 slices of at
+// least 16 blocks, whose float32 partial sums a second kernel adds. Not for
+// calls run in row chunks (activations of 2^31 bytes or more).
+int qgemm_k_slices(const qlinear_layout& L, int M) {
+  if (M <= 0 || (int64_t)M * L.K * 2 >= ((int64_t)1 << 31)) return 1;
+  const int64_t tiles = (int64_t)((L.N + 127) / 128) * ((M + 127) / 128);
+  int64_t s = std::min<int64_t>(16, 1024 / tiles);
+  s = std::min<int64_t>(s, (L.K / kBlockRows) / 16);
+  return (int)std::max<int64_t>(s, 1);
+}
+
+// Whether a call without two-level scales takes the LDS-dequant kernel:
+// several widths not computed run by run, or one width on a grid of at most
+// half a round of 256 x 256 tiles, where the 128 x 128 tiles fill the chip
+// better. Measured on MI355X (GPTQ 4-bit g128, us, register-dequant vs LDS
+// kernel, both without split K): 4096 -> 4096 at M = 128 / 1024 / 2048 (16 /
+// 64 / 128 tiles): 112.9 / 120.7 / 131.4 vs 95.2 / 105.2 / 126.5; 4096 ->
+// 11008 at M = 1024 (172 tiles): 137.0 vs 148.0; 5120 -> 13824 at M = 1024 /
+// 2048 (216 / 432 tiles): 182.1 / 355.4 vs 223.5 / 400.1.
+bool qgemm_lds_path(const qlinear_layout& L, int M) {
+  unsigned set = 0;
+  for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
+  if ((set & (set - 1)) != 0) return !qgemm_split_runs(L, M);
+  const int64_t tiles = (int64_t)((L.N + BN - 1) / BN) * ((M + BM - 1) / BM);
+  return tiles <= 128;
+}
+
 size_t qgemm_workspace_bytes(const qlinear_layout& L, int M) {
   const size_t xq = ((size_t)M * L.K * 2 + 255) / 256 * 256;
-  return xq + (qgemm_split_runs(L, M) ? (size_t)M * L.N * 4 : 0);
+  // Float32 partial sums after the activations: [M][N] for a layout computed
+  // run by run, [slices][M][N] for split K (two-level-scale calls take the
+  // LDS kernel whatever the layout, so the slices count whenever there are
+  // several).
+  const size_t runs = qgemm_split_runs(L, M) ? (size_t)M * L.N * 4 : 0;
+  const int slices = qgemm_k_slices(L, M);
+  const size_t split = slices > 1 ? (size_t)slices * M * L.N * 4 : 0;
+  return xq + std::max(runs, split);
 }
 
 bool qgemm_supported(const qlinear_layout& L) {
@@ -392,8 +428,6 @@ bool qgemm_supported(const qlinear_layout& L) {
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, void* ws, const Epilogue& epi, hipStream_t stream) {
-  unsigned set = 0;
-  for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
   // Row chunks whose gathered activations stay below 2^31 bytes (32-bit
   // buffer offsets); a chunk is a whole number of 256-row tiles.
   const int64_t rows_fit = (((int64_t)1 << 31) - 1) / ((int64_t)L.K * 2);
@@ -401,11 +435,11 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
   for (int m0 = 0; m0 < M; m0 += chunk) {
     const int mc = std::min(chunk, M - m0);
     uint32_t* xq = reinterpret_cast<uint32_t*>(ws);
-    // Many runs of several code widths, or two-level scales (whose codes only
-    // that kernel reads): the kernel that dequantizes into LDS. MFMA pair
-    // order for the register-dequant kernel; natural order for the other.
-    const bool mixed = (set & (set - 1)) != 0;
-    const bool lds = (mixed && !qgemm_split_runs(L, M)) || epi.scale_max != nullptr;
+    // Several code widths not run by run, one width on a small grid, or
+    // two-level scales (whose codes only that kernel reads): the kernel that
+    // dequantizes into LDS, with split K on small grids. MFMA pair order for
+    // the register-dequant kernel; natural order for the other.
+    const bool lds = qgemm_lds_path(L, M) || epi.scale_max != nullptr;
     hipError_t e = launch_gather_rows(runs, x + (size_t)m0 * L.K, perm, mc, L.K, xq, !lds, stream);
     if (e != hipSuccess) return e;
     uint16_t* yc = y + (size_t)m0 * L.N;
@@ -413,8 +447,9 @@ hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_
     if (ec.residual) ec.residual += (size_t)m0 * L.N;
     if (ec.addend) ec.addend += (size_t)m0 * L.N;
     if (lds) {
+      float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (((size_t)M * L.K * 2 + 255) / 256 * 256));
       e = launch_qgemm_lds(L, runs, reinterpret_cast<const uint16_t*>(xq), mc, qweight, scales, zeros, yc, ec,
-                           stream);
+                           qgemm_k_slices(L, M), part, stream);
       if (e != hipSuccess) return e;
       continue;
     }

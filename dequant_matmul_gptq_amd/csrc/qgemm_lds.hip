@@ -14,6 +14,8 @@
 // zero-point modes are template parameters for the same reason. A block's
 // width and first packed row come from a scalar run cursor that moves along K
 // with the blocks.
+#include <algorithm>
+
 #include "mfma_frag.hpp"
 
 namespace qlinear {
@@ -56,6 +58,11 @@ struct LdsGemmArgs {
   uint16_t* y;
   int M, K, N;
   int xq_bytes, qweight_bytes, scale_bytes, zero_bytes;
+  // Split K: slice blockIdx.z covers blocks [z * slice_blocks, + slice_blocks)
+  // and writes float32 partial sums part[z][M][N] (the epilogue comes in
+  // split_sum_kernel); part == nullptr: one slice, float16 output.
+  float* part;
+  int slice_blocks;
   Runs runs;
   Epilogue epi;
 };
@@ -261,13 +268,18 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_lds_kernel(LdsGemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = {0.f, 0.f, 0.f, 0.f};
 
+  // The blocks of this workgroup's K slice (all of K without split); slices
+  // start at even blocks, so only the last can end in the odd-block tail.
+  const int kb_begin = a.part ? (int)blockIdx.z * a.slice_blocks : 0;
+  const int kb_end = a.part ? min(nblk, kb_begin + a.slice_blocks) : nblk;
   RunCursor cur{0, 0, a.runs.run_row[0], a.runs.run_bits[0], a.runs.run_block[1]};
-  const int nfull = nblk & ~1;   // steps whose two blocks are both inside K
-  for (int kb = 0; kb < nfull; kb += BK / kBlockRows)
+  const int nfull = kb_begin + ((kb_end - kb_begin) & ~1);   // steps whose two blocks are both inside K
+  for (int kb = kb_begin; kb < nfull; kb += BK / kBlockRows)
     k_step<kTL, kZeros, false>(a, rs, cur, off, lo, tid, bsub, kb, nblk, ncol, As, Bs, acc);
-  if (nfull < nblk) k_step<kTL, kZeros, true>(a, rs, cur, off, lo, tid, bsub, nfull, nblk, ncol, As, Bs, acc);
+  if (nfull < kb_end) k_step<kTL, kZeros, true>(a, rs, cur, off, lo, tid, bsub, nfull, nblk, ncol, As, Bs, acc);
 
   // Epilogue: lane holds C[4*(lane/16) + r][lane % 16] of each 16 x 16 tile.
+  float* const part = a.part ? a.part + (size_t)blockIdx.z * a.M * a.N : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -277,18 +289,44 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_lds_kernel(LdsGemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wr * 64 + i * 16 + 4 * (lane >> 4) + r;
-        if (m < a.M)
+        if (m >= a.M) continue;
+        if (part)
+          part[(size_t)m * a.N + n] = acc[i][j][r];
+        else
           a.y[(size_t)m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(a.epi, acc[i][j][r], m, n, a.N));
       }
     }
   }
 }
 
+// The slices' partial sums added in slice order (the same order on every
+// call), then the epilogue and the float16 rounding: 4 consecutive outputs
+// per thread (N is a multiple of 8, so they share a row).
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int slices, int M, int N,
+                                                        uint16_t* __restrict__ y, Epilogue epi) {
+  const size_t total = (size_t)M * N;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= total) return;
+  float4_t v = *reinterpret_cast<const float4_t*>(part + i);
+  for (int s = 1; s < slices; ++s) {
+    const float4_t w = *reinterpret_cast<const float4_t*>(part + (size_t)s * total + i);
+    v = v + w;
+  }
+  const int m = (int)(i / N), n = (int)(i % N);
+  uint16_t h[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) h[c] = __builtin_bit_cast(uint16_t, (_Float16)apply_epilogue(epi, v[c], m, n + c, N));
+  uint2 o;
+  o.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+  o.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+  *reinterpret_cast<uint2*>(y + i) = o;
+}
+
 }  // namespace
 
 hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uint16_t* xq, int M,
                             const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y,
-                            const Epilogue& epi, hipStream_t stream) {
+                            const Epilogue& epi, int slices, float* part, hipStream_t stream) {
   LdsGemmArgs a;
   a.xq = xq;
   a.qweight = qweight;
@@ -307,7 +345,14 @@ hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uin
   a.zero_bytes = (int)((size_t)L.groups * L.N);
   a.runs = runs;
   a.epi = epi;
-  const dim3 grid((L.N + BN - 1) / BN, (M + BM - 1) / BM, 1);
+  // Slices of an even number of blocks, as equal as that allows.
+  const int nblk = L.K / kBlockRows;
+  const int steps = (nblk + 1) / 2;
+  slices = slices > 1 && part ? std::min(slices, steps) : 1;
+  a.slice_blocks = 2 * ((steps + slices - 1) / slices);
+  slices = (nblk + a.slice_blocks - 1) / a.slice_blocks;
+  a.part = slices > 1 ? part : nullptr;
+  const dim3 grid((L.N + BN - 1) / BN, (M + BM - 1) / BM, slices);
   if (tl) {
     if (zeros)
       hipLaunchKernelGGL((gemm_lds_kernel<true, true>), grid, dim3(kThreads), 0, stream, a);
@@ -318,6 +363,13 @@ hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uin
       hipLaunchKernelGGL((gemm_lds_kernel<false, true>), grid, dim3(kThreads), 0, stream, a);
     else
       hipLaunchKernelGGL((gemm_lds_kernel<false, false>), grid, dim3(kThreads), 0, stream, a);
+  }
+  if (a.part) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t quads = ((size_t)M * L.N) / 4;
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream, a.part, slices, M,
+                       L.N, y, epi);
   }
   return hipGetLastError();
 }

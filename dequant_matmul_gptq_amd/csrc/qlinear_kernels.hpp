@@ -61,9 +61,11 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
 // Prefill layer. ws holds the gathered activations, float16 [M][K].
 // launch_qgemm_lds: the multiplication for layouts with several code widths,
 // from activations already gathered (xq, float16 [M][K]).
+// slices > 1 with part: K cut into that many slices whose float32 partial
+// sums part[slices][M][N] are then added (split_sum_kernel).
 hipError_t launch_qgemm_lds(const qlinear_layout& L, const Runs& runs, const uint16_t* xq, int M,
                             const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, uint16_t* y,
-                            const Epilogue& epi, hipStream_t stream);
+                            const Epilogue& epi, int slices, float* part, hipStream_t stream);
 // Decode layer on the matrix cores in factored form, 1 <= M <= 16, any set
 // of code widths (qgemv_mx.hip). One launch with the act-order gather inside
 // the kernel when qgemv_mx_one_launch() holds; otherwise a gather kernel
@@ -84,6 +86,10 @@ hipError_t launch_qgemv_mx(const qlinear_layout& L, const Runs& runs, const uint
 size_t qgemm_workspace_bytes(const qlinear_layout& L, int M);
 // Whether a call of M rows on a layout of several widths runs one launch per run.
 bool qgemm_split_runs(const qlinear_layout& L, int M);
+// Whether a call of M rows without two-level scales takes the LDS-dequant
+// kernel, and into how many K slices that kernel cuts it.
+bool qgemm_lds_path(const qlinear_layout& L, int M);
+int qgemm_k_slices(const qlinear_layout& L, int M);
 // Whether the packed words and scales fit the prefill kernel's 32-bit offsets.
 bool qgemm_supported(const qlinear_layout& L);
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,

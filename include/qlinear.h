@@ -238,10 +238,12 @@ int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32
 /* Workspace of qlinear_qgemm for M tokens, in bytes (no initialization needed;
  * the act-order gather of the README's "EXL2 quantization" and the partial
  * sums of layouts with several widths):
- * the gathered activations, float16 [M][K], and for a layout with several
- * code widths that has at least 16384 rows of K per run boundary, when
- * ceil(N / 256) * ceil(M / 256) >= 256, also float32 partial sums [M][N]
- * (such a call is computed one launch per run). */
+ * the gathered activations, float16 [M][K], then float32 partial sums:
+ * [M][N] for a layout with several code widths that has at least 16384 rows
+ * of K per run boundary when ceil(N / 256) * ceil(M / 256) >= 256 (such a
+ * call is computed one launch per run); [S][M][N] when the call cuts K into
+ * S = min(16, 1024 / (ceil(N / 128) * ceil(M / 128)), K / 512) > 1 slices
+ * (grids of few tiles, activations below 2^31 bytes); the larger of the two. */
 int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes);
 
 /*

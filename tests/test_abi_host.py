@@ -257,21 +257,30 @@ def test_workspace_sizes():
     L = _layout(N=4096, K=4096, gs=128)
     # gathered activations float16 [16][K] + block sums float2 [16][K/32], 256-byte rounded
     assert dq.qgemv_workspace_bytes(L) == 16 * 4096 * 2 + 16 * 128 * 8
-    assert dq.qgemm_workspace_bytes(L, 2048) == 2048 * 4096 * 2
+    # One width on a grid of more than 128 tiles of 256 x 256: the gathered
+    # activations only.
+    assert dq.qgemm_workspace_bytes(L, 4096) == 4096 * 4096 * 2
+    # A smaller grid: the LDS-dequant kernel with K in slices, whose float32
+    # partial sums [slices][M][N] follow the 256-byte rounded activations:
+    # slices = min(16, 1024 // (128 x 128 tiles), K / 32 / 16).
+    assert dq.qgemm_workspace_bytes(L, 2048) == 2048 * 4096 * 2 + 2 * 2048 * 4096 * 4   # 512 tiles: 2 slices
+    small = _layout(N=512, K=4096, gs=128)
+    assert dq.qgemm_workspace_bytes(small, 100) == (100 * 4096 * 2 + 255) // 256 * 256 + 8 * 100 * 512 * 4
     # Several code widths with >= 16384 rows of K per run boundary and at
-    # least 256 tiles of 256 x 256: one launch per run, whose float32 partial
-    # sums [M][N] follow the 256-byte rounded activations.
+    # least 256 tiles of 256 x 256: one launch per run, float32 partial sums
+    # [M][N].
     few = _layout(K=32768, N=4096, gs=32, bits=np.array([6] * 64 + [4] * 448 + [3] * 512, np.uint8))
     assert few.nruns == 3
     assert dq.qgemm_workspace_bytes(few, 4096) == (4096 * 32768 * 2 + 255) // 256 * 256 + 4096 * 4096 * 4
-    # Fewer tiles (16 x 8 at M = 2048), or fewer rows per boundary: the kernel
-    # that dequantizes into LDS, no partial sums.
-    assert dq.qgemm_workspace_bytes(few, 2048) == 2048 * 32768 * 2
+    # Fewer tiles: the LDS kernel, here in 2 slices.
+    assert dq.qgemm_workspace_bytes(few, 2048) == 2048 * 32768 * 2 + 2 * 2048 * 4096 * 4
+    # Fewer rows per boundary on a full grid (1024 tiles of 128 x 128): the LDS kernel in one slice.
     short = _layout(K=8192, N=4096, gs=32, bits=np.array([6] * 16 + [4] * 176 + [3] * 64, np.uint8))
     assert dq.qgemm_workspace_bytes(short, 4096) == 4096 * 8192 * 2
+    # A small grid of several widths: 8 slices (K / 32 / 16).
     many = _layout(K=4096, N=512, gs=32, bits=np.array([4, 3] * 10 + [4] * 108, np.uint8))
     assert many.nruns == 21
-    assert dq.qgemm_workspace_bytes(many, 100) == (100 * 4096 * 2 + 255) // 256 * 256
+    assert dq.qgemm_workspace_bytes(many, 100) == (100 * 4096 * 2 + 255) // 256 * 256 + 8 * 100 * 512 * 4
 
 
 def test_two_level_scale_validation_before_launch():

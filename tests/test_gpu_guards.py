@@ -41,7 +41,8 @@ CASES = [
     ("qgemv", [3] * 40, 776, 16),
     ("qgemm", [4] * 11, 520, 300),        # prefill, one width
     ("qgemm", MIXED, 392, 130),           # prefill, several widths (LDS dequant)
-    ("qgemm", [3] * 128 + [2] * 128, 264, 70),   # prefill, two long runs on a small grid (LDS dequant)
+    ("qgemm", [3] * 128 + [2] * 128, 264, 70),   # prefill, two long runs on a small grid (LDS dequant, K in slices)
+    ("qgemm", [4] * 128, 392, 40),              # prefill, one width on a small grid (K in 8 slices)
 ]
 
 

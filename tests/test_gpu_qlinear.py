@@ -183,6 +183,56 @@ def test_qgemm_uniform_widths(b, gs):
     assert_close(y, _ref(inp), f"qgemm b={b} gs={gs}")
 
 
+@pytest.mark.parametrize("b", (2, 3, 4, 5, 6, 8))
+def test_qgemm_uniform_widths_large_grid(b):
+    """One code width on a grid of 16 x 9 tiles of 256 x 256 (N = 4096,
+    M = 2304): the register-dequant kernel's instance for that width. The
+    oracle checks every 32nd row and the last."""
+    say(f"qgemm uniform large grid b={b}")
+    M = 2304
+    inp = _mixed_inputs([b] * 8, 128, 4096, M, seed=b * 23, zeros=True)
+    y = GpuLayer(inp).qgemm(inp.x)
+    rows = np.unique(np.concatenate([np.arange(0, M, 32), [M - 1]]))
+    assert_close(y[torch.from_numpy(rows).to(y.device)], _ref(inp, inp.x[rows]), f"qgemm b={b} large grid")
+
+
+SPLIT_K_CASES = [
+    # (bits per group, group size, N, M, zero points)
+    ([4] * 32, 128, 392, 17, True),                  # one width, K = 4096: 8 slices
+    ([4] * 32, 128, 392, 130, False),                # two tile rows
+    ([3] * 32, 128, 1040, 64, True),                 # 3-bit, 9 tile columns
+    ([6] * 11 + [5] * 40 + [4] * 50 + [3] * 30, 32, 392, 50, False),   # 131 blocks: odd, the tail in the last slice
+    ([2, 8] * 20 + [5] * 24, 32, 136, 33, True),     # 40 one-block runs and a long one; N ragged over 128
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_K_CASES)))
+@pytest.mark.parametrize("two_level", (False, True))
+def test_qgemm_split_k(case, two_level):
+    """Small grids on the LDS-dequant kernel with K cut into slices: each
+    slice writes float32 partial sums to the workspace and a second kernel
+    adds them in slice order before the epilogue, against the oracle."""
+    bits, gs, N, M, zeros = SPLIT_K_CASES[case]
+    zeros = zeros and not two_level
+    say(f"qgemm split K case {case} two_level={two_level} M={M} N={N}")
+    inp = _mixed_inputs(bits, gs, N, M, seed=case * 19 + 7, zeros=zeros)
+    lay = GpuLayer(inp)
+    K = inp.spec.K
+    assert dq.qgemm_workspace_bytes(lay.layout, M) > (M * K * 2 + 255) // 256 * 256, "expected split K"
+    if not two_level:
+        assert_close(lay.qgemm(inp.x), _ref(inp), f"split K case {case}")
+        return
+    rng = np.random.default_rng(case)
+    G = len(inp.bits)
+    codes = rng.integers(0, 16, size=(G, N), dtype=np.uint8)
+    smax = rng.uniform(0.005, 0.02, size=N).astype(np.float16)
+    dev = device()
+    y = dq.qgemm_qscale(lay.layout, lay.x(inp.x), lay.qweight, dq.pack_qscale(torch.from_numpy(codes).to(dev)),
+                        torch.from_numpy(smax).to(dev), lay.perm)
+    ref = oracle.qlinear_qscale(inp.x, inp.q, oracle.qscale_pack(codes), smax, inp.bits, gs, inp.perm)
+    assert_close(y, ref, f"split K case {case} two-level")
+
+
 MX_FEW_ROW_BITS = {
     "mid": [6, 5, 5, 4, 4, 4, 3, 3],     # widths 3-6: one launch, gather in the kernel
     "low": [3, 3, 3, 2, 2],              # widths 2-3
@@ -543,36 +593,38 @@ def test_nonfinite_activations(op, bits, gs, M, exact):
 # ------------------------------------------------------------------ fused epilogue
 
 EPILOGUE_PATHS = [
-    ("qgemv", [4] * 11, 1),        # single-row kernel
-    ("qgemv", [4] * 11, 2),        # single-row kernel, 2-row instance
-    ("qgemv", [4] * 11, 3),        # single-row kernel, 4-row instance
-    ("qgemv", MIXED_BITS, 1),      # one-launch several-width kernel (with an addend: gather + multi-row VALU kernel)
-    ("qgemv", LONG_MIXED, 1),      # gather + multi-row VALU kernel (K past the one-launch LDS limit)
-    ("qgemv", MIXED_BITS, 2),      # one-launch several-width kernel, 2 rows
-    ("qgemv", [4] * 11, 5),        # MFMA decode kernel
-    ("qgemv", MIXED_BITS, 16),     # MFMA decode kernel, several widths
-    ("qgemm", [4] * 11, 100),      # prefill, register dequant
-    ("qgemm", MIXED_BITS, 100),    # prefill, LDS dequant
-    ("qgemm", [3] * 128 + [2] * 128, 100),   # prefill, one launch per run
+    ("qgemv", [4] * 11, 1, 520),        # single-row kernel
+    ("qgemv", [4] * 11, 2, 520),        # single-row kernel, 2-row instance
+    ("qgemv", [4] * 11, 3, 520),        # single-row kernel, 4-row instance
+    ("qgemv", MIXED_BITS, 1, 520),      # one-launch several-width kernel (with an addend: gather + multi-row VALU kernel)
+    ("qgemv", LONG_MIXED, 1, 520),      # gather + multi-row VALU kernel (K past the one-launch LDS limit)
+    ("qgemv", MIXED_BITS, 2, 520),      # one-launch several-width kernel, 2 rows
+    ("qgemv", [4] * 11, 5, 520),        # MFMA decode kernel
+    ("qgemv", MIXED_BITS, 16, 520),     # MFMA decode kernel, several widths
+    ("qgemm", [4] * 11, 2304, 4096),    # prefill, register dequant (144 tiles of 256 x 256)
+    ("qgemm", [4] * 11, 100, 520),      # prefill, one width on a small grid: LDS dequant
+    ("qgemm", MIXED_BITS, 100, 520),    # prefill, LDS dequant
+    ("qgemm", [3] * 128 + [2] * 128, 100, 520),   # prefill, LDS dequant with K in 16 slices
+    ("qgemm", [3] * 256 + [2] * 256, 4096, 4096),  # prefill, one launch per run
 ]
 
 
-@pytest.mark.parametrize("op,bits,M", EPILOGUE_PATHS,
+@pytest.mark.parametrize("op,bits,M,N", EPILOGUE_PATHS,
                          ids=["row", "row-M2", "row-M3", "rowmix-M1", "gather-valu-M1", "rowmix-M2", "mfma-M5", "mfma-M16", "qgemm",
-                              "qgemm-mixed", "qgemm-runs"])
+                              "qgemm-small-grid", "qgemm-mixed", "qgemm-split-k", "qgemm-runs"])
 @pytest.mark.parametrize("terms", ["bias", "residual", "bias-silu-residual", "silu-inplace-residual",
                                    "lora-bias-silu"])
-def test_fused_epilogue(op, bits, M, terms):
+def test_fused_epilogue(op, bits, M, N, terms):
     """y = RNE(act(x W + addend + bias) + residual) on every kernel path,
     against the float64 oracle's layer output followed by its epilogue. The
     addend is an on-the-fly LoRA update (rank 8) from qlinear_lora_delta;
     calls with one do not run the single-launch decode kernel (the "row"
     cases then run the gather and multi-row or MFMA kernels)."""
-    say(f"fused epilogue {op} M={M} {terms}")
-    inp = _mixed_inputs(bits, 32, 520, M, seed=300 + M, zeros=True)
+    say(f"fused epilogue {op} M={M} N={N} {terms}")
+    inp = _mixed_inputs(bits, 32, N, M, seed=300 + M, zeros=True)
     lay = GpuLayer(inp)
     rng = np.random.default_rng(41)
-    N, K = inp.spec.N, inp.spec.K
+    K = inp.spec.K
     bias = rng.standard_normal(N).astype(np.float16) if "bias" in terms else None
     resid = rng.standard_normal((M, N)).astype(np.float16) if "residual" in terms else None
     act = dq.ACT_SILU if "silu" in terms else dq.ACT_NONE
@@ -593,9 +645,13 @@ def test_fused_epilogue(op, bits, M, terms):
     extra = (lay.ws,) if op == "qgemv" else (None,)
     out = call(lay.layout, x, lay.qweight, lay.scales, lay.zeros, lay.perm, *extra, y=y, bias=b_t, residual=r_t,
                activation=act, addend=add_t)
-    ref = oracle.apply_epilogue(_ref(inp), bias, resid, act, addend=add_ref)
-    assert_close(out, ref, f"{op} M={M} {terms}")
+    # Large outputs: every 32nd row and the last, in full float64.
+    rows = np.arange(M) if M * N <= 1 << 20 else np.unique(np.concatenate([np.arange(0, M, 32), [M - 1]]))
+    sub = (lambda a: None if a is None else a[rows])
+    base = _ref(inp, inp.x[rows])
+    ref = oracle.apply_epilogue(base, bias, sub(resid), act, addend=sub(add_ref))
+    assert_close(out[torch.from_numpy(rows).to(out.device)], ref, f"{op} M={M} {terms}")
     if add_ref is not None:
         # the update is large enough that dropping it would fail the check above
-        plain = oracle.apply_epilogue(_ref(inp), bias, resid, act)
+        plain = oracle.apply_epilogue(base, bias, sub(resid), act)
         assert np.linalg.norm(ref - plain) > 0.05 * np.linalg.norm(ref)

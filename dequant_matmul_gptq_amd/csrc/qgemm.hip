@@ -415,7 +415,18 @@ size_t qgemm_workspace_bytes(const qlinear_layout& L, int M) {
   const size_t runs = qgemm_split_runs(L, M) ? (size_t)M * L.N * 4 : 0;
   const int slices = qgemm_k_slices(L, M);
   const size_t split = slices > 1 ? (size_t)slices * M * L.N * 4 : 0;
-  return xq + std::max(runs, split);
+  const size_t bytes = xq + std::max(runs, split);
+  // Calls run as decode launches use the decode workspace.
+  return qgemm_as_decode(L, M) ? std::max(bytes, qgemv_workspace_bytes(L.K)) : bytes;
+}
+
+// 17..32 rows: two decode launches of at most 16 rows each (the matrix-core
+// decode kernel) take less time than the prefill kernels there, whose tiles
+// are 128 rows. Measured on MI355X (GPTQ 4-bit g128 act-order, us): one
+// 16-row decode launch 10.2 / 15.1 / 16.5 on 4096 -> 4096 / 4096 -> 11008 /
+// 11008 -> 4096, against 39 / 45 / 52 for the prefill path at M = 128.
+bool qgemm_as_decode(const qlinear_layout& L, int M) {
+  return M > QLINEAR_GEMV_MAX_M && M <= 2 * QLINEAR_GEMV_MAX_M && qgemv_mx_supported(L);
 }
 
 bool qgemm_supported(const qlinear_layout& L) {
@@ -428,6 +439,19 @@ bool qgemm_supported(const qlinear_layout& L) {
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, void* ws, const Epilogue& epi, hipStream_t stream) {
+  if (qgemm_as_decode(L, M)) {
+    for (int m0 = 0; m0 < M; m0 += QLINEAR_GEMV_MAX_M) {
+      const int mc = std::min(QLINEAR_GEMV_MAX_M, M - m0);
+      Epilogue ec = epi;   // the chunk's rows of the residual and the addend
+      if (ec.residual) ec.residual += (size_t)m0 * L.N;
+      if (ec.addend) ec.addend += (size_t)m0 * L.N;
+      uint16_t* yc = y + (size_t)m0 * L.N;
+      const hipError_t e = launch_qgemv(L, runs, x + (size_t)m0 * L.K, mc, perm, 1, &qweight, &scales,
+                                        zeros ? &zeros : nullptr, &yc, ws, ec, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   // Row chunks whose gathered activations stay below 2^31 bytes (32-bit
   // buffer offsets); a chunk is a whole number of 256-row tiles.
   const int64_t rows_fit = (((int64_t)1 << 31) - 1) / ((int64_t)L.K * 2);

@@ -90,6 +90,8 @@ bool qgemm_split_runs(const qlinear_layout& L, int M);
 // kernel, and into how many K slices that kernel cuts it.
 bool qgemm_lds_path(const qlinear_layout& L, int M);
 int qgemm_k_slices(const qlinear_layout& L, int M);
+// Whether a prefill call of M rows runs as decode launches of 16 rows.
+bool qgemm_as_decode(const qlinear_layout& L, int M);
 // Whether the packed words and scales fit the prefill kernel's 32-bit offsets.
 bool qgemm_supported(const qlinear_layout& L);
 hipError_t launch_qgemm(const qlinear_layout& L, const Runs& runs, const uint16_t* x, int M,

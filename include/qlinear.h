@@ -243,7 +243,8 @@ int qlinear_qgemv_grouped(const qlinear_layout* layout, const uint16_t* x, int32
  * of K per run boundary when ceil(N / 256) * ceil(M / 256) >= 256 (such a
  * call is computed one launch per run); [S][M][N] when the call cuts K into
  * S = min(16, 1024 / (ceil(N / 128) * ceil(M / 128)), K / 512) > 1 slices
- * (grids of few tiles, activations below 2^31 bytes); the larger of the two. */
+ * (grids of few tiles, activations below 2^31 bytes); the larger of the two.
+ * For 17..32 rows at least qlinear_qgemv_workspace_bytes (see qlinear_qgemm). */
 int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_t* bytes);
 
 /*
@@ -252,7 +253,9 @@ int qlinear_qgemm_workspace_bytes(const qlinear_layout* layout, int32_t M, size_
  * (blog, "How the Fused CUDA Kernel Works": the real kernel uses tensor
  * cores), dequantizing each weight once per tile of tokens.
  * The workspace receives the act-order-gathered activations (and the partial
- * sums described at qlinear_qgemm_workspace_bytes).
+ * sums described at qlinear_qgemm_workspace_bytes). Calls of 17..32 rows run
+ * as two qlinear_qgemv launches (16 rows, then the rest) where the decode
+ * kernels support the layout.
  * Errors as for qlinear_qgemv; UNSUPPORTED also for M > 65535 * 128, or for
  * packed words or scales of 2^31 bytes or more.
  */

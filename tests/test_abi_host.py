@@ -281,6 +281,9 @@ def test_workspace_sizes():
     many = _layout(K=4096, N=512, gs=32, bits=np.array([4, 3] * 10 + [4] * 108, np.uint8))
     assert many.nruns == 21
     assert dq.qgemm_workspace_bytes(many, 100) == (100 * 4096 * 2 + 255) // 256 * 256 + 8 * 100 * 512 * 4
+    # 17..32 rows run as decode launches: at least the decode workspace.
+    for M in (17, 24, 32):
+        assert dq.qgemm_workspace_bytes(small, M) >= dq.qgemv_workspace_bytes(small)
 
 
 def test_two_level_scale_validation_before_launch():

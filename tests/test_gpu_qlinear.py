@@ -233,6 +233,51 @@ def test_qgemm_split_k(case, two_level):
     assert_close(y, ref, f"split K case {case} two-level")
 
 
+MID_ROW_CASES = [
+    # (bits per group, group size, zero points)
+    ([4] * 32, 128, True),                               # GPTQ 4-bit g128 (K = 4096)
+    ([6] * 13 + [5] * 13 + [4] * 64 + [3] * 38, 32, False),   # the EXL2 4.0 bpw mix
+]
+
+
+@pytest.mark.parametrize("M", (17, 24, 32))
+@pytest.mark.parametrize("case", range(len(MID_ROW_CASES)))
+@pytest.mark.parametrize("kind", ("plain", "fused", "two-level"))
+def test_qgemm_mid_rows(case, M, kind):
+    """17..32 rows through qlinear_qgemm run as two decode launches (16 rows,
+    then the rest), the second with its rows of the residual and addend;
+    against the oracle (with its epilogue, or with two-level scales)."""
+    bits, gs, zeros = MID_ROW_CASES[case]
+    zeros = zeros and kind != "two-level"
+    say(f"qgemm mid rows case {case} M={M} {kind}")
+    N = 392
+    inp = _mixed_inputs(bits, gs, N, M, seed=case * 5 + M, zeros=zeros)
+    lay = GpuLayer(inp)
+    assert dq.qgemm_workspace_bytes(lay.layout, M) >= dq.qgemv_workspace_bytes(lay.layout)
+    dev = device()
+    if kind == "plain":
+        assert_close(lay.qgemm(inp.x), _ref(inp), f"mid rows case {case} M={M}")
+    elif kind == "fused":
+        rng = np.random.default_rng(M)
+        bias = rng.standard_normal(N).astype(np.float16)
+        resid = rng.standard_normal((M, N)).astype(np.float16)
+        addend = (rng.standard_normal((M, N)) * 0.25).astype(np.float32)
+        y = dq.qgemm(lay.layout, lay.x(inp.x), lay.qweight, lay.scales, lay.zeros, lay.perm,
+                     bias=torch.from_numpy(bias).to(dev), residual=torch.from_numpy(resid).to(dev),
+                     activation=dq.ACT_SILU, addend=torch.from_numpy(addend).to(dev))
+        ref = oracle.apply_epilogue(_ref(inp), bias, resid, oracle.ACT_SILU, addend=addend)
+        assert_close(y, ref, f"mid rows fused case {case} M={M}")
+    else:
+        rng = np.random.default_rng(M + 1)
+        G = len(inp.bits)
+        codes = rng.integers(0, 16, size=(G, N), dtype=np.uint8)
+        smax = rng.uniform(0.005, 0.02, size=N).astype(np.float16)
+        y = dq.qgemm_qscale(lay.layout, lay.x(inp.x), lay.qweight, dq.pack_qscale(torch.from_numpy(codes).to(dev)),
+                            torch.from_numpy(smax).to(dev), lay.perm)
+        ref = oracle.qlinear_qscale(inp.x, inp.q, oracle.qscale_pack(codes), smax, inp.bits, gs, inp.perm)
+        assert_close(y, ref, f"mid rows two-level case {case} M={M}")
+
+
 MX_FEW_ROW_BITS = {
     "mid": [6, 5, 5, 4, 4, 4, 3, 3],     # widths 3-6: one launch, gather in the kernel
     "low": [3, 3, 3, 2, 2],              # widths 2-3

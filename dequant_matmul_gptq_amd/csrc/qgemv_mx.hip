@@ -1,6 +1,7 @@
 // Host side of the matrix-core decode kernel (qgemv_mx.hpp): the launch
 // shape and mode, and the gather kernel of the two-launch mode.
 #include <string.h>
+#include <algorithm>
 
 #include "qgemv_mx.hpp"
 
@@ -35,11 +36,15 @@ __global__ __launch_bounds__(256) void gather_mx_kernel(const uint16_t* __restri
 
 }  // namespace mxk
 
+// Fragment rows stored per block in the one-launch modes: 4 up to 4 rows
+// (the LDS that leaves for x and perm), else 8.
+static int mx_rows_per_block(int M) { return M <= 4 ? 4 : 8; }
+
 // Bytes of LDS of the one-launch modes: x rows, perm and fragments (the
 // first two rounded up to whole 1 KiB pieces of the staging loads); at
 // least the partial tiles of the final reduction.
 static size_t mx_lds_bytes(int M, int K, bool perm, int FN, int& off_perm, int& off_xg) {
-  const int MS = 4;
+  const int MS = mx_rows_per_block(M);
   const int nblk = K / kBlockRows;
   const size_t xb = ((size_t)M * K * 2 + 1023) / 1024 * 1024;
   const size_t pb = perm ? ((size_t)K * 4 + 1023) / 1024 * 1024 : 0;
@@ -50,12 +55,35 @@ static size_t mx_lds_bytes(int M, int K, bool perm, int FN, int& off_perm, int& 
   return total > red ? total : red;
 }
 
-// LDS a one-launch workgroup may take.
+// LDS a one-launch workgroup may take, and the CUs that share the grid.
 constexpr size_t kMxLdsBudget = 160 * 1024;
+constexpr int kMxCus = 256;
 
+// When one launch beats the gather kernel + this kernel (measured on MI355X,
+// us at M = 3 / 4 unless noted, weights from HBM, one launch vs two):
+// - one code width, 5..8 rows: 7B 4096 -> 4096 at M = 5 / 8 9.25 / 9.37 vs
+//   11.67 / 11.50, 4096 -> 11008 12.08 / 12.84 vs 13.71 / 13.88;
+// - widths 2-3 (EXL2 2.5 bpw, two runs): 4096^2 9.83 / 9.54 vs 12.33 / 12.37,
+//   5120^2 12.78 / 12.88 vs 15.07 / 14.47, 8192^2 17.14 / 17.16 vs 18.48 /
+//   18.09, 4096 -> 11008 15.47 / 15.25 vs 16.27 / 15.74, but 8192 -> 28672
+//   47.69 / 48.13 vs 44.57 / 43.86 (every workgroup gathers its x rows run by
+//   run: too many workgroups);
+// - widths 3-6 (EXL2 4.0 bpw, four runs): 2048 -> 8192 12.27 / 12.30 vs 13.01
+//   / 12.48, 4096^2 12.79 / 12.89 vs 13.48 / 12.44, but 5120^2 17.05 / 17.26
+//   vs 16.09 / 15.79, 8192^2 23.97 / 23.95 vs 23.02 / 22.61, 4096 -> 11008
+//   19.70 / 19.75 vs 18.93 / 18.49 (21.49 vs 18.54 at M = 8).
 bool qgemv_mx_one_launch(const qlinear_layout& L, int M, bool perm) {
   int a, b;
-  return M <= 4 && mx_lds_bytes(M, L.K, perm, 4, a, b) <= kMxLdsBudget;
+  unsigned set = 0;
+  for (int r = 0; r < L.nruns; ++r) set |= 1u << L.run_bits[r];
+  bool fast;
+  if ((set & (set - 1)) == 0)
+    fast = M <= 8;
+  else if ((set & ~stream::kLowBits) == 0)
+    fast = M <= 4 && (int64_t)L.nruns * L.N <= 32768;
+  else
+    fast = M <= 4 && (int64_t)L.K * L.N <= (int64_t)4096 * 4096;
+  return fast && mx_lds_bytes(M, L.K, perm, 4, a, b) <= kMxLdsBudget;
 }
 
 bool qgemv_mx_supported(const qlinear_layout& L) {
@@ -120,14 +148,23 @@ hipError_t launch_qgemv_mx(const qlinear_layout& L, const Runs& runs, const uint
   // the grid keeps at least ~160 workgroups of 4 columns per lane, else 2
   // columns with >= 256 workgroups, else 1).
   const auto strips = [&](int fn) { return mats * ((L.N + kPanel * fn - 1) / (kPanel * fn)); };
-  const int fn = strips(4) >= 160 ? 4 : strips(2) >= 256 ? 2 : 1;
+  int fn = strips(4) >= 160 ? 4 : strips(2) >= 256 ? 2 : 1;
 
   int mode;
   size_t lds = 0;
   const bool all = (set & ~stream::kMidBits) != 0 && (set & ~stream::kLowBits) != 0 && set != mxk::kSet4;
   if (!all && qgemv_mx_one_launch(L, M, perm != nullptr)) {
     mode = mxk::kFewRows;
+    // The staged rows can leave room for only one workgroup per CU: then
+    // take wider strips while that saves a round of workgroups (measured on
+    // MI355X, us: 5120^2 at M = 5 / 6 10.43 / 10.81 with 160 workgroups of 2
+    // columns per lane against 18.18 / 19.10 with 320 of 1; EXL2 4.0 bpw
+    // 5120^2 at M = 3 17.07 against 23.66).
+    const int per_round = kMxCus * (int)std::max<size_t>(1, kMxLdsBudget / mx_lds_bytes(M, L.K, perm != nullptr, fn, a.lds_perm, a.lds_xg));
+    const auto rounds = [&](int f) { return (strips(f) + per_round - 1) / per_round; };
+    while (fn < 4 && rounds(2 * fn) < rounds(fn)) fn *= 2;
     lds = mx_lds_bytes(M, L.K, perm != nullptr, fn, a.lds_perm, a.lds_xg);
+    a.ms = mx_rows_per_block(M);
   } else {
     // Two launches (the set of all widths, 8-bit runs mixed with others,
     // always runs this way: its one-launch instances are not built).

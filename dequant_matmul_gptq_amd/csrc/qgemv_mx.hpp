@@ -20,7 +20,7 @@
 // partial tiles are summed through LDS at the end (no split-K, no atomics).
 // Strips are dealt to the 8 XCDs in contiguous ranges.
 //
-// Activations. In one-launch mode (M <= 4, LDS permitting) the workgroup
+// Activations. In one-launch mode (M <= 8, LDS permitting) the workgroup
 // gathers them itself: the x rows and the permutation are copied into LDS
 // with global-to-LDS loads issued before any weight load (they use no
 // registers, and complete before the weights because loads complete in
@@ -60,7 +60,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 
 enum Mode : int {
-  kFewRows = 1,   // one launch, M <= 4
+  kFewRows = 1,   // one launch, M <= 8
   kExact = 4,     // flag: B dequantized exactly (no sums MFMA, no per-unit epilogue)
   kGathered = 2,  // activations gathered by the gather kernel into the workspace
 };
@@ -70,9 +70,10 @@ enum Mode : int {
 constexpr int base_mode(int m) { return m & 3; }
 constexpr bool exact_mode(int m) { return (m & kExact) != 0; }
 
+// (one-launch mode: at most 8; MxArgs::ms holds the call's 4 or 8).
 template <int kMode>
 constexpr int rows_stored() {
-  return base_mode(kMode) == kFewRows ? 4 : 16;
+  return base_mode(kMode) == kFewRows ? 8 : 16;
 }
 
 struct MxArgs {
@@ -89,6 +90,7 @@ struct MxArgs {
   int scale_row_bytes;   // bytes per group row of the scales operand
   int two_level;         // 1: the scales operand holds two-level scale codes
   int lds_perm, lds_xg;   // byte offsets of the LDS regions (one-launch modes)
+  int ms;                 // one-launch modes: fragment rows stored per block, 4 (M <= 4) or 8
   // Each wave's blocks [b0, b1) (whole groups) and its first segment (the
   // part of the run holding b0): its end block, first packed row and width.
   int wave_b0[kWaves], wave_b1[kWaves], wave_send[kWaves], wave_row0[kWaves], wave_bits0[kWaves];
@@ -235,9 +237,9 @@ __device__ __forceinline__ void issue_params(const Lane& L, int blk, int grp, in
 template <int UB, int kMode>
 __device__ __forceinline__ void lds_frags(const MxArgs& a, const Lane& L, const unsigned char* lds, int blk,
                                           half8_t (&af)[UB]) {
-  constexpr int MS = rows_stored<kMode>();
+  const int ms = a.ms;
 #pragma unroll
-  for (int b = 0; b < UB; ++b) af[b] = *reinterpret_cast<const half8_t*>(lds + a.lds_xg + (blk + b) * MS * 64 + L.xoff);
+  for (int b = 0; b < UB; ++b) af[b] = *reinterpret_cast<const half8_t*>(lds + a.lds_xg + (blk + b) * ms * 64 + L.xoff);
 }
 
 template <int FN>
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_mx_kernel(MxArgs a) {
                 [&](int j) { return perm ? (int)min((unsigned)pl[j], (unsigned)(K - 1)) : j; },
                 [&](int m, int f) { return xr[m * K + f]; },
                 [&](int m, u32x4 v) {
-                  *reinterpret_cast<u32x4*>(lds + lds_xg + (blk * MS + m) * 64 + gq * 16) = v;
+                  *reinterpret_cast<u32x4*>(lds + lds_xg + (blk * a.ms + m) * 64 + gq * 16) = v;
                 });
           }
         });

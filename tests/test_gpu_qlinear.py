@@ -297,6 +297,31 @@ def test_qgemv_matrix_core_few_rows(name, M, zeros):
     assert_close(y, _ref(inp), f"qgemv {name} M={M}")
 
 
+@pytest.mark.parametrize("K,M", [(4096, 5), (4096, 8), (5376, 5), (4608, 8), (4096, 16)])
+@pytest.mark.parametrize("b,gs", [(4, 128), (3, 32), (8, 32)])
+def test_qgemv_matrix_core_one_width_rows(b, gs, K, M):
+    """5-8 rows of a single-width layer run the matrix-core kernel in one
+    launch while 8 x rows, perm and fragments fit in LDS (K = 4096 at 8 rows,
+    5376 at 5), else with the gather kernel first (4608 at 8 rows; 16 rows
+    always); act-order, 520 columns leave a ragged last strip."""
+    say(f"qgemv matrix-core one width b={b} gs={gs} K={K} M={M}")
+    inp = _mixed_inputs([b] * (K // gs), gs, 520, M, seed=500 + b * 31 + K % 97 + M, zeros=True)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv one width b={b} K={K} M={M}")
+
+
+@pytest.mark.parametrize("bits,gs,M", [([4] * 40, 128, 5), ([3] * 80 + [2] * 80, 32, 3)],
+                         ids=("4bit-M5", "exl2-low-M3"))
+def test_qgemv_matrix_core_one_launch_wide_strips(bits, gs, M):
+    """K = 5120 in one launch leaves LDS for one workgroup per CU: 321 panels
+    (5128 columns, the last one ragged) then run as 161 workgroups of 2
+    columns per lane instead of two rounds of 1."""
+    say(f"qgemv matrix-core one launch, wide strips, gs={gs} M={M}")
+    inp = _mixed_inputs(bits, gs, 5128, M, seed=600 + M, zeros=True)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv wide strips gs={gs} M={M}")
+
+
 @pytest.mark.parametrize("M", (3, 4))
 def test_qgemv_matrix_core_large_uniform(M):
     """3-4 rows of a single-width layer above 2 * 4096^2 weights run the

@@ -85,54 +85,65 @@ __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __res
 }
 
 // Prefill variant (no scaling, no sums): a workgroup stages R whole rows of
-// x in LDS with 16-byte loads, then each thread takes pairs idx = tid,
-// tid + 256, ...; a pair's rows and perm entries are looked up once and
-// serve all R rows, whose values come from LDS. Rows of xq are written 1 KiB
-// per iteration, contiguous.
-__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
-                                                          const int32_t* __restrict__ perm,
-                                                          uint32_t* __restrict__ xq, int M, int K, int R,
-                                                          int mfma, Runs runs) {
+// x in LDS with 16-byte loads. Each thread then takes quads of 4 consecutive
+// pairs (one block, so one width lookup), looks their rows and perm entries
+// up once for all R rows, and writes each row's quad as one 16-byte store:
+// a wave writes 1 KiB of a row of xq, contiguous.
+template <int kT>
+__global__ __launch_bounds__(kT) void gather_rows_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+                                                         uint32_t* __restrict__ xq, int M, int K, int R, int mfma,
+                                                         Runs runs) {
   extern __shared__ __align__(16) uint16_t xs[];   // R rows of K float16
-  // Both loops below keep kBatch loads per thread in flight: all loads of a
-  // batch are issued before any of them is used.
-  constexpr int kBatch = 8;
+  // Loads per thread in flight in the staging loop, quads in the gather loop.
+  constexpr int kBatch = 8, kQuads = 2;
   const int m0 = blockIdx.x * R;
   const int rows = min(R, M - m0);
   const int n16 = K / 8;   // 16-byte pieces per row (K is a multiple of 32)
   const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)m0 * K);
   uint4* dst = reinterpret_cast<uint4*>(xs);
   const int total = rows * n16;
-  for (int base = threadIdx.x; base < total; base += 256 * kBatch) {
+  for (int base = threadIdx.x; base < total; base += kT * kBatch) {
     uint4 v[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) v[u] = src[min(base + u * 256, total - 1)];
+    for (int u = 0; u < kBatch; ++u) v[u] = src[min(base + u * kT, total - 1)];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
-      if (base + u * 256 < total) dst[base + u * 256] = v[u];
+      if (base + u * kT < total) dst[base + u * kT] = v[u];
   }
   __syncthreads();
   const int pairs = (K / kBlockRows) * kPairsPerBlock;
-  for (int base = threadIdx.x; base < pairs; base += 256 * kBatch) {
-    int flo[kBatch], fhi[kBatch];
+  const int quads = pairs / 4;
+  for (int base = threadIdx.x; base < quads; base += kT * kQuads) {
+    int flo[kQuads][4], fhi[kQuads][4];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int idx = min(base + u * 256, pairs - 1);
-      const int blk = idx / kPairsPerBlock, p = idx % kPairsPerBlock;
+    for (int u = 0; u < kQuads; ++u) {
+      const int q = min(base + u * kT, quads - 1);
+      const int blk = q / (kPairsPerBlock / 4);
       const int bits = block_bits_scan(runs, blk);
-      int lo, hi;
-      pair_rows(bits, mfma ? mfma_pair(bits, p) : p, lo, hi);
-      const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;
-      // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
-      flo[u] = perm ? (int)min((unsigned)perm[jlo], (unsigned)(K - 1)) : jlo;
-      fhi[u] = perm ? (int)min((unsigned)perm[jhi], (unsigned)(K - 1)) : jhi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = (q % (kPairsPerBlock / 4)) * 4 + e;
+        int lo, hi;
+        pair_rows(bits, mfma ? mfma_pair(bits, p) : p, lo, hi);
+        const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;
+        // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
+        flo[u][e] = perm ? (int)min((unsigned)perm[jlo], (unsigned)(K - 1)) : jlo;
+        fhi[u][e] = perm ? (int)min((unsigned)perm[jhi], (unsigned)(K - 1)) : jhi;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int idx = base + u * 256;
-      if (idx < pairs)
-        for (int r = 0; r < rows; ++r)
-          xq[(size_t)(m0 + r) * pairs + idx] = (uint32_t)xs[r * K + flo[u]] | ((uint32_t)xs[r * K + fhi[u]] << 16);
+    for (int u = 0; u < kQuads; ++u) {
+      const int q = base + u * kT;
+      if (q < quads)
+        for (int r = 0; r < rows; ++r) {
+          const uint16_t* xr = xs + r * K;
+          uint4 o;
+          o.x = (uint32_t)xr[flo[u][0]] | ((uint32_t)xr[fhi[u][0]] << 16);
+          o.y = (uint32_t)xr[flo[u][1]] | ((uint32_t)xr[fhi[u][1]] << 16);
+          o.z = (uint32_t)xr[flo[u][2]] | ((uint32_t)xr[fhi[u][2]] << 16);
+          o.w = (uint32_t)xr[flo[u][3]] | ((uint32_t)xr[fhi[u][3]] << 16);
+          reinterpret_cast<uint4*>(xq + (size_t)(m0 + r) * pairs)[q] = o;
+        }
     }
   }
 }
@@ -143,11 +154,21 @@ hipError_t launch_gather_rows(const Runs& runs, const uint16_t* x, const int32_t
                               uint32_t* xq, bool mfma, hipStream_t stream) {
   const size_t row_bytes = (size_t)K * 2;
   if (row_bytes > kGatherRowsLds) return launch_gather_pairs(runs, x, perm, M, K, xq, nullptr, false, mfma, stream);
-  // Up to 4 rows per workgroup within 32 KiB, at least one row.
-  const int R = (int)std::max<size_t>(1, std::min<size_t>(4, (size_t)32768 / row_bytes));
+  // Up to 4 rows per workgroup within 32 KiB; 2 rows within 64 KiB where
+  // 32 KiB holds only one (K = 13824 at M = 2048: 47 us instead of 55-74 us
+  // with one row); at least one row.
+  const size_t r32 = std::min<size_t>(4, (size_t)32768 / row_bytes), r64 = std::min<size_t>(2, kGatherRowsLds / row_bytes);
+  const int R = (int)std::max<size_t>(1, std::max(r32, r64));
   const int grid = (M + R - 1) / R;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), (size_t)R * row_bytes, stream, x, perm, xq, M, K,
-                     R, mfma ? 1 : 0, runs);
+  const size_t lds = (size_t)R * row_bytes;
+  // Past 40 KiB of rows a CU holds at most 3 workgroups: 1024 threads each
+  // keep enough loads in flight.
+  if (lds > 40 * 1024)
+    hipLaunchKernelGGL(gather_rows_kernel<1024>, dim3(grid), dim3(1024), lds, stream, x, perm, xq, M, K, R,
+                       mfma ? 1 : 0, runs);
+  else
+    hipLaunchKernelGGL(gather_rows_kernel<256>, dim3(grid), dim3(256), lds, stream, x, perm, xq, M, K, R,
+                       mfma ? 1 : 0, runs);
   return hipGetLastError();
 }
 

@@ -196,6 +196,31 @@ def test_qgemm_uniform_widths_large_grid(b):
     assert_close(y[torch.from_numpy(rows).to(y.device)], _ref(inp, inp.x[rows]), f"qgemm b={b} large grid")
 
 
+GATHER_ROW_CASES = [
+    # (K, N, M): rows per workgroup of the prefill gather and its thread count
+    (4096, 48, 37),       # 4 rows (32 KiB), 256 threads; last workgroup 1 row
+    (10240, 48, 37),      # 2 rows (40 KiB), 256 threads
+    (11008, 48, 37),      # 2 rows (43 KiB), 1024 threads
+    (28672, 48, 37),      # 1 row (56 KiB), 1024 threads
+    (32768, 48, 37),      # 1 row of exactly 64 KiB, 1024 threads
+    (11008, 4096, 2304),  # 2 rows, 1024 threads, pair order of the register-dequant kernel (144 tiles)
+]
+
+
+@pytest.mark.parametrize("K,N,M", GATHER_ROW_CASES)
+def test_qgemm_gather_rows(K, N, M):
+    """Act-order prefill across the gather's row and thread configurations;
+    the oracle checks every 32nd row and the last on the large grid."""
+    say(f"qgemm gather rows K={K} N={N} M={M}")
+    inp = _mixed_inputs([4] * (K // 128), 128, N, M, seed=K % 101 + M, zeros=True)
+    y = GpuLayer(inp).qgemm(inp.x)
+    if M * N > 1 << 20:
+        rows = np.unique(np.concatenate([np.arange(0, M, 32), [M - 1]]))
+        assert_close(y[torch.from_numpy(rows).to(y.device)], _ref(inp, inp.x[rows]), f"qgemm gather K={K} M={M}")
+    else:
+        assert_close(y, _ref(inp), f"qgemm gather K={K} M={M}")
+
+
 SPLIT_K_CASES = [
     # (bits per group, group size, N, M, zero points)
     ([4] * 32, 128, 392, 17, True),                  # one width, K = 4096: 8 slices

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void gather_pairs_kernel(const uint16_t* __res
 template <int kT>
 __global__ __launch_bounds__(kT) void gather_rows_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
                                                          uint32_t* __restrict__ xq, int M, int K, int R, int mfma,
-                                                         Runs runs) {
+                                                         int perm16, Runs runs) {
   extern __shared__ __align__(16) uint16_t xs[];   // R rows of K float16
   // Loads per thread in flight in the staging loop, quads in the gather loop.
   constexpr int kBatch = 8, kQuads = 2;
@@ -118,14 +118,33 @@ __global__ __launch_bounds__(kT) void gather_rows_kernel(const uint16_t* __restr
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) {
       const int q = min(base + u * kT, quads - 1);
-      const int blk = q / (kPairsPerBlock / 4);
+      const int blk = q / (kPairsPerBlock / 4), t = q % (kPairsPerBlock / 4);
       const int bits = block_bits_scan(runs, blk);
+      const int row0 = blk * kBlockRows;
+      if (perm16 && (bits == 2 || bits == 4 || bits == 8)) {
+        // Both pair orders put the quad's rows in two aligned runs of 4: rows
+        // 8t..8t+7 at 4 and 8 bits, 16(t/2) + 4(t%2) + 0..3 and + 8..11 at 2
+        // bits. Two 16-byte perm loads instead of eight 4-byte ones.
+        const int a0 = bits == 2 ? 16 * (t >> 1) + 4 * (t & 1) : 8 * t;
+        const int a1 = bits == 2 ? a0 + 8 : a0 + 4;
+        const int4 p0 = *reinterpret_cast<const int4*>(perm + row0 + a0);
+        const int4 p1 = *reinterpret_cast<const int4*>(perm + row0 + a1);
+        const auto c = [K](int v) { return (int)min((unsigned)v, (unsigned)(K - 1)); };
+        if (bits == 8) {   // pair e: rows 8t + 4(e/2) + e%2 and that + 2
+          flo[u][0] = c(p0.x), flo[u][1] = c(p0.y), flo[u][2] = c(p1.x), flo[u][3] = c(p1.y);
+          fhi[u][0] = c(p0.z), fhi[u][1] = c(p0.w), fhi[u][2] = c(p1.z), fhi[u][3] = c(p1.w);
+        } else {           // pair e: rows a0 + e and a1 + e
+          flo[u][0] = c(p0.x), flo[u][1] = c(p0.y), flo[u][2] = c(p0.z), flo[u][3] = c(p0.w);
+          fhi[u][0] = c(p1.x), fhi[u][1] = c(p1.y), fhi[u][2] = c(p1.z), fhi[u][3] = c(p1.w);
+        }
+        continue;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int p = (q % (kPairsPerBlock / 4)) * 4 + e;
+        const int p = t * 4 + e;
         int lo, hi;
         pair_rows(bits, mfma ? mfma_pair(bits, p) : p, lo, hi);
-        const int jlo = blk * kBlockRows + lo, jhi = blk * kBlockRows + hi;
+        const int jlo = row0 + lo, jhi = row0 + hi;
         // perm entries are clamped into [0, K): a malformed perm cannot address outside the row.
         flo[u][e] = perm ? (int)min((unsigned)perm[jlo], (unsigned)(K - 1)) : jlo;
         fhi[u][e] = perm ? (int)min((unsigned)perm[jhi], (unsigned)(K - 1)) : jhi;
@@ -161,14 +180,15 @@ hipError_t launch_gather_rows(const Runs& runs, const uint16_t* x, const int32_t
   const int R = (int)std::max<size_t>(1, std::max(r32, r64));
   const int grid = (M + R - 1) / R;
   const size_t lds = (size_t)R * row_bytes;
+  const int perm16 = perm != nullptr && ((uintptr_t)perm & 15) == 0;
   // Past 40 KiB of rows a CU holds at most 3 workgroups: 1024 threads each
   // keep enough loads in flight.
   if (lds > 40 * 1024)
     hipLaunchKernelGGL(gather_rows_kernel<1024>, dim3(grid), dim3(1024), lds, stream, x, perm, xq, M, K, R,
-                       mfma ? 1 : 0, runs);
+                       mfma ? 1 : 0, perm16, runs);
   else
     hipLaunchKernelGGL(gather_rows_kernel<256>, dim3(grid), dim3(256), lds, stream, x, perm, xq, M, K, R,
-                       mfma ? 1 : 0, runs);
+                       mfma ? 1 : 0, perm16, runs);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     Layout,
     QlinearError,
     dequant,
+    group_order,
     lib,
     lora_delta,
     lora_workspace_bytes,
@@ -29,6 +30,7 @@ from ._lib import (  # noqa: F401
     NOALLOC_MAX_K,
     qgemv_workspace,
     qgemv_workspace_bytes,
+    reorder_groups,
     status_string,
     unpack,
     pack_qscale,

@@ -32,6 +32,7 @@ ERR_HIP = 5
 EXPORTS = (
     "qlinear_status_string",
     "qlinear_layout_init",
+    "qlinear_group_order",
     "qlinear_pack_weights",
     "qlinear_unpack",
     "qlinear_dequant",
@@ -104,6 +105,7 @@ def lib() -> ctypes.CDLL:
         L.qlinear_status_string.restype = ctypes.c_char_p
         L.qlinear_status_string.argtypes = [ctypes.c_int]
         L.qlinear_layout_init.argtypes = [lp, i32, i32, i32, vp]
+        L.qlinear_group_order.argtypes = [vp, i32, vp]
         L.qlinear_pack_weights.argtypes = [lp, vp, vp, vp]
         L.qlinear_unpack.argtypes = [lp, vp, vp, vp]
         L.qlinear_dequant.argtypes = [lp, vp, vp, vp, vp, vp]
@@ -181,6 +183,38 @@ class Layout:
     @property
     def ref(self):
         return ctypes.byref(self.c)
+
+
+def group_order(bits) -> np.ndarray:
+    """qlinear_group_order: the storage order of the groups (int32, original
+    index of the group stored i-th) that leaves at most 6 width runs."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint8).reshape(-1))
+    order = np.empty(b.size, dtype=np.int32)
+    _check(lib().qlinear_group_order(b.ctypes.data_as(ctypes.c_void_p), int(b.size),
+                                     order.ctypes.data_as(ctypes.c_void_p)), "qlinear_group_order")
+    return order
+
+
+def reorder_groups(order, group_size: int, bits, q: torch.Tensor, per_group=(), perm: torch.Tensor | None = None):
+    """Move the groups of a matrix into `order` (from group_order), once, before packing.
+
+    q is uint8 [K][N] in stored row order; each tensor of per_group has one row
+    per group (scales, zero points, two-level scale codes); perm is the int32
+    act-order permutation or None. Returns (bits, q, per_group, perm): group
+    order[i]'s rows at position i, and perm composed with that row move
+    (stored row i * group_size + r takes perm[order[i] * group_size + r]), so
+    the product is unchanged. Tensors stay on their devices.
+    """
+    o = np.asarray(order, dtype=np.int64)
+    rows = (o[:, None] * int(group_size) + np.arange(int(group_size))).reshape(-1)
+    r = torch.from_numpy(rows).to(q.device)
+    q2 = q.index_select(0, r)
+    pg = tuple(t.index_select(0, torch.from_numpy(o).to(t.device)) for t in per_group)
+    if perm is None:
+        p2 = r.to(torch.int32)
+    else:
+        p2 = perm.index_select(0, r.to(perm.device)).to(torch.int32)
+    return np.asarray(bits, dtype=np.uint8)[o], q2, pg, p2
 
 
 def pack_weights(layout: Layout, q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

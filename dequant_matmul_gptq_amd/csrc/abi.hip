@@ -150,6 +150,20 @@ const char* qlinear_status_string(int status) {
   }
 }
 
+int qlinear_group_order(const uint8_t* group_bits, int32_t groups, int32_t* order) {
+  if (!group_bits || !order || groups <= 0) return QLINEAR_ERR_INVALID_ARGUMENT;
+  static const int kWidths[] = {8, 6, 5, 4, 3, 2};   // widest first
+  for (int g = 0; g < groups; ++g) {
+    const int b = group_bits[g];
+    if (b != 2 && b != 3 && b != 4 && b != 5 && b != 6 && b != 8) return QLINEAR_ERR_UNSUPPORTED;
+  }
+  int n = 0;
+  for (int b : kWidths)
+    for (int g = 0; g < groups; ++g)
+      if (group_bits[g] == b) order[n++] = g;
+  return QLINEAR_OK;
+}
+
 int qlinear_layout_init(qlinear_layout* layout, int32_t K, int32_t N, int32_t group_size,
                         const uint8_t* bits_host) {
   if (!layout || !bits_host) return QLINEAR_ERR_INVALID_ARGUMENT;

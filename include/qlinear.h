@@ -129,6 +129,27 @@ int qlinear_layout_init(qlinear_layout* layout, int32_t K, int32_t N, int32_t gr
                         const uint8_t* bits_host);
 
 /*
+ * A storage order of the groups under which any per-group width map has at
+ * most 6 runs. EXL2 lets each group of a matrix take its own width (blog,
+ * "Finding 3: The EXL2 format enables better quality-per-bit") and stores a
+ * row permutation with every matrix (blog, "How the EXL2 Quantization
+ * Pipeline Works Under the Hood": q_groups and q_invperm). Moving whole
+ * groups is a row permutation as well, so a map with more than
+ * QLINEAR_MAX_RUNS runs is served by storing its groups in this order.
+ * order[i] is the original index of the group stored i-th: widest widths
+ * first, original order kept within a width. The caller moves that group's
+ * code rows, scale row and zero-point row to position i, and composes the
+ * act-order permutation: stored row i * group_size + r takes
+ * perm[order[i] * group_size + r], or order[i] * group_size + r without
+ * act-order. The product is unchanged up to float rounding order.
+ * group_bits (read) and order (written) are HOST arrays of `groups` entries.
+ * Host-only; touches no GPU.
+ * Errors: INVALID_ARGUMENT (NULL, groups <= 0), UNSUPPORTED (a width outside
+ * {2,3,4,5,6,8}); order is not written on error.
+ */
+int qlinear_group_order(const uint8_t* group_bits, int32_t groups, int32_t* order);
+
+/*
  * Pack codes into the format above: the q_weights tensor, packed values of
  * varying bit width in uint32 words (blog, Step 3 of the EXL2 pipeline), 4-bit
  * codes least significant first as in the blog's kernel sketch ("How the

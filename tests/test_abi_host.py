@@ -86,6 +86,63 @@ def test_layout_init_rejects_bits_and_runs():
     assert _layout(K=64 * 32, N=64, gs=32, bits=ok).nruns == 64
 
 
+@pytest.mark.parametrize("groups,seed", [(1, 0), (7, 1), (128, 2), (896, 3)])
+def test_group_order_leaves_at_most_six_runs(groups, seed):
+    """Any per-group width map (here shuffled over all six widths) in the
+    returned order: a permutation, widest widths first, original order kept
+    within a width, at most 6 runs, so qlinear_layout_init accepts it."""
+    rng = np.random.default_rng(seed)
+    bits = rng.choice(np.array([2, 3, 4, 5, 6, 8], np.uint8), size=groups)
+    order = dq.group_order(bits)
+    assert sorted(order.tolist()) == list(range(groups))
+    b = bits[order]
+    assert np.all(np.diff(b.astype(int)) <= 0)
+    for w in np.unique(bits):
+        idx = order[b == w]
+        assert np.all(np.diff(idx) > 0)
+    L = dq.Layout(groups * 32, 64, 32, b)
+    assert L.nruns == len(np.unique(bits)) <= 6
+
+
+def test_group_order_errors():
+    L = dq.lib()
+    with pytest.raises(dq.QlinearError) as e:
+        dq.group_order(np.array([4, 7, 4], np.uint8))
+    assert e.value.status == _lib.ERR_UNSUPPORTED
+    out = np.full(3, -5, np.int32)
+    bits = np.array([4, 3, 4], np.uint8)
+    assert L.qlinear_group_order(bits.ctypes.data_as(ctypes.c_void_p), 0,
+                                 out.ctypes.data_as(ctypes.c_void_p)) == _lib.ERR_INVALID_ARGUMENT
+    assert L.qlinear_group_order(None, 3, out.ctypes.data_as(ctypes.c_void_p)) == _lib.ERR_INVALID_ARGUMENT
+    assert L.qlinear_group_order(bits.ctypes.data_as(ctypes.c_void_p), 3, None) == _lib.ERR_INVALID_ARGUMENT
+    assert np.all(out == -5)
+
+
+@pytest.mark.parametrize("act_order", (True, False))
+def test_reorder_groups_keeps_the_product(act_order):
+    """The oracle's product on a shuffled 80-run map equals its product on the
+    groups moved into group_order's order with the composed permutation."""
+    import torch
+    from oracle import qlinear_oracle as oracle
+    rng = np.random.default_rng(11)
+    gs, G, N, M = 32, 80, 24, 3
+    bits = np.array([4, 3] * 40, np.uint8)
+    rng.shuffle(bits)
+    K = G * gs
+    q = np.concatenate([rng.integers(0, 1 << int(b), size=(gs, N), dtype=np.uint8) for b in bits])
+    s = rng.uniform(0.005, 0.02, size=(G, N)).astype(np.float16)
+    z = rng.integers(0, 8, size=(G, N), dtype=np.uint8)
+    perm = rng.permutation(K).astype(np.int32) if act_order else None
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    b2, q2, (s2, z2), p2 = dq.reorder_groups(dq.group_order(bits), gs, bits, torch.from_numpy(q),
+                                             (torch.from_numpy(s), torch.from_numpy(z)),
+                                             None if perm is None else torch.from_numpy(perm))
+    assert dq.Layout(K, N, gs, b2).nruns == 2
+    ref = oracle.qlinear(x, q, s, z, bits, gs, perm)
+    got = oracle.qlinear(x, q2.numpy(), s2.numpy(), z2.numpy(), b2, gs, p2.numpy())
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
 def test_layout_init_null():
     L = dq.lib()
     assert L.qlinear_layout_init(None, 256, 512, 32, None) == _lib.ERR_INVALID_ARGUMENT

@@ -750,3 +750,38 @@ def test_fused_epilogue(op, bits, M, N, terms):
         # the update is large enough that dropping it would fail the check above
         plain = oracle.apply_epilogue(base, bias, sub(resid), act)
         assert np.linalg.norm(ref - plain) > 0.05 * np.linalg.norm(ref)
+
+
+SHUFFLED_MAPS = {
+    # name: (widths drawn per group, K, group size, N, zero points)
+    "2.5bpw-256-groups": ((2, 3), 8192, 32, 520, False),
+    "all-widths-128-groups": ((2, 3, 4, 5, 6, 8), 4096, 32, 520, True),
+}
+
+
+@pytest.mark.parametrize("M", (1, 4, 16, 64))
+@pytest.mark.parametrize("name", sorted(SHUFFLED_MAPS))
+def test_shuffled_width_map_via_group_order(name, M):
+    """A per-group width map drawn at random (far more than 64 runs) is
+    stored in qlinear_group_order's order with the composed act-order
+    permutation; decode and prefill on it match the oracle on the original,
+    shuffled layout."""
+    widths, K, gs, N, zeros = SHUFFLED_MAPS[name]
+    say(f"shuffled width map {name} M={M}")
+    rng = np.random.default_rng(700 + M + K)
+    bits = rng.choice(np.array(widths, np.uint8), size=K // gs)
+    inp = _mixed_inputs(bits, gs, N, M, seed=800 + M, zeros=zeros)
+    dev = torch.device("cuda")
+    per_group = (torch.from_numpy(inp.scales).to(dev),) + (() if inp.zeros is None else (torch.from_numpy(inp.zeros).to(dev),))
+    b2, q2, pg, p2 = dq.reorder_groups(dq.group_order(inp.bits), gs, inp.bits, torch.from_numpy(inp.q).to(dev),
+                                       per_group, torch.from_numpy(inp.perm).to(dev))
+    L = dq.Layout(K, N, gs, b2)
+    assert L.nruns == len(np.unique(bits))
+    qw = dq.pack_weights(L, q2)
+    z2 = pg[1] if len(pg) > 1 else None
+    x = torch.from_numpy(inp.x).to(dev)
+    if M <= dq.GEMV_MAX_M:
+        y = dq.qgemv(L, x, qw, pg[0], z2, p2, dq.qgemv_workspace(L, dev))
+    else:
+        y = dq.qgemm(L, x, qw, pg[0], z2, p2)
+    assert_close(y, _ref(inp), f"shuffled {name} M={M}")

@@ -785,3 +785,31 @@ def test_shuffled_width_map_via_group_order(name, M):
     else:
         y = dq.qgemm(L, x, qw, pg[0], z2, p2)
     assert_close(y, _ref(inp), f"shuffled {name} M={M}")
+
+
+@pytest.mark.parametrize("M", (1, 8, 64))
+def test_shuffled_width_map_two_level_scales(M):
+    """Two-level scales on a shuffled 2/3-bit map: the per-group scale codes
+    move with their groups before packing; the result matches the oracle on
+    the original layout (symmetric codes, as two-level scales require)."""
+    say(f"shuffled width map, two-level scales, M={M}")
+    rng = np.random.default_rng(900 + M)
+    gs, K, N = 32, 4096, 264
+    bits = rng.choice(np.array([2, 3], np.uint8), size=K // gs)
+    inp = _mixed_inputs(bits, gs, N, M, seed=910 + M, zeros=False)
+    codes = rng.integers(0, 16, size=(K // gs, N), dtype=np.uint8)
+    smax = rng.uniform(0.005, 0.02, size=N).astype(np.float16)
+    dev = torch.device("cuda")
+    b2, q2, (c2,), p2 = dq.reorder_groups(dq.group_order(inp.bits), gs, inp.bits, torch.from_numpy(inp.q).to(dev),
+                                          (torch.from_numpy(codes).to(dev),), torch.from_numpy(inp.perm).to(dev))
+    L = dq.Layout(K, N, gs, b2)
+    qw = dq.pack_weights(L, q2)
+    x = torch.from_numpy(inp.x).to(dev)
+    qs = dq.pack_qscale(c2.contiguous())
+    sm = torch.from_numpy(smax).to(dev)
+    if M <= dq.GEMV_MAX_M:
+        y = dq.qgemv_qscale(L, x, qw, qs, sm, p2, dq.qgemv_workspace(L, dev))
+    else:
+        y = dq.qgemm_qscale(L, x, qw, qs, sm, p2)
+    ref = oracle.qlinear_qscale(inp.x, inp.q, oracle.qscale_pack(codes), smax, inp.bits, gs, inp.perm)
+    assert_close(y, ref, f"shuffled two-level M={M}")

@@ -174,8 +174,8 @@ hipError_t launch_gather_rows(const Runs& runs, const uint16_t* x, const int32_t
   const size_t row_bytes = (size_t)K * 2;
   if (row_bytes > kGatherRowsLds) return launch_gather_pairs(runs, x, perm, M, K, xq, nullptr, false, mfma, stream);
   // Up to 4 rows per workgroup within 32 KiB; 2 rows within 64 KiB where
-  // 32 KiB holds only one (K = 13824 at M = 2048: 47 us instead of 55-74 us
-  // with one row); at least one row.
+  // 32 KiB holds only one (K = 13824 at M = 2048, measured with 4-byte perm
+  // loads: 47 us instead of 55-74 us with one row); at least one row.
   const size_t r32 = std::min<size_t>(4, (size_t)32768 / row_bytes), r64 = std::min<size_t>(2, kGatherRowsLds / row_bytes);
   const int R = (int)std::max<size_t>(1, std::max(r32, r64));
   const int grid = (M + R - 1) / R;

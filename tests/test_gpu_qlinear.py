@@ -323,7 +323,7 @@ def test_qgemv_matrix_core_few_rows(name, M, zeros):
 
 
 @pytest.mark.parametrize("K,M", [(4096, 5), (4096, 8), (5376, 5), (4608, 8), (4096, 16)])
-@pytest.mark.parametrize("b,gs", [(4, 128), (3, 32), (8, 32)])
+@pytest.mark.parametrize("b,gs", [(4, 128), (2, 32), (3, 32), (5, 32), (6, 64), (8, 32)])
 def test_qgemv_matrix_core_one_width_rows(b, gs, K, M):
     """5-8 rows of a single-width layer run the matrix-core kernel in one
     launch while 8 x rows, perm and fragments fit in LDS (K = 4096 at 8 rows,

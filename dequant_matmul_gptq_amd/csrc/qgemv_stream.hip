@@ -59,12 +59,17 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   // matrix-core kernel; at 3-4 rows the single-row kernel still wins on
   // layers of up to 2 * 4096 * 4096 weights and the matrix-core kernel on
   // larger ones (1.1-1.4x); from 5 rows on the matrix-core kernel wins (up
-  // to 1.4x; within 8% on 8-bit layouts).
+  // to 1.4x; within 8% on 8-bit layouts). 4-bit layers at 3-4 rows take the
+  // matrix-core kernel from 4096^2 weights on, since its one-launch mode
+  // widens strips (eager, us at M = 3 / 4: 5120^2 9.96 / 10.10 against 13.02
+  // / 12.75, 4096 -> 8192 9.33 / 9.35 against 10.35 / 9.96; 4096^2 equal;
+  // 3-, 6- and 8-bit layers stay faster on the single-row kernel).
   // Two-level scales run the kernels that read scale codes: the matrix-core
   // kernel, and the multi-row kernel's several-width instances.
   const bool tl = epi.scale_max != nullptr;
   const bool row = !tl && stream::single_row(M, L.K, set);
-  if (M >= 3 && !(row && (int64_t)L.K * L.N <= (int64_t)2 * 4096 * 4096))
+  const int64_t row_max = set == (1u << 4) ? (int64_t)4096 * 4096 : (int64_t)2 * 4096 * 4096;
+  if (M >= 3 && !(row && (int64_t)L.K * L.N <= row_max))
     return launch_qgemv_mx(L, runs, x, M, perm, mats, qweights, scales, zeros, ys, ws, epi, stream);
   // A float32 addend (a LoRA update) runs instances of their own: reading one
   // more kernel argument in the prologue cost 3% on the 7B decode step

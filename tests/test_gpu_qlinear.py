@@ -335,8 +335,9 @@ def test_qgemv_matrix_core_one_width_rows(b, gs, K, M):
     assert_close(y, _ref(inp), f"qgemv one width b={b} K={K} M={M}")
 
 
-@pytest.mark.parametrize("bits,gs,M", [([4] * 40, 128, 5), ([3] * 80 + [2] * 80, 32, 3)],
-                         ids=("4bit-M5", "exl2-low-M3"))
+@pytest.mark.parametrize("bits,gs,M", [([4] * 40, 128, 3), ([4] * 40, 128, 4), ([4] * 40, 128, 5),
+                                       ([3] * 80 + [2] * 80, 32, 3)],
+                         ids=("4bit-M3", "4bit-M4", "4bit-M5", "exl2-low-M3"))
 def test_qgemv_matrix_core_one_launch_wide_strips(bits, gs, M):
     """K = 5120 in one launch leaves LDS for one workgroup per CU: 321 panels
     (5128 columns, the last one ragged) then run as 161 workgroups of 2

@@ -59,16 +59,21 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   // matrix-core kernel; at 3-4 rows the single-row kernel still wins on
   // layers of up to 2 * 4096 * 4096 weights and the matrix-core kernel on
   // larger ones (1.1-1.4x); from 5 rows on the matrix-core kernel wins (up
-  // to 1.4x; within 8% on 8-bit layouts). 4-bit layers at 3-4 rows take the
-  // matrix-core kernel from 4096^2 weights on, since its one-launch mode
-  // widens strips (eager, us at M = 3 / 4: 5120^2 9.96 / 10.10 against 13.02
-  // / 12.75, 4096 -> 8192 9.33 / 9.35 against 10.35 / 9.96; 4096^2 equal;
-  // 3-, 6- and 8-bit layers stay faster on the single-row kernel).
+  // to 1.4x; within 8% on 8-bit layouts). 3-, 4- and 8-bit layers at 3-4
+  // rows take the matrix-core kernel above 4096^2 weights, since its
+  // one-launch mode widens strips (eager, us at M = 3 / 4, matrix-core vs
+  // single-row: 4-bit 5120^2 9.96 / 10.10 vs 13.02 / 12.75, 4096 -> 8192
+  // 9.33 / 9.35 vs 10.35 / 9.96; 3-bit 5120^2 13.37 / 13.53 vs 16.03 / 15.76,
+  // 4096 -> 8192 equal; 8-bit 5120^2 15.79 / 15.70 vs 19.39 / 19.01, 4096 ->
+  // 8192 14.15 / 14.31 vs 16.88 / 16.50; at 4096^2 the single-row kernel is
+  // equal or faster). 2-, 5- and 6-bit layers measured equal or faster on
+  // the single-row kernel up to 2 * 4096^2.
   // Two-level scales run the kernels that read scale codes: the matrix-core
   // kernel, and the multi-row kernel's several-width instances.
   const bool tl = epi.scale_max != nullptr;
   const bool row = !tl && stream::single_row(M, L.K, set);
-  const int64_t row_max = set == (1u << 4) ? (int64_t)4096 * 4096 : (int64_t)2 * 4096 * 4096;
+  const bool mx_early = set == (1u << 3) || set == (1u << 4) || set == (1u << 8);
+  const int64_t row_max = mx_early ? (int64_t)4096 * 4096 : (int64_t)2 * 4096 * 4096;
   if (M >= 3 && !(row && (int64_t)L.K * L.N <= row_max))
     return launch_qgemv_mx(L, runs, x, M, perm, mats, qweights, scales, zeros, ys, ws, epi, stream);
   // A float32 addend (a LoRA update) runs instances of their own: reading one

@@ -349,6 +349,18 @@ def test_qgemv_matrix_core_one_launch_wide_strips(bits, gs, M):
 
 
 @pytest.mark.parametrize("M", (3, 4))
+@pytest.mark.parametrize("b", (3, 8))
+def test_qgemv_matrix_core_3_4_rows_above_4096_squared(b, M):
+    """3-4 rows of a 3- or 8-bit layer above 4096^2 weights (5120 x 5128)
+    run the matrix-core kernel: one launch with wide strips at 3 bits, the
+    gather kernel first at 8 bits."""
+    say(f"qgemv matrix-core b={b} 5120x5128 M={M}")
+    inp = _mixed_inputs([b] * 160, 32, 5128, M, seed=650 + b + M, zeros=True)
+    y = GpuLayer(inp).qgemv(inp.x)
+    assert_close(y, _ref(inp), f"qgemv b={b} 5120x5128 M={M}")
+
+
+@pytest.mark.parametrize("M", (3, 4))
 def test_qgemv_matrix_core_large_uniform(M):
     """3-4 rows of a single-width layer above 2 * 4096^2 weights run the
     matrix-core kernel (4-bit, 128-row groups: scale units of 4 blocks), with

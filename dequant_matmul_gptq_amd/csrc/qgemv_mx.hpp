@@ -1,4 +1,5 @@
-// Decode-sized layer (3 <= M <= 16 as dispatched) on the matrix cores, in
+// Decode-sized layer (3 <= M <= 16, and 2 rows of wide 4-bit layers, as
+// dispatched) on the matrix cores, in
 // factored form.
 //
 // Each 32-row block is one v_mfma_f32_16x16x32_f16 step: A holds the token

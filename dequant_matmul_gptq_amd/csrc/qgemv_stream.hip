@@ -74,7 +74,14 @@ hipError_t launch_qgemv(const qlinear_layout& L, const Runs& runs, const uint16_
   const bool row = !tl && stream::single_row(M, L.K, set);
   const bool mx_early = set == (1u << 3) || set == (1u << 4) || set == (1u << 8);
   const int64_t row_max = mx_early ? (int64_t)4096 * 4096 : (int64_t)2 * 4096 * 4096;
-  if (M >= 3 && !(row && (int64_t)L.K * L.N <= row_max))
+  // 2 rows of a 4-bit layer with K above 4096 and N of 8192 or more also run
+  // the matrix-core kernel (eager, us, matrix-core vs single-row: 5120 ->
+  // 13824 13.17 vs 16.35, 5120 -> 15360 13.84 vs 17.12, 8192^2 13.09 vs
+  // 14.59, 8192 -> 28672 equal; the K = 4096 layers, 11008 -> 4096 and
+  // 5120^2 stay faster on the single-row kernel).
+  const bool mx2 = M == 2 && row && set == (1u << 4) && L.K > 4096 && L.N >= 8192 && !epi.addend &&
+                   qgemv_mx_supported(L);
+  if (mx2 || (M >= 3 && !(row && (int64_t)L.K * L.N <= row_max)))
     return launch_qgemv_mx(L, runs, x, M, perm, mats, qweights, scales, zeros, ys, ws, epi, stream);
   // A float32 addend (a LoRA update) runs instances of their own: reading one
   // more kernel argument in the prologue cost 3% on the 7B decode step

@@ -360,6 +360,27 @@ def test_qgemv_matrix_core_3_4_rows_above_4096_squared(b, M):
     assert_close(y, _ref(inp), f"qgemv b={b} 5120x5128 M={M}")
 
 
+@pytest.mark.parametrize("K,gs", [(5120, 128), (8192, 32), (16384, 128)])
+@pytest.mark.parametrize("mats", (1, 2))
+def test_qgemv_two_rows_matrix_core(K, gs, mats):
+    """2 rows of a 4-bit layer with K above 4096 and N >= 8192 run the
+    matrix-core kernel (one launch at K = 5120 and 8192, the gather kernel
+    first at 16384; 32-row groups: a scale per block), alone and as a grouped
+    launch of two matrices; 8200 columns leave a ragged last strip. The oracle
+    checks every output."""
+    say(f"qgemv matrix-core two rows K={K} gs={gs} mats={mats}")
+    inp = _mixed_inputs([4] * (K // gs), gs, 8200, 2, seed=660 + K % 97 + mats, zeros=True)
+    lay = GpuLayer(inp)
+    ref = _ref(inp)
+    if mats == 1:
+        assert_close(lay.qgemv(inp.x), ref, f"qgemv two rows K={K}")
+        return
+    ys = dq.qgemv_grouped(lay.layout, lay.x(inp.x), [lay.qweight, lay.qweight], [lay.scales, lay.scales],
+                          [lay.zeros, lay.zeros], lay.perm, lay.ws)
+    for y in ys:
+        assert_close(y, ref, f"qgemv grouped two rows K={K}")
+
+
 @pytest.mark.parametrize("M", (3, 4))
 def test_qgemv_matrix_core_large_uniform(M):
     """3-4 rows of a single-width layer above 2 * 4096^2 weights run the

@@ -1,6 +1,5 @@
 // Decode-sized layer (3 <= M <= 16, and 2 rows of wide 4-bit layers, as
-// dispatched) on the matrix cores, in
-// factored form.
+// dispatched) on the matrix cores, in factored form.
 //
 // Each 32-row block is one v_mfma_f32_16x16x32_f16 step: A holds the token
 // rows (M <= 16 of the MFMA's 16), B the block's codes as float16
